@@ -1,0 +1,316 @@
+"""Thin Python binding of libgdn (include/gdn.h): same names as the C entry points.
+
+Only argument marshalling happens here: tensors become device pointers, lists
+become host int32 arrays, and shapes, dtypes and devices are checked against
+the call's dims so that no buffer the C library cannot size-check is ever
+under-allocated.  Every step of the computation runs in the HIP kernels; if the
+built library is missing this module raises instead of falling back to anything.
+PyTorch only provides device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+_lib = None
+
+GDN_OK = 0
+ROUTE_RECURRENT = 0
+ROUTE_CHUNKED = 1
+MAX_K = 3
+
+_ERRORS = {-1: "GDN_E_NULL", -2: "GDN_E_UNSUPPORTED", -3: "GDN_E_RANGE", -4: "GDN_E_ALIAS",
+           -5: "GDN_E_ALIGN", -6: "GDN_E_WORKSPACE", -7: "GDN_E_HIP"}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__("%s returned %s (%d)" % (fn, _ERRORS.get(code, "?"), code))
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("n_qk_heads", ctypes.c_int32), ("n_v_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("k_max", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    n_qk_heads: int
+    n_v_heads: int
+    d_k: int
+    d_v: int
+    k_max: int = 3
+
+    def c(self) -> _Dims:
+        return _Dims(self.n_qk_heads, self.n_v_heads, self.d_k, self.d_v, self.k_max)
+
+
+_VP = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_SIGS = {
+    "gdn_decode_step": [ctypes.POINTER(_Dims), ctypes.c_int32] + [_VP] * 8 + [ctypes.c_int32] + [_VP] * 4,
+    "gdn_verify_window": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
+                         [ctypes.c_int32, _I32P, _VP, _VP, _VP],
+    "gdn_commit_accepted": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _VP, _VP, _VP,
+                            ctypes.c_int32, _I32P, _VP, _VP],
+    "gdn_chunked_workspace_bytes": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, ctypes.c_int32],
+    "gdn_chunked_prefill_with_checkpoints": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P,
+                                             ctypes.c_int32, _I32P] + [_VP] * 8 +
+                                            [ctypes.c_int32, _I32P, _I32P, _VP, _VP, _VP,
+                                             ctypes.c_size_t, _VP],
+    "gdn_plan_transaction": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _I32P],
+    "gdn_run_transaction": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _I32P] + [_VP] * 8 +
+                           [ctypes.c_int32, _I32P, _I32P, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "gdn_status_str": [ctypes.c_int],
+    "gdn_version": [],
+}
+_RES = {"gdn_chunked_workspace_bytes": ctypes.c_size_t, "gdn_status_str": ctypes.c_char_p}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libgdn.so is not built (%s); run "
+                              "`python -m gateddeltanet_linear_attention_amd.build`" % LIB_PATH)
+        l = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = _RES.get(name, ctypes.c_int)
+        _lib = l
+    return _lib
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _i32(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32).ravel())
+
+
+def _ip(arr: np.ndarray):
+    return arr.ctypes.data_as(_I32P)
+
+
+def _dev(t, name: str, dtype, shape):
+    """Pointer of a contiguous device tensor after checking dtype and shape."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return _VP(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _VP(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(fn: str, rc: int):
+    if rc != GDN_OK:
+        raise GdnError(fn, rc)
+
+
+def _token_ptrs(dims: Dims, N: int, q, k, v, a, b, A_log, dt_bias, o):
+    import torch
+    Hq, Hv, d = dims.n_qk_heads, dims.n_v_heads, dims.d_k
+    return [_dev(q, "q", torch.bfloat16, (N, Hq, d)), _dev(k, "k", torch.bfloat16, (N, Hq, d)),
+            _dev(v, "v", torch.bfloat16, (N, Hv, dims.d_v)),
+            _dev(a, "a", torch.float32, (N, Hv)), _dev(b, "b", torch.float32, (N, Hv)),
+            _dev(A_log, "A_log", torch.float32, (Hv,)), _dev(dt_bias, "dt_bias", torch.float32, (Hv,))], \
+        _dev(o, "o", torch.bfloat16, (N, Hv, dims.d_v))
+
+
+def _pool(dims: Dims, state_pool):
+    import torch
+    n_slots = int(state_pool.shape[0]) if hasattr(state_pool, "shape") else 0
+    return _dev(state_pool, "state_pool", torch.float32,
+                (n_slots, dims.n_v_heads, dims.d_v, dims.d_k)), n_slots
+
+
+def _ckpt(dims: Dims, ckpt, n_rows: int):
+    import torch
+    return _dev(ckpt, "ckpt", torch.float32,
+                (n_rows, dims.k_max + 1, dims.n_v_heads, dims.d_v, dims.d_k))
+
+
+# ------------------------------------------------------------------ entry points
+
+def gdn_version() -> int:
+    return lib().gdn_version()
+
+
+def gdn_status_str(code: int) -> str:
+    return lib().gdn_status_str(code).decode()
+
+
+def gdn_decode_step(dims: Dims, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot, dst_slot, o,
+                    stream=None) -> None:
+    """One token per row; new state of row r to slot dst_slot[r]."""
+    src, dst = _i32(src_slot), _i32(dst_slot)
+    n_rows = src.size
+    if dst.size != n_rows:
+        raise ValueError("src_slot and dst_slot lengths differ")
+    toks, op = _token_ptrs(dims, n_rows, q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    rc = lib().gdn_decode_step(ctypes.byref(dims.c()), n_rows, *toks, pp, n_slots, _ip(src), _ip(dst),
+                               op, _stream(stream))
+    _check("gdn_decode_step", rc)
+
+
+def gdn_verify_window(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot,
+                      ckpt, o, stream=None) -> None:
+    """Each row's window from its committed slot; writes o and checkpoint slots 0..T_r-1."""
+    T, src = _i32(row_tokens), _i32(src_slot)
+    n_rows = T.size
+    if src.size != n_rows:
+        raise ValueError("row_tokens and src_slot lengths differ")
+    N = int(T.sum())
+    toks, op = _token_ptrs(dims, N, q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    cp = _ckpt(dims, ckpt, n_rows)
+    rc = lib().gdn_verify_window(ctypes.byref(dims.c()), n_rows, _ip(T), *toks, pp, n_slots, _ip(src),
+                                 cp, op, _stream(stream))
+    _check("gdn_verify_window", rc)
+
+
+def gdn_commit_accepted(dims: Dims, row_tokens, ckpt, accepted, state_pool, dst_slot, status,
+                        stream=None) -> None:
+    """Copy checkpoint slot accepted[r] (device int32) of each row to slot dst_slot[r]."""
+    import torch
+    T, dst = _i32(row_tokens), _i32(dst_slot)
+    n_rows = T.size
+    if dst.size != n_rows:
+        raise ValueError("row_tokens and dst_slot lengths differ")
+    cp = _ckpt(dims, ckpt, n_rows)
+    ap = _dev(accepted, "accepted", torch.int32, (n_rows,))
+    sp = _dev(status, "status", torch.int32, ((n_rows + 31) // 32,))
+    pp, n_slots = _pool(dims, state_pool)
+    rc = lib().gdn_commit_accepted(ctypes.byref(dims.c()), n_rows, _ip(T), cp, ap, pp, n_slots,
+                                   _ip(dst), sp, _stream(stream))
+    _check("gdn_commit_accepted", rc)
+
+
+def gdn_chunked_workspace_bytes(dims: Dims, row_tokens, chunk: int = 64) -> int:
+    T = _i32(row_tokens)
+    return int(lib().gdn_chunked_workspace_bytes(ctypes.byref(dims.c()), T.size, _ip(T), chunk))
+
+
+def gdn_chunked_prefill_with_checkpoints(dims: Dims, row_tokens, n_tail, q, k, v, a, b, A_log,
+                                         dt_bias, state_pool, src_slot, dst_slot, ckpt, o,
+                                         workspace, chunk: int = 64, stream=None) -> None:
+    """Long rows in the chunked form; final state to dst_slot (-1: none), tail checkpoints."""
+    import torch
+    T, nt, src, dst = _i32(row_tokens), _i32(n_tail), _i32(src_slot), _i32(dst_slot)
+    n_rows = T.size
+    if not (nt.size == src.size == dst.size == n_rows):
+        raise ValueError("per-row arrays differ in length")
+    N = int(T.sum())
+    toks, op = _token_ptrs(dims, N, q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    cp = _ckpt(dims, ckpt, n_rows)
+    need = gdn_chunked_workspace_bytes(dims, T, chunk)
+    if workspace is None:
+        wp, wb = _VP(0), 0
+    else:
+        wp = _dev(workspace, "workspace", torch.uint8, (workspace.numel(),))
+        wb = workspace.numel()
+    if wb < need:
+        raise GdnError("gdn_chunked_prefill_with_checkpoints", -6)
+    rc = lib().gdn_chunked_prefill_with_checkpoints(
+        ctypes.byref(dims.c()), n_rows, _ip(T), chunk, _ip(nt), *toks, pp, n_slots, _ip(src), _ip(dst),
+        cp, op, wp, wb, _stream(stream))
+    _check("gdn_chunked_prefill_with_checkpoints", rc)
+
+
+def gdn_plan_transaction(dims: Dims, row_tokens) -> np.ndarray:
+    """Route per row: ROUTE_RECURRENT (0) or ROUTE_CHUNKED (1)."""
+    T = _i32(row_tokens)
+    route = np.zeros(T.size, np.int32)
+    rc = lib().gdn_plan_transaction(ctypes.byref(dims.c()), T.size, _ip(T), _ip(route))
+    _check("gdn_plan_transaction", rc)
+    return route
+
+
+def gdn_run_transaction(dims: Dims, row_tokens, n_ckpt, q, k, v, a, b, A_log, dt_bias, state_pool,
+                        src_slot, dst_slot, ckpt, o, workspace=None, stream=None) -> None:
+    """A mixed ragged transaction, planned per row and launched on both routes."""
+    import torch
+    T, nc, src, dst = _i32(row_tokens), _i32(n_ckpt), _i32(src_slot), _i32(dst_slot)
+    n_rows = T.size
+    if not (nc.size == src.size == dst.size == n_rows):
+        raise ValueError("per-row arrays differ in length")
+    N = int(T.sum())
+    toks, op = _token_ptrs(dims, N, q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    cp = _ckpt(dims, ckpt, n_rows)
+    if workspace is None:
+        wp, wb = _VP(0), 0
+    else:
+        wp = _dev(workspace, "workspace", torch.uint8, (workspace.numel(),))
+        wb = workspace.numel()
+    rc = lib().gdn_run_transaction(ctypes.byref(dims.c()), n_rows, _ip(T), _ip(nc), *toks, pp, n_slots,
+                                   _ip(src), _ip(dst), cp, op, wp, wb, _stream(stream))
+    _check("gdn_run_transaction", rc)
+
+
+# ------------------------------------------------------------------ prepared calls
+
+class PreparedCall:
+    """One entry-point call with its arguments checked and marshalled once; calling it
+    re-issues the same C call (same buffers, same stream).  For tight loops where the
+    per-call Python checks would dominate the host time."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self.name = name
+        self._fn = getattr(lib(), name)
+        self._args = args
+        self._keep = keep  # host arrays the pointers refer to
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != GDN_OK:
+            raise GdnError(self.name, rc)
+
+
+def prepare_verify_window(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool,
+                          src_slot, ckpt, o, stream=None) -> PreparedCall:
+    T, src = _i32(row_tokens), _i32(src_slot)
+    n_rows = T.size
+    N = int(T.sum())
+    toks, op = _token_ptrs(dims, N, q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    cp = _ckpt(dims, ckpt, n_rows)
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, _ip(T), *toks, pp, n_slots, _ip(src), cp, op, _stream(stream))
+    return PreparedCall("gdn_verify_window", args, (cd, T, src))
+
+
+def prepare_commit_accepted(dims: Dims, row_tokens, ckpt, accepted, state_pool, dst_slot, status,
+                            stream=None) -> PreparedCall:
+    import torch
+    T, dst = _i32(row_tokens), _i32(dst_slot)
+    n_rows = T.size
+    cp = _ckpt(dims, ckpt, n_rows)
+    ap = _dev(accepted, "accepted", torch.int32, (n_rows,))
+    sp = _dev(status, "status", torch.int32, ((n_rows + 31) // 32,))
+    pp, n_slots = _pool(dims, state_pool)
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, _ip(T), cp, ap, pp, n_slots, _ip(dst), sp, _stream(stream))
+    return PreparedCall("gdn_commit_accepted", args, (cd, T, dst))

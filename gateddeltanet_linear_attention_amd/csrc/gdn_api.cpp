@@ -1,0 +1,293 @@
+// gdn_api.cpp -- the libgdn C ABI (include/gdn.h): host-side validation, the
+// per-row planner and kernel launches.  Everything is checked before the first
+// launch, so a call that returns an error has written nothing (fail closed).
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+using gdn::kRowsPerLaunch;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void *p, size_t pb, const void *q, size_t qb) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return pb && qb && a < b + qb && b < a + pb;
+}
+
+int check_dims(const gdn_dims *d) {
+  if (!d) return GDN_E_NULL;
+  if (d->d_k != d->d_v || (d->d_k != 16 && d->d_k != 128)) return GDN_E_UNSUPPORTED;
+  if (d->n_qk_heads <= 0 || d->n_v_heads <= 0 || d->n_v_heads % d->n_qk_heads)
+    return GDN_E_UNSUPPORTED;
+  if (d->n_v_heads > (1 << 16)) return GDN_E_UNSUPPORTED;
+  if (d->k_max < 0 || d->k_max > GDN_MAX_K) return GDN_E_UNSUPPORTED;
+  return GDN_OK;
+}
+
+struct Sizes {
+  size_t unit_floats;  // d_v * d_k
+  size_t row_floats;   // H_v * unit
+  size_t ck_row_floats;  // (k_max + 1) * row
+};
+
+Sizes sizes_of(const gdn_dims *d) {
+  Sizes s;
+  s.unit_floats = size_t(d->d_v) * size_t(d->d_k);
+  s.row_floats = size_t(d->n_v_heads) * s.unit_floats;
+  s.ck_row_floats = size_t(d->k_max + 1) * s.row_floats;
+  return s;
+}
+
+// Token inputs shared by every compute call.
+int check_tokens(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                 const float *b, const float *A_log, const float *dt_bias, const uint16_t *o) {
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !o) return GDN_E_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return GDN_E_ALIGN;
+  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(A_log, 4) || !aligned(dt_bias, 4))
+    return GDN_E_ALIGN;
+  return GDN_OK;
+}
+
+// Source slots may be -1 (zero state); destination slots must be distinct and
+// must not be read by another row of the same launch set.
+int check_slots(int32_t n_rows, int32_t n_slots, const int32_t *src, const int32_t *dst) {
+  for (int32_t r = 0; r < n_rows; ++r) {
+    if (src && (src[r] < -1 || src[r] >= n_slots)) return GDN_E_RANGE;
+    if (dst && (dst[r] < -1 || dst[r] >= n_slots)) return GDN_E_RANGE;
+  }
+  if (!dst) return GDN_OK;
+  std::vector<int32_t> d;
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (dst[r] >= 0) d.push_back(dst[r]);
+  std::vector<int32_t> sorted = d;
+  std::sort(sorted.begin(), sorted.end());
+  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return GDN_E_ALIAS;
+  if (src)
+    for (int32_t r = 0; r < n_rows; ++r) {
+      if (dst[r] < 0) continue;
+      for (int32_t r2 = 0; r2 < n_rows; ++r2)
+        if (r2 != r && src[r2] == dst[r]) return GDN_E_ALIAS;
+    }
+  return GDN_OK;
+}
+
+void fill_common(gdn::RecurrentArgs &ra, const gdn_dims *d, const uint16_t *q,
+                 const uint16_t *k, const uint16_t *v, const float *a, const float *b,
+                 const float *A_log, const float *dt_bias, const float *state_in,
+                 float *state_out, float *ckpt, uint16_t *o) {
+  memset(&ra, 0, sizeof(ra));
+  ra.q = q; ra.k = k; ra.v = v; ra.a = a; ra.b = b; ra.A_log = A_log; ra.dt_bias = dt_bias;
+  ra.state_in = state_in; ra.state_out = state_out; ra.ckpt = ckpt; ra.o = o;
+  ra.n_qk = d->n_qk_heads; ra.n_v = d->n_v_heads;
+  ra.group = d->n_v_heads / d->n_qk_heads;
+  ra.ck_slots = d->k_max + 1;
+}
+
+// Runs rows `rows` (indices into the call's rows) through the recurrent kernel,
+// kRowsPerLaunch at a time; row r keeps its own token offset and checkpoint row.
+int launch_recurrent_rows(const gdn_dims *d, const gdn::RecurrentArgs &proto,
+                          const std::vector<int32_t> &rows, const std::vector<int64_t> &cu,
+                          const int32_t *ntok, const int32_t *src, const int32_t *dst,
+                          const int32_t *n_ck, hipStream_t stream) {
+  for (size_t base = 0; base < rows.size(); base += kRowsPerLaunch) {
+    gdn::RecurrentArgs ra = proto;
+    const size_t n = std::min<size_t>(kRowsPerLaunch, rows.size() - base);
+    ra.n_rows = int32_t(n);
+    for (size_t j = 0; j < n; ++j) {
+      const int32_t r = rows[base + j];
+      ra.tok0[j] = int32_t(cu[r]);
+      ra.ntok[j] = ntok[r];
+      ra.src[j] = src ? src[r] : -1;
+      ra.dst[j] = dst ? dst[r] : -1;
+      ra.ck_first[j] = n_ck ? ntok[r] - n_ck[r] : ntok[r];
+      ra.ck_row[j] = r;
+    }
+    if (gdn::launch_recurrent(ra, d->d_k, stream) != hipSuccess) return GDN_E_HIP;
+  }
+  return GDN_OK;
+}
+
+std::vector<int64_t> prefix(int32_t n_rows, const int32_t *ntok) {
+  std::vector<int64_t> cu(size_t(n_rows) + 1, 0);
+  for (int32_t r = 0; r < n_rows; ++r) cu[r + 1] = cu[r] + ntok[r];
+  return cu;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_version(void) { return GDN_VERSION; }
+
+const char *gdn_status_str(int code) {
+  switch (code) {
+    case GDN_OK: return "ok";
+    case GDN_E_NULL: return "null pointer";
+    case GDN_E_UNSUPPORTED: return "unsupported shape";
+    case GDN_E_RANGE: return "token count, slot or checkpoint count out of range";
+    case GDN_E_ALIAS: return "aliasing slots or overlapping buffers";
+    case GDN_E_ALIGN: return "misaligned device pointer";
+    case GDN_E_WORKSPACE: return "workspace missing or too small";
+    case GDN_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int gdn_decode_step(const gdn_dims *dims, int32_t n_rows, const uint16_t *q, const uint16_t *k,
+                    const uint16_t *v, const float *a, const float *b, const float *A_log,
+                    const float *dt_bias, float *state_pool, int32_t n_slots,
+                    const int32_t *src_slot, const int32_t *dst_slot, uint16_t *o,
+                    void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if ((rc = check_tokens(q, k, v, a, b, A_log, dt_bias, o))) return rc;
+  if (!state_pool || !src_slot || !dst_slot) return GDN_E_NULL;
+  if (!aligned(state_pool, 16)) return GDN_E_ALIGN;
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (dst_slot[r] < 0) return GDN_E_RANGE;
+  if ((rc = check_slots(n_rows, n_slots, src_slot, dst_slot))) return rc;
+  const Sizes s = sizes_of(dims);
+  if (overlap(o, size_t(n_rows) * s.row_floats / dims->d_k * 2, state_pool,
+              size_t(n_slots) * s.row_floats * 4))
+    return GDN_E_ALIAS;
+
+  std::vector<int32_t> ones(static_cast<size_t>(n_rows), 1), rows(static_cast<size_t>(n_rows));
+  for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
+  const std::vector<int64_t> cu = prefix(n_rows, ones.data());
+  gdn::RecurrentArgs proto;
+  fill_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, state_pool, nullptr, o);
+  return launch_recurrent_rows(dims, proto, rows, cu, ones.data(), src_slot, dst_slot, nullptr,
+                               static_cast<hipStream_t>(stream));
+}
+
+int gdn_verify_window(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                      const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                      const float *b, const float *A_log, const float *dt_bias,
+                      const float *state_pool, int32_t n_slots, const int32_t *src_slot,
+                      float *ckpt, uint16_t *o, void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if (!row_tokens) return GDN_E_NULL;
+  if ((rc = check_tokens(q, k, v, a, b, A_log, dt_bias, o))) return rc;
+  if (!state_pool || !src_slot || !ckpt) return GDN_E_NULL;
+  if (!aligned(state_pool, 16) || !aligned(ckpt, 16)) return GDN_E_ALIGN;
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+  if ((rc = check_slots(n_rows, n_slots, src_slot, nullptr))) return rc;
+  const Sizes s = sizes_of(dims);
+  const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
+  const size_t ck_b = size_t(n_rows) * s.ck_row_floats * 4;
+  const size_t o_b = size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2;
+  if (overlap(ckpt, ck_b, state_pool, pool_b) || overlap(o, o_b, ckpt, ck_b) ||
+      overlap(o, o_b, state_pool, pool_b))
+    return GDN_E_ALIAS;
+
+  std::vector<int32_t> rows(static_cast<size_t>(n_rows));
+  for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
+  gdn::RecurrentArgs proto;
+  fill_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, nullptr, ckpt, o);
+  return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, src_slot, nullptr, row_tokens,
+                               static_cast<hipStream_t>(stream));
+}
+
+int gdn_commit_accepted(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                        const float *ckpt, const int32_t *accepted, float *state_pool,
+                        int32_t n_slots, const int32_t *dst_slot, uint32_t *status,
+                        void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if (!row_tokens || !ckpt || !accepted || !state_pool || !dst_slot || !status) return GDN_E_NULL;
+  if (!aligned(ckpt, 16) || !aligned(state_pool, 16) || !aligned(accepted, 4) ||
+      !aligned(status, 4))
+    return GDN_E_ALIGN;
+  for (int32_t r = 0; r < n_rows; ++r) {
+    if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+    if (dst_slot[r] < 0) return GDN_E_RANGE;
+  }
+  if ((rc = check_slots(n_rows, n_slots, nullptr, dst_slot))) return rc;
+  const Sizes s = sizes_of(dims);
+  if (overlap(ckpt, size_t(n_rows) * s.ck_row_floats * 4, state_pool,
+              size_t(n_slots) * s.row_floats * 4))
+    return GDN_E_ALIAS;
+
+  for (int32_t r0 = 0; r0 < n_rows; r0 += kRowsPerLaunch) {
+    gdn::CommitArgs ca;
+    memset(&ca, 0, sizeof(ca));
+    const int32_t n = std::min<int32_t>(kRowsPerLaunch, n_rows - r0);
+    ca.ckpt = ckpt + size_t(r0) * s.ck_row_floats;
+    ca.pool = state_pool;
+    ca.accepted = accepted + r0;
+    ca.status = status;
+    ca.row_floats = int64_t(s.row_floats);
+    ca.ck_slots = dims->k_max + 1;
+    ca.n_rows = n;
+    ca.row_base = r0;
+    for (int32_t j = 0; j < n; ++j) {
+      ca.ntok[j] = row_tokens[r0 + j];
+      ca.dst[j] = dst_slot[r0 + j];
+    }
+    if (gdn::launch_commit(ca, static_cast<hipStream_t>(stream)) != hipSuccess) return GDN_E_HIP;
+  }
+  return GDN_OK;
+}
+
+int gdn_plan_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                         int32_t *route) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if (!row_tokens || !route) return GDN_E_NULL;
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (row_tokens[r] < 1) return GDN_E_RANGE;
+  for (int32_t r = 0; r < n_rows; ++r)
+    route[r] = row_tokens[r] <= dims->k_max + 1 ? GDN_ROUTE_RECURRENT : GDN_ROUTE_CHUNKED;
+  return GDN_OK;
+}
+
+size_t gdn_chunked_workspace_bytes(const gdn_dims *dims, int32_t n_rows,
+                                   const int32_t *row_tokens, int32_t chunk) {
+  (void)dims; (void)n_rows; (void)row_tokens; (void)chunk;
+  return 0;
+}
+
+int gdn_chunked_prefill_with_checkpoints(
+    const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens, int32_t chunk,
+    const int32_t *n_tail, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+    const float *a, const float *b, const float *A_log, const float *dt_bias,
+    float *state_pool, int32_t n_slots, const int32_t *src_slot, const int32_t *dst_slot,
+    float *ckpt, uint16_t *o, void *workspace, size_t ws_bytes, void *stream) {
+  (void)dims; (void)n_rows; (void)row_tokens; (void)chunk; (void)n_tail; (void)q; (void)k;
+  (void)v; (void)a; (void)b; (void)A_log; (void)dt_bias; (void)state_pool; (void)n_slots;
+  (void)src_slot; (void)dst_slot; (void)ckpt; (void)o; (void)workspace; (void)ws_bytes;
+  (void)stream;
+  return GDN_E_UNSUPPORTED;
+}
+
+int gdn_run_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                        const int32_t *n_ckpt, const uint16_t *q, const uint16_t *k,
+                        const uint16_t *v, const float *a, const float *b, const float *A_log,
+                        const float *dt_bias, float *state_pool, int32_t n_slots,
+                        const int32_t *src_slot, const int32_t *dst_slot, float *ckpt,
+                        uint16_t *o, void *workspace, size_t ws_bytes, void *stream) {
+  (void)dims; (void)n_rows; (void)row_tokens; (void)n_ckpt; (void)q; (void)k; (void)v; (void)a;
+  (void)b; (void)A_log; (void)dt_bias; (void)state_pool; (void)n_slots; (void)src_slot;
+  (void)dst_slot; (void)ckpt; (void)o; (void)workspace; (void)ws_bytes; (void)stream;
+  return GDN_E_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// gdn_internal.h -- launch interface between the C-ABI layer (gdn_api.cpp) and
+// the HIP kernels.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Rows per kernel launch: per-row metadata travels in the kernel argument
+// block (validated on the host, read by the kernel from scalar registers), so a
+// call with more rows is split into several launches on the same stream.
+constexpr int kRowsPerLaunch = 64;
+
+// Recurrent (token-by-token) kernel shared by decode, verify and the short rows
+// of a transaction.  Row r of the launch runs ntok[r] tokens starting at packed
+// token tok0[r] from pool slot src[r] (-1: zero state); the state after token t
+// is stored to slot t - ck_first[r] of checkpoint row ck_row[r] when
+// t >= ck_first[r]; the final
+// state goes to pool slot dst[r] when dst[r] >= 0.
+struct RecurrentArgs {
+  const uint16_t *q, *k, *v;        // bf16 bits
+  const float *a, *b, *A_log, *dt_bias;
+  const float *state_in;            // pool (read)
+  float *state_out;                 // pool (final-state write); may alias state_in
+  float *ckpt;                      // checkpoint buffer of the whole call
+  uint16_t *o;                      // bf16 bits
+  int32_t n_qk, n_v, group;         // heads; group = n_v / n_qk
+  int32_t ck_slots;                 // k_max + 1
+  int32_t n_rows;                   // rows in this launch
+  int32_t tok0[kRowsPerLaunch];
+  int32_t ntok[kRowsPerLaunch];
+  int32_t src[kRowsPerLaunch];
+  int32_t dst[kRowsPerLaunch];
+  int32_t ck_first[kRowsPerLaunch];
+  int32_t ck_row[kRowsPerLaunch];   // checkpoint row (index of the row in the call)
+};
+
+// Commit: row r copies checkpoint slot accepted[r] of its ckpt row to pool slot
+// dst[r] if 0 <= accepted[r] < ntok[r], else sets bit row_base+r of status.
+struct CommitArgs {
+  const float *ckpt;                // checkpoint rows of this launch
+  float *pool;
+  const int32_t *accepted;          // device, this launch's rows
+  uint32_t *status;                 // device, whole call
+  int64_t row_floats;               // H_v * d_v * d_k
+  int32_t ck_slots;
+  int32_t n_rows;
+  int32_t row_base;                 // index of this launch's first row in the call
+  int32_t ntok[kRowsPerLaunch];
+  int32_t dst[kRowsPerLaunch];
+};
+
+hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream);
+hipError_t launch_commit(const CommitArgs &args, hipStream_t stream);
+
+}  // namespace gdn

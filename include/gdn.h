@@ -1,0 +1,190 @@
+/*
+ * gdn.h -- C ABI of libgdn: the gated-delta-rule (GatedDeltaNet) recurrent-state
+ * hot path of K-draft multi-token-prediction speculative decoding, on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation.  Per (row r, value head h), with the q/k head hq = h / (H_v/H_qk)
+ * (contiguous groups of value heads share one q/k head), and S a d_v x d_k fp32
+ * matrix (row-major, k contiguous):
+ *     alpha_t = exp(-exp(A_log[h]) * softplus(a_t + dt_bias[h])),  beta_t = sigmoid(b_t)
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t
+ * This is the gated delta rule (Yang, Kautz & Hatamizadeh, "Gated Delta Networks:
+ * Improving Mamba2 with Delta Rule", ICLR 2025).  Gates are evaluated in fp32 and
+ * the state update is rounded identically in decode and in verification ("Native
+ * three-step MTP", section "What changed").  Verification publishes the state
+ * after every window token so that a rejected draft is undone by restoring the
+ * checkpoint at the accepted length; a long prefill in the same ragged batch goes
+ * through a chunked form that still publishes the checkpoints its row asks for
+ * (onnxruntime-genai pull request "Run chained MTP drafting in the batch Engine",
+ * sections "Correctness fix" and "Rollback fix and corrected quality disposition").
+ *
+ * Conventions shared by every call.
+ *  - Supported shapes: d_k == d_v in {16, 128}; H_v a multiple of H_qk; 0 <= k_max <= 3.
+ *    Anything else returns GDN_E_UNSUPPORTED.
+ *  - Rows are packed in order; row r owns tokens [cu_r, cu_r + L_r) of the packed
+ *    token dimension N, cu_r = L_0 + ... + L_{r-1}; a row's tokens are in time order.
+ *  - Device arrays (caller-allocated, caller-owned; the library allocates nothing):
+ *      q, k   bf16 bits [N][H_qk][d_k]        v    bf16 bits [N][H_v][d_v]
+ *      a, b   fp32 [N][H_v] (gate logits)     A_log, dt_bias fp32 [H_v]
+ *      o      bf16 bits [N][H_v][d_v]         (round to nearest even)
+ *      state_pool fp32 [n_slots][H_v][d_v][d_k]   committed states, one slot per row
+ *      ckpt   fp32 [n_rows][k_max+1][H_v][d_v][d_k]  checkpoint slot j of row r
+ *  - Host arrays (validated before anything is launched): per-row token counts,
+ *    slot indices and checkpoint counts.  A source slot of -1 means the zero state.
+ *  - Alignment: q, k, v, o, state_pool, ckpt and the workspace 16 B; a, b, A_log,
+ *    dt_bias 4 B.  Otherwise GDN_E_ALIGN.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronises the host.  Ordering across streams (publish a
+ *    prefill before a dependent verify, "Native three-step MTP", section "What
+ *    changed") is the caller's, through events.
+ *  - Fail closed: on any error code nothing is launched and nothing is written.
+ *  - The library holds no mutable global state; calls are thread-safe.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_VERSION 1
+#define GDN_MAX_K 3 /* largest k_max: at most 4 checkpoint slots per row */
+
+typedef struct gdn_dims {
+  int32_t n_qk_heads; /* H_qk */
+  int32_t n_v_heads;  /* H_v, a multiple of H_qk */
+  int32_t d_k;        /* key / query width */
+  int32_t d_v;        /* value width (== d_k) */
+  int32_t k_max;      /* largest draft count per row; checkpoint slots per row = k_max + 1 */
+} gdn_dims;
+
+enum {
+  GDN_OK = 0,
+  GDN_E_NULL = -1,        /* a required pointer is NULL */
+  GDN_E_UNSUPPORTED = -2, /* shape outside the supported set */
+  GDN_E_RANGE = -3,       /* a token count, slot index or checkpoint count is out of range */
+  GDN_E_ALIAS = -4,       /* two rows write one slot, a row writes a slot another reads, or buffers overlap */
+  GDN_E_ALIGN = -5,       /* a device pointer is misaligned */
+  GDN_E_WORKSPACE = -6,   /* workspace missing or too small */
+  GDN_E_HIP = -7          /* the HIP runtime refused a launch */
+};
+
+/* Routes chosen by gdn_plan_transaction. */
+enum { GDN_ROUTE_RECURRENT = 0, GDN_ROUTE_CHUNKED = 1 };
+
+/*
+ * gdn_decode_step -- one token per row (token r belongs to row r, N = n_rows).
+ * Reads the state of slot src_slot[r] (-1: zero state), applies the rule once,
+ * writes o[r] and the new state to slot dst_slot[r] (== src_slot[r] updates in
+ * place).  Decode is the single-token case of the verify window below: both run
+ * one device routine, so verify checkpoint j is bit-identical to j+1 decode calls.
+ * Errors: GDN_E_RANGE for a slot outside [0, n_slots) (src may be -1);
+ * GDN_E_ALIAS if two rows share a dst slot or a dst slot is another row's src.
+ */
+int gdn_decode_step(const gdn_dims *dims, int32_t n_rows, const uint16_t *q,
+                    const uint16_t *k, const uint16_t *v, const float *a,
+                    const float *b, const float *A_log, const float *dt_bias,
+                    float *state_pool, int32_t n_slots, const int32_t *src_slot,
+                    const int32_t *dst_slot, uint16_t *o, void *stream);
+
+/*
+ * gdn_verify_window -- draft verification.  Row r runs T_r = row_tokens[r] tokens
+ * (1 <= T_r <= k_max + 1: the previous bonus token and K_r = T_r - 1 drafts) from
+ * the committed state in slot src_slot[r] (-1: zero state).  Writes o for all N
+ * tokens and checkpoint slot j of row r = the state after j + 1 window tokens,
+ * for j < T_r; slots j >= T_r are not touched.  The state pool is only read:
+ * nothing is published until gdn_commit_accepted (transactional publication, the
+ * pull request's "Summary").  ckpt must not overlap state_pool or o (GDN_E_ALIAS).
+ */
+int gdn_verify_window(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                      const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const float *a, const float *b, const float *A_log,
+                      const float *dt_bias, const float *state_pool, int32_t n_slots,
+                      const int32_t *src_slot, float *ckpt, uint16_t *o, void *stream);
+
+/*
+ * gdn_commit_accepted -- rollback to the accepted length.  accepted (device
+ * int32 [n_rows]) holds a_r, the number of accepted drafts of row r; the committed
+ * state becomes checkpoint slot a_r (the state after the bonus token and a_r
+ * drafts), copied bit for bit to slot dst_slot[r].  row_tokens[r] is the row's
+ * window length T_r.  A row whose a_r is outside [0, T_r - 1] is left untouched
+ * and bit (r % 32) of status[r / 32] is set (status: device uint32
+ * [(n_rows + 31) / 32]; bits are OR-ed in, the caller clears them).  Accepted
+ * lengths stay on the device: no host readback.
+ */
+int gdn_commit_accepted(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                        const float *ckpt, const int32_t *accepted, float *state_pool,
+                        int32_t n_slots, const int32_t *dst_slot, uint32_t *status,
+                        void *stream);
+
+/*
+ * gdn_chunked_workspace_bytes -- device workspace that gdn_chunked_prefill_with_
+ * checkpoints and gdn_run_transaction need for these rows (0 on a bad argument).
+ */
+size_t gdn_chunked_workspace_bytes(const gdn_dims *dims, int32_t n_rows,
+                                   const int32_t *row_tokens, int32_t chunk);
+
+/*
+ * gdn_chunked_prefill_with_checkpoints -- long rows in the chunkwise (UT / WY)
+ * form of the rule, chunk = 64 tokens, chunks starting at each row's first token
+ * (the last chunk of a row may be partial; chunks never span rows).  Row r runs
+ * L_r = row_tokens[r] >= 1 tokens from slot src_slot[r] (-1: zero state), writes
+ * o for all its tokens, the final state to slot dst_slot[r] (-1: not written),
+ * and checkpoint slot j = the state after L_r - n_tail[r] + j + 1 tokens for
+ * j < n_tail[r] <= min(L_r, k_max + 1), the same slot meaning as a verify window,
+ * so gdn_commit_accepted works on either path.  Matches the sequential rule to
+ * fp32 rounding, not bit for bit.
+ * Errors: GDN_E_WORKSPACE if ws_bytes < gdn_chunked_workspace_bytes(...);
+ * GDN_E_UNSUPPORTED for chunk != 64; slot checks as gdn_decode_step.
+ */
+int gdn_chunked_prefill_with_checkpoints(
+    const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens, int32_t chunk,
+    const int32_t *n_tail, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+    const float *a, const float *b, const float *A_log, const float *dt_bias,
+    float *state_pool, int32_t n_slots, const int32_t *src_slot,
+    const int32_t *dst_slot, float *ckpt, uint16_t *o, void *workspace,
+    size_t ws_bytes, void *stream);
+
+/*
+ * gdn_plan_transaction -- the per-row execution plan of a packed ragged batch
+ * (pure host function, deterministic).  A row of at most k_max + 1 tokens goes to
+ * the recurrent kernel shared with decode (route GDN_ROUTE_RECURRENT), so its
+ * checkpoints are bit-consistent with decode; a longer row goes to the chunked
+ * kernels (GDN_ROUTE_CHUNKED).  Every row gets the checkpoints it asks for on
+ * either route: one plan is never forced on the whole batch, the fault described
+ * in the pull request's "Correctness fix".  route: host int32 [n_rows].
+ */
+int gdn_plan_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                         int32_t *route);
+
+/*
+ * gdn_run_transaction -- one mixed ragged transaction: plans the rows
+ * (gdn_plan_transaction) and launches both routes on `stream`.  Row r runs
+ * row_tokens[r] tokens from src_slot[r] (-1: zero state), writes o for its tokens,
+ * checkpoint slots j < n_ckpt[r] <= min(L_r, k_max + 1) (state after
+ * L_r - n_ckpt[r] + j + 1 tokens) and, if dst_slot[r] >= 0, its final state.
+ * A verify row passes n_ckpt = T_r and dst = -1 (commit later); a prefill row
+ * passes n_ckpt = 0 and its dst slot.  workspace as gdn_chunked_workspace_bytes
+ * (may be NULL/0 when no row is longer than k_max + 1).
+ */
+int gdn_run_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                        const int32_t *n_ckpt, const uint16_t *q, const uint16_t *k,
+                        const uint16_t *v, const float *a, const float *b,
+                        const float *A_log, const float *dt_bias, float *state_pool,
+                        int32_t n_slots, const int32_t *src_slot, const int32_t *dst_slot,
+                        float *ckpt, uint16_t *o, void *workspace, size_t ws_bytes,
+                        void *stream);
+
+/* Human-readable name of a return code. */
+const char *gdn_status_str(int code);
+
+/* GDN_VERSION of the built library. */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H_ */

@@ -90,7 +90,19 @@ def gates(a, b, A_log: float, dt_bias: float) -> tuple[np.ndarray, np.ndarray]:
     return al, be
 
 
-def _run(fn_name, row_tokens, q, k, v, a, b, A_log, dt_bias, S0, n_tail, n_slot, chunk, n_threads):
+def _out(buf, shape):
+    """A caller-provided output array of the right shape, or a fresh one."""
+    if buf is None:
+        fresh = np.empty(shape)
+        fresh.fill(0.0)  # first touch on one thread: page faults under OpenMP are slow
+        return fresh
+    if buf.shape != tuple(shape) or buf.dtype != np.float64 or not buf.flags.c_contiguous:
+        raise ValueError("output buffer must be contiguous float64 of shape %s" % (tuple(shape),))
+    return buf
+
+
+def _run(fn_name, row_tokens, q, k, v, a, b, A_log, dt_bias, S0, n_tail, n_slot, chunk, n_threads,
+         nan_fill=True, out=None):
     q, k, v, a, b = map(_f64, (q, k, v, a, b))
     A_log, dt_bias = _f64(A_log).ravel(), _f64(dt_bias).ravel()
     N, Hqk, dk = q.shape
@@ -104,9 +116,14 @@ def _run(fn_name, row_tokens, q, k, v, a, b, A_log, dt_bias, S0, n_tail, n_slot,
     nt = np.zeros(B, np.int32) if n_tail is None else np.ascontiguousarray(np.asarray(n_tail, np.int32).ravel())
     if n_slot is None:
         n_slot = int(nt.max()) if B else 0
-    S_final = np.empty((B, Hv, dv, dk))
-    ckpt = np.full((B, max(n_slot, 0), Hv, dv, dk), np.nan) if n_slot > 0 else None
-    o = np.empty((N, Hv, dv))
+    out = out or {}
+    S_final = _out(out.get("S_final"), (B, Hv, dv, dk))
+    ckpt = None
+    if n_slot > 0:
+        ckpt = _out(out.get("ckpt"), (B, n_slot, Hv, dv, dk))
+        if nan_fill:
+            ckpt.fill(np.nan)  # also takes the page faults on one thread
+    o = _out(out.get("o"), (N, Hv, dv))
     nthr = default_threads() if n_threads is None else int(n_threads)
     lib = _load()
     args = [B, Hqk, Hv, dk, dv, L.ctypes.data_as(_I), nt.ctypes.data_as(_I), n_slot]
@@ -121,25 +138,28 @@ def _run(fn_name, row_tokens, q, k, v, a, b, A_log, dt_bias, S0, n_tail, n_slot,
 
 
 def run_sequential(row_tokens, q, k, v, a, b, A_log, dt_bias, S0=None, n_tail=None, n_slot=None,
-                   n_threads=None):
+                   n_threads=None, nan_fill=True, out=None):
     """Token-by-token recurrence over a packed ragged batch.
 
     Returns (S_final [B][H_v][d_v][d_k], ckpt [B][n_slot][H_v][d_v][d_k] or None,
     o [N][H_v][d_v]); checkpoint slot j of row r is the state after
-    L_r - n_tail_r + j + 1 of its tokens; slots >= n_tail_r hold NaN.
+    L_r - n_tail_r + j + 1 of its tokens; slots >= n_tail_r hold NaN (or are left
+    uninitialised with nan_fill=False).  `out` may hold preallocated float64 arrays
+    under the keys "S_final", "ckpt" and "o" (reused buffers avoid page faults).
     """
     return _run("gdn_oracle_sequential", row_tokens, q, k, v, a, b, A_log, dt_bias, S0, n_tail,
-                n_slot, None, n_threads)
+                n_slot, None, n_threads, nan_fill, out)
 
 
 def run_chunked(row_tokens, q, k, v, a, b, A_log, dt_bias, S0=None, n_tail=None, n_slot=None,
-                chunk=64, n_threads=None):
+                chunk=64, n_threads=None, nan_fill=True):
     """Same function as run_sequential, evaluated in the chunkwise UT form."""
     return _run("gdn_oracle_chunked", row_tokens, q, k, v, a, b, A_log, dt_bias, S0, n_tail,
-                n_slot, chunk, n_threads)
+                n_slot, chunk, n_threads, nan_fill)
 
 
-def verify_window(row_tokens, q, k, v, a, b, A_log, dt_bias, S_committed, k_max=3, n_threads=None):
+def verify_window(row_tokens, q, k, v, a, b, A_log, dt_bias, S_committed, k_max=3, n_threads=None,
+                  nan_fill=True, out=None):
     """Run each row's window (T_r = row_tokens[r] <= k_max+1 tokens) from its committed
     state, keeping checkpoint slot j = state after j+1 window tokens, j < T_r.
 
@@ -147,7 +167,7 @@ def verify_window(row_tokens, q, k, v, a, b, A_log, dt_bias, S_committed, k_max=
     T = np.asarray(row_tokens, np.int32)
     assert np.all((T >= 1) & (T <= k_max + 1))
     _, ckpt, o = run_sequential(T, q, k, v, a, b, A_log, dt_bias, S_committed, n_tail=T,
-                                n_slot=k_max + 1, n_threads=n_threads)
+                                n_slot=k_max + 1, n_threads=n_threads, nan_fill=nan_fill, out=out)
     return ckpt, o
 
 

@@ -38,7 +38,8 @@
  *   q, k    [N][H_qk][d_k]      v     [N][H_v][d_v]      a, b [N][H_v]
  *   A_log, dt_bias [H_v]
  *   S0      [B][H_v][d_v][d_k]  start state of each row (read only)
- *   S_final [B][H_v][d_v][d_k]  state after the row's last token (may be NULL)
+ *   S_final [B][H_v][d_v][d_k]  state after the row's last token (also the work
+ *           buffer of the sequential form)
  *   ckpt    [B][n_slot][H_v][d_v][d_k]: slot j of row r holds the state after
  *           L_r - n_tail_r + j + 1 tokens, for j < n_tail_r <= min(L_r, n_slot);
  *           the other slots are not written (ckpt may be NULL if all n_tail are 0)
@@ -98,7 +99,7 @@ int gdn_oracle_sequential(int B, int Hqk, int Hv, int dk, int dv, const int *L,
                           const double *dt_bias, const double *S0,
                           double *S_final, double *ckpt, double *o,
                           int n_threads) {
-  if (check_rows(B, Hqk, Hv, dk, dv, L, n_tail, n_slot)) return -1;
+  if (check_rows(B, Hqk, Hv, dk, dv, L, n_tail, n_slot) || !S_final) return -1;
   long *cu = malloc(sizeof(long) * (B + 1));
   cu[0] = 0;
   for (int r = 0; r < B; ++r) cu[r + 1] = cu[r] + L[r];
@@ -110,7 +111,7 @@ int gdn_oracle_sequential(int B, int Hqk, int Hv, int dk, int dv, const int *L,
   for (long unit = 0; unit < (long)B * Hv; ++unit) {
     if (unit == 0) record_threads();
     const int r = (int)(unit / Hv), h = (int)(unit % Hv), hq = h / group;
-    double *S = malloc(sizeof(double) * unit_sz);
+    double *S = S_final + unit * unit_sz; /* the state evolves in place in S_final */
     double *u = malloc(sizeof(double) * dv);
     memcpy(S, S0 + unit * unit_sz, sizeof(double) * unit_sz);
     const int nt = n_tail ? n_tail[r] : 0;
@@ -143,8 +144,6 @@ int gdn_oracle_sequential(int B, int Hqk, int Hv, int dk, int dv, const int *L,
         memcpy(ckpt + (((long)r * n_slot + slot) * Hv + h) * unit_sz, S,
                sizeof(double) * unit_sz);
     }
-    if (S_final) memcpy(S_final + unit * unit_sz, S, sizeof(double) * unit_sz);
-    free(S);
     free(u);
   }
   free(cu);

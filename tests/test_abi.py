@@ -1,0 +1,173 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point that
+include/gdn.h declares, and its host-side validation fails closed.
+
+Every call here is built to be rejected by host validation before any launch
+(it never reaches a kernel).  As a guard these tests do not run where a GPU is
+visible: there the GPU tests cover the same paths with real buffers.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gateddeltanet_linear_attention_amd import binding as gb
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gdn.h")
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+no_gpu = pytest.mark.skipif(_gpu_visible(), reason="host-validation probes run only where no kernel can launch")
+
+
+def declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"gdn_decode_step", "gdn_verify_window", "gdn_commit_accepted",
+            "gdn_chunked_prefill_with_checkpoints", "gdn_chunked_workspace_bytes",
+            "gdn_plan_transaction", "gdn_run_transaction", "gdn_status_str", "gdn_version"} <= set(names)
+    lib = gb.lib()
+    for n in names:
+        assert hasattr(lib, n), "libgdn.so does not export %s" % n
+
+
+def test_version_and_status_strings():
+    m = re.search(r"#define GDN_VERSION (\d+)", open(HEADER).read())
+    assert gb.gdn_version() == int(m.group(1))
+    for code in range(-7, 1):
+        assert gb.gdn_status_str(code) and gb.gdn_status_str(code) != "unknown status"
+    assert gb.gdn_status_str(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("k_max", [0, 1, 2, 3])
+def test_planner_routes_short_rows_to_the_recurrent_kernel(k_max):
+    dims = gb.Dims(16, 32, 128, 128, k_max)
+    lens = np.arange(1, 200)
+    route = gb.gdn_plan_transaction(dims, lens)
+    assert np.array_equal(route, np.where(lens <= k_max + 1, gb.ROUTE_RECURRENT, gb.ROUTE_CHUNKED))
+
+
+def test_planner_is_per_row_on_a_mixed_batch():
+    dims = gb.Dims(16, 32, 128, 128, 3)
+    lens = [4, 883, 4, 1, 3702, 2, 3]
+    route = gb.gdn_plan_transaction(dims, lens)
+    assert route.tolist() == [0, 1, 0, 0, 1, 0, 0]
+    with pytest.raises(gb.GdnError) as e:
+        gb.gdn_plan_transaction(dims, [4, 0, 2])
+    assert e.value.code == -3
+
+
+# ---------------------------------------------------------------- raw-ABI validation
+
+class Bufs:
+    """Aligned host buffers standing in for device pointers.  Never dereferenced:
+    every call below is rejected before a launch."""
+
+    def __init__(self):
+        self._keep = []
+
+    def ptr(self, nbytes=256, misalign=0):
+        a = np.zeros(nbytes + 64, np.uint8)
+        self._keep.append(a)
+        base = a.ctypes.data
+        return ctypes.c_void_p(((base + 15) // 16) * 16 + misalign)
+
+
+def _dims(**kw):
+    d = dict(n_qk_heads=16, n_v_heads=32, d_k=128, d_v=128, k_max=3)
+    d.update(kw)
+    return gb._Dims(d["n_qk_heads"], d["n_v_heads"], d["d_k"], d["d_v"], d["k_max"])
+
+
+def _i32(x):
+    arr = np.ascontiguousarray(np.asarray(x, np.int32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _verify(dims, T, src, n_slots=8, bufs=None, ckpt=None, pool=None, misalign=0, null_q=False):
+    bufs = bufs or Bufs()
+    Ta, Tp = _i32(T)
+    sa, sp = _i32(src)
+    toks = [ctypes.c_void_p(0) if null_q else bufs.ptr(misalign=misalign)] + [bufs.ptr() for _ in range(6)]
+    return gb.lib().gdn_verify_window(ctypes.byref(dims), len(Ta), Tp, *toks,
+                                      pool or bufs.ptr(), n_slots, sp, ckpt or bufs.ptr(), bufs.ptr(),
+                                      ctypes.c_void_p(0))
+
+
+@no_gpu
+def test_verify_validation_codes():
+    d = _dims()
+    assert _verify(_dims(d_k=64, d_v=64), [1], [0]) == -2          # unsupported width
+    assert _verify(_dims(d_k=128, d_v=16), [1], [0]) == -2         # d_k != d_v
+    assert _verify(_dims(n_v_heads=30), [1], [0]) == -2            # H_v % H_qk != 0
+    assert _verify(_dims(k_max=4), [1], [0]) == -2                 # k_max > 3
+    assert _verify(d, [1, 5], [0, 1]) == -3                        # T_r > k_max + 1
+    assert _verify(d, [1, 0], [0, 1]) == -3                        # T_r < 1
+    assert _verify(_dims(k_max=1), [3], [0]) == -3                 # T_r > k_max + 1 (k_max 1)
+    assert _verify(d, [2, 2], [0, 8]) == -3                        # slot >= n_slots
+    assert _verify(d, [2, 2], [0, -2]) == -3                       # slot < -1
+    assert _verify(d, [2], [0], misalign=8) == -5                  # misaligned q
+    assert _verify(d, [2], [0], null_q=True) == -1                 # NULL q
+    assert gb.lib().gdn_verify_window(None, 1, None, *[None] * 8, 1, None, None, None, None) == -1
+    # checkpoint buffer overlapping the state pool
+    b = Bufs()
+    p = b.ptr(1 << 20)
+    assert _verify(d, [2], [0], bufs=b, pool=p, ckpt=ctypes.c_void_p(p.value + 4096)) == -4
+
+
+@no_gpu
+def test_zero_rows_is_a_no_op():
+    assert _verify(_dims(), [], []) == 0
+
+
+@no_gpu
+def test_decode_and_commit_validation_codes():
+    lib = gb.lib()
+    b = Bufs()
+    d = _dims()
+
+    def decode(src, dst, n_slots=8):
+        sa, sp = _i32(src)
+        da, dp = _i32(dst)
+        return lib.gdn_decode_step(ctypes.byref(d), len(sa), *[b.ptr() for _ in range(7)], b.ptr(),
+                                   n_slots, sp, dp, b.ptr(), ctypes.c_void_p(0))
+
+    assert decode([0, 1], [1, 1]) == -4      # two rows write one slot
+    assert decode([0, 1], [1, 0]) == -4      # row 0 writes the slot row 1 reads
+    assert decode([0, 1], [0, 8]) == -3      # dst out of range
+    assert decode([0, 1], [0, -1]) == -3     # decode must publish its state
+
+    def commit(T, dst, n_slots=8, ckpt=None, pool=None):
+        Ta, Tp = _i32(T)
+        da, dp = _i32(dst)
+        return lib.gdn_commit_accepted(ctypes.byref(d), len(Ta), Tp, ckpt or b.ptr(), b.ptr(),
+                                       pool or b.ptr(), n_slots, dp, b.ptr(), ctypes.c_void_p(0))
+
+    assert commit([4, 4], [3, 3]) == -4      # duplicate destination
+    assert commit([4, 5], [1, 2]) == -3      # T_r > k_max + 1
+    assert commit([4, 2], [1, 9]) == -3      # slot out of range
+    p = b.ptr(1 << 20)
+    assert commit([4], [0], pool=p, ckpt=p) == -4  # checkpoint buffer is the pool
+
+
+@no_gpu
+def test_binding_rejects_host_tensors_before_the_library():
+    torch = pytest.importorskip("torch")
+    dims = gb.Dims(1, 1, 16, 16, 3)
+    t = torch.zeros(1, 1, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gb.gdn_decode_step(dims, t, t, t, torch.zeros(1, 1), torch.zeros(1, 1), torch.zeros(1),
+                           torch.zeros(1), torch.zeros(1, 1, 16, 16), [0], [0], t)

@@ -24,8 +24,8 @@ MUTANTS = {
     "output_uses_key": ("acc += S[i * dk + j] * qt[j];", "acc += S[i * dk + j] * kt[j];"),
     "beta_outside_decay": ("alpha * (S[i * dk + j] - beta * u[i] * kt[j])",
                            "alpha * S[i * dk + j] - beta * u[i] * kt[j]"),
-    "head_interleaved": ("hq = h / group;\n    double *S = malloc(sizeof(double) * unit_sz);\n    double *u",
-                         "hq = h % Hqk;\n    double *S = malloc(sizeof(double) * unit_sz);\n    double *u"),
+    "head_interleaved": ("hq = h / group;\n    double *S = S_final + unit * unit_sz;",
+                         "hq = h % Hqk;\n    double *S = S_final + unit * unit_sz;"),
     "checkpoint_off_by_one": ("const int slot = t - (L[r] - nt);", "const int slot = t - (L[r] - nt) - 1;"),
     "softplus_sign": ("log1p(exp(-fabs(x)))", "log1p(exp(fabs(x)))"),
     "sigmoid_sign": ("beta[i] = 1.0 / (1.0 + exp(-b[i]));", "beta[i] = 1.0 / (1.0 + exp(b[i]));"),
