@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Throughput of the K=3 draft-verification step of the gated delta rule on one MI355X.
+
+A step is one speculative-decoding verification of a batch for one GatedDeltaNet
+layer: gdn_verify_window (each row runs its previous bonus token and 3 drafts
+from the committed state, publishing the state after every token) followed by
+gdn_commit_accepted (rollback of each row to its accepted length, accepted counts
+~ Binomial(3, 0.85) resident on the device).  Inputs are synthetic (seeded), at
+the head shape of a hybrid GatedDeltaNet layer: 16 q/k heads, 32 value heads,
+d_k = d_v = 128, fp32 128x128 state per value head, bf16 q/k/v/o.
+
+Workload of the headline line: 16 concurrent requests, every row K=3 (4 tokens per
+window): 16 x 32 x 4 = 2048 head-token updates per step.  Four independent buffer
+sets (state pool + checkpoints + tokens, 160 MiB each, like four layers) are used
+in rotation so the step streams from HBM rather than from the 256 MB last-level
+cache.  The batch-1 K=3 figures are reported alongside.
+
+Prints one JSON line (see --help).  --gpus N>1 is refused: the path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN verify head-token updates/s + HBM GB/s vs peak, K=3, batch 1 and 16"
+HBM_PEAK_GBPS = 8000.0
+STATE_BYTES = 128 * 128 * 4          # one value head's fp32 state
+TOKEN_BYTES = 776                    # per head-token: q,k (shared by 2 v-heads) 256 + v 256 + a,b 8 + o 256
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_conc16_k3_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gateddeltanet_linear_attention_amd", "csrc", f)
+                  for f in ("gdn_recurrent.hip", "gdn_internal.h")]
+
+
+def verify_bytes(n_units: int, T: int) -> int:
+    """Algorithmic HBM bytes of one verify launch: per (row, v-head) unit, read the
+    committed state once, write T checkpoints, and move 776 B of token I/O per token."""
+    return n_units * ((1 + T) * STATE_BYTES + TOKEN_BYTES * T)
+
+
+def commit_bytes(n_units: int) -> int:
+    return n_units * 2 * STATE_BYTES
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(n_launch_bytes: int):
+    """HBM bytes per verify launch from the committed counter summary, or None when
+    it is missing or was taken on a different kernel source."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+class VerifySet:
+    """One buffer set: state pool, checkpoints, a window of tokens, accepted counts,
+    and the two prepared C-ABI calls of a step."""
+
+    def __init__(self, gb, synth, dims, B, T, seed, stream):
+        import numpy as np
+        import torch
+        shape = synth.FULL
+        Hv, d = shape.n_v_heads, shape.d
+        g = synth.streams(seed, 3)
+        A_log, dt_bias = synth.head_params(g[0], shape)
+        tok = synth.tokens(g[1], shape, B * T)
+        acc = synth.accepted_counts(g[2], np.full(B, T - 1))
+        dev = "cuda"
+        self.t = dict(q=torch.from_numpy(tok.q).to(torch.bfloat16).to(dev),
+                      k=torch.from_numpy(tok.k).to(torch.bfloat16).to(dev),
+                      v=torch.from_numpy(tok.v).to(torch.bfloat16).to(dev),
+                      a=torch.from_numpy(tok.a).to(dev), b=torch.from_numpy(tok.b).to(dev),
+                      A_log=torch.from_numpy(A_log).to(dev), dt_bias=torch.from_numpy(dt_bias).to(dev))
+        gen = torch.Generator(device="cpu").manual_seed(seed)
+        self.pool = (0.05 * torch.randn(B, Hv, d, d, generator=gen)).to(dev)
+        self.ckpt = torch.empty(B, 4, Hv, d, d, device=dev)
+        self.o = torch.empty(B * T, Hv, d, dtype=torch.bfloat16, device=dev)
+        self.acc = torch.from_numpy(acc).to(dev)
+        self.status = torch.zeros((B + 31) // 32, dtype=torch.int32, device=dev)
+        rows = np.arange(B, dtype=np.int32)
+        Ts = np.full(B, T, np.int32)
+        self.verify = gb.prepare_verify_window(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
+                                               ckpt=self.ckpt, o=self.o, stream=stream)
+        self.commit = gb.prepare_commit_accepted(dims, Ts, self.ckpt, self.acc, self.pool, dst_slot=rows,
+                                                 status=self.status, stream=stream)
+        # the window's tokens, for the CPU baseline
+        self.tok, self.A_log, self.dt_bias, self.T, self.B = tok, A_log, dt_bias, Ts, B
+
+
+def run_steps(sets, steps, warmup, stream, torch):
+    """Warm-up, then `steps` timed steps (rotating buffer sets), each bracketed by
+    synchronisation.  Events on the launch stream time every verify launch."""
+    for i in range(warmup):
+        s = sets[i % len(sets)]
+        s.verify()
+        s.commit()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        s = sets[i % len(sets)]
+        ev[i][0].record(stream)
+        s.verify()
+        ev[i][1].record(stream)
+        s.commit()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    verify_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall, verify_ms
+
+
+def cpu_baseline(s: "VerifySet", seconds: float):
+    """The fp64 oracle on the host, on the same window as the GPU step (a bounded
+    sample: repeated windows for about `seconds` of work)."""
+    import numpy as np
+    import oracle
+    tok = s.tok
+    S0 = s.pool.double().cpu().numpy()
+    out = dict(S_final=np.zeros(S0.shape), ckpt=np.zeros((s.B, 4) + S0.shape[1:]),
+               o=np.zeros((int(s.T.sum()),) + S0.shape[1:3]))
+    oracle.verify_window(s.T, tok.q, tok.k, tok.v, tok.a, tok.b, s.A_log, s.dt_bias, S0,
+                         nan_fill=False, out=out)  # first touch of the buffers, untimed
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.verify_window(s.T, tok.q, tok.k, tok.v, tok.a, tok.b, s.A_log, s.dt_bias, S0,
+                             nan_fill=False, out=out)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    upd = n * int(s.T.sum()) * S0.shape[1]
+    return {"value": upd / el, "unit": "head-token updates/s", "cores": oracle.threads_used(),
+            "kind": "oracle",
+            "sample": "%d repetitions of one %d-row K=%d verify window (%d head-token updates each), "
+                      "fp64, %.1f s" % (n, s.B, int(s.T[0]) - 1, int(s.T.sum()) * S0.shape[1], el)}
+
+
+def measure(gb, synth, torch, B, T, steps, warmup, n_sets, stream, seed0):
+    dims = gb.Dims(16, 32, 128, 128, 3)
+    sets = [VerifySet(gb, synth, dims, B, T, seed0 + i, stream) for i in range(n_sets)]
+    wall, verify_ms = run_steps(sets, steps, warmup, stream, torch)
+    for s in sets:
+        assert int(s.status.abs().sum()) == 0
+    units = B * 32
+    upd = units * T
+    vb = verify_bytes(units, T)
+    vms = sum(verify_ms) / len(verify_ms)
+    srt = sorted(verify_ms)
+    return sets, {
+        "ms_per_step": 1e3 * wall / steps,
+        "updates_per_s": upd * steps / wall,
+        "verify_ms_mean": vms,
+        "verify_ms_p10": srt[len(srt) // 10],
+        "verify_ms_p50": srt[len(srt) // 2],
+        "verify_ms_p90": srt[(9 * len(srt)) // 10],
+        "verify_updates_per_s": upd / (vms * 1e-3),
+        "verify_bytes": vb,
+        "verify_gbps": vb / (vms * 1e-3) / 1e9,
+        "step_gbps": (vb + commit_bytes(units)) * steps / wall / 1e9,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--sets", type=int, default=4, help="buffer sets in rotation (4 x 160 MiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batch1", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this path runs on one GPU; --gpus %d is not supported "
+              "(rows and heads are independent, see the design notes on sharding)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gateddeltanet_linear_attention_amd import binding as gb
+    from gateddeltanet_linear_attention_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    gb.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    sets16, r16 = measure(gb, synth, torch, 16, 4, args.steps, args.warmup, args.sets, stream, 500)
+    out_b1 = None
+    if not args.no_batch1:
+        _, r1 = measure(gb, synth, torch, 1, 4, args.steps, args.warmup, args.sets, stream, 600)
+        out_b1 = {"head_token_updates_per_s": r1["updates_per_s"], "ms_per_step": r1["ms_per_step"],
+                  "verify_us_mean": 1e3 * r1["verify_ms_mean"], "verify_gbps": r1["verify_gbps"],
+                  "verify_frac_of_hbm_peak": r1["verify_gbps"] / HBM_PEAK_GBPS}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(sets16[0], args.cpu_seconds)
+
+    traffic = traffic_from_profile(r16["verify_bytes"])
+    line = {
+        "metric": METRIC,
+        "value": r16["updates_per_s"],
+        "unit": "head-token updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r16["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": "conc16_k3_verify_commit", "rows": 16, "drafts_per_row": 3,
+                   "tokens_per_window": 4, "qk_heads": 16, "v_heads": 32, "d_k": 128, "d_v": 128,
+                   "state": "fp32", "io": "bf16", "buffer_sets": args.sets},
+        "roofline": {"bound": "hbm", "achieved": r16["verify_gbps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": r16["verify_gbps"] / HBM_PEAK_GBPS,
+                     "traffic": traffic, "kernel": "recurrent_kernel<128,8,4> (gdn_verify_window)",
+                     "algorithmic_bytes_per_launch": r16["verify_bytes"],
+                     "launch_us_mean": 1e3 * r16["verify_ms_mean"],
+                     "launch_us_p10": 1e3 * r16["verify_ms_p10"],
+                     "launch_us_p50": 1e3 * r16["verify_ms_p50"],
+                     "launch_us_p90": 1e3 * r16["verify_ms_p90"]},
+        "verify_head_token_updates_per_s": r16["verify_updates_per_s"],
+        "step_gbps": r16["step_gbps"],
+        "batch1": out_b1,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
