@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <climits>
 #include <vector>
 
 #include "gdn.h"
@@ -111,6 +112,100 @@ int launch_recurrent_rows(const gdn_dims *d, const gdn::RecurrentArgs &proto,
     }
     if (gdn::launch_recurrent(ra, d->d_k, stream) != hipSuccess) return GDN_E_HIP;
   }
+  return GDN_OK;
+}
+
+int64_t chunks_of(int32_t len) { return (int64_t(len) + gdn::kChunk - 1) / gdn::kChunk; }
+
+// Runs rows `rows` through the two chunked kernels, kRowsPerLaunch at a time;
+// workspace chunks are numbered over all of `rows`.
+int launch_chunked_rows(const gdn_dims *d, const gdn::ChunkArgs &proto,
+                        const std::vector<int32_t> &rows, const std::vector<int64_t> &cu,
+                        const int32_t *len, const int32_t *n_tail, const int32_t *src,
+                        const int32_t *dst, hipStream_t stream) {
+  int64_t chunk_base = 0;
+  for (size_t base = 0; base < rows.size(); base += kRowsPerLaunch) {
+    gdn::ChunkArgs ca = proto;
+    const size_t n = std::min<size_t>(kRowsPerLaunch, rows.size() - base);
+    ca.n_rows = int32_t(n);
+    int32_t local = 0;
+    for (size_t j = 0; j < n; ++j) {
+      const int32_t r = rows[base + j];
+      ca.tok0[j] = int32_t(cu[r]);
+      ca.len[j] = len[r];
+      ca.chunk_start[j] = local;
+      ca.chunk0[j] = int32_t(chunk_base + local);
+      ca.src[j] = src ? src[r] : -1;
+      ca.dst[j] = dst ? dst[r] : -1;
+      ca.n_tail[j] = n_tail ? n_tail[r] : 0;
+      ca.ck_row[j] = r;
+      local += int32_t(chunks_of(len[r]));
+    }
+    if (gdn::launch_chunked(ca, d->d_k, local, stream) != hipSuccess) return GDN_E_HIP;
+    chunk_base += local;
+  }
+  return GDN_OK;
+}
+
+size_t chunked_ws_bytes(const gdn_dims *d, const std::vector<int32_t> &rows, const int32_t *len) {
+  int64_t chunks = 0;
+  for (int32_t r : rows) chunks += chunks_of(len[r]);
+  return size_t(chunks) * size_t(d->n_v_heads) * size_t(gdn::chunk_ws_unit_floats(d->d_k)) * 4;
+}
+
+void fill_chunk_common(gdn::ChunkArgs &ca, const gdn_dims *d, const uint16_t *q, const uint16_t *k,
+                       const uint16_t *v, const float *a, const float *b, const float *A_log,
+                       const float *dt_bias, float *pool, float *ckpt, uint16_t *o, void *ws) {
+  memset(&ca, 0, sizeof(ca));
+  ca.q = q; ca.k = k; ca.v = v; ca.a = a; ca.b = b; ca.A_log = A_log; ca.dt_bias = dt_bias;
+  ca.state_in = pool; ca.state_out = pool; ca.ckpt = ckpt; ca.o = o;
+  ca.ws = static_cast<float *>(ws);
+  ca.n_qk = d->n_qk_heads; ca.n_v = d->n_v_heads;
+  ca.group = d->n_v_heads / d->n_qk_heads;
+  ca.ck_slots = d->k_max + 1;
+}
+
+// Shared checks of a packed batch whose rows run from src to dst slots with some
+// checkpoints each (chunked prefill and transactions).  Fills cu on success.
+int check_packed(const gdn_dims *dims, int32_t n_rows, const int32_t *len, const int32_t *n_ck,
+                 const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                 const float *b, const float *A_log, const float *dt_bias, float *state_pool,
+                 int32_t n_slots, const int32_t *src_slot, const int32_t *dst_slot, float *ckpt,
+                 uint16_t *o, std::vector<int64_t> &cu) {
+  int rc;
+  if (!len || !n_ck || !src_slot || !dst_slot) return GDN_E_NULL;
+  if ((rc = check_tokens(q, k, v, a, b, A_log, dt_bias, o))) return rc;
+  if (!state_pool) return GDN_E_NULL;
+  if (!aligned(state_pool, 16)) return GDN_E_ALIGN;
+  bool any_ck = false;
+  for (int32_t r = 0; r < n_rows; ++r) {
+    if (len[r] < 1) return GDN_E_RANGE;
+    if (n_ck[r] < 0 || n_ck[r] > len[r] || n_ck[r] > dims->k_max + 1) return GDN_E_RANGE;
+    any_ck |= n_ck[r] > 0;
+  }
+  if (any_ck && !ckpt) return GDN_E_NULL;
+  if (ckpt && !aligned(ckpt, 16)) return GDN_E_ALIGN;
+  if ((rc = check_slots(n_rows, n_slots, src_slot, dst_slot))) return rc;
+  cu.assign(size_t(n_rows) + 1, 0);
+  for (int32_t r = 0; r < n_rows; ++r) cu[r + 1] = cu[r] + len[r];
+  if (cu[n_rows] > INT32_MAX) return GDN_E_RANGE;
+  const Sizes s = sizes_of(dims);
+  const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
+  const size_t ck_b = ckpt ? size_t(n_rows) * s.ck_row_floats * 4 : 0;
+  const size_t o_b = size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2;
+  if (overlap(ckpt, ck_b, state_pool, pool_b) || overlap(o, o_b, ckpt, ck_b) ||
+      overlap(o, o_b, state_pool, pool_b))
+    return GDN_E_ALIAS;
+  return GDN_OK;
+}
+
+int check_workspace(void *ws, size_t ws_bytes, size_t need, const void *pool, size_t pool_b,
+                    const void *ckpt, size_t ck_b, const void *o, size_t o_b) {
+  if (need == 0) return GDN_OK;
+  if (!ws || ws_bytes < need) return GDN_E_WORKSPACE;
+  if (!aligned(ws, 16)) return GDN_E_ALIGN;
+  if (overlap(ws, need, pool, pool_b) || overlap(ws, need, ckpt, ck_b) || overlap(ws, need, o, o_b))
+    return GDN_E_ALIAS;
   return GDN_OK;
 }
 
@@ -261,8 +356,15 @@ int gdn_plan_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *ro
 
 size_t gdn_chunked_workspace_bytes(const gdn_dims *dims, int32_t n_rows,
                                    const int32_t *row_tokens, int32_t chunk) {
-  (void)dims; (void)n_rows; (void)row_tokens; (void)chunk;
-  return 0;
+  if (check_dims(dims) || n_rows < 0 || chunk != gdn::kChunk) return 0;
+  if (n_rows == 0) return 0;
+  if (!row_tokens) return 0;
+  std::vector<int32_t> rows;
+  for (int32_t r = 0; r < n_rows; ++r) {
+    if (row_tokens[r] < 1) return 0;
+    rows.push_back(r);
+  }
+  return chunked_ws_bytes(dims, rows, row_tokens);
 }
 
 int gdn_chunked_prefill_with_checkpoints(
@@ -271,11 +373,27 @@ int gdn_chunked_prefill_with_checkpoints(
     const float *a, const float *b, const float *A_log, const float *dt_bias,
     float *state_pool, int32_t n_slots, const int32_t *src_slot, const int32_t *dst_slot,
     float *ckpt, uint16_t *o, void *workspace, size_t ws_bytes, void *stream) {
-  (void)dims; (void)n_rows; (void)row_tokens; (void)chunk; (void)n_tail; (void)q; (void)k;
-  (void)v; (void)a; (void)b; (void)A_log; (void)dt_bias; (void)state_pool; (void)n_slots;
-  (void)src_slot; (void)dst_slot; (void)ckpt; (void)o; (void)workspace; (void)ws_bytes;
-  (void)stream;
-  return GDN_E_UNSUPPORTED;
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (chunk != gdn::kChunk) return GDN_E_UNSUPPORTED;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  std::vector<int64_t> cu;
+  if ((rc = check_packed(dims, n_rows, row_tokens, n_tail, q, k, v, a, b, A_log, dt_bias,
+                         state_pool, n_slots, src_slot, dst_slot, ckpt, o, cu)))
+    return rc;
+  std::vector<int32_t> rows(static_cast<size_t>(n_rows));
+  for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
+  const Sizes s = sizes_of(dims);
+  const size_t need = chunked_ws_bytes(dims, rows, row_tokens);
+  if ((rc = check_workspace(workspace, ws_bytes, need, state_pool, size_t(n_slots) * s.row_floats * 4,
+                            ckpt, ckpt ? size_t(n_rows) * s.ck_row_floats * 4 : 0, o,
+                            size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2)))
+    return rc;
+  gdn::ChunkArgs proto;
+  fill_chunk_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, ckpt, o, workspace);
+  return launch_chunked_rows(dims, proto, rows, cu, row_tokens, n_tail, src_slot, dst_slot,
+                             static_cast<hipStream_t>(stream));
 }
 
 int gdn_run_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
@@ -284,10 +402,32 @@ int gdn_run_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *row
                         const float *dt_bias, float *state_pool, int32_t n_slots,
                         const int32_t *src_slot, const int32_t *dst_slot, float *ckpt,
                         uint16_t *o, void *workspace, size_t ws_bytes, void *stream) {
-  (void)dims; (void)n_rows; (void)row_tokens; (void)n_ckpt; (void)q; (void)k; (void)v; (void)a;
-  (void)b; (void)A_log; (void)dt_bias; (void)state_pool; (void)n_slots; (void)src_slot;
-  (void)dst_slot; (void)ckpt; (void)o; (void)workspace; (void)ws_bytes; (void)stream;
-  return GDN_E_UNSUPPORTED;
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  std::vector<int64_t> cu;
+  if ((rc = check_packed(dims, n_rows, row_tokens, n_ckpt, q, k, v, a, b, A_log, dt_bias,
+                         state_pool, n_slots, src_slot, dst_slot, ckpt, o, cu)))
+    return rc;
+  std::vector<int32_t> route(static_cast<size_t>(n_rows));
+  if ((rc = gdn_plan_transaction(dims, n_rows, row_tokens, route.data()))) return rc;
+  std::vector<int32_t> rec, chk;
+  for (int32_t r = 0; r < n_rows; ++r) (route[r] == GDN_ROUTE_RECURRENT ? rec : chk).push_back(r);
+  const Sizes s = sizes_of(dims);
+  const size_t need = chunked_ws_bytes(dims, chk, row_tokens);
+  if ((rc = check_workspace(workspace, ws_bytes, need, state_pool, size_t(n_slots) * s.row_floats * 4,
+                            ckpt, ckpt ? size_t(n_rows) * s.ck_row_floats * 4 : 0, o,
+                            size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2)))
+    return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  gdn::RecurrentArgs rproto;
+  fill_common(rproto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, state_pool, ckpt, o);
+  if ((rc = launch_recurrent_rows(dims, rproto, rec, cu, row_tokens, src_slot, dst_slot, n_ckpt, st)))
+    return rc;
+  gdn::ChunkArgs cproto;
+  fill_chunk_common(cproto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, ckpt, o, workspace);
+  return launch_chunked_rows(dims, cproto, chk, cu, row_tokens, n_ckpt, src_slot, dst_slot, st);
 }
 
 }  // extern "C"

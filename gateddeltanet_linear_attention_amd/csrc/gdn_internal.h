@@ -52,7 +52,43 @@ struct CommitArgs {
   int32_t dst[kRowsPerLaunch];
 };
 
+// Chunked prefill (chunk = 64 tokens).  Launch-local row r owns chunks
+// [chunk_start[r], chunk_start[r] + ceil(len[r] / 64)) of the prep grid and
+// workspace chunks starting at chunk0[r] (numbered over the whole call); its
+// tail checkpoint j (j < n_tail[r]) is the state after len[r] - n_tail[r] + j + 1
+// tokens, stored to checkpoint row ck_row[r].
+constexpr int kChunk = 64;
+
+// Workspace floats per (chunk, value head): W [64][d], U' [64][d], P [64][64],
+// and the 64 fp64 prefix sums of the log-decay.
+constexpr int64_t chunk_ws_unit_floats(int d) {
+  return 2 * int64_t(kChunk) * d + int64_t(kChunk) * kChunk + 2 * kChunk;
+}
+
+struct ChunkArgs {
+  const uint16_t *q, *k, *v;
+  const float *a, *b, *A_log, *dt_bias;
+  const float *state_in;
+  float *state_out;
+  float *ckpt;
+  uint16_t *o;
+  float *ws;
+  int32_t n_qk, n_v, group;
+  int32_t ck_slots;
+  int32_t n_rows;
+  int32_t tok0[kRowsPerLaunch];
+  int32_t len[kRowsPerLaunch];
+  int32_t chunk_start[kRowsPerLaunch];
+  int32_t chunk0[kRowsPerLaunch];
+  int32_t src[kRowsPerLaunch];
+  int32_t dst[kRowsPerLaunch];
+  int32_t n_tail[kRowsPerLaunch];
+  int32_t ck_row[kRowsPerLaunch];
+  static constexpr int64_t ws_unit_floats(int d) { return chunk_ws_unit_floats(d); }
+};
+
 hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream);
+hipError_t launch_chunked(const ChunkArgs &args, int d, int n_chunks, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &args, hipStream_t stream);
 
 }  // namespace gdn

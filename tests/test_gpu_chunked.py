@@ -1,0 +1,331 @@
+"""GPU parity of the chunked prefill (with tail checkpoints) and of mixed ragged
+transactions, against the fp64 oracle's sequential definition, through the C ABI.
+
+* one 2048-token prefill at the full head shape, chunk 64, checkpoints at the last 4
+  positions: outputs, final state and checkpoints vs the token-by-token recurrence;
+* ragged rows whose tails straddle chunk boundaries, zero and non-zero start states,
+  both head widths, a slow-decay stress case;
+* a 16-row transaction mixing 4 long prefills and 12 K=3 verify windows: every
+  verify row gets its per-token checkpoints although long prefills share the step
+  (the fault of the onnxruntime-genai pull request "Run chained MTP drafting in the
+  batch Engine", section "Correctness fix"), then commit and 64 decode-only windows;
+* verify rows of a transaction are bit-identical to gdn_verify_window;
+* a prefill published on one stream is seen by a verify on another after an event
+  ("Native three-step MTP", section "What changed": publish pending prefill state
+  before a dependent verification).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gateddeltanet_linear_attention_amd import binding as gb
+from gateddeltanet_linear_attention_amd import synth
+from tests.gpu_common import (assert_o, assert_state, bits, dev_params, dev_tokens, dims_of, host,
+                              index_tokens, say)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+POISON = 0x7FC0DEAD
+
+
+def _poison(shape):
+    t = torch.empty(shape, dtype=torch.float32, device="cuda")
+    t.view(torch.int32).fill_(POISON)
+    return t
+
+
+def _ws(dims, lens):
+    nb = gb.gdn_chunked_workspace_bytes(dims, lens)
+    return torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+
+
+def run_chunked_case(shape, lens, n_tail, src_kind, seed, gate_shift=0.0, what=""):
+    dims = dims_of(shape)
+    B, Hv, d = len(lens), shape.n_v_heads, shape.d
+    lens = np.asarray(lens, np.int32)
+    n_tail = np.asarray(n_tail, np.int32)
+    g = synth.streams(seed, 3)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    tok = synth.tokens(g[1], shape, int(lens.sum()), gate_shift)
+    n_slots = 2 * B
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    pool = (0.3 * torch.randn(n_slots, Hv, d, d, generator=gen)).cuda()
+    src = np.arange(B, dtype=np.int32) if src_kind == "state" else np.full(B, -1, np.int32)
+    if src_kind == "mixed":
+        src[::2] = np.arange(B, dtype=np.int32)[::2]
+    dst = np.arange(B, 2 * B, dtype=np.int32)
+    before = pool.clone()
+    ckpt = _poison((B, 4, Hv, d, d))
+    o = torch.empty(int(lens.sum()), Hv, d, dtype=torch.bfloat16, device="cuda")
+    gb.gdn_chunked_prefill_with_checkpoints(dims, lens, n_tail, **dev_tokens(tok), **dev_params(A_log, dt_bias),
+                                            state_pool=pool, src_slot=src, dst_slot=dst, ckpt=ckpt, o=o,
+                                            workspace=_ws(dims, lens))
+    S0 = host(before[:B])
+    S0[src < 0] = 0.0
+    S_ref, ck_ref, o_ref = oracle.run_sequential(lens, tok.q, tok.k, tok.v, tok.a, tok.b, A_log, dt_bias,
+                                                 S0, n_tail=n_tail, n_slot=4)
+    torch.cuda.synchronize()
+    mo = assert_o(host(o), o_ref, what + " outputs")
+    ms = assert_state(host(pool[B:]), S_ref, what + " final states")
+    for r in range(B):
+        if n_tail[r]:
+            ms = max(ms, assert_state(host(ckpt[r, :n_tail[r]]), ck_ref[r, :n_tail[r]],
+                                      what + " row %d checkpoints" % r))
+        assert bool((bits(ckpt[r, n_tail[r]:]) == POISON).all()), what + " row %d: extra slot written" % r
+    assert torch.equal(bits(pool[:B]), bits(before[:B])), what + ": a source slot was written"
+    say("%s: max |do| %.2e, state rel %.2e" % (what, mo, ms))
+
+
+def test_prefill_2048_tokens_with_last_four_checkpoints():
+    w = synth.prefill_workload()
+    dims = dims_of(w.shape)
+    Hv, d = w.shape.n_v_heads, w.shape.d
+    tok = w.tokens()
+    L = int(w.lens[0])
+    pool = torch.zeros(1, Hv, d, d, device="cuda")
+    ckpt = _poison((1, 4, Hv, d, d))
+    o = torch.empty(L, Hv, d, dtype=torch.bfloat16, device="cuda")
+    gb.gdn_chunked_prefill_with_checkpoints(dims, w.lens, w.n_tail, **dev_tokens(tok),
+                                            **dev_params(w.A_log, w.dt_bias), state_pool=pool,
+                                            src_slot=[-1], dst_slot=[0], ckpt=ckpt, o=o,
+                                            workspace=_ws(dims, w.lens))
+    S_ref, ck_ref, o_ref = oracle.run_sequential(w.lens, tok.q, tok.k, tok.v, tok.a, tok.b, w.A_log,
+                                                 w.dt_bias, n_tail=w.n_tail, n_slot=4)
+    torch.cuda.synchronize()
+    mo = assert_o(host(o), o_ref, "prefill outputs")
+    ms = assert_state(host(pool), S_ref, "prefill final state")
+    ms = max(ms, assert_state(host(ckpt[0]), ck_ref[0], "prefill checkpoints (last 4 positions)"))
+    # checkpoint 3 is the final state; checkpoint j is the state after L-3+j tokens
+    assert_state(host(ckpt[0, 3]), host(pool[0]), "last checkpoint vs final state")
+    say("prefill 2048: max |do| %.2e, state rel %.2e" % (mo, ms))
+
+
+@pytest.mark.parametrize("src_kind", ["zero", "state", "mixed"])
+def test_ragged_rows_tails_straddling_chunks(src_kind):
+    lens = [1, 5, 63, 64, 65, 66, 130, 200]
+    n_tail = [1, 4, 4, 3, 4, 4, 4, 2]
+    run_chunked_case(synth.HeadShape(2, 4, 128), lens, n_tail, src_kind, 61, what="ragged/" + src_kind)
+
+
+def test_tiny_head_width():
+    run_chunked_case(synth.TINY, [8, 70, 129], [4, 4, 1], "mixed", 62, what="d16")
+
+
+def test_slow_decay_long_memory():
+    run_chunked_case(synth.HeadShape(1, 2, 128), [300, 257], [4, 0], "state", 63, gate_shift=-8.0,
+                     what="slow decay")
+
+
+def test_chunked_matches_verify_within_tolerance_and_commit_works_on_it():
+    """Commit is path-agnostic: tail slots of a chunked row mean what verify slots mean."""
+    shape = synth.FULL
+    dims = dims_of(shape)
+    Hv, d = shape.n_v_heads, shape.d
+    g = synth.streams(64, 2)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    P = dev_params(A_log, dt_bias)
+    tok = synth.tokens(g[1], shape, 4)
+    td = dev_tokens(tok)
+    gen = torch.Generator(device="cpu").manual_seed(3)
+    pool = (0.3 * torch.randn(3, Hv, d, d, generator=gen)).cuda()
+    ck_v = torch.empty(1, 4, Hv, d, d, device="cuda")
+    ck_c = torch.empty(1, 4, Hv, d, d, device="cuda")
+    o_v = torch.empty(4, Hv, d, dtype=torch.bfloat16, device="cuda")
+    o_c = torch.empty_like(o_v)
+    gb.gdn_verify_window(dims, [4], **td, **P, state_pool=pool, src_slot=[0], ckpt=ck_v, o=o_v)
+    gb.gdn_chunked_prefill_with_checkpoints(dims, [4], [4], **td, **P, state_pool=pool, src_slot=[0],
+                                            dst_slot=[1], ckpt=ck_c, o=o_c, workspace=_ws(dims, [4]))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gb.gdn_commit_accepted(dims, [4], ck_c, torch.tensor([2], dtype=torch.int32, device="cuda"), pool,
+                           dst_slot=[2], status=status)
+    torch.cuda.synchronize()
+    assert_state(host(ck_c[0]), host(ck_v[0]), "chunked vs verify checkpoints")
+    assert_o(host(o_c), host(o_v), "chunked vs verify outputs")
+    assert torch.equal(bits(pool[2]), bits(ck_c[0, 2]))
+    assert torch.equal(bits(pool[1]), bits(ck_c[0, 3]))
+
+
+# ---------------------------------------------------------------- mixed transaction
+
+def test_mixed_transaction_then_decode_only_windows():
+    m = synth.mixed_workload()
+    shape = m.shape
+    dims = dims_of(shape)
+    B, Hv, d = m.n_rows, shape.n_v_heads, shape.d
+    P = dev_params(m.A_log, m.dt_bias)
+    rows = np.arange(B, dtype=np.int32)
+    is_pf = m.is_prefill
+    pool = torch.zeros(B, Hv, d, d, device="cuda")
+
+    # warm the verify rows (zero state, chunked prefill without checkpoints)
+    warm = m.warm_tokens()
+    wrows = rows[~is_pf]
+    wl = m.warm_lens[~is_pf]
+    ow = torch.empty(warm.n, Hv, d, dtype=torch.bfloat16, device="cuda")
+    gb.gdn_chunked_prefill_with_checkpoints(dims, wl, np.zeros_like(wl), **dev_tokens(warm), **P,
+                                            state_pool=pool, src_slot=np.full(len(wrows), -1), dst_slot=wrows,
+                                            ckpt=torch.empty(len(wrows), 4, Hv, d, d, device="cuda"), o=ow,
+                                            workspace=_ws(dims, wl))
+    S_w, _, o_wref = oracle.run_sequential(wl, warm.q, warm.k, warm.v, warm.a, warm.b, m.A_log, m.dt_bias)
+    S_o = np.zeros((B, Hv, d, d))
+    S_o[wrows] = S_w
+    torch.cuda.synchronize()
+    assert_o(host(ow), o_wref, "warm-up outputs")
+    assert_state(host(pool), S_o, "warmed states")
+
+    # the transaction: 4 prefills from zero (publish final state), 12 K=3 windows (checkpoints)
+    lens = m.transaction_lens()
+    assert np.array_equal(gb.gdn_plan_transaction(dims, lens),
+                          np.where(is_pf, gb.ROUTE_CHUNKED, gb.ROUTE_RECURRENT))
+    n_ck = np.where(is_pf, 0, 4).astype(np.int32)
+    src = np.where(is_pf, -1, rows).astype(np.int32)
+    dst = np.where(is_pf, rows, -1).astype(np.int32)
+    tx = m.transaction_tokens()
+    ckpt = _poison((B, 4, Hv, d, d))
+    o = torch.empty(tx.n, Hv, d, dtype=torch.bfloat16, device="cuda")
+    ws = _ws(dims, lens)
+    gb.gdn_run_transaction(dims, lens, n_ck, **dev_tokens(tx), **P, state_pool=pool, src_slot=src,
+                           dst_slot=dst, ckpt=ckpt, o=o, workspace=ws)
+    acc = m.transaction_accepted()
+    vrows = rows[~is_pf]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gb.gdn_commit_accepted(dims, np.full(len(vrows), 4), ckpt[torch.as_tensor(vrows, device="cuda")].contiguous(),
+                           torch.from_numpy(acc[vrows]).cuda(), pool, dst_slot=vrows, status=status)
+    S0 = S_o.copy()
+    S_t, ck_t, o_t = oracle.run_sequential(lens, tx.q, tx.k, tx.v, tx.a, tx.b, m.A_log, m.dt_bias, S0,
+                                           n_tail=n_ck, n_slot=4)
+    torch.cuda.synchronize()
+    assert_o(host(o), o_t, "transaction outputs")
+    for r in vrows:  # every verify row got all four checkpoints, and they are right
+        assert_state(host(ckpt[r]), ck_t[r], "transaction verify row %d checkpoints" % r)
+    for r in rows[is_pf]:
+        assert bool((bits(ckpt[r]) == POISON).all()), "prefill row %d wrote checkpoints it did not ask for" % r
+    S_o[is_pf] = S_t[is_pf]
+    for r in vrows:
+        S_o[r] = ck_t[r, acc[r]]
+    assert int(status[0]) == 0
+    assert_state(host(pool), S_o, "committed states after the transaction")
+    say("mixed transaction ok; prefill lengths %s" % m.prefill_lens[is_pf].tolist())
+
+    # 64 decode-only K=3 windows over all 16 rows
+    T = np.full(B, 4, np.int32)
+    ckw = torch.empty(B, 4, Hv, d, d, device="cuda")
+    ow = torch.empty(4 * B, Hv, d, dtype=torch.bfloat16, device="cuda")
+    out = dict(S_final=np.zeros_like(S_o), ckpt=np.zeros((B, 4, Hv, d, d)), o=np.zeros((4 * B, Hv, d)))
+    S_bufs, cur = [S_o, np.zeros_like(S_o)], 0
+    worst = 0.0
+    for i in range(m.n_windows):
+        win = m.window_tokens(i)
+        a = m.accepted(i)
+        gb.gdn_verify_window(dims, T, **dev_tokens(win), **P, state_pool=pool, src_slot=rows, ckpt=ckw, o=ow)
+        gb.gdn_commit_accepted(dims, T, ckw, torch.from_numpy(a).cuda(), pool, dst_slot=rows, status=status)
+        ck_o, o_o = oracle.verify_window(T, win.q, win.k, win.v, win.a, win.b, m.A_log, m.dt_bias, S_bufs[cur],
+                                         nan_fill=False, out=out)
+        cur = 1 - cur
+        for r in range(B):
+            S_bufs[cur][r] = ck_o[r, a[r]]
+        worst = max(worst, assert_o(host(ow), o_o, "decode-only window %d" % i))
+    torch.cuda.synchronize()
+    assert int(status[0]) == 0
+    e = assert_state(host(pool), S_bufs[cur], "states after 64 decode-only windows")
+    say("decode-only windows ok: max |do| %.2e, state rel %.2e" % (worst, e))
+
+
+def test_transaction_verify_rows_bit_identical_to_verify_window():
+    shape = synth.FULL
+    dims = dims_of(shape)
+    Hv, d = shape.n_v_heads, shape.d
+    lens = np.array([4, 300, 2, 1, 3, 130], np.int32)
+    n_ck = np.array([4, 0, 2, 1, 3, 4], np.int32)
+    B = len(lens)
+    g = synth.streams(65, 2)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    P = dev_params(A_log, dt_bias)
+    tok = synth.tokens(g[1], shape, int(lens.sum()))
+    td = dev_tokens(tok)
+    gen = torch.Generator(device="cpu").manual_seed(4)
+    pool = (0.3 * torch.randn(B, Hv, d, d, generator=gen)).cuda()
+    ckpt = _poison((B, 4, Hv, d, d))
+    o = torch.empty(int(lens.sum()), Hv, d, dtype=torch.bfloat16, device="cuda")
+    gb.gdn_run_transaction(dims, lens, n_ck, **td, **P, state_pool=pool, src_slot=np.arange(B),
+                           dst_slot=np.full(B, -1), ckpt=ckpt, o=o, workspace=_ws(dims, lens))
+    short = np.nonzero(lens <= 4)[0]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    idx = np.concatenate([np.arange(cu[r], cu[r + 1]) for r in short])
+    ck2 = _poison((len(short), 4, Hv, d, d))
+    o2 = torch.empty(len(idx), Hv, d, dtype=torch.bfloat16, device="cuda")
+    gb.gdn_verify_window(dims, lens[short], **index_tokens(td, idx), **P, state_pool=pool,
+                         src_slot=short.astype(np.int32), ckpt=ck2, o=o2)
+    torch.cuda.synchronize()
+    for j, r in enumerate(short):
+        assert torch.equal(bits(ckpt[r, :n_ck[r]]), bits(ck2[j, lens[r] - n_ck[r]:lens[r]]))
+    assert torch.equal(o[torch.as_tensor(idx, device="cuda")].view(torch.int16), o2.view(torch.int16))
+    # the long rows' checkpoints are the oracle's
+    S_ref, ck_ref, o_ref = oracle.run_sequential(lens, tok.q, tok.k, tok.v, tok.a, tok.b, A_log, dt_bias,
+                                                 host(pool), n_tail=n_ck, n_slot=4)
+    assert_o(host(o), o_ref, "transaction outputs")
+    assert_state(host(ckpt[5, :4]), ck_ref[5, :4], "chunked row checkpoints")
+
+
+def test_prefill_published_on_one_stream_is_seen_by_verify_on_another():
+    shape = synth.HeadShape(2, 4, 128)
+    dims = dims_of(shape)
+    Hv, d = shape.n_v_heads, shape.d
+    g = synth.streams(66, 3)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    P = dev_params(A_log, dt_bias)
+    pre = dev_tokens(synth.tokens(g[1], shape, 1000))
+    win = dev_tokens(synth.tokens(g[2], shape, 4))
+    ws = _ws(dims, [1000])
+
+    def run(two_streams):
+        pool = torch.zeros(1, Hv, d, d, device="cuda")
+        o_p = torch.empty(1000, Hv, d, dtype=torch.bfloat16, device="cuda")
+        ck = torch.empty(1, 4, Hv, d, d, device="cuda")
+        o_v = torch.empty(4, Hv, d, dtype=torch.bfloat16, device="cuda")
+        s1 = torch.cuda.Stream()
+        s2 = torch.cuda.Stream() if two_streams else s1
+        torch.cuda.synchronize()
+        gb.gdn_chunked_prefill_with_checkpoints(dims, [1000], [0], **pre, **P, state_pool=pool, src_slot=[-1],
+                                                dst_slot=[0], ckpt=ck, o=o_p, workspace=ws, stream=s1)
+        if two_streams:
+            ev = torch.cuda.Event()
+            ev.record(s1)
+            s2.wait_event(ev)
+        gb.gdn_verify_window(dims, [4], **win, **P, state_pool=pool, src_slot=[0], ckpt=ck, o=o_v, stream=s2)
+        torch.cuda.synchronize()
+        return ck.clone(), o_v.clone()
+
+    a = run(False)
+    b = run(True)
+    assert torch.equal(bits(a[0]), bits(b[0]))
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+
+
+def test_chunked_errors_write_nothing():
+    shape = synth.HeadShape(1, 2, 128)
+    dims = dims_of(shape)
+    Hv, d = shape.n_v_heads, shape.d
+    g = synth.streams(67, 2)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    td = dev_tokens(synth.tokens(g[1], shape, 100))
+    pool = torch.zeros(2, Hv, d, d, device="cuda")
+    ckpt = _poison((1, 4, Hv, d, d))
+    o = torch.empty(100, Hv, d, dtype=torch.bfloat16, device="cuda")
+    ws = _ws(dims, [100])
+    small = torch.empty(ws.numel() - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gb.GdnError) as e:  # workspace too small
+        gb.gdn_chunked_prefill_with_checkpoints(dims, [100], [4], **td, **dev_params(A_log, dt_bias),
+                                                state_pool=pool, src_slot=[-1], dst_slot=[0], ckpt=ckpt,
+                                                o=o, workspace=small)
+    assert e.value.code == -6
+    with pytest.raises(gb.GdnError) as e:  # more tail checkpoints than slots
+        gb.gdn_chunked_prefill_with_checkpoints(dims, [100], [5], **td, **dev_params(A_log, dt_bias),
+                                                state_pool=pool, src_slot=[-1], dst_slot=[0], ckpt=ckpt,
+                                                o=o, workspace=ws)
+    assert e.value.code == -3
+    torch.cuda.synchronize()
+    assert float(pool.abs().sum()) == 0.0
+    assert bool((bits(ckpt) == POISON).all())
