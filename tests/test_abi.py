@@ -73,17 +73,17 @@ def test_planner_is_per_row_on_a_mixed_batch():
 # ---------------------------------------------------------------- raw-ABI validation
 
 class Bufs:
-    """Aligned host buffers standing in for device pointers.  Never dereferenced:
-    every call below is rejected before a launch."""
+    """Synthetic, far-apart, 16-byte-aligned addresses standing in for device
+    pointers (1 TiB apart, so no two claimed buffers overlap).  Never dereferenced:
+    every call below is rejected by host validation before a launch."""
 
     def __init__(self):
-        self._keep = []
+        self._next = 1 << 44
 
     def ptr(self, nbytes=256, misalign=0):
-        a = np.zeros(nbytes + 64, np.uint8)
-        self._keep.append(a)
-        base = a.ctypes.data
-        return ctypes.c_void_p(((base + 15) // 16) * 16 + misalign)
+        p = self._next
+        self._next += 1 << 40
+        return ctypes.c_void_p(p + misalign)
 
 
 def _dims(**kw):
@@ -171,3 +171,47 @@ def test_binding_rejects_host_tensors_before_the_library():
     with pytest.raises(ValueError):
         gb.gdn_decode_step(dims, t, t, t, torch.zeros(1, 1), torch.zeros(1, 1), torch.zeros(1),
                            torch.zeros(1), torch.zeros(1, 1, 16, 16), [0], [0], t)
+
+
+@no_gpu
+def test_chunked_and_transaction_validation_codes():
+    lib = gb.lib()
+    b = Bufs()
+    d = _dims()
+    need = gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100, 64, 1])
+    assert need == (2 + 1 + 1) * 32 * (2 * 64 * 128 + 64 * 64 + 128) * 4
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100], chunk=32) == 0
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [0]) == 0
+
+    def chunked(L, nt, src, dst, chunk=64, ws=None, ws_bytes=1 << 40, ckpt=None, pool=None):
+        La, Lp = _i32(L)
+        na, np_ = _i32(nt)
+        sa, sp = _i32(src)
+        da, dp = _i32(dst)
+        return lib.gdn_chunked_prefill_with_checkpoints(
+            ctypes.byref(d), len(La), Lp, chunk, np_, *[b.ptr() for _ in range(7)], pool or b.ptr(), 8, sp, dp,
+            ckpt or b.ptr(), b.ptr(), ws if ws is not None else b.ptr(), ws_bytes, ctypes.c_void_p(0))
+
+    assert chunked([100], [4], [0], [1], chunk=32) == -2        # chunk size other than 64
+    assert chunked([100], [5], [0], [1]) == -3                  # n_tail > k_max + 1
+    assert chunked([3], [4], [0], [1]) == -3                    # n_tail > L
+    assert chunked([0], [0], [0], [1]) == -3                    # empty row
+    assert chunked([100, 50], [0, 0], [0, 1], [1, 2]) == -4     # row 0 writes row 1's source
+    assert chunked([100, 50], [0, 0], [0, 1], [3, 3]) == -4     # duplicate destination
+    assert chunked([100], [0], [0], [1], ws_bytes=16) == -6     # workspace too small
+    assert chunked([100], [0], [0], [1], ws=ctypes.c_void_p(0)) == -6
+    p = b.ptr(1 << 20)
+    assert chunked([100], [4], [0], [1], pool=p, ckpt=ctypes.c_void_p(p.value + 256)) == -4
+
+    def tx(L, nc, src, dst, ws=None, ws_bytes=1 << 40):
+        La, Lp = _i32(L)
+        na, np_ = _i32(nc)
+        sa, sp = _i32(src)
+        da, dp = _i32(dst)
+        return lib.gdn_run_transaction(ctypes.byref(d), len(La), Lp, np_, *[b.ptr() for _ in range(7)], b.ptr(), 8,
+                                       sp, dp, b.ptr(), b.ptr(), ws if ws is not None else b.ptr(), ws_bytes,
+                                       ctypes.c_void_p(0))
+
+    assert tx([4, 100], [4, 0], [0, -1], [-1, 1], ws_bytes=100) == -6  # the long row needs workspace
+    assert tx([4, 100], [5, 0], [0, -1], [-1, 1]) == -3                # checkpoints > k_max + 1
+    assert tx([4, 100], [4, 0], [0, -1], [-1, 0]) == -4                # prefill row overwrites a verify source
