@@ -1,19 +1,22 @@
 #!/usr/bin/env python3
 """Throughput of the K=3 draft-verification step of the gated delta rule on one MI355X.
 
-A step is one speculative-decoding verification of a batch for one GatedDeltaNet
-layer: gdn_verify_window (each row runs its previous bonus token and 3 drafts
-from the committed state, publishing the state after every token) followed by
-gdn_commit_accepted (rollback of each row to its accepted length, accepted counts
-~ Binomial(3, 0.85) resident on the device).  Inputs are synthetic (seeded), at
-the head shape of a hybrid GatedDeltaNet layer: 16 q/k heads, 32 value heads,
-d_k = d_v = 128, fp32 128x128 state per value head, bf16 q/k/v/o.
+A step is one speculative-decoding verification round of a batch through L
+GatedDeltaNet layers, in the order a target model runs it: gdn_verify_window for
+every layer (each row runs its previous bonus token and 3 drafts from the
+committed state, publishing the state after every token), then, once acceptance
+is known, gdn_commit_accepted for every layer (rollback of each row to its
+accepted length; accepted counts ~ Binomial(3, 0.85) resident on the device).
+Inputs are synthetic (seeded), at the head shape of a hybrid GatedDeltaNet layer:
+16 q/k heads, 32 value heads, d_k = d_v = 128, fp32 128x128 state per value head,
+bf16 q/k/v/o.
 
 Workload of the headline line: 16 concurrent requests, every row K=3 (4 tokens per
-window): 16 x 32 x 4 = 2048 head-token updates per step.  Four independent buffer
-sets (state pool + checkpoints + tokens, 160 MiB each, like four layers) are used
-in rotation so the step streams from HBM rather than from the 256 MB last-level
-cache.  The batch-1 K=3 figures are reported alongside.
+window): 16 x 32 x 4 = 2048 head-token updates per layer, L = 12 layers per step
+by default.  Every layer has its own state pool, checkpoints and tokens (160 MiB),
+so a step touches 1.9 GB and the state a verify reads was written a whole step
+earlier: it streams from HBM, not from the 256 MB last-level cache.  The batch-1
+K=3 figures are reported alongside.
 
 Prints one JSON line (see --help).  --gpus N>1 is refused: the path runs on one GPU.
 """
@@ -104,26 +107,32 @@ class VerifySet:
         self.tok, self.A_log, self.dt_bias, self.T, self.B = tok, A_log, dt_bias, Ts, B
 
 
-def run_steps(sets, steps, warmup, stream, torch):
-    """Warm-up, then `steps` timed steps (rotating buffer sets), each bracketed by
-    synchronisation.  Events on the launch stream time every verify launch."""
-    for i in range(warmup):
-        s = sets[i % len(sets)]
-        s.verify()
-        s.commit()
+def run_steps(layers, steps, warmup, stream, torch):
+    """Warm-up, then `steps` timed steps, bracketed by synchronisation.  A step runs
+    every layer's verify back to back, then every layer's commit.  Events recorded
+    on the launch stream around each step's run of verify launches give the mean
+    verify launch duration (their span / L)."""
+    def step():
+        for s in layers:
+            s.verify()
+        for s in layers:
+            s.commit()
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        s = sets[i % len(sets)]
         ev[i][0].record(stream)
-        s.verify()
+        for s in layers:
+            s.verify()
         ev[i][1].record(stream)
-        s.commit()
+        for s in layers:
+            s.commit()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    verify_ms = [a.elapsed_time(b) for a, b in ev]
+    verify_ms = [a.elapsed_time(b) / len(layers) for a, b in ev]
     return wall, verify_ms
 
 
@@ -153,14 +162,14 @@ def cpu_baseline(s: "VerifySet", seconds: float):
                       "fp64, %.1f s" % (n, s.B, int(s.T[0]) - 1, int(s.T.sum()) * S0.shape[1], el)}
 
 
-def measure(gb, synth, torch, B, T, steps, warmup, n_sets, stream, seed0):
+def measure(gb, synth, torch, B, T, steps, warmup, n_layers, stream, seed0):
     dims = gb.Dims(16, 32, 128, 128, 3)
-    sets = [VerifySet(gb, synth, dims, B, T, seed0 + i, stream) for i in range(n_sets)]
+    sets = [VerifySet(gb, synth, dims, B, T, seed0 + i, stream) for i in range(n_layers)]
     wall, verify_ms = run_steps(sets, steps, warmup, stream, torch)
     for s in sets:
         assert int(s.status.abs().sum()) == 0
     units = B * 32
-    upd = units * T
+    upd = units * T * n_layers
     vb = verify_bytes(units, T)
     vms = sum(verify_ms) / len(verify_ms)
     srt = sorted(verify_ms)
@@ -171,19 +180,20 @@ def measure(gb, synth, torch, B, T, steps, warmup, n_sets, stream, seed0):
         "verify_ms_p10": srt[len(srt) // 10],
         "verify_ms_p50": srt[len(srt) // 2],
         "verify_ms_p90": srt[(9 * len(srt)) // 10],
-        "verify_updates_per_s": upd / (vms * 1e-3),
+        "verify_updates_per_s": units * T / (vms * 1e-3),
         "verify_bytes": vb,
         "verify_gbps": vb / (vms * 1e-3) / 1e9,
-        "step_gbps": (vb + commit_bytes(units)) * steps / wall / 1e9,
+        "step_gbps": (vb + commit_bytes(units)) * n_layers * steps / wall / 1e9,
     }
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--sets", type=int, default=4, help="buffer sets in rotation (4 x 160 MiB)")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=12,
+                    help="GatedDeltaNet layers per step, each with its own 160 MiB of buffers")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch1", action="store_true")
@@ -204,11 +214,12 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
-    sets16, r16 = measure(gb, synth, torch, 16, 4, args.steps, args.warmup, args.sets, stream, 500)
+    sets16, r16 = measure(gb, synth, torch, 16, 4, args.steps, args.warmup, args.layers, stream, 500)
     out_b1 = None
     if not args.no_batch1:
-        _, r1 = measure(gb, synth, torch, 1, 4, args.steps, args.warmup, args.sets, stream, 600)
-        out_b1 = {"head_token_updates_per_s": r1["updates_per_s"], "ms_per_step": r1["ms_per_step"],
+        _, r1 = measure(gb, synth, torch, 1, 4, args.steps, args.warmup, args.layers, stream, 600)
+        out_b1 = {"head_token_updates_per_s": r1["updates_per_s"],
+                  "ms_per_layer": r1["ms_per_step"] / args.layers,
                   "verify_us_mean": 1e3 * r1["verify_ms_mean"], "verify_gbps": r1["verify_gbps"],
                   "verify_frac_of_hbm_peak": r1["verify_gbps"] / HBM_PEAK_GBPS}
     cpu = None
@@ -231,15 +242,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": "conc16_k3_verify_commit", "rows": 16, "drafts_per_row": 3,
                    "tokens_per_window": 4, "qk_heads": 16, "v_heads": 32, "d_k": 128, "d_v": 128,
-                   "state": "fp32", "io": "bf16", "buffer_sets": args.sets},
+                   "state": "fp32", "io": "bf16", "layers_per_step": args.layers},
         "roofline": {"bound": "hbm", "achieved": r16["verify_gbps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": r16["verify_gbps"] / HBM_PEAK_GBPS,
-                     "traffic": traffic, "kernel": "recurrent_kernel<128,8,4> (gdn_verify_window)",
+                     "traffic": traffic, "kernel": "recurrent_kernel<128,16,1,8> (gdn_verify_window)",
                      "algorithmic_bytes_per_launch": r16["verify_bytes"],
                      "launch_us_mean": 1e3 * r16["verify_ms_mean"],
                      "launch_us_p10": 1e3 * r16["verify_ms_p10"],
                      "launch_us_p50": 1e3 * r16["verify_ms_p50"],
                      "launch_us_p90": 1e3 * r16["verify_ms_p90"]},
+        "ms_per_layer": r16["ms_per_step"] / args.layers,
         "verify_head_token_updates_per_s": r16["verify_updates_per_s"],
         "step_gbps": r16["step_gbps"],
         "batch1": out_b1,

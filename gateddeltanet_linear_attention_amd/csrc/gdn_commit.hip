@@ -14,6 +14,8 @@
 namespace gdn {
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr int kF4PerThread = 4;
 constexpr int kF4PerBlock = kThreads * kF4PerThread;  // 16 KiB per block
@@ -38,12 +40,19 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs args, int b
 #pragma unroll
   for (int m = 0; m < kF4PerThread; ++m) {
     const int64_t idx = base + int64_t(m) * kThreads;
-    if (idx < n4) x[m] = src[idx];
+    if (idx < n4) {  // each checkpoint is read once: keep it out of the caches
+      const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + idx));
+      x[m] = make_float4(y[0], y[1], y[2], y[3]);
+    }
   }
 #pragma unroll
   for (int m = 0; m < kF4PerThread; ++m) {
     const int64_t idx = base + int64_t(m) * kThreads;
-    if (idx < n4) dst[idx] = x[m];
+    // the committed state is read again only by the row's next call, a whole model
+    // step later: write it through, leaving no dirty lines to be evicted later
+    if (idx < n4)
+      __builtin_nontemporal_store(f32x4{x[m].x, x[m].y, x[m].z, x[m].w},
+                                  reinterpret_cast<f32x4 *>(dst + idx));
   }
 }
 

@@ -11,10 +11,14 @@
 //
 // Mapping.  LPR lanes own one state row; lane `sub` of the group holds the
 // float4 columns {sub + LPR*j}, so one wave-wide float4 access covers 64/LPR
-// rows in LPR*16-byte contiguous runs (128 B runs at d = 128): coalesced HBM
+// rows in LPR*16-byte contiguous runs (256 B runs at d = 128): coalesced HBM
 // reads of the state and writes of every checkpoint.  The two dot products per
-// token are a fixed-order in-lane FMA chain followed by an xor butterfly over the
+// token are a fixed-order in-lane FMA chain followed by a DPP butterfly over the
 // LPR lanes, which leaves every lane of the group with bit-identical sums.
+// A block stages the window's q, k, v slice and gates in LDS once (one memory
+// latency per block instead of one per token), and checkpoints are written with
+// non-temporal stores: the traffic is one state read to T checkpoint writes, and
+// streaming the writes past the caches is what lets it approach the HBM peak.
 //
 // Bit-exactness.  Decode, verify and transaction rows all run this one kernel
 // instantiation per d; the per-row arithmetic (element ownership, FMA order,
@@ -53,104 +57,174 @@ __device__ __forceinline__ void eval_gates(float a, float b, float A_log, float 
   beta = 1.0f / (1.0f + expf(-b));
 }
 
+// Sum over the LPR (4, 8 or 16) consecutive lanes of a row group with DPP lane
+// moves: swap neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), add
+// the mirrored half-row (lane i <- 7-i, the other quad's sum), then the mirrored
+// row (lane i <- 15-i, the other half-row's sum).  Each step adds two partial sums
+// of the same shape, so every lane of the group ends with the same bits.
+__device__ __forceinline__ float dpp_add(float p, int ctrl_id) {
+  int moved;
+  switch (ctrl_id) {
+    case 0: moved = __builtin_amdgcn_mov_dpp(__float_as_int(p), 0xB1, 0xF, 0xF, false); break;
+    case 1: moved = __builtin_amdgcn_mov_dpp(__float_as_int(p), 0x4E, 0xF, 0xF, false); break;
+    case 2: moved = __builtin_amdgcn_mov_dpp(__float_as_int(p), 0x141, 0xF, 0xF, false); break;
+    default: moved = __builtin_amdgcn_mov_dpp(__float_as_int(p), 0x140, 0xF, 0xF, false); break;
+  }
+  return p + __int_as_float(moved);
+}
+
 template <int LPR>
 __device__ __forceinline__ float group_sum(float p) {
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) p += __shfl_xor(p, m, 64);
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16, "row groups of 4, 8 or 16 lanes");
+  p = dpp_add(p, 0);
+  p = dpp_add(p, 1);
+  if (LPR >= 8) p = dpp_add(p, 2);
+  if (LPR == 16) p = dpp_add(p, 3);
   return p;
 }
 
-template <int D, int LPR, int WAVES>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Checkpoints are written once and read at most once (by commit), after the whole
+// window: stream them past the caches.
+__device__ __forceinline__ void store_nt(float *p, const float (&x)[4]) {
+  f32x4 v = {x[0], x[1], x[2], x[3]};
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+}
+
+template <int D, int LPR, int RPL, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs args) {
   constexpr int NV = D / LPR / 4;                  // float4 per lane per state row
-  constexpr int ROWS = WAVES * 64 / LPR;           // state rows per block
+  constexpr int ROWS = WAVES * 64 / LPR * RPL;     // state rows per block
   constexpr int TILES = D / ROWS;                  // blocks per (row, head)
+  constexpr int TB = 4;                            // tokens staged per batch
   static_assert(NV >= 1 && D % (LPR * 4) == 0 && D % ROWS == 0, "bad tiling");
   constexpr size_t UNIT = size_t(D) * D;
+  // One batch of up to TB tokens' inputs, shared by the block: k and q widened to
+  // fp32 once, the block's slice of v, and the two gates.
+  __shared__ float4 sK[TB][D / 4], sQ[TB][D / 4];
+  __shared__ float sV[TB][ROWS];
+  __shared__ float sAlpha[TB], sBeta[TB];
+  __shared__ uint16_t sO[TB][ROWS];  // outputs, written back coalesced per batch
 
-  const int sub = threadIdx.x % LPR;
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;
   int bid = blockIdx.x;
   const int tile = bid % TILES;
   bid /= TILES;
   const int h = bid % args.n_v;
   const int r = bid / args.n_v;
   const int hq = h / args.group;
-  const int i = tile * ROWS + int(threadIdx.x) / LPR;  // state row (value channel)
+  const int i_local = (tid / LPR) * RPL;  // first of this lane's RPL state rows in the block
+  const int i0 = tile * ROWS + i_local;
 
   const int ntok = args.ntok[r], tok0 = args.tok0[r];
   const int src = args.src[r], dst = args.dst[r], ck_first = args.ck_first[r];
   const int ck_row = args.ck_row[r];
   const int n_v = args.n_v, n_qk = args.n_qk;
 
-  float s[NV][4];
-  if (src >= 0) {
-    const float4 *p = reinterpret_cast<const float4 *>(
-        args.state_in + (size_t(src) * n_v + h) * UNIT + size_t(i) * D);
+  float s[RPL][NV][4];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const float4 x = p[sub + LPR * j];
-      s[j][0] = x.x; s[j][1] = x.y; s[j][2] = x.z; s[j][3] = x.w;
+  for (int q = 0; q < RPL; ++q) {
+    if (src >= 0) {
+      const float4 *p = reinterpret_cast<const float4 *>(
+          args.state_in + (size_t(src) * n_v + h) * UNIT + size_t(i0 + q) * D);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const float4 x = p[sub + LPR * j];
+        s[q][j][0] = x.x; s[q][j][1] = x.y; s[q][j][2] = x.z; s[q][j][3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) s[q][j][0] = s[q][j][1] = s[q][j][2] = s[q][j][3] = 0.0f;
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) s[j][0] = s[j][1] = s[j][2] = s[j][3] = 0.0f;
   }
-  const float A_log = args.A_log[h], dt_bias = args.dt_bias[h];
 
-  for (int t = 0; t < ntok; ++t) {
-    const size_t tok = size_t(tok0) + t;
-    float alpha, beta;
-    eval_gates(args.a[tok * n_v + h], args.b[tok * n_v + h], A_log, dt_bias, alpha, beta);
-    const uint2 *kp = reinterpret_cast<const uint2 *>(args.k + (tok * n_qk + hq) * D);
-    const uint2 *qp = reinterpret_cast<const uint2 *>(args.q + (tok * n_qk + hq) * D);
-    float kk[NV][4], qq[NV][4];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const uint2 kw = kp[sub + LPR * j], qw = qp[sub + LPR * j];
-      kk[j][0] = bf16_lo(kw.x); kk[j][1] = bf16_hi(kw.x);
-      kk[j][2] = bf16_lo(kw.y); kk[j][3] = bf16_hi(kw.y);
-      qq[j][0] = bf16_lo(qw.x); qq[j][1] = bf16_hi(qw.x);
-      qq[j][2] = bf16_lo(qw.y); qq[j][3] = bf16_hi(qw.y);
+  for (int t0 = 0; t0 < ntok; t0 += TB) {
+    const int nb = min(TB, ntok - t0);
+    // stage this batch's token inputs (issued while the state loads are in flight)
+    for (int x = tid; x < nb * (D / 4); x += 64 * WAVES) {
+      const int t = x / (D / 4), c = x % (D / 4);
+      const size_t tok = size_t(tok0) + t0 + t;
+      const uint2 kw = reinterpret_cast<const uint2 *>(args.k + (tok * n_qk + hq) * D)[c];
+      const uint2 qw = reinterpret_cast<const uint2 *>(args.q + (tok * n_qk + hq) * D)[c];
+      sK[t][c] = make_float4(bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y));
+      sQ[t][c] = make_float4(bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y));
     }
-    const float vi = __uint_as_float(uint32_t(args.v[(tok * n_v + h) * D + i]) << 16);
+    for (int x = tid; x < nb * ROWS; x += 64 * WAVES) {
+      const int t = x / ROWS, rr = x % ROWS;
+      const size_t tok = size_t(tok0) + t0 + t;
+      sV[t][rr] = __uint_as_float(uint32_t(args.v[(tok * n_v + h) * D + tile * ROWS + rr]) << 16);
+    }
+    if (tid < nb) {
+      const size_t tok = size_t(tok0) + t0 + tid;
+      eval_gates(args.a[tok * n_v + h], args.b[tok * n_v + h], args.A_log[h], args.dt_bias[h],
+                 sAlpha[tid], sBeta[tid]);
+    }
+    __syncthreads();
 
-    // u = S[i,:] . k
-    float p = 0.0f;
+#pragma unroll 1
+    for (int t = 0; t < nb; ++t) {
+      const float alpha = sAlpha[t], beta = sBeta[t];
+      float kk[NV][4];
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
+      for (int j = 0; j < NV; ++j) {
+        const float4 kw = sK[t][sub + LPR * j];
+        kk[j][0] = kw.x; kk[j][1] = kw.y; kk[j][2] = kw.z; kk[j][3] = kw.w;
+      }
+      const int tt = t0 + t;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p = fmaf(s[j][e], kk[j][e], p);
-    const float u = group_sum<LPR>(p);
-    // S[i,:] <- alpha S[i,:] + beta (v_i - alpha u) k
-    const float c = beta * (vi - alpha * u);
+      for (int q = 0; q < RPL; ++q) {
+        const float vi = sV[t][i_local + q];
+        // u = S[i,:] . k
+        float p = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
+        for (int j = 0; j < NV; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[j][e] = fmaf(c, kk[j][e], alpha * s[j][e]);
-    // o_i = S[i,:] . q
-    float po = 0.0f;
+          for (int e = 0; e < 4; ++e) p = fmaf(s[q][j][e], kk[j][e], p);
+        const float u = group_sum<LPR>(p);
+        // S[i,:] <- alpha S[i,:] + beta (v_i - alpha u) k
+        const float c = beta * (vi - alpha * u);
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
+        for (int j = 0; j < NV; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) po = fmaf(s[j][e], qq[j][e], po);
-    const float oi = group_sum<LPR>(po);
-    if (sub == 0) args.o[(tok * n_v + h) * D + i] = to_bf16(oi);
-
-    if (t >= ck_first) {
-      float4 *cp = reinterpret_cast<float4 *>(
-          args.ckpt + ((size_t(ck_row) * args.ck_slots + (t - ck_first)) * n_v + h) * UNIT +
-          size_t(i) * D);
+          for (int e = 0; e < 4; ++e) s[q][j][e] = fmaf(c, kk[j][e], alpha * s[q][j][e]);
+        // o_i = S[i,:] . q
+        float po = 0.0f;
 #pragma unroll
-      for (int j = 0; j < NV; ++j)
-        cp[sub + LPR * j] = make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
+        for (int j = 0; j < NV; ++j) {
+          const float4 qw = sQ[t][sub + LPR * j];
+          po = fmaf(s[q][j][0], qw.x, po);
+          po = fmaf(s[q][j][1], qw.y, po);
+          po = fmaf(s[q][j][2], qw.z, po);
+          po = fmaf(s[q][j][3], qw.w, po);
+        }
+        const float oi = group_sum<LPR>(po);
+        if (sub == 0) sO[t][i_local + q] = to_bf16(oi);
+        if (tt >= ck_first) {
+          float *cp = args.ckpt + ((size_t(ck_row) * args.ck_slots + (tt - ck_first)) * n_v + h) * UNIT +
+                      size_t(i0 + q) * D;
+#pragma unroll
+          for (int j = 0; j < NV; ++j) store_nt(cp + 4 * (sub + LPR * j), s[q][j]);
+        }
+      }
+    }
+    __syncthreads();  // the next batch overwrites the staged inputs
+    for (int x = tid; x < nb * ROWS; x += 64 * WAVES) {
+      const int t = x / ROWS, rr = x % ROWS;
+      args.o[((size_t(tok0) + t0 + t) * n_v + h) * D + tile * ROWS + rr] = sO[t][rr];
     }
   }
 
   if (dst >= 0) {
-    float4 *p = reinterpret_cast<float4 *>(args.state_out + (size_t(dst) * n_v + h) * UNIT +
-                                           size_t(i) * D);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) p[sub + LPR * j] = make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
+    for (int q = 0; q < RPL; ++q) {
+      float4 *p = reinterpret_cast<float4 *>(args.state_out + (size_t(dst) * n_v + h) * UNIT +
+                                             size_t(i0 + q) * D);
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        p[sub + LPR * j] = make_float4(s[q][j][0], s[q][j][1], s[q][j][2], s[q][j][3]);
+    }
   }
 }
 
@@ -159,15 +233,15 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream) {
   if (args.n_rows <= 0) return hipSuccess;
   if (d == 128) {
-    constexpr int D = 128, LPR = 8, WAVES = 4;
-    constexpr int TILES = D / (WAVES * 64 / LPR);
+    constexpr int D = 128, LPR = 16, RPL = 1, WAVES = 8;
+    constexpr int TILES = D / (WAVES * 64 / LPR * RPL);
     dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * TILES);
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, WAVES>), grid, dim3(64 * WAVES), 0, stream, args);
+    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES>), grid, dim3(64 * WAVES), 0, stream, args);
   } else if (d == 16) {
-    constexpr int D = 16, LPR = 4, WAVES = 1;
-    constexpr int TILES = D / (WAVES * 64 / LPR);
+    constexpr int D = 16, LPR = 4, RPL = 1, WAVES = 1;
+    constexpr int TILES = D / (WAVES * 64 / LPR * RPL);
     dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * TILES);
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, WAVES>), grid, dim3(64 * WAVES), 0, stream, args);
+    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES>), grid, dim3(64 * WAVES), 0, stream, args);
   } else {
     return hipErrorInvalidValue;
   }
