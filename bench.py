@@ -162,6 +162,56 @@ def cpu_baseline(s: "VerifySet", seconds: float):
                       "fp64, %.1f s" % (n, s.B, int(s.T[0]) - 1, int(s.T.sum()) * S0.shape[1], el)}
 
 
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def prefill_flops(L: int, n_heads: int = 32, d: int = 128, C: int = 64) -> float:
+    """Algorithmic flops of the chunked prefill, every chunk contraction counted as a
+    dense 64-token tile: KK^T, QK^T, W = T K, U' = T V (4 x 2 C^2 d), W S^T, Q S^T,
+    U^T K (3 x 2 C d^2) and P U (2 C^2 d) per (chunk, value head)."""
+    per_chunk = 4 * 2 * C * C * d + 3 * 2 * C * d * d + 2 * C * C * d
+    return float((L + C - 1) // C) * n_heads * per_chunk
+
+
+def measure_prefill(gb, synth, torch, stream, reps):
+    """The 2048-token chunked prefill (1 row, 32 value heads, chunk 64, checkpoints at
+    the last 4 positions), timed with events on the launch stream."""
+    w = synth.prefill_workload()
+    dims = gb.Dims(16, 32, 128, 128, 3)
+    tok = w.tokens()
+    dev = "cuda"
+    t = dict(q=torch.from_numpy(tok.q).to(torch.bfloat16).to(dev),
+             k=torch.from_numpy(tok.k).to(torch.bfloat16).to(dev),
+             v=torch.from_numpy(tok.v).to(torch.bfloat16).to(dev),
+             a=torch.from_numpy(tok.a).to(dev), b=torch.from_numpy(tok.b).to(dev),
+             A_log=torch.from_numpy(w.A_log).to(dev), dt_bias=torch.from_numpy(w.dt_bias).to(dev))
+    L = int(w.lens[0])
+    pool = torch.zeros(1, 32, 128, 128, device=dev)
+    ckpt = torch.empty(1, 4, 32, 128, 128, device=dev)
+    o = torch.empty(L, 32, 128, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gb.gdn_chunked_workspace_bytes(dims, w.lens), dtype=torch.uint8, device=dev)
+
+    def call():
+        gb.gdn_chunked_prefill_with_checkpoints(dims, w.lens, w.n_tail, **t, state_pool=pool, src_slot=[-1],
+                                                dst_slot=[0], ckpt=ckpt, o=o, workspace=ws, stream=stream)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / reps
+    fl = prefill_flops(L)
+    return {"workload": "prefill_2048_chunk64_tail4", "tokens": L, "us_per_call": us,
+            "head_token_updates_per_s": L * 32 / (us * 1e-6),
+            "algorithmic_tflops": fl / (us * 1e-6) / 1e12, "mfma_f32_peak_tflops": MFMA_F32_PEAK_TFLOPS,
+            "frac_of_mfma_f32_peak": fl / (us * 1e-6) / 1e12 / MFMA_F32_PEAK_TFLOPS,
+            "algorithmic_flops_per_call": fl}
+
+
 def measure(gb, synth, torch, B, T, steps, warmup, n_layers, stream, seed0):
     dims = gb.Dims(16, 32, 128, 128, 3)
     sets = [VerifySet(gb, synth, dims, B, T, seed0 + i, stream) for i in range(n_layers)]
@@ -197,6 +247,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch1", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this path runs on one GPU; --gpus %d is not supported "
@@ -222,6 +273,7 @@ def main():
                   "ms_per_layer": r1["ms_per_step"] / args.layers,
                   "verify_us_mean": 1e3 * r1["verify_ms_mean"], "verify_gbps": r1["verify_gbps"],
                   "verify_frac_of_hbm_peak": r1["verify_gbps"] / HBM_PEAK_GBPS}
+    prefill = None if args.no_prefill else measure_prefill(gb, synth, torch, stream, 20)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(sets16[0], args.cpu_seconds)
@@ -255,6 +307,7 @@ def main():
         "verify_head_token_updates_per_s": r16["verify_updates_per_s"],
         "step_gbps": r16["step_gbps"],
         "batch1": out_b1,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
