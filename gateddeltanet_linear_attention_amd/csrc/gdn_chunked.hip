@@ -21,14 +21,17 @@
 // Two kernels, same stream:
 //   chunk_prep_kernel  one block per (chunk, value head), all chunks in parallel:
 //       gates, fp64 prefix sum of g, K K^T and Q K^T, forward substitution for T,
-//       W and U' -> workspace.
+//       W, U' and the decay factors -> workspace.
 //   chunk_scan_kernel  one block per (row, value head, 16 state rows), chunks in
 //       order: U, outputs, tail checkpoints, state carry (state tile stays in LDS).
 // Every contraction runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, 157 TF
 // dense on MI355X): the state tolerance (relative 1e-4) rules out rounding the fp32
-// operands T, W, U, S to bf16.  Decays are formed only as differences G_t - G_s
-// with s <= t, from an fp64 prefix sum (|G| reaches hundreds within a chunk under
-// strong decay, where fp32 differences would lose ~1e-5 relative).
+// operands T, W, U, S to bf16.  A wave loads all operand fragments of a product
+// before its first matrix instruction and interleaves independent accumulation
+// chains, so global-memory latency is paid once per phase, not once per k step.
+// Decays are formed only as differences G_t - G_s with s <= t, from an fp64 prefix
+// sum (|G| reaches hundreds within a chunk under strong decay, where differences of
+// fp32 sums would lose ~1e-5 relative).
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
@@ -36,9 +39,10 @@
 namespace gdn {
 namespace {
 
-constexpr int C = 64;      // chunk length
-constexpr int VT = 16;     // state rows per scan block
-constexpr int LDC = C + 4; // padded LDS row length for C-wide rows
+constexpr int C = 64;       // chunk length
+constexpr int VT = 16;      // state rows per scan block
+constexpr int LDC = C + 4;  // padded LDS row length (floats) for C-wide rows
+constexpr int LDB = C + 4;  // padded LDS row length (bf16) for C-wide rows
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -55,22 +59,20 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 }
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.0f, 0.0f, 0.0f, 0.0f}; }
+__device__ __forceinline__ float4 zf4() { return make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
+__device__ __forceinline__ float4 mul4(float4 a, float4 b) {
+  return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
 
-// acc(16x16) += A(16 x K) * B(K x 16) on the matrix cores.  Lane l (r = l % 16,
-// g = l / 16) feeds, for each 16-wide k block kb, A[r][kb+4g+e] and B[kb+4g+e][r]
-// for e = 0..3 (a permutation of k inside the block, the same on both sides):
-// la(k) returns A[r][k..k+3] and lb(k) returns B[k..k+3][r], i.e. row r of B^T.
-// Output: lane l holds C[4g + v][r] in acc[v].
-template <class LA, class LB>
-__device__ __forceinline__ floatx4 mma(floatx4 acc, int K, LA la, LB lb) {
-  const int g = (threadIdx.x & 63) >> 4;
-  for (int kb = 0; kb < K; kb += 16) {
-    const float4 a = la(kb + 4 * g), b = lb(kb + 4 * g);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
-  }
+// One 16-wide k block of acc(16x16) += A(16 x K) * B(K x 16) on the matrix cores.
+// Lane l (r = l % 16, g = l / 16) holds a = A[r][kb+4g .. kb+4g+3] and
+// b = B[kb+4g .. kb+4g+3][r]: a permutation of k inside the block, the same on
+// both sides.  After all k blocks, lane l holds C[4g + v][r] in acc[v].
+__device__ __forceinline__ floatx4 mma4(floatx4 acc, float4 a, float4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
   return acc;
 }
 
@@ -82,14 +84,33 @@ __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
   return row;
 }
 
+// Workspace of one (chunk, value head): W [C][D], U' [C][D], P [C][C], G [C] fp64,
+// eG[t] = e^{G_t}, eL[s] = e^{G_{n-1} - G_s} (s < n, else 0), and K^T [D][C] bf16.
+template <int D>
+struct Ws {
+  float *W, *U, *P, *eG, *eL;
+  double *G;
+  uint16_t *Kt;
+  __device__ Ws(float *base) {
+    W = base;
+    U = base + C * D;
+    P = base + 2 * C * D;
+    G = reinterpret_cast<double *>(base + 2 * C * D + C * C);
+    eG = base + 2 * C * D + C * C + 2 * C;
+    eL = eG + C;
+    Kt = reinterpret_cast<uint16_t *>(eL + C);
+  }
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
-  constexpr int LDK = LDC;
+  constexpr int NKB = D / 16;  // 16-wide k blocks over d
   __shared__ double sG[C];
-  __shared__ float sBeta[C];
-  __shared__ float sA[C * LDC];   // strictly lower A, then T = (I + A)^{-1}
-  __shared__ float sKt[D * LDK];  // (diag(beta e^G) K)^T: row d, column token m
-  __shared__ float sVt[D * LDK];  // (diag(beta) V)^T
+  __shared__ __attribute__((aligned(16))) float sBeta[C];  // beta_m
+  __shared__ __attribute__((aligned(16))) float sSK[C];    // beta_m e^{G_m}
+  __shared__ __attribute__((aligned(16))) float sA[C * LDC];  // strictly lower A, then T = (I + A)^{-1}
+  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * LDB];  // K^T (bf16): row d, column token m
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDB];  // V^T (bf16)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -104,11 +125,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   const uint16_t *Kc = args.k + tok_base * ldqk + int64_t(hq) * D;
   const uint16_t *Qc = args.q + tok_base * ldqk + int64_t(hq) * D;
   const uint16_t *Vc = args.v + tok_base * ldv + int64_t(h) * D;
-  float *ws = args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * ChunkArgs::ws_unit_floats(D);
-  float *wsW = ws, *wsU = ws + C * D, *wsP = ws + 2 * C * D;
-  double *wsG = reinterpret_cast<double *>(ws + 2 * C * D + C * C);
+  Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * ChunkArgs::ws_unit_floats(D));
 
-  // 1. gates and the fp64 inclusive prefix sum of g (tokens t >= n: g = beta = 0)
+  auto row_frag = [&](const uint16_t *base, int64_t ld, int t, int kb) -> float4 {
+    if (t >= n) return zf4();
+    return unpack_bf16x4(*reinterpret_cast<const uint2 *>(base + int64_t(t) * ld + 16 * kb + 4 * g4));
+  };
+
+  // 1. gates and the fp64 inclusive prefix sum of g (tokens t >= n: g = beta = 0);
+  //    K^T and V^T staged in LDS; K-row fragments of this wave's tiles loaded.
   if (w == 0) {
     float gf = 0.0f, bt = 0.0f;
     if (lane < n) {
@@ -126,133 +151,178 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     }
     sG[lane] = G;
     sBeta[lane] = bt;
+    sSK[lane] = bt * float(exp(G));
+    const double Gl = __shfl(G, n - 1, 64);
+    ws.G[lane] = G;
+    ws.eG[lane] = float(exp(G));
+    ws.eL[lane] = lane < n ? float(exp(Gl - G)) : 0.0f;
+  }
+  // Transposing stage: lane (m_lo, dg) of wave mh loads 4 dims of token
+  // m = 16 mh + m_lo, so the 16 lanes of a group write 16 consecutive columns of a
+  // K^T row and the 4 groups land on disjoint banks (row pitch 136 B).
+  {
+    const int m = 16 * w + (lane & 15), dg = lane >> 4;
+    for (int it = 0; it < D / 16; ++it) {
+      const int d4 = (4 * it + dg) * 4;
+      uint2 kw = make_uint2(0u, 0u), vw = kw;
+      if (m < n) {
+        kw = *reinterpret_cast<const uint2 *>(Kc + int64_t(m) * ldqk + d4);
+        vw = *reinterpret_cast<const uint2 *>(Vc + int64_t(m) * ldv + d4);
+      }
+      sKt[(d4 + 0) * LDB + m] = uint16_t(kw.x);
+      sKt[(d4 + 1) * LDB + m] = uint16_t(kw.x >> 16);
+      sKt[(d4 + 2) * LDB + m] = uint16_t(kw.y);
+      sKt[(d4 + 3) * LDB + m] = uint16_t(kw.y >> 16);
+      sVt[(d4 + 0) * LDB + m] = uint16_t(vw.x);
+      sVt[(d4 + 1) * LDB + m] = uint16_t(vw.x >> 16);
+      sVt[(d4 + 2) * LDB + m] = uint16_t(vw.y);
+      sVt[(d4 + 3) * LDB + m] = uint16_t(vw.y >> 16);
+    }
   }
   __syncthreads();
+  // K^T to the workspace for the scan kernel: row d is 64 contiguous bf16
+  for (int idx = tid; idx < D * (C / 4); idx += 256) {
+    const int d = idx / (C / 4), m4 = (idx % (C / 4)) * 4;
+    *reinterpret_cast<uint2 *>(ws.Kt + d * C + m4) = *reinterpret_cast<const uint2 *>(sKt + d * LDB + m4);
+  }
 
-  // 2. K K^T -> A (strictly lower, scaled), Q K^T -> P (lower with diagonal, scaled).
-  //    Wave w owns row tile w (tokens 16w..16w+15).
-  auto bf_rows = [&](const uint16_t *base, int64_t ld, int row0) {
-    return [=](int k) -> float4 {
-      const int t = row0 + r16;
-      if (t >= n) return make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      return unpack_bf16x4(*reinterpret_cast<const uint2 *>(base + int64_t(t) * ld + k));
-    };
-  };
-  for (int tj = 0; tj < C / 16; ++tj) {
+  // 2. K K^T -> A (strictly lower, scaled) and Q K^T -> P (lower with diagonal).
+  //    The 10 lower 16x16 tiles (ti >= tj) are dealt round-robin to the 4 waves.
+  for (int tile = w; tile < 10; tile += 4) {
+    int ti = 0;
+    while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
+    const int tj = tile - ti * (ti + 1) / 2;
+    float4 ak[NKB], aq[NKB], bk[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      ak[kb] = row_frag(Kc, ldqk, 16 * ti + r16, kb);
+      aq[kb] = row_frag(Qc, ldqk, 16 * ti + r16, kb);
+      bk[kb] = row_frag(Kc, ldqk, 16 * tj + r16, kb);
+    }
     floatx4 kk = zero4(), qk = zero4();
-    if (tj <= w) {
-      kk = mma(kk, D, bf_rows(Kc, ldqk, 16 * w), bf_rows(Kc, ldqk, 16 * tj));
-      qk = mma(qk, D, bf_rows(Qc, ldqk, 16 * w), bf_rows(Kc, ldqk, 16 * tj));
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      kk = mma4(kk, ak[kb], bk[kb]);
+      qk = mma4(qk, aq[kb], bk[kb]);
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int t = 16 * w + 4 * g4 + v, s = 16 * tj + r16;
+      const int t = 16 * ti + 4 * g4 + v, s = 16 * tj + r16;
       float av = 0.0f, pv = 0.0f;
       if (s <= t) {
-        const float dec = float(exp(sG[t] - sG[s]));
+        const float dec = expf(float(sG[t] - sG[s]));
         pv = dec * qk[v];
         if (s < t) av = sBeta[t] * dec * kk[v];
       }
       sA[t * LDC + s] = av;
-      wsP[t * C + s] = pv;
+      ws.P[t * C + s] = pv;
     }
   }
-  // 3. stage (diag(beta e^G) K)^T and (diag(beta) V)^T
-  for (int idx = tid; idx < C * (D / 4); idx += 256) {
-    const int m = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-    float4 kv = make_float4(0.0f, 0.0f, 0.0f, 0.0f), vv = kv;
-    float sk = 0.0f, sv = 0.0f;
-    if (m < n) {
-      kv = unpack_bf16x4(*reinterpret_cast<const uint2 *>(Kc + int64_t(m) * ldqk + d4));
-      vv = unpack_bf16x4(*reinterpret_cast<const uint2 *>(Vc + int64_t(m) * ldv + d4));
-      sv = sBeta[m];
-      sk = sv * float(exp(sG[m]));
+  for (int tile = w; tile < 6; tile += 4) {  // the 6 upper tiles are zero
+    int ti = 0, tj = 1;
+    for (int q = 0; q < tile; ++q) {
+      if (++tj == 4) { ++ti; tj = ti + 1; }
     }
-    sKt[(d4 + 0) * LDK + m] = kv.x * sk;
-    sKt[(d4 + 1) * LDK + m] = kv.y * sk;
-    sKt[(d4 + 2) * LDK + m] = kv.z * sk;
-    sKt[(d4 + 3) * LDK + m] = kv.w * sk;
-    sVt[(d4 + 0) * LDK + m] = vv.x * sv;
-    sVt[(d4 + 1) * LDK + m] = vv.y * sv;
-    sVt[(d4 + 2) * LDK + m] = vv.z * sv;
-    sVt[(d4 + 3) * LDK + m] = vv.w * sv;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = 16 * ti + 4 * g4 + v, s = 16 * tj + r16;
+      sA[t * LDC + s] = 0.0f;
+      ws.P[t * C + s] = 0.0f;
+    }
   }
   __syncthreads();
 
-  // 4. T = (I + A)^{-1} by forward substitution on one wave: lane j holds column j,
-  //    T[t][j] = [t == j] - sum_{m<t} A[t][m] T[m][j]  (A row t is a broadcast read)
+  // 3. T = (I + A)^{-1} by forward substitution on one wave: lane j holds column j,
+  //    T[t][j] = [t == j] - sum_{m<t} A[t][m] T[m][j]; A row t is read as broadcast
+  //    float4s and summed in four interleaved partial sums.
   if (w == 0) {
-    float Tc[C];
+    float Tc[C];  // T[t][lane], starting from the identity column
 #pragma unroll
-    for (int t = 0; t < C; ++t) {
-      float acc = (t == lane) ? 1.0f : 0.0f;
+    for (int t = 0; t < C; ++t) Tc[t] = (t == lane) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int m = 0; m < t; ++m) acc = fmaf(-sA[t * LDC + m], Tc[m], acc);
-      Tc[t] = acc;
+    for (int t = 1; t < C; ++t) {
+      float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+#pragma unroll
+      for (int m = 0; m < t; m += 4) {
+        const float4 ar = *reinterpret_cast<const float4 *>(sA + t * LDC + m);
+        p0 = fmaf(ar.x, Tc[m + 0], p0);
+        p1 = fmaf(ar.y, Tc[m + 1], p1);
+        p2 = fmaf(ar.z, Tc[m + 2], p2);
+        p3 = fmaf(ar.w, Tc[m + 3], p3);
+      }
+      Tc[t] -= (p0 + p1) + (p2 + p3);  // A[t][m] = 0 for m >= t, so the tail terms vanish
     }
 #pragma unroll
     for (int t = 0; t < C; ++t) sA[t * LDC + lane] = Tc[t];
   }
   __syncthreads();
 
-  // 5. W = T (diag(beta e^G) K), U' = T (diag(beta) V); wave w owns row tile w, and
-  //    T is lower triangular so only k < 16(w+1) contributes.
-  auto lds_rows = [&](const float *base, int ld, int row0) {
-    return [=](int k) -> float4 {
-      return *reinterpret_cast<const float4 *>(base + (row0 + r16) * ld + k);
-    };
-  };
-  for (int nt = 0; nt < D / 16; ++nt) {
-    const floatx4 wa = mma(zero4(), 16 * (w + 1), lds_rows(sA, LDC, 16 * w), lds_rows(sKt, LDK, 16 * nt));
-    const floatx4 ua = mma(zero4(), 16 * (w + 1), lds_rows(sA, LDC, 16 * w), lds_rows(sVt, LDK, 16 * nt));
+  // 4. W = T diag(beta e^G) K and U' = T diag(beta) V.  Wave w owns column tiles
+  //    {2w, 2w+1} of every row tile (T is lower triangular: k < 16(ti+1)).
+  for (int nt = 2 * w; nt < 2 * w + 2 && nt < D / 16; ++nt) {
+    for (int ti = 0; ti < 4; ++ti) {
+      floatx4 wa = zero4(), ua = zero4();
+      for (int kb = 0; kb <= ti; ++kb) {
+        const int k0 = 16 * kb + 4 * g4;
+        const float4 tr = *reinterpret_cast<const float4 *>(sA + (16 * ti + r16) * LDC + k0);
+        const float4 sk = *reinterpret_cast<const float4 *>(sSK + k0);
+        const float4 sb = *reinterpret_cast<const float4 *>(sBeta + k0);
+        const int d = 16 * nt + r16;
+        const float4 kt = unpack_bf16x4(*reinterpret_cast<const uint2 *>(sKt + d * LDB + k0));
+        const float4 vt = unpack_bf16x4(*reinterpret_cast<const uint2 *>(sVt + d * LDB + k0));
+        wa = mma4(wa, mul4(tr, sk), kt);
+        ua = mma4(ua, mul4(tr, sb), vt);
+      }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = 16 * w + 4 * g4 + v, d = 16 * nt + r16;
-      wsW[t * D + d] = wa[v];
-      wsU[t * D + d] = ua[v];
+      for (int v = 0; v < 4; ++v) {
+        const int t = 16 * ti + 4 * g4 + v, d = 16 * nt + r16;
+        ws.W[t * D + d] = wa[v];
+        ws.U[t * D + d] = ua[v];
+      }
     }
   }
-  if (tid < C) wsG[tid] = sG[tid];
 }
 
+// One block per CU at the sizes this serves (a few hundred (unit, tile) chains), so
+// a wave may use the whole register file: the operand fragments of a chunk stay live.
 template <int D>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs args) {
-  constexpr int LDS_ = D + 4, LDU = LDC, LDK = LDC;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void chunk_scan_kernel(ChunkArgs args, int n_units) {
+  constexpr int LDS_ = D + 4;
   constexpr int TILES = D / VT;
+  constexpr int NKB = D / 16;
+  constexpr int NT_W = (D / 16 + 3) / 4;  // state column tiles per wave
   constexpr size_t UNIT = size_t(D) * D;
-  __shared__ float sS[VT * LDS_];  // state tile: row i (value channel), column d
-  __shared__ float sUt[VT * LDU];  // U^T of this tile: row i, column token s
-  __shared__ float sKt[D * LDK];   // K^T of the chunk: row d, column token s
-  __shared__ double sG[C];
+  __shared__ __attribute__((aligned(16))) float sS[VT * LDS_];    // state tile: row i, column d
+  __shared__ __attribute__((aligned(16))) float sUt[VT * LDC];    // U^T of this tile: row i, token s
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  int bid = blockIdx.x;
-  const int tile = bid % TILES;
-  bid /= TILES;
-  const int h = bid % args.n_v;
-  const int row = bid / args.n_v;
+  // Blocks of one (row, head) unit are spaced 8 apart in launch order, which places
+  // all its tiles on one of the 8 chiplets and lets them share that L2's copy of the
+  // chunk operands (W, P, Q, K).
+  const int b = blockIdx.x;
+  const int k8 = b >> 3;
+  const int tile = k8 % TILES;
+  const int unit = (k8 / TILES) * 8 + (b & 7);
+  if (unit >= n_units) return;
+  const int h = unit % args.n_v;
+  const int row = unit / args.n_v;
   const int i0 = tile * VT;
   const int L = args.len[row];
   const int nch = (L + C - 1) / C;
   const int n_v = args.n_v, n_qk = args.n_qk, hq = h / args.group;
-  const int64_t ldqk = int64_t(n_qk) * D, ldv = int64_t(n_v) * D;
+  const int64_t ldqk = int64_t(n_qk) * D;
   const int src = args.src[row], dst = args.dst[row], n_tail = args.n_tail[row];
 
   for (int idx = tid; idx < VT * (D / 4); idx += 256) {
     const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-    float4 x = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float4 x = zf4();
     if (src >= 0)
       x = *reinterpret_cast<const float4 *>(args.state_in + (int64_t(src) * n_v + h) * UNIT +
                                             int64_t(i0 + i) * D + d4);
     *reinterpret_cast<float4 *>(sS + i * LDS_ + d4) = x;
   }
-
-  auto lds_rows = [&](const float *base, int ld, int row0) {
-    return [=](int k) -> float4 {
-      return *reinterpret_cast<const float4 *>(base + (row0 + r16) * ld + k);
-    };
-  };
 
   for (int c = 0; c < nch; ++c) {
     const int c0 = c * C;
@@ -260,100 +330,124 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs args) {
     const int64_t tok_base = int64_t(args.tok0[row]) + c0;
     const uint16_t *Kc = args.k + tok_base * ldqk + int64_t(hq) * D;
     const uint16_t *Qc = args.q + tok_base * ldqk + int64_t(hq) * D;
-    const float *ws = args.ws + (int64_t(args.chunk0[row] + c) * n_v + h) * ChunkArgs::ws_unit_floats(D);
-    const float *wsW = ws, *wsU = ws + C * D, *wsP = ws + 2 * C * D;
-    const double *wsG = reinterpret_cast<const double *>(ws + 2 * C * D + C * C);
+    Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + c) * n_v + h) * ChunkArgs::ws_unit_floats(D));
+    const int t_me = 16 * w + r16;  // token row this lane feeds as an A operand
 
-    for (int idx = tid; idx < C * (D / 4); idx += 256) {
-      const int m = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-      float4 kv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (m < n) kv = unpack_bf16x4(*reinterpret_cast<const uint2 *>(Kc + int64_t(m) * ldqk + d4));
-      sKt[(d4 + 0) * LDK + m] = kv.x;
-      sKt[(d4 + 1) * LDK + m] = kv.y;
-      sKt[(d4 + 2) * LDK + m] = kv.z;
-      sKt[(d4 + 3) * LDK + m] = kv.w;
+    // operand fragments of this chunk, all loads issued before any matrix work
+    float4 wf[NKB], qf[NKB], pf[4], el[4];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      wf[kb] = *reinterpret_cast<const float4 *>(ws.W + t_me * D + 16 * kb + 4 * g4);
+      qf[kb] = t_me < n ? unpack_bf16x4(*reinterpret_cast<const uint2 *>(
+                              Qc + int64_t(t_me) * ldqk + 16 * kb + 4 * g4))
+                        : zf4();
     }
-    if (tid < C) sG[tid] = wsG[tid];
-    __syncthreads();  // state tile, K^T and G of this chunk in place
-
-    // U = U' - W S_c^T for tokens 16w..16w+15 of this tile's 16 value channels
-    floatx4 u = mma(zero4(), D,
-                    [=](int k) { return *reinterpret_cast<const float4 *>(wsW + (16 * w + r16) * D + k); },
-                    lds_rows(sS, LDS_, 0));
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      pf[kb] = kb <= w ? *reinterpret_cast<const float4 *>(ws.P + t_me * C + 16 * kb + 4 * g4) : zf4();
+      el[kb] = *reinterpret_cast<const float4 *>(ws.eL + 16 * kb + 4 * g4);
+    }
+    float up[4], eg[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int t = 16 * w + 4 * g4 + v;
-      u[v] = wsU[t * D + i0 + r16] - u[v];
-      sUt[r16 * LDU + t] = u[v];
+      up[v] = ws.U[t * D + i0 + r16];
+      eg[v] = ws.eG[t];
     }
-    // O (first term) = e^{G_t} Q S_c^T
-    floatx4 o = mma(zero4(), D,
-                    [=](int k) -> float4 {
-                      const int t = 16 * w + r16;
-                      if (t >= n) return make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                      return unpack_bf16x4(*reinterpret_cast<const uint2 *>(Qc + int64_t(t) * ldqk + k));
-                    },
-                    lds_rows(sS, LDS_, 0));
+    const float e_last = ws.eG[n - 1];
+    // K^T fragments of this wave's state column tiles (B operand of the carry)
+    float4 kf[NT_W][4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) o[v] *= float(exp(sG[16 * w + 4 * g4 + v]));
+    for (int q = 0; q < NT_W; ++q) {
+      const int nt = w + 4 * q;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        kf[q][kb] = nt < D / 16 ? unpack_bf16x4(*reinterpret_cast<const uint2 *>(
+                                      ws.Kt + (16 * nt + r16) * C + 16 * kb + 4 * g4))
+                                : zf4();
+    }
+    __syncthreads();  // the state tile of this chunk is in place
+
+    // U = U' - W S_c^T and the first output term Q S_c^T share the B fragments
+    floatx4 ua = zero4(), oa = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float4 sb = *reinterpret_cast<const float4 *>(sS + r16 * LDS_ + 16 * kb + 4 * g4);
+      ua = mma4(ua, wf[kb], sb);
+      oa = mma4(oa, qf[kb], sb);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = 16 * w + 4 * g4 + v;
+      sUt[r16 * LDC + t] = up[v] - ua[v];
+      oa[v] *= eg[v];
+    }
     __syncthreads();  // U^T of the tile complete
 
-    // O += (Gamma o Q K^T) U: P is lower triangular, tokens s < 16(w+1)
-    o = mma(o, 16 * (w + 1),
-            [=](int k) { return *reinterpret_cast<const float4 *>(wsP + (16 * w + r16) * C + k); },
-            lds_rows(sUt, LDU, 0));
+    // O += (Gamma o Q K^T) U over tokens s < 16(w+1)
+    for (int kb = 0; kb <= w; ++kb)
+      oa = mma4(oa, pf[kb], *reinterpret_cast<const float4 *>(sUt + r16 * LDC + 16 * kb + 4 * g4));
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int t = 16 * w + 4 * g4 + v;
-      if (t < n) args.o[((tok_base + t) * n_v + h) * D + i0 + r16] = to_bf16(o[v]);
+      if (t < n) args.o[((tok_base + t) * n_v + h) * D + i0 + r16] = to_bf16(oa[v]);
     }
 
-    // State after in-chunk position j (0-based): e^{G_j} S_c + U^T diag(e^{G_j - G_s} [s <= j]) K.
-    // The A operand (U^T rows scaled per token) is built once and reused over column tiles.
-    auto state_at = [&](int j, float *out_regs /* [D/16/4 * 4] */) {
-      float4 af[C / 16];
+    // state after in-chunk position j: e^{G_j} S_c + U^T diag(scale) K, with
+    // scale_s = e^{G_j - G_s} for s <= j (else 0); columns {16 nt + r16} of the tile
+    auto state_at = [&](const float4 (&sc)[4], float ej, floatx4 (&out)[NT_W]) {
+      float4 af[4];
 #pragma unroll
-      for (int kb = 0; kb < C / 16; ++kb) {
-        const int s0 = 16 * kb + 4 * g4;
-        float4 x = *reinterpret_cast<const float4 *>(sUt + r16 * LDU + s0);
-        x.x *= (s0 + 0 <= j) ? float(exp(sG[j] - sG[s0 + 0])) : 0.0f;
-        x.y *= (s0 + 1 <= j) ? float(exp(sG[j] - sG[s0 + 1])) : 0.0f;
-        x.z *= (s0 + 2 <= j) ? float(exp(sG[j] - sG[s0 + 2])) : 0.0f;
-        x.w *= (s0 + 3 <= j) ? float(exp(sG[j] - sG[s0 + 3])) : 0.0f;
-        af[kb] = x;
-      }
-      const float ej = float(exp(sG[j]));
-      int q = 0;
-      for (int nt = w; nt < D / 16; nt += 4, ++q) {
-        floatx4 acc;
+      for (int kb = 0; kb < 4; ++kb)
+        af[kb] = mul4(*reinterpret_cast<const float4 *>(sUt + r16 * LDC + 16 * kb + 4 * g4), sc[kb]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = ej * sS[(4 * g4 + v) * LDS_ + 16 * nt + r16];
-        acc = mma(acc, C, [&](int k) { return af[k / 16]; }, lds_rows(sKt, LDK, 16 * nt));
+      for (int q = 0; q < NT_W; ++q) {
+        const int nt = w + 4 * q;
+        floatx4 acc = zero4();
+        if (nt < D / 16) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) out_regs[4 * q + v] = acc[v];
+          for (int v = 0; v < 4; ++v) acc[v] = ej * sS[(4 * g4 + v) * LDS_ + 16 * nt + r16];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) acc = mma4(acc, af[kb], kf[q][kb]);
+        }
+        out[q] = acc;
       }
     };
 
     for (int j = 0; j < n_tail; ++j) {
       const int p = L - n_tail + j;  // checkpoint slot j: state after p + 1 tokens
       if (p < c0 || p >= c0 + n) continue;
-      float ck[(D / 16 + 3) / 4 * 4];
-      state_at(p - c0, ck);
+      const int jj = p - c0;
+      float4 sc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int s0 = 16 * kb + 4 * g4;
+        sc[kb].x = s0 + 0 <= jj ? float(exp(ws.G[jj] - ws.G[s0 + 0])) : 0.0f;
+        sc[kb].y = s0 + 1 <= jj ? float(exp(ws.G[jj] - ws.G[s0 + 1])) : 0.0f;
+        sc[kb].z = s0 + 2 <= jj ? float(exp(ws.G[jj] - ws.G[s0 + 2])) : 0.0f;
+        sc[kb].w = s0 + 3 <= jj ? float(exp(ws.G[jj] - ws.G[s0 + 3])) : 0.0f;
+      }
+      floatx4 ck[NT_W];
+      state_at(sc, ws.eG[jj], ck);
       float *cdst = args.ckpt + ((int64_t(args.ck_row[row]) * args.ck_slots + j) * n_v + h) * UNIT;
-      int q = 0;
-      for (int nt = w; nt < D / 16; nt += 4, ++q)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          cdst[int64_t(i0 + 4 * g4 + v) * D + 16 * nt + r16] = ck[4 * q + v];
+      for (int q = 0; q < NT_W; ++q) {
+        const int nt = w + 4 * q;
+        if (nt < D / 16)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            cdst[int64_t(i0 + 4 * g4 + v) * D + 16 * nt + r16] = ck[q][v];
+      }
     }
-    float snew[(D / 16 + 3) / 4 * 4];
-    state_at(n - 1, snew);
-    __syncthreads();  // every read of sS / sUt / sKt for this chunk is done
-    {
-      int q = 0;
-      for (int nt = w; nt < D / 16; nt += 4, ++q)
+    floatx4 snew[NT_W];
+    state_at(el, e_last, snew);
+    __syncthreads();  // every read of sS / sUt for this chunk is done
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sS[(4 * g4 + v) * LDS_ + 16 * nt + r16] = snew[4 * q + v];
+    for (int q = 0; q < NT_W; ++q) {
+      const int nt = w + 4 * q;
+      if (nt < D / 16)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sS[(4 * g4 + v) * LDS_ + 16 * nt + r16] = snew[q][v];
     }
   }
   __syncthreads();
@@ -367,24 +461,24 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ChunkArgs args) {
   }
 }
 
+template <int D>
+hipError_t launch_d(const ChunkArgs &args, int n_chunks, hipStream_t stream) {
+  hipLaunchKernelGGL(chunk_prep_kernel<D>, dim3(unsigned(n_chunks), unsigned(args.n_v)), dim3(256), 0,
+                     stream, args);
+  const int n_units = args.n_rows * args.n_v;
+  const int groups = (n_units + 7) / 8;  // units are dealt to the 8 chiplets in groups of 8
+  hipLaunchKernelGGL(chunk_scan_kernel<D>, dim3(unsigned(groups * 8 * (D / VT))), dim3(256), 0, stream,
+                     args, n_units);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_chunked(const ChunkArgs &args, int d, int n_chunks, hipStream_t stream) {
   if (args.n_rows <= 0 || n_chunks <= 0) return hipSuccess;
-  if (d == 128) {
-    hipLaunchKernelGGL(chunk_prep_kernel<128>, dim3(unsigned(n_chunks), unsigned(args.n_v)), dim3(256),
-                       0, stream, args);
-    hipLaunchKernelGGL(chunk_scan_kernel<128>, dim3(unsigned(args.n_rows * args.n_v * (128 / VT))),
-                       dim3(256), 0, stream, args);
-  } else if (d == 16) {
-    hipLaunchKernelGGL(chunk_prep_kernel<16>, dim3(unsigned(n_chunks), unsigned(args.n_v)), dim3(256),
-                       0, stream, args);
-    hipLaunchKernelGGL(chunk_scan_kernel<16>, dim3(unsigned(args.n_rows * args.n_v * (16 / VT))),
-                       dim3(256), 0, stream, args);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (d == 128) return launch_d<128>(args, n_chunks, stream);
+  if (d == 16) return launch_d<16>(args, n_chunks, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gdn
