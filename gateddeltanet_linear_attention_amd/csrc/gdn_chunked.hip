@@ -18,12 +18,18 @@
 // rollback needs (the gap named in the onnxruntime-genai pull request "Run chained
 // MTP drafting in the batch Engine", section "Correctness fix").
 //
-// Two kernels, same stream:
+// Four kernels, same stream:
 //   chunk_prep_kernel  one block per (chunk, value head), all chunks in parallel:
 //       gates, fp64 prefix sum of g, K K^T and Q K^T, forward substitution for T,
-//       W, U' and the decay factors -> workspace.
+//       W, U', K^T and the decay factors -> workspace.
 //   chunk_scan_kernel  one block per (row, value head, 16 state rows), chunks in
-//       order: U, outputs, tail checkpoints, state carry (state tile stays in LDS).
+//       order, only the sequential part: U = U' - W S_c^T and the state carry (the
+//       state tile stays in LDS; the next chunk's operands are fetched during the
+//       current one); each chunk's start state and U^T -> workspace.
+//   chunk_out_kernel   one block per (chunk, value head, half of the value
+//       channels), all in parallel: the outputs O.
+//   chunk_ckpt_kernel  one block per (row, tail checkpoint, value head, 16 value
+//       rows): the requested checkpoints, from the recorded chunk state.
 // Every contraction runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, 157 TF
 // dense on MI355X): the state tolerance (relative 1e-4) rules out rounding the fp32
 // operands T, W, U, S to bf16.  A wave loads all operand fragments of a product
@@ -34,6 +40,7 @@
 // fp32 sums would lose ~1e-5 relative).
 #include <hip/hip_runtime.h>
 
+#include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -45,18 +52,6 @@ constexpr int LDC = C + 4;  // padded LDS row length (floats) for C-wide rows
 constexpr int LDB = C + 4;  // padded LDS row length (bf16) for C-wide rows
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float4 unpack_bf16x4(uint2 w) {
-  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
-}
-
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.0f, 0.0f, 0.0f, 0.0f}; }
 __device__ __forceinline__ float4 zf4() { return make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
@@ -85,10 +80,11 @@ __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
 }
 
 // Workspace of one (chunk, value head): W [C][D], U' [C][D], P [C][C], G [C] fp64,
-// eG[t] = e^{G_t}, eL[s] = e^{G_{n-1} - G_s} (s < n, else 0), and K^T [D][C] bf16.
+// eG[t] = e^{G_t}, eL[s] = e^{G_{n-1} - G_s} (s < n, else 0), K^T [D][C] bf16, the
+// chunk's start state Sc [D][D] and U^T [D][C].
 template <int D>
 struct Ws {
-  float *W, *U, *P, *eG, *eL;
+  float *W, *U, *P, *eG, *eL, *Sc, *Ut;
   double *G;
   uint16_t *Kt;
   __device__ Ws(float *base) {
@@ -99,6 +95,8 @@ struct Ws {
     eG = base + 2 * C * D + C * C + 2 * C;
     eL = eG + C;
     Kt = reinterpret_cast<uint16_t *>(eL + C);
+    Sc = eL + C + D * C / 2;
+    Ut = Sc + D * D;
   }
 };
 
@@ -179,7 +177,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
       sVt[(d4 + 3) * LDB + m] = uint16_t(vw.y >> 16);
     }
   }
-  __syncthreads();
+  lds_barrier();
   // K^T to the workspace for the scan kernel: row d is 64 contiguous bf16
   for (int idx = tid; idx < D * (C / 4); idx += 256) {
     const int d = idx / (C / 4), m4 = (idx % (C / 4)) * 4;
@@ -230,7 +228,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
       ws.P[t * C + s] = 0.0f;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // 3. T = (I + A)^{-1} by forward substitution on one wave: lane j holds column j,
   //    T[t][j] = [t == j] - sum_{m<t} A[t][m] T[m][j]; A row t is read as broadcast
@@ -255,7 +253,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
 #pragma unroll
     for (int t = 0; t < C; ++t) sA[t * LDC + lane] = Tc[t];
   }
-  __syncthreads();
+  lds_barrier();
 
   // 4. W = T diag(beta e^G) K and U' = T diag(beta) V.  Wave w owns column tiles
   //    {2w, 2w+1} of every row tile (T is lower triangular: k < 16(ti+1)).
@@ -283,8 +281,41 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   }
 }
 
+// Operands of one chunk that a scan wave needs: its W rows, its U' values, the
+// carry's decay factors and the K^T fragments of its state column tiles.
+template <int D>
+struct ScanFrag {
+  static constexpr int NKB = D / 16;
+  static constexpr int NT_W = (D / 16 + 3) / 4;
+  float4 wf[NKB], el[4], kf[NT_W][4];
+  float up[4];
+  float e_last;
+  __device__ void load(const Ws<D> &ws, int n, int w, int r16, int g4, int i0) {
+    const int t_me = 16 * w + r16;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      wf[kb] = *reinterpret_cast<const float4 *>(ws.W + t_me * D + 16 * kb + 4 * g4);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) el[kb] = *reinterpret_cast<const float4 *>(ws.eL + 16 * kb + 4 * g4);
+#pragma unroll
+    for (int q = 0; q < NT_W; ++q) {
+      // a wave without a q-th column tile loads the last tile and never uses it:
+      // unconditional loads keep the prefetch free of branches, whose waits would
+      // expose its latency
+      const int nt = min(w + 4 * q, D / 16 - 1);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        kf[q][kb] = unpack_bf16x4(
+            *reinterpret_cast<const uint2 *>(ws.Kt + (16 * nt + r16) * C + 16 * kb + 4 * g4));
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) up[v] = ws.U[(16 * w + 4 * g4 + v) * D + i0 + r16];
+    e_last = ws.eG[n - 1];
+  }
+};
+
 // One block per CU at the sizes this serves (a few hundred (unit, tile) chains), so
-// a wave may use the whole register file: the operand fragments of a chunk stay live.
+// a wave may use the whole register file: two chunks' operands stay live.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunk_scan_kernel(ChunkArgs args, int n_units) {
@@ -293,14 +324,14 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
   constexpr int NKB = D / 16;
   constexpr int NT_W = (D / 16 + 3) / 4;  // state column tiles per wave
   constexpr size_t UNIT = size_t(D) * D;
-  __shared__ __attribute__((aligned(16))) float sS[VT * LDS_];    // state tile: row i, column d
-  __shared__ __attribute__((aligned(16))) float sUt[VT * LDC];    // U^T of this tile: row i, token s
+  __shared__ __attribute__((aligned(16))) float sS[VT * LDS_];  // state tile: row i, column d
+  __shared__ __attribute__((aligned(16))) float sUt[VT * LDC];  // U^T of this tile: row i, token s
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   // Blocks of one (row, head) unit are spaced 8 apart in launch order, which places
   // all its tiles on one of the 8 chiplets and lets them share that L2's copy of the
-  // chunk operands (W, P, Q, K).
+  // chunk operands (W, K^T).
   const int b = blockIdx.x;
   const int k8 = b >> 3;
   const int tile = k8 % TILES;
@@ -311,9 +342,11 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
   const int i0 = tile * VT;
   const int L = args.len[row];
   const int nch = (L + C - 1) / C;
-  const int n_v = args.n_v, n_qk = args.n_qk, hq = h / args.group;
-  const int64_t ldqk = int64_t(n_qk) * D;
-  const int src = args.src[row], dst = args.dst[row], n_tail = args.n_tail[row];
+  const int n_v = args.n_v;
+  const int src = args.src[row], dst = args.dst[row];
+  auto ws_of = [&](int c) {
+    return Ws<D>(args.ws + (int64_t(args.chunk0[row] + c) * n_v + h) * ChunkArgs::ws_unit_floats(D));
+  };
 
   for (int idx = tid; idx < VT * (D / 4); idx += 256) {
     const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
@@ -324,124 +357,54 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
     *reinterpret_cast<float4 *>(sS + i * LDS_ + d4) = x;
   }
 
-  for (int c = 0; c < nch; ++c) {
-    const int c0 = c * C;
-    const int n = min(C, L - c0);
-    const int64_t tok_base = int64_t(args.tok0[row]) + c0;
-    const uint16_t *Kc = args.k + tok_base * ldqk + int64_t(hq) * D;
-    const uint16_t *Qc = args.q + tok_base * ldqk + int64_t(hq) * D;
-    Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + c) * n_v + h) * ChunkArgs::ws_unit_floats(D));
-    const int t_me = 16 * w + r16;  // token row this lane feeds as an A operand
+  // One chunk of the recurrence with its operand fragments f.
+  auto body = [&](int c, const ScanFrag<D> &f) {
+    const Ws<D> ws = ws_of(c);
+    lds_barrier();  // the state tile of this chunk is in place
 
-    // operand fragments of this chunk, all loads issued before any matrix work
-    float4 wf[NKB], qf[NKB], pf[4], el[4];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      wf[kb] = *reinterpret_cast<const float4 *>(ws.W + t_me * D + 16 * kb + 4 * g4);
-      qf[kb] = t_me < n ? unpack_bf16x4(*reinterpret_cast<const uint2 *>(
-                              Qc + int64_t(t_me) * ldqk + 16 * kb + 4 * g4))
-                        : zf4();
+    // record S_c for the output and checkpoint kernels
+    for (int idx = tid; idx < VT * (D / 4); idx += 256) {
+      const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+      *reinterpret_cast<float4 *>(ws.Sc + int64_t(i0 + i) * D + d4) =
+          *reinterpret_cast<const float4 *>(sS + i * LDS_ + d4);
     }
+    // U = U' - W S_c^T for tokens 16w..16w+15 of this tile's 16 value channels,
+    // in two interleaved partial chains
+    floatx4 ua = zero4(), ub = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      pf[kb] = kb <= w ? *reinterpret_cast<const float4 *>(ws.P + t_me * C + 16 * kb + 4 * g4) : zf4();
-      el[kb] = *reinterpret_cast<const float4 *>(ws.eL + 16 * kb + 4 * g4);
+    for (int kb = 0; kb < NKB; kb += 2) {
+      ua = mma4(ua, f.wf[kb], *reinterpret_cast<const float4 *>(sS + r16 * LDS_ + 16 * kb + 4 * g4));
+      if (kb + 1 < NKB)
+        ub = mma4(ub, f.wf[kb + 1], *reinterpret_cast<const float4 *>(sS + r16 * LDS_ + 16 * (kb + 1) + 4 * g4));
     }
-    float up[4], eg[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int t = 16 * w + 4 * g4 + v;
-      up[v] = ws.U[t * D + i0 + r16];
-      eg[v] = ws.eG[t];
+      const float u = f.up[v] - (ua[v] + ub[v]);
+      sUt[r16 * LDC + t] = u;
+      ws.Ut[(i0 + r16) * C + t] = u;
     }
-    const float e_last = ws.eG[n - 1];
-    // K^T fragments of this wave's state column tiles (B operand of the carry)
-    float4 kf[NT_W][4];
+    lds_barrier();  // U^T of the tile complete
+
+    // S_{c+1} = e^{G_n} S_c + U^T diag(e^{G_n - G}) K on this wave's column tiles
+    float4 af[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      af[kb] = mul4(*reinterpret_cast<const float4 *>(sUt + r16 * LDC + 16 * kb + 4 * g4), f.el[kb]);
+    floatx4 snew[NT_W];
 #pragma unroll
     for (int q = 0; q < NT_W; ++q) {
       const int nt = w + 4 * q;
+      floatx4 acc = zero4();
+      if (nt < D / 16) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        kf[q][kb] = nt < D / 16 ? unpack_bf16x4(*reinterpret_cast<const uint2 *>(
-                                      ws.Kt + (16 * nt + r16) * C + 16 * kb + 4 * g4))
-                                : zf4();
-    }
-    __syncthreads();  // the state tile of this chunk is in place
-
-    // U = U' - W S_c^T and the first output term Q S_c^T share the B fragments
-    floatx4 ua = zero4(), oa = zero4();
+        for (int v = 0; v < 4; ++v) acc[v] = f.e_last * sS[(4 * g4 + v) * LDS_ + 16 * nt + r16];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const float4 sb = *reinterpret_cast<const float4 *>(sS + r16 * LDS_ + 16 * kb + 4 * g4);
-      ua = mma4(ua, wf[kb], sb);
-      oa = mma4(oa, qf[kb], sb);
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = 16 * w + 4 * g4 + v;
-      sUt[r16 * LDC + t] = up[v] - ua[v];
-      oa[v] *= eg[v];
-    }
-    __syncthreads();  // U^T of the tile complete
-
-    // O += (Gamma o Q K^T) U over tokens s < 16(w+1)
-    for (int kb = 0; kb <= w; ++kb)
-      oa = mma4(oa, pf[kb], *reinterpret_cast<const float4 *>(sUt + r16 * LDC + 16 * kb + 4 * g4));
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = 16 * w + 4 * g4 + v;
-      if (t < n) args.o[((tok_base + t) * n_v + h) * D + i0 + r16] = to_bf16(oa[v]);
-    }
-
-    // state after in-chunk position j: e^{G_j} S_c + U^T diag(scale) K, with
-    // scale_s = e^{G_j - G_s} for s <= j (else 0); columns {16 nt + r16} of the tile
-    auto state_at = [&](const float4 (&sc)[4], float ej, floatx4 (&out)[NT_W]) {
-      float4 af[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        af[kb] = mul4(*reinterpret_cast<const float4 *>(sUt + r16 * LDC + 16 * kb + 4 * g4), sc[kb]);
-#pragma unroll
-      for (int q = 0; q < NT_W; ++q) {
-        const int nt = w + 4 * q;
-        floatx4 acc = zero4();
-        if (nt < D / 16) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[v] = ej * sS[(4 * g4 + v) * LDS_ + 16 * nt + r16];
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) acc = mma4(acc, af[kb], kf[q][kb]);
-        }
-        out[q] = acc;
+        for (int kb = 0; kb < 4; ++kb) acc = mma4(acc, af[kb], f.kf[q][kb]);
       }
-    };
-
-    for (int j = 0; j < n_tail; ++j) {
-      const int p = L - n_tail + j;  // checkpoint slot j: state after p + 1 tokens
-      if (p < c0 || p >= c0 + n) continue;
-      const int jj = p - c0;
-      float4 sc[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int s0 = 16 * kb + 4 * g4;
-        sc[kb].x = s0 + 0 <= jj ? float(exp(ws.G[jj] - ws.G[s0 + 0])) : 0.0f;
-        sc[kb].y = s0 + 1 <= jj ? float(exp(ws.G[jj] - ws.G[s0 + 1])) : 0.0f;
-        sc[kb].z = s0 + 2 <= jj ? float(exp(ws.G[jj] - ws.G[s0 + 2])) : 0.0f;
-        sc[kb].w = s0 + 3 <= jj ? float(exp(ws.G[jj] - ws.G[s0 + 3])) : 0.0f;
-      }
-      floatx4 ck[NT_W];
-      state_at(sc, ws.eG[jj], ck);
-      float *cdst = args.ckpt + ((int64_t(args.ck_row[row]) * args.ck_slots + j) * n_v + h) * UNIT;
-#pragma unroll
-      for (int q = 0; q < NT_W; ++q) {
-        const int nt = w + 4 * q;
-        if (nt < D / 16)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            cdst[int64_t(i0 + 4 * g4 + v) * D + 16 * nt + r16] = ck[q][v];
-      }
+      snew[q] = acc;
     }
-    floatx4 snew[NT_W];
-    state_at(el, e_last, snew);
-    __syncthreads();  // every read of sS / sUt for this chunk is done
+    lds_barrier();  // every read of sS / sUt for this chunk is done
 #pragma unroll
     for (int q = 0; q < NT_W; ++q) {
       const int nt = w + 4 * q;
@@ -449,8 +412,24 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) sS[(4 * g4 + v) * LDS_ + 16 * nt + r16] = snew[q][v];
     }
+  };
+  auto frag_load = [&](ScanFrag<D> &f, int c) {
+    c = min(c, nch - 1);  // past the end: reload the last chunk, never read
+    f.load(ws_of(c), min(C, L - c * C), w, r16, g4, i0);
+  };
+
+  // Chunks in pairs with two fragment sets: the next chunk's operands are in flight
+  // while this chunk's products run.
+  ScanFrag<D> fa, fb;
+  frag_load(fa, 0);
+  for (int c = 0; c < nch; c += 2) {
+    frag_load(fb, c + 1);
+    body(c, fa);
+    if (c + 1 >= nch) break;
+    frag_load(fa, c + 2);
+    body(c + 1, fb);
   }
-  __syncthreads();
+  lds_barrier();
   if (dst >= 0) {
     for (int idx = tid; idx < VT * (D / 4); idx += 256) {
       const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
@@ -458,6 +437,127 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
                                   int64_t(i0 + i) * D + d4) =
           *reinterpret_cast<const float4 *>(sS + i * LDS_ + d4);
     }
+  }
+}
+
+// Outputs of one (chunk, value head, half of the value channels), from the chunk's
+// start state S_c and U recorded by the scan: O = diag(e^G) Q S_c^T + P U (wave w:
+// tokens 16w..16w+15).
+template <int D>
+__global__ __launch_bounds__(256) void chunk_out_kernel(ChunkArgs args) {
+  constexpr int NKB = D / 16;
+  constexpr int NH = D / 16 >= 2 ? 2 : 1;  // value-channel parts per chunk
+  constexpr int NTP = D / 16 / NH;        // 16-wide column tiles per part
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int cl = blockIdx.x, h = blockIdx.y, part = blockIdx.z;
+  const int row = row_of_chunk(args, cl);
+  const int cin = cl - args.chunk_start[row];
+  const int c0 = cin * C;
+  const int n = min(C, args.len[row] - c0);
+  const int64_t tok_base = int64_t(args.tok0[row]) + c0;
+  const int n_v = args.n_v, n_qk = args.n_qk, hq = h / args.group;
+  const int64_t ldqk = int64_t(n_qk) * D;
+  const Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * ChunkArgs::ws_unit_floats(D));
+
+  const int t_me = 16 * w + r16;
+  const uint16_t *Qc = args.q + tok_base * ldqk + int64_t(hq) * D;
+  float4 qf[NKB], pf[4];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+    qf[kb] = t_me < n ? unpack_bf16x4(*reinterpret_cast<const uint2 *>(Qc + int64_t(t_me) * ldqk + 16 * kb + 4 * g4))
+                      : zf4();
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    pf[kb] = kb <= w ? *reinterpret_cast<const float4 *>(ws.P + t_me * C + 16 * kb + 4 * g4) : zf4();
+  float eg[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) eg[v] = ws.eG[16 * w + 4 * g4 + v];
+  // B fragments of column tile nt (S_c rows and U^T rows), all loaded up front
+  float4 sf[NTP][NKB], uf[NTP][4];
+#pragma unroll
+  for (int q = 0; q < NTP; ++q) {
+    const int i = 16 * (part * NTP + q) + r16;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      sf[q][kb] = *reinterpret_cast<const float4 *>(ws.Sc + int64_t(i) * D + 16 * kb + 4 * g4);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      uf[q][kb] = kb <= w ? *reinterpret_cast<const float4 *>(ws.Ut + i * C + 16 * kb + 4 * g4) : zf4();
+  }
+#pragma unroll
+  for (int q = 0; q < NTP; ++q) {
+    const int i = 16 * (part * NTP + q) + r16;
+    floatx4 oa = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) oa = mma4(oa, qf[kb], sf[q][kb]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) oa[v] *= eg[v];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      if (kb <= w) oa = mma4(oa, pf[kb], uf[q][kb]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = 16 * w + 4 * g4 + v;
+      if (t < n) args.o[((tok_base + t) * n_v + h) * D + i] = to_bf16(oa[v]);
+    }
+  }
+}
+
+// Tail checkpoint j of a row, 16 value rows (tile mi) of one head per block, from
+// the start state S_c and U of the chunk that holds its position p (j' = p - c0):
+// S_p = e^{G_j'} S_c + U^T diag(e^{G_j' - G_s} [s <= j']) K.  Wave w computes the
+// column tiles {2w, 2w+1}.
+template <int D>
+__global__ __launch_bounds__(256) void chunk_ckpt_kernel(ChunkArgs args) {
+  constexpr size_t UNIT = size_t(D) * D;
+  constexpr int MT = D / 16;
+  __shared__ __attribute__((aligned(16))) float sScale[C];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  int b = blockIdx.x;
+  const int mi = b % MT;
+  b /= MT;
+  const int h = b % args.n_v;
+  b /= args.n_v;
+  const int j = b % args.ck_slots;
+  const int row = b / args.ck_slots;
+  const int n_tail = args.n_tail[row];
+  if (j >= n_tail) return;
+  const int L = args.len[row];
+  const int p = L - n_tail + j;  // checkpoint slot j: state after p + 1 tokens
+  const int cin = p / C;
+  const int jj = p - cin * C;
+  const int n_v = args.n_v;
+  const Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * ChunkArgs::ws_unit_floats(D));
+  // scale_s = e^{G_j' - G_s} for s <= j' (else 0, a select so an overflowed
+  // exponential on the masked side cannot become a NaN), rounded exactly as the
+  // carry's factors, so the checkpoint at a row's last position is bit-identical
+  // to the final state the scan publishes
+  if (w == 0) sScale[lane] = lane <= jj ? float(exp(ws.G[jj] - ws.G[lane])) : 0.0f;
+  lds_barrier();
+  float4 af[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    af[kb] = mul4(*reinterpret_cast<const float4 *>(ws.Ut + (16 * mi + r16) * C + 16 * kb + 4 * g4),
+                  *reinterpret_cast<const float4 *>(sScale + 16 * kb + 4 * g4));
+  const float ej = ws.eG[jj];
+  float *cdst = args.ckpt + ((int64_t(args.ck_row[row]) * args.ck_slots + j) * n_v + h) * UNIT;
+  for (int nt = 2 * w; nt < 2 * w + 2 && nt < D / 16; ++nt) {
+    float4 kf[4];
+    float sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      kf[kb] = unpack_bf16x4(*reinterpret_cast<const uint2 *>(ws.Kt + (16 * nt + r16) * C + 16 * kb + 4 * g4));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sc[v] = ws.Sc[int64_t(16 * mi + 4 * g4 + v) * D + 16 * nt + r16];
+    floatx4 acc;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = ej * sc[v];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc = mma4(acc, af[kb], kf[kb]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) cdst[int64_t(16 * mi + 4 * g4 + v) * D + 16 * nt + r16] = acc[v];
   }
 }
 
@@ -469,6 +569,13 @@ hipError_t launch_d(const ChunkArgs &args, int n_chunks, hipStream_t stream) {
   const int groups = (n_units + 7) / 8;  // units are dealt to the 8 chiplets in groups of 8
   hipLaunchKernelGGL(chunk_scan_kernel<D>, dim3(unsigned(groups * 8 * (D / VT))), dim3(256), 0, stream,
                      args, n_units);
+  hipLaunchKernelGGL(chunk_out_kernel<D>, dim3(unsigned(n_chunks), unsigned(args.n_v), unsigned(D / 16 >= 2 ? 2 : 1)),
+                     dim3(256), 0, stream, args);
+  int any_tail = 0;
+  for (int r = 0; r < args.n_rows; ++r) any_tail |= args.n_tail[r];
+  if (any_tail)
+    hipLaunchKernelGGL(chunk_ckpt_kernel<D>, dim3(unsigned(args.n_rows * args.ck_slots * args.n_v * (D / 16))),
+                       dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -60,10 +60,11 @@ struct CommitArgs {
 constexpr int kChunk = 64;
 
 // Workspace floats per (chunk, value head): W [64][d], U' [64][d], P [64][64],
-// the 64 fp64 prefix sums of the log-decay, two 64-float decay vectors, and K^T
-// [d][64] in bf16.
+// the 64 fp64 prefix sums of the log-decay, two 64-float decay vectors, K^T
+// [d][64] in bf16, the chunk's start state [d][d] and U^T [d][64].
 constexpr int64_t chunk_ws_unit_floats(int d) {
-  return 2 * int64_t(kChunk) * d + int64_t(kChunk) * kChunk + 4 * kChunk + int64_t(d) * kChunk / 2;
+  return 2 * int64_t(kChunk) * d + int64_t(kChunk) * kChunk + 4 * kChunk + int64_t(d) * kChunk / 2 +
+         int64_t(d) * d + int64_t(d) * kChunk;
 }
 
 struct ChunkArgs {

@@ -31,21 +31,11 @@
 // -ffp-contract=off; every fused multiply-add is an explicit fmaf.
 #include <hip/hip_runtime.h>
 
+#include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
 
 // fp32 gates: alpha = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b),
 // softplus(x) = max(x, 0) + log1p(exp(-|x|)) (no overflow for any x).
@@ -161,7 +151,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
       eval_gates(args.a[tok * n_v + h], args.b[tok * n_v + h], args.A_log[h], args.dt_bias[h],
                  sAlpha[tid], sBeta[tid]);
     }
-    __syncthreads();
+    lds_barrier();
 
 #pragma unroll 1
     for (int t = 0; t < nb; ++t) {
@@ -209,7 +199,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
         }
       }
     }
-    __syncthreads();  // the next batch overwrites the staged inputs
+    lds_barrier();  // the next batch overwrites the staged inputs
     for (int x = tid; x < nb * ROWS; x += 64 * WAVES) {
       const int t = x / ROWS, rr = x % ROWS;
       args.o[((size_t(tok0) + t0 + t) * n_v + h) * D + tile * ROWS + rr] = sO[t][rr];

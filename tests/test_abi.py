@@ -179,7 +179,7 @@ def test_chunked_and_transaction_validation_codes():
     b = Bufs()
     d = _dims()
     need = gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100, 64, 1])
-    assert need == (2 + 1 + 1) * 32 * (2 * 64 * 128 + 64 * 64 + 256 + 128 * 32) * 4
+    assert need == (2 + 1 + 1) * 32 * (2 * 64 * 128 + 64 * 64 + 256 + 128 * 32 + 128 * 128 + 128 * 64) * 4
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100], chunk=32) == 0
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [0]) == 0
 
