@@ -38,13 +38,14 @@ STATE_BYTES = 128 * 128 * 4          # one value head's fp32 state
 TOKEN_BYTES = 776                    # per head-token: q,k (shared by 2 v-heads) 256 + v 256 + a,b 8 + o 256
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_conc16_k3_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gateddeltanet_linear_attention_amd", "csrc", f)
-                  for f in ("gdn_recurrent.hip", "gdn_internal.h")]
+                  for f in ("gdn_recurrent.hip", "gdn_internal.h", "gdn_device.h")]
+V_HEADS = 32
 
 
-def verify_bytes(n_units: int, T: int) -> int:
+def verify_bytes(row_tokens) -> int:
     """Algorithmic HBM bytes of one verify launch: per (row, v-head) unit, read the
-    committed state once, write T checkpoints, and move 776 B of token I/O per token."""
-    return n_units * ((1 + T) * STATE_BYTES + TOKEN_BYTES * T)
+    committed state once, write T_r checkpoints, and move 776 B of token I/O per token."""
+    return sum(V_HEADS * ((1 + int(T)) * STATE_BYTES + TOKEN_BYTES * int(T)) for T in row_tokens)
 
 
 def commit_bytes(n_units: int) -> int:
@@ -76,15 +77,17 @@ class VerifySet:
     """One buffer set: state pool, checkpoints, a window of tokens, accepted counts,
     and the two prepared C-ABI calls of a step."""
 
-    def __init__(self, gb, synth, dims, B, T, seed, stream):
+    def __init__(self, gb, synth, dims, Ts, seed, stream):
         import numpy as np
         import torch
         shape = synth.FULL
         Hv, d = shape.n_v_heads, shape.d
+        Ts = np.asarray(Ts, np.int32)
+        B, N = int(Ts.size), int(Ts.sum())
         g = synth.streams(seed, 3)
         A_log, dt_bias = synth.head_params(g[0], shape)
-        tok = synth.tokens(g[1], shape, B * T)
-        acc = synth.accepted_counts(g[2], np.full(B, T - 1))
+        tok = synth.tokens(g[1], shape, N)
+        acc = synth.accepted_counts(g[2], Ts - 1)
         dev = "cuda"
         self.t = dict(q=torch.from_numpy(tok.q).to(torch.bfloat16).to(dev),
                       k=torch.from_numpy(tok.k).to(torch.bfloat16).to(dev),
@@ -94,11 +97,10 @@ class VerifySet:
         gen = torch.Generator(device="cpu").manual_seed(seed)
         self.pool = (0.05 * torch.randn(B, Hv, d, d, generator=gen)).to(dev)
         self.ckpt = torch.empty(B, 4, Hv, d, d, device=dev)
-        self.o = torch.empty(B * T, Hv, d, dtype=torch.bfloat16, device=dev)
+        self.o = torch.empty(N, Hv, d, dtype=torch.bfloat16, device=dev)
         self.acc = torch.from_numpy(acc).to(dev)
         self.status = torch.zeros((B + 31) // 32, dtype=torch.int32, device=dev)
         rows = np.arange(B, dtype=np.int32)
-        Ts = np.full(B, T, np.int32)
         self.verify = gb.prepare_verify_window(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
                                                ckpt=self.ckpt, o=self.o, stream=stream)
         self.commit = gb.prepare_commit_accepted(dims, Ts, self.ckpt, self.acc, self.pool, dst_slot=rows,
@@ -110,8 +112,8 @@ class VerifySet:
 def run_steps(layers, steps, warmup, stream, torch):
     """Warm-up, then `steps` timed steps, bracketed by synchronisation.  A step runs
     every layer's verify back to back, then every layer's commit.  Events recorded
-    on the launch stream around each step's run of verify launches give the mean
-    verify launch duration (their span / L)."""
+    on the launch stream around each step's run of verify launches, and of commit
+    launches, give the mean launch durations (their span / L)."""
     def step():
         for s in layers:
             s.verify()
@@ -120,8 +122,7 @@ def run_steps(layers, steps, warmup, stream, torch):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
@@ -130,36 +131,53 @@ def run_steps(layers, steps, warmup, stream, torch):
         ev[i][1].record(stream)
         for s in layers:
             s.commit()
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    verify_ms = [a.elapsed_time(b) / len(layers) for a, b in ev]
-    return wall, verify_ms
+    verify_ms = [a.elapsed_time(b) / len(layers) for a, b, _ in ev]
+    commit_ms = [b.elapsed_time(c) / len(layers) for _, b, c in ev]
+    return wall, verify_ms, commit_ms
 
 
-def cpu_baseline(s: "VerifySet", seconds: float):
+def cpu_baseline(s: "VerifySet", seconds: float, seconds_1thread: float):
     """The fp64 oracle on the host, on the same window as the GPU step (a bounded
-    sample: repeated windows for about `seconds` of work)."""
+    sample: repeated windows for about `seconds` of work), with every host core the
+    oracle uses and again on one thread."""
     import numpy as np
     import oracle
     tok = s.tok
     S0 = s.pool.double().cpu().numpy()
     out = dict(S_final=np.zeros(S0.shape), ckpt=np.zeros((s.B, 4) + S0.shape[1:]),
                o=np.zeros((int(s.T.sum()),) + S0.shape[1:3]))
-    oracle.verify_window(s.T, tok.q, tok.k, tok.v, tok.a, tok.b, s.A_log, s.dt_bias, S0,
-                         nan_fill=False, out=out)  # first touch of the buffers, untimed
-    n, t0 = 0, time.perf_counter()
-    while True:
+
+    def rate(budget, n_threads):
         oracle.verify_window(s.T, tok.q, tok.k, tok.v, tok.a, tok.b, s.A_log, s.dt_bias, S0,
-                             nan_fill=False, out=out)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    upd = n * int(s.T.sum()) * S0.shape[1]
-    return {"value": upd / el, "unit": "head-token updates/s", "cores": oracle.threads_used(),
+                             n_threads=n_threads, nan_fill=False, out=out)  # untimed first pass
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.verify_window(s.T, tok.q, tok.k, tok.v, tok.a, tok.b, s.A_log, s.dt_bias, S0,
+                                 n_threads=n_threads, nan_fill=False, out=out)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return n, el, n * int(s.T.sum()) * S0.shape[1] / el
+
+    n, el, value = rate(seconds, None)
+    cores = oracle.threads_used()
+    n1, el1, value1 = rate(seconds_1thread, 1)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": value, "unit": "head-token updates/s", "cores": cores,
             "kind": "oracle",
             "sample": "%d repetitions of one %d-row K=%d verify window (%d head-token updates each), "
-                      "fp64, %.1f s" % (n, s.B, int(s.T[0]) - 1, int(s.T.sum()) * S0.shape[1], el)}
+                      "fp64, %.1f s" % (n, s.B, int(s.T[0]) - 1, int(s.T.sum()) * S0.shape[1], el),
+            "value_1thread": value1,
+            "sample_1thread": "%d repetitions, %.1f s" % (n1, el1),
+            "cpu_model": cpu_model}
 
 
 MFMA_F32_PEAK_TFLOPS = 157.3
@@ -212,27 +230,31 @@ def measure_prefill(gb, synth, torch, stream, reps):
             "algorithmic_flops_per_call": fl}
 
 
-def measure(gb, synth, torch, B, T, steps, warmup, n_layers, stream, seed0):
+def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0):
+    """Steps over n_layers layers of windows with per-row token counts Ts."""
     dims = gb.Dims(16, 32, 128, 128, 3)
-    sets = [VerifySet(gb, synth, dims, B, T, seed0 + i, stream) for i in range(n_layers)]
-    wall, verify_ms = run_steps(sets, steps, warmup, stream, torch)
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream) for i in range(n_layers)]
+    wall, verify_ms, commit_ms = run_steps(sets, steps, warmup, stream, torch)
     for s in sets:
         assert int(s.status.abs().sum()) == 0
-    units = B * 32
-    upd = units * T * n_layers
-    vb = verify_bytes(units, T)
+    units = len(Ts) * V_HEADS
+    upd_per_layer = int(sum(Ts)) * V_HEADS
+    vb = verify_bytes(Ts)
     vms = sum(verify_ms) / len(verify_ms)
+    cms = sum(commit_ms) / len(commit_ms)
     srt = sorted(verify_ms)
     return sets, {
         "ms_per_step": 1e3 * wall / steps,
-        "updates_per_s": upd * steps / wall,
+        "updates_per_s": upd_per_layer * n_layers * steps / wall,
         "verify_ms_mean": vms,
         "verify_ms_p10": srt[len(srt) // 10],
         "verify_ms_p50": srt[len(srt) // 2],
         "verify_ms_p90": srt[(9 * len(srt)) // 10],
-        "verify_updates_per_s": units * T / (vms * 1e-3),
+        "verify_updates_per_s": upd_per_layer / (vms * 1e-3),
         "verify_bytes": vb,
         "verify_gbps": vb / (vms * 1e-3) / 1e9,
+        "commit_ms_mean": cms,
+        "commit_gbps": commit_bytes(units) / (cms * 1e-3) / 1e9,
         "step_gbps": (vb + commit_bytes(units)) * n_layers * steps / wall / 1e9,
     }
 
@@ -245,9 +267,14 @@ def main():
     ap.add_argument("--layers", type=int, default=12,
                     help="GatedDeltaNet layers per step, each with its own 160 MiB of buffers")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds-1thread", type=float, default=4.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch1", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the 2048-token chunked prefill and print its figures")
+    ap.add_argument("--prefill-reps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this path runs on one GPU; --gpus %d is not supported "
@@ -265,18 +292,32 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
-    sets16, r16 = measure(gb, synth, torch, 16, 4, args.steps, args.warmup, args.layers, stream, 500)
-    out_b1 = None
+    if args.prefill_only:
+        print(json.dumps(measure_prefill(gb, synth, torch, stream, args.prefill_reps)), flush=True)
+        return
+
+    import numpy as np
+    sets16, r16 = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500)
+
+    def side(r, Ts):
+        return {"row_tokens": [int(t) for t in Ts],
+                "head_token_updates_per_s": r["updates_per_s"],
+                "ms_per_layer": r["ms_per_step"] / args.layers,
+                "verify_us_mean": 1e3 * r["verify_ms_mean"], "verify_us_p50": 1e3 * r["verify_ms_p50"],
+                "verify_gbps": r["verify_gbps"], "verify_frac_of_hbm_peak": r["verify_gbps"] / HBM_PEAK_GBPS,
+                "commit_us_mean": 1e3 * r["commit_ms_mean"], "commit_gbps": r["commit_gbps"]}
+    out_b1 = out_mixed = None
     if not args.no_batch1:
-        _, r1 = measure(gb, synth, torch, 1, 4, args.steps, args.warmup, args.layers, stream, 600)
-        out_b1 = {"head_token_updates_per_s": r1["updates_per_s"],
-                  "ms_per_layer": r1["ms_per_step"] / args.layers,
-                  "verify_us_mean": 1e3 * r1["verify_ms_mean"], "verify_gbps": r1["verify_gbps"],
-                  "verify_frac_of_hbm_peak": r1["verify_gbps"] / HBM_PEAK_GBPS}
-    prefill = None if args.no_prefill else measure_prefill(gb, synth, torch, stream, 20)
+        _, r1 = measure(gb, synth, torch, [4], args.steps, args.warmup, args.layers, stream, 600)
+        out_b1 = side(r1, [4])
+    if not args.no_mixed:
+        Ts = (synth.verify_workload("conc16").draft_lens + 1).astype(np.int32)
+        _, rm = measure(gb, synth, torch, Ts, args.steps, args.warmup, args.layers, stream, 700)
+        out_mixed = side(rm, Ts)
+    prefill = None if args.no_prefill else measure_prefill(gb, synth, torch, stream, args.prefill_reps)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(sets16[0], args.cpu_seconds)
+        cpu = cpu_baseline(sets16[0], args.cpu_seconds, args.cpu_seconds_1thread)
 
     traffic = traffic_from_profile(r16["verify_bytes"])
     line = {
@@ -305,8 +346,11 @@ def main():
                      "launch_us_p90": 1e3 * r16["verify_ms_p90"]},
         "ms_per_layer": r16["ms_per_step"] / args.layers,
         "verify_head_token_updates_per_s": r16["verify_updates_per_s"],
+        "commit_us_mean": 1e3 * r16["commit_ms_mean"],
+        "commit_gbps": r16["commit_gbps"],
         "step_gbps": r16["step_gbps"],
         "batch1": out_b1,
+        "conc16_mixed_k": out_mixed,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }
