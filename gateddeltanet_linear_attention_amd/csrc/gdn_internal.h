@@ -13,8 +13,12 @@ namespace gdn {
 // call with more rows is split into several launches on the same stream.
 constexpr int kRowsPerLaunch = 64;
 
+// Longest row the recurrent kernel runs: a verify window of k_max + 1 <= 4 tokens
+// (decode rows have 1; longer transaction rows take the chunked path).
+constexpr int kMaxWindow = 4;
+
 // Recurrent (token-by-token) kernel shared by decode, verify and the short rows
-// of a transaction.  Row r of the launch runs ntok[r] tokens starting at packed
+// of a transaction.  Row r of the launch runs 1 <= ntok[r] <= kMaxWindow tokens starting at packed
 // token tok0[r] from pool slot src[r] (-1: zero state); the state after token t
 // is stored to slot t - ck_first[r] of checkpoint row ck_row[r] when
 // t >= ck_first[r]; the final

@@ -54,11 +54,13 @@ __device__ __forceinline__ void eval_gates(float a, float b, float A_log, float 
 // of the same shape, so every lane of the group ends with the same bits.
 __device__ __forceinline__ float dpp_add(float p, int ctrl_id) {
   int moved;
+  // Every source lane of these patterns lies in the same row, so bound_ctrl never
+  // applies; setting it lets the compiler fold the move into the add (v_add_f32_dpp).
   switch (ctrl_id) {
-    case 0: moved = __builtin_amdgcn_mov_dpp(__float_as_int(p), 0xB1, 0xF, 0xF, false); break;
-    case 1: moved = __builtin_amdgcn_mov_dpp(__float_as_int(p), 0x4E, 0xF, 0xF, false); break;
-    case 2: moved = __builtin_amdgcn_mov_dpp(__float_as_int(p), 0x141, 0xF, 0xF, false); break;
-    default: moved = __builtin_amdgcn_mov_dpp(__float_as_int(p), 0x140, 0xF, 0xF, false); break;
+    case 0: moved = __builtin_amdgcn_update_dpp(0, __float_as_int(p), 0xB1, 0xF, 0xF, true); break;
+    case 1: moved = __builtin_amdgcn_update_dpp(0, __float_as_int(p), 0x4E, 0xF, 0xF, true); break;
+    case 2: moved = __builtin_amdgcn_update_dpp(0, __float_as_int(p), 0x141, 0xF, 0xF, true); break;
+    default: moved = __builtin_amdgcn_update_dpp(0, __float_as_int(p), 0x140, 0xF, 0xF, true); break;
   }
   return p + __int_as_float(moved);
 }
@@ -87,15 +89,15 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   constexpr int NV = D / LPR / 4;                  // float4 per lane per state row
   constexpr int ROWS = WAVES * 64 / LPR * RPL;     // state rows per block
   constexpr int TILES = D / ROWS;                  // blocks per (row, head)
-  constexpr int TB = 4;                            // tokens staged per batch
+  constexpr int TB = kMaxWindow;                   // every row's tokens are staged at once
   static_assert(NV >= 1 && D % (LPR * 4) == 0 && D % ROWS == 0, "bad tiling");
   constexpr size_t UNIT = size_t(D) * D;
-  // One batch of up to TB tokens' inputs, shared by the block: k and q widened to
-  // fp32 once, the block's slice of v, and the two gates.
+  // The row's tokens' inputs, shared by the block: k and q widened to fp32 once,
+  // the block's slice of v, and the two gates.
   __shared__ float4 sK[TB][D / 4], sQ[TB][D / 4];
   __shared__ float sV[TB][ROWS];
   __shared__ float sAlpha[TB], sBeta[TB];
-  __shared__ uint16_t sO[TB][ROWS];  // outputs, written back coalesced per batch
+  __shared__ uint16_t sO[TB][ROWS];  // outputs, written back coalesced at the end
 
   const int tid = threadIdx.x;
   const int sub = tid % LPR;
@@ -130,80 +132,76 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     }
   }
 
-  for (int t0 = 0; t0 < ntok; t0 += TB) {
-    const int nb = min(TB, ntok - t0);
-    // stage this batch's token inputs (issued while the state loads are in flight)
-    for (int x = tid; x < nb * (D / 4); x += 64 * WAVES) {
-      const int t = x / (D / 4), c = x % (D / 4);
-      const size_t tok = size_t(tok0) + t0 + t;
-      const uint2 kw = reinterpret_cast<const uint2 *>(args.k + (tok * n_qk + hq) * D)[c];
-      const uint2 qw = reinterpret_cast<const uint2 *>(args.q + (tok * n_qk + hq) * D)[c];
-      sK[t][c] = make_float4(bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y));
-      sQ[t][c] = make_float4(bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y));
-    }
-    for (int x = tid; x < nb * ROWS; x += 64 * WAVES) {
-      const int t = x / ROWS, rr = x % ROWS;
-      const size_t tok = size_t(tok0) + t0 + t;
-      sV[t][rr] = __uint_as_float(uint32_t(args.v[(tok * n_v + h) * D + tile * ROWS + rr]) << 16);
-    }
-    if (tid < nb) {
-      const size_t tok = size_t(tok0) + t0 + tid;
-      eval_gates(args.a[tok * n_v + h], args.b[tok * n_v + h], args.A_log[h], args.dt_bias[h],
-                 sAlpha[tid], sBeta[tid]);
-    }
-    lds_barrier();
+  // stage the row's token inputs (issued while the state loads are in flight)
+  for (int x = tid; x < ntok * (D / 4); x += 64 * WAVES) {
+    const int t = x / (D / 4), c = x % (D / 4);
+    const size_t tok = size_t(tok0) + t;
+    const uint2 kw = reinterpret_cast<const uint2 *>(args.k + (tok * n_qk + hq) * D)[c];
+    const uint2 qw = reinterpret_cast<const uint2 *>(args.q + (tok * n_qk + hq) * D)[c];
+    sK[t][c] = make_float4(bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y));
+    sQ[t][c] = make_float4(bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y));
+  }
+  for (int x = tid; x < ntok * ROWS; x += 64 * WAVES) {
+    const int t = x / ROWS, rr = x % ROWS;
+    const size_t tok = size_t(tok0) + t;
+    sV[t][rr] = __uint_as_float(uint32_t(args.v[(tok * n_v + h) * D + tile * ROWS + rr]) << 16);
+  }
+  if (tid < ntok) {
+    const size_t tok = size_t(tok0) + tid;
+    eval_gates(args.a[tok * n_v + h], args.b[tok * n_v + h], args.A_log[h], args.dt_bias[h],
+               sAlpha[tid], sBeta[tid]);
+  }
+  lds_barrier();
 
 #pragma unroll 1
-    for (int t = 0; t < nb; ++t) {
-      const float alpha = sAlpha[t], beta = sBeta[t];
-      float kk[NV][4];
+  for (int t = 0; t < ntok; ++t) {
+    const float alpha = sAlpha[t], beta = sBeta[t];
+    float kk[NV][4];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const float4 kw = sK[t][sub + LPR * j];
+      kk[j][0] = kw.x; kk[j][1] = kw.y; kk[j][2] = kw.z; kk[j][3] = kw.w;
+    }
+#pragma unroll
+    for (int q = 0; q < RPL; ++q) {
+      const float vi = sV[t][i_local + q];
+      // u = S[i,:] . k
+      float p = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p = fmaf(s[q][j][e], kk[j][e], p);
+      const float u = group_sum<LPR>(p);
+      // S[i,:] <- alpha S[i,:] + beta (v_i - alpha u) k
+      const float c = beta * (vi - alpha * u);
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[q][j][e] = fmaf(c, kk[j][e], alpha * s[q][j][e]);
+      // o_i = S[i,:] . q
+      float po = 0.0f;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const float4 kw = sK[t][sub + LPR * j];
-        kk[j][0] = kw.x; kk[j][1] = kw.y; kk[j][2] = kw.z; kk[j][3] = kw.w;
+        const float4 qw = sQ[t][sub + LPR * j];
+        po = fmaf(s[q][j][0], qw.x, po);
+        po = fmaf(s[q][j][1], qw.y, po);
+        po = fmaf(s[q][j][2], qw.z, po);
+        po = fmaf(s[q][j][3], qw.w, po);
       }
-      const int tt = t0 + t;
+      const float oi = group_sum<LPR>(po);
+      if (sub == 0) sO[t][i_local + q] = to_bf16(oi);
+      if (t >= ck_first) {
+        float *cp = args.ckpt + ((size_t(ck_row) * args.ck_slots + (t - ck_first)) * n_v + h) * UNIT +
+                    size_t(i0 + q) * D;
 #pragma unroll
-      for (int q = 0; q < RPL; ++q) {
-        const float vi = sV[t][i_local + q];
-        // u = S[i,:] . k
-        float p = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p = fmaf(s[q][j][e], kk[j][e], p);
-        const float u = group_sum<LPR>(p);
-        // S[i,:] <- alpha S[i,:] + beta (v_i - alpha u) k
-        const float c = beta * (vi - alpha * u);
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[q][j][e] = fmaf(c, kk[j][e], alpha * s[q][j][e]);
-        // o_i = S[i,:] . q
-        float po = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const float4 qw = sQ[t][sub + LPR * j];
-          po = fmaf(s[q][j][0], qw.x, po);
-          po = fmaf(s[q][j][1], qw.y, po);
-          po = fmaf(s[q][j][2], qw.z, po);
-          po = fmaf(s[q][j][3], qw.w, po);
-        }
-        const float oi = group_sum<LPR>(po);
-        if (sub == 0) sO[t][i_local + q] = to_bf16(oi);
-        if (tt >= ck_first) {
-          float *cp = args.ckpt + ((size_t(ck_row) * args.ck_slots + (tt - ck_first)) * n_v + h) * UNIT +
-                      size_t(i0 + q) * D;
-#pragma unroll
-          for (int j = 0; j < NV; ++j) store_nt(cp + 4 * (sub + LPR * j), s[q][j]);
-        }
+        for (int j = 0; j < NV; ++j) store_nt(cp + 4 * (sub + LPR * j), s[q][j]);
       }
     }
-    lds_barrier();  // the next batch overwrites the staged inputs
-    for (int x = tid; x < nb * ROWS; x += 64 * WAVES) {
-      const int t = x / ROWS, rr = x % ROWS;
-      args.o[((size_t(tok0) + t0 + t) * n_v + h) * D + tile * ROWS + rr] = sO[t][rr];
-    }
+  }
+  lds_barrier();  // every output of the block is in sO
+  for (int x = tid; x < ntok * ROWS; x += 64 * WAVES) {
+    const int t = x / ROWS, rr = x % ROWS;
+    args.o[((size_t(tok0) + t) * n_v + h) * D + tile * ROWS + rr] = sO[t][rr];
   }
 
   if (dst >= 0) {
@@ -222,6 +220,9 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 
 hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream) {
   if (args.n_rows <= 0) return hipSuccess;
+  if (args.n_rows > kRowsPerLaunch) return hipErrorInvalidValue;
+  for (int r = 0; r < args.n_rows; ++r)  // the kernel stages a row's tokens in fixed LDS arrays
+    if (args.ntok[r] < 1 || args.ntok[r] > kMaxWindow) return hipErrorInvalidValue;
   if (d == 128) {
     constexpr int D = 128, LPR = 16, RPL = 1, WAVES = 8;
     constexpr int TILES = D / (WAVES * 64 / LPR * RPL);
