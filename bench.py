@@ -52,6 +52,19 @@ def commit_bytes(n_units: int) -> int:
     return n_units * 2 * STATE_BYTES
 
 
+REPLAY_TOKEN_BYTES = 392  # per head-token replayed: k (shared by 2 v-heads) 128 + v 256 + a,b 8
+
+
+def verify_nockpt_bytes(row_tokens) -> int:
+    """Verify without checkpoints: read the committed state, token I/O incl. outputs."""
+    return sum(V_HEADS * (STATE_BYTES + TOKEN_BYTES * int(T)) for T in row_tokens)
+
+
+def replay_bytes(accepted) -> int:
+    """Replay commit: read and write the state, re-read a_r + 1 tokens' inputs."""
+    return sum(V_HEADS * (2 * STATE_BYTES + REPLAY_TOKEN_BYTES * (int(a) + 1)) for a in accepted)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -77,7 +90,7 @@ class VerifySet:
     """One buffer set: state pool, checkpoints, a window of tokens, accepted counts,
     and the two prepared C-ABI calls of a step."""
 
-    def __init__(self, gb, synth, dims, Ts, seed, stream):
+    def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False):
         import numpy as np
         import torch
         shape = synth.FULL
@@ -96,15 +109,25 @@ class VerifySet:
                       A_log=torch.from_numpy(A_log).to(dev), dt_bias=torch.from_numpy(dt_bias).to(dev))
         gen = torch.Generator(device="cpu").manual_seed(seed)
         self.pool = (0.05 * torch.randn(B, Hv, d, d, generator=gen)).to(dev)
-        self.ckpt = torch.empty(B, 4, Hv, d, d, device=dev)
+        self.ckpt = None if replay else torch.empty(B, 4, Hv, d, d, device=dev)
         self.o = torch.empty(N, Hv, d, dtype=torch.bfloat16, device=dev)
         self.acc = torch.from_numpy(acc).to(dev)
         self.status = torch.zeros((B + 31) // 32, dtype=torch.int32, device=dev)
         rows = np.arange(B, dtype=np.int32)
-        self.verify = gb.prepare_verify_window(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
-                                               ckpt=self.ckpt, o=self.o, stream=stream)
-        self.commit = gb.prepare_commit_accepted(dims, Ts, self.ckpt, self.acc, self.pool, dst_slot=rows,
-                                                 status=self.status, stream=stream)
+        if replay:  # no checkpoints: commit re-runs the accepted prefix in place
+            self.ckpt = None
+            self.verify = gb.prepare_verify_window(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
+                                                   ckpt=None, o=self.o, stream=stream)
+            tin = {k: v for k, v in self.t.items()}
+            self.commit = gb.prepare_commit_replay(dims, Ts, **tin, accepted=self.acc, state_pool=self.pool,
+                                                   src_slot=rows, dst_slot=rows, status=self.status,
+                                                   stream=stream)
+        else:
+            self.verify = gb.prepare_verify_window(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
+                                                   ckpt=self.ckpt, o=self.o, stream=stream)
+            self.commit = gb.prepare_commit_accepted(dims, Ts, self.ckpt, self.acc, self.pool, dst_slot=rows,
+                                                     status=self.status, stream=stream)
+        self.acc_host = acc
         # the window's tokens, for the CPU baseline
         self.tok, self.A_log, self.dt_bias, self.T, self.B = tok, A_log, dt_bias, Ts, B
 
@@ -230,16 +253,18 @@ def measure_prefill(gb, synth, torch, stream, reps):
             "algorithmic_flops_per_call": fl}
 
 
-def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0):
-    """Steps over n_layers layers of windows with per-row token counts Ts."""
+def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay=False):
+    """Steps over n_layers layers of windows with per-row token counts Ts (replay:
+    verify without checkpoints, commit by replay)."""
     dims = gb.Dims(16, 32, 128, 128, 3)
-    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream) for i in range(n_layers)]
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay) for i in range(n_layers)]
     wall, verify_ms, commit_ms = run_steps(sets, steps, warmup, stream, torch)
     for s in sets:
         assert int(s.status.abs().sum()) == 0
     units = len(Ts) * V_HEADS
     upd_per_layer = int(sum(Ts)) * V_HEADS
-    vb = verify_bytes(Ts)
+    vb = verify_nockpt_bytes(Ts) if replay else verify_bytes(Ts)
+    cb = (sum(replay_bytes(s.acc_host) for s in sets) / len(sets)) if replay else commit_bytes(units)
     vms = sum(verify_ms) / len(verify_ms)
     cms = sum(commit_ms) / len(commit_ms)
     srt = sorted(verify_ms)
@@ -254,8 +279,9 @@ def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0):
         "verify_bytes": vb,
         "verify_gbps": vb / (vms * 1e-3) / 1e9,
         "commit_ms_mean": cms,
-        "commit_gbps": commit_bytes(units) / (cms * 1e-3) / 1e9,
-        "step_gbps": (vb + commit_bytes(units)) * n_layers * steps / wall / 1e9,
+        "commit_bytes": cb,
+        "commit_gbps": cb / (cms * 1e-3) / 1e9,
+        "step_gbps": (vb + cb) * n_layers * steps / wall / 1e9,
     }
 
 
@@ -272,6 +298,7 @@ def main():
     ap.add_argument("--no-batch1", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--no-replay", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the 2048-token chunked prefill and print its figures")
     ap.add_argument("--prefill-reps", type=int, default=20)
@@ -314,6 +341,17 @@ def main():
         Ts = (synth.verify_workload("conc16").draft_lens + 1).astype(np.int32)
         _, rm = measure(gb, synth, torch, Ts, args.steps, args.warmup, args.layers, stream, 700)
         out_mixed = side(rm, Ts)
+    out_replay = None
+    if not args.no_replay:
+        _, rr = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
+                        replay=True)
+        out_replay = {"mode": "verify without checkpoints + commit by replay of the accepted prefix",
+                      "head_token_updates_per_s": rr["updates_per_s"],
+                      "ms_per_layer": rr["ms_per_step"] / args.layers,
+                      "verify_us_mean": 1e3 * rr["verify_ms_mean"], "verify_gbps": rr["verify_gbps"],
+                      "replay_us_mean": 1e3 * rr["commit_ms_mean"], "replay_gbps": rr["commit_gbps"],
+                      "step_gbps": rr["step_gbps"],
+                      "step_algorithmic_bytes_per_layer": rr["verify_bytes"] + rr["commit_bytes"]}
     prefill = None if args.no_prefill else measure_prefill(gb, synth, torch, stream, args.prefill_reps)
     cpu = None
     if not args.no_cpu_baseline:
@@ -351,6 +389,7 @@ def main():
         "step_gbps": r16["step_gbps"],
         "batch1": out_b1,
         "conc16_mixed_k": out_mixed,
+        "conc16_k3_replay": out_replay,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

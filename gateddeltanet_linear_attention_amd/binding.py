@@ -59,6 +59,8 @@ _SIGS = {
                          [ctypes.c_int32, _I32P, _VP, _VP, _VP],
     "gdn_commit_accepted": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _VP, _VP, _VP,
                             ctypes.c_int32, _I32P, _VP, _VP],
+    "gdn_commit_replay": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
+                         [_VP, ctypes.c_int32, _I32P, _I32P, _VP, _VP],
     "gdn_chunked_workspace_bytes": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, ctypes.c_int32],
     "gdn_chunked_prefill_with_checkpoints": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P,
                                              ctypes.c_int32, _I32P] + [_VP] * 8 +
@@ -144,10 +146,21 @@ def _pool(dims: Dims, state_pool):
                 (n_slots, dims.n_v_heads, dims.d_v, dims.d_k)), n_slots
 
 
-def _ckpt(dims: Dims, ckpt, n_rows: int):
+def _ckpt(dims: Dims, ckpt, n_rows: int, optional: bool = False):
     import torch
+    if ckpt is None and optional:
+        return _VP(0)
     return _dev(ckpt, "ckpt", torch.float32,
                 (n_rows, dims.k_max + 1, dims.n_v_heads, dims.d_v, dims.d_k))
+
+
+def _token_in_ptrs(dims: Dims, N: int, q, k, v, a, b, A_log, dt_bias):
+    import torch
+    Hq, Hv, d = dims.n_qk_heads, dims.n_v_heads, dims.d_k
+    return [_dev(q, "q", torch.bfloat16, (N, Hq, d)), _dev(k, "k", torch.bfloat16, (N, Hq, d)),
+            _dev(v, "v", torch.bfloat16, (N, Hv, dims.d_v)),
+            _dev(a, "a", torch.float32, (N, Hv)), _dev(b, "b", torch.float32, (N, Hv)),
+            _dev(A_log, "A_log", torch.float32, (Hv,)), _dev(dt_bias, "dt_bias", torch.float32, (Hv,))]
 
 
 # ------------------------------------------------------------------ entry points
@@ -176,7 +189,8 @@ def gdn_decode_step(dims: Dims, q, k, v, a, b, A_log, dt_bias, state_pool, src_s
 
 def gdn_verify_window(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot,
                       ckpt, o, stream=None) -> None:
-    """Each row's window from its committed slot; writes o and checkpoint slots 0..T_r-1."""
+    """Each row's window from its committed slot; writes o and checkpoint slots 0..T_r-1
+    (ckpt None: outputs only, for commit by replay)."""
     T, src = _i32(row_tokens), _i32(src_slot)
     n_rows = T.size
     if src.size != n_rows:
@@ -184,7 +198,7 @@ def gdn_verify_window(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, sta
     N = int(T.sum())
     toks, op = _token_ptrs(dims, N, q, k, v, a, b, A_log, dt_bias, o)
     pp, n_slots = _pool(dims, state_pool)
-    cp = _ckpt(dims, ckpt, n_rows)
+    cp = _ckpt(dims, ckpt, n_rows, optional=True)
     rc = lib().gdn_verify_window(ctypes.byref(dims.c()), n_rows, _ip(T), *toks, pp, n_slots, _ip(src),
                                  cp, op, _stream(stream))
     _check("gdn_verify_window", rc)
@@ -205,6 +219,32 @@ def gdn_commit_accepted(dims: Dims, row_tokens, ckpt, accepted, state_pool, dst_
     rc = lib().gdn_commit_accepted(ctypes.byref(dims.c()), n_rows, _ip(T), cp, ap, pp, n_slots,
                                    _ip(dst), sp, _stream(stream))
     _check("gdn_commit_accepted", rc)
+
+
+def _replay_args(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted, state_pool,
+                 src_slot, dst_slot, status, stream):
+    import torch
+    T, src, dst = _i32(row_tokens), _i32(src_slot), _i32(dst_slot)
+    n_rows = T.size
+    if not (src.size == dst.size == n_rows):
+        raise ValueError("per-row arrays differ in length")
+    toks = _token_in_ptrs(dims, int(T.sum()), q, k, v, a, b, A_log, dt_bias)
+    ap = _dev(accepted, "accepted", torch.int32, (n_rows,))
+    sp = _dev(status, "status", torch.int32, ((n_rows + 31) // 32,))
+    pp, n_slots = _pool(dims, state_pool)
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, _ip(T), *toks, ap, pp, n_slots, _ip(src), _ip(dst), sp,
+            _stream(stream))
+    return args, (cd, T, src, dst)
+
+
+def gdn_commit_replay(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted, state_pool,
+                      src_slot, dst_slot, status, stream=None) -> None:
+    """Re-run each row's first accepted[r] + 1 window tokens (device int32) from slot
+    src_slot[r]; the resulting state goes to slot dst_slot[r]."""
+    args, _keep = _replay_args(dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted, state_pool,
+                               src_slot, dst_slot, status, stream)
+    _check("gdn_commit_replay", lib().gdn_commit_replay(*args))
 
 
 def gdn_chunked_workspace_bytes(dims: Dims, row_tokens, chunk: int = 64) -> int:
@@ -296,10 +336,17 @@ def prepare_verify_window(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias,
     N = int(T.sum())
     toks, op = _token_ptrs(dims, N, q, k, v, a, b, A_log, dt_bias, o)
     pp, n_slots = _pool(dims, state_pool)
-    cp = _ckpt(dims, ckpt, n_rows)
+    cp = _ckpt(dims, ckpt, n_rows, optional=True)
     cd = dims.c()
     args = (ctypes.byref(cd), n_rows, _ip(T), *toks, pp, n_slots, _ip(src), cp, op, _stream(stream))
     return PreparedCall("gdn_verify_window", args, (cd, T, src))
+
+
+def prepare_commit_replay(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted, state_pool,
+                          src_slot, dst_slot, status, stream=None) -> PreparedCall:
+    args, keep = _replay_args(dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted, state_pool,
+                              src_slot, dst_slot, status, stream)
+    return PreparedCall("gdn_commit_replay", args, keep)
 
 
 def prepare_commit_accepted(dims: Dims, row_tokens, ckpt, accepted, state_pool, dst_slot, status,

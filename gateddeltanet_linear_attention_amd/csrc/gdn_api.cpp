@@ -46,11 +46,13 @@ Sizes sizes_of(const gdn_dims *d) {
   return s;
 }
 
-// Token inputs shared by every compute call.
+// Token inputs shared by every compute call (o may be absent only where the call
+// writes no outputs).
 int check_tokens(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
-                 const float *b, const float *A_log, const float *dt_bias, const uint16_t *o) {
-  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !o) return GDN_E_NULL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return GDN_E_ALIGN;
+                 const float *b, const float *A_log, const float *dt_bias, const uint16_t *o,
+                 bool need_o = true) {
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || (need_o && !o)) return GDN_E_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || (o && !aligned(o, 16))) return GDN_E_ALIGN;
   if (!aligned(a, 4) || !aligned(b, 4) || !aligned(A_log, 4) || !aligned(dt_bias, 4))
     return GDN_E_ALIGN;
   return GDN_OK;
@@ -275,15 +277,15 @@ int gdn_verify_window(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
   if (n_rows == 0) return GDN_OK;
   if (!row_tokens) return GDN_E_NULL;
   if ((rc = check_tokens(q, k, v, a, b, A_log, dt_bias, o))) return rc;
-  if (!state_pool || !src_slot || !ckpt) return GDN_E_NULL;
-  if (!aligned(state_pool, 16) || !aligned(ckpt, 16)) return GDN_E_ALIGN;
+  if (!state_pool || !src_slot) return GDN_E_NULL;
+  if (!aligned(state_pool, 16) || (ckpt && !aligned(ckpt, 16))) return GDN_E_ALIGN;
   for (int32_t r = 0; r < n_rows; ++r)
     if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
   if ((rc = check_slots(n_rows, n_slots, src_slot, nullptr))) return rc;
   const Sizes s = sizes_of(dims);
   const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
   const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
-  const size_t ck_b = size_t(n_rows) * s.ck_row_floats * 4;
+  const size_t ck_b = ckpt ? size_t(n_rows) * s.ck_row_floats * 4 : 0;
   const size_t o_b = size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2;
   if (overlap(ckpt, ck_b, state_pool, pool_b) || overlap(o, o_b, ckpt, ck_b) ||
       overlap(o, o_b, state_pool, pool_b))
@@ -293,7 +295,38 @@ int gdn_verify_window(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
   for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
   gdn::RecurrentArgs proto;
   fill_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, nullptr, ckpt, o);
-  return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, src_slot, nullptr, row_tokens,
+  return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, src_slot, nullptr,
+                               ckpt ? row_tokens : nullptr, static_cast<hipStream_t>(stream));
+}
+
+int gdn_commit_replay(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                      const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                      const float *b, const float *A_log, const float *dt_bias,
+                      const int32_t *accepted, float *state_pool, int32_t n_slots,
+                      const int32_t *src_slot, const int32_t *dst_slot, uint32_t *status,
+                      void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if (!row_tokens) return GDN_E_NULL;
+  if ((rc = check_tokens(q, k, v, a, b, A_log, dt_bias, nullptr, false))) return rc;
+  if (!accepted || !state_pool || !src_slot || !dst_slot || !status) return GDN_E_NULL;
+  if (!aligned(state_pool, 16) || !aligned(accepted, 4) || !aligned(status, 4)) return GDN_E_ALIGN;
+  for (int32_t r = 0; r < n_rows; ++r) {
+    if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+    if (dst_slot[r] < 0) return GDN_E_RANGE;
+  }
+  if ((rc = check_slots(n_rows, n_slots, src_slot, dst_slot))) return rc;
+
+  std::vector<int32_t> rows(static_cast<size_t>(n_rows));
+  for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
+  const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  gdn::RecurrentArgs proto;
+  fill_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, state_pool, nullptr, nullptr);
+  proto.accepted = accepted;
+  proto.status = status;
+  return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, src_slot, dst_slot, nullptr,
                                static_cast<hipStream_t>(stream));
 }
 

@@ -28,8 +28,13 @@ struct RecurrentArgs {
   const float *a, *b, *A_log, *dt_bias;
   const float *state_in;            // pool (read)
   float *state_out;                 // pool (final-state write); may alias state_in
-  float *ckpt;                      // checkpoint buffer of the whole call
-  uint16_t *o;                      // bf16 bits
+  float *ckpt;                      // checkpoint buffer of the whole call (may be null: none stored)
+  uint16_t *o;                      // bf16 bits (may be null: outputs not written)
+  // Replay (may be null): row r runs only its first accepted[ck_row[r]] + 1 tokens,
+  // read on the device; a count outside [0, ntok[r]) leaves the row untouched and
+  // sets bit ck_row[r] of status.
+  const int32_t *accepted;
+  uint32_t *status;
   int32_t n_qk, n_v, group;         // heads; group = n_v / n_qk
   int32_t ck_slots;                 // k_max + 1
   int32_t n_rows;                   // rows in this launch

@@ -20,7 +20,12 @@
 // non-temporal stores: the traffic is one state read to T checkpoint writes, and
 // streaming the writes past the caches is what lets it approach the HBM peak.
 //
-// Bit-exactness.  Decode, verify and transaction rows all run this one kernel
+// Replay.  With a device array of accepted counts the kernel runs only each row's
+// accepted prefix (bonus token + a_r drafts) from the committed state and writes
+// the resulting state, no outputs and no checkpoints: rollback by re-running the
+// accepted tokens instead of storing a state per window token.
+//
+// Bit-exactness.  Decode, verify, replay and transaction rows all run this one kernel
 // instantiation per d; the per-row arithmetic (element ownership, FMA order,
 // butterfly, gate code) does not depend on the row's token count, the launch's
 // row count or the grid.  So the checkpoint after j+1 verify tokens is
@@ -110,10 +115,23 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   const int i_local = (tid / LPR) * RPL;  // first of this lane's RPL state rows in the block
   const int i0 = tile * ROWS + i_local;
 
-  const int ntok = args.ntok[r], tok0 = args.tok0[r];
+  int ntok = args.ntok[r];
+  const int tok0 = args.tok0[r];
   const int src = args.src[r], dst = args.dst[r], ck_first = args.ck_first[r];
   const int ck_row = args.ck_row[r];
   const int n_v = args.n_v, n_qk = args.n_qk;
+  if (args.accepted) {
+    // Replay of the accepted prefix: the bonus token and a_r drafts, the same
+    // sequence of operations as the first a_r + 1 tokens of the window, so the
+    // state it leaves is bit-identical to that window's checkpoint slot a_r.
+    const int acc = args.accepted[ck_row];
+    if (acc < 0 || acc >= ntok) {
+      if (tile == 0 && h == 0 && tid == 0) atomicOr(args.status + (ck_row >> 5), 1u << (ck_row & 31));
+      return;  // the whole block leaves before any barrier
+    }
+    ntok = acc + 1;
+  }
+  const bool write_o = args.o != nullptr;
 
   float s[RPL][NV][4];
 #pragma unroll
@@ -137,9 +155,11 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     const int t = x / (D / 4), c = x % (D / 4);
     const size_t tok = size_t(tok0) + t;
     const uint2 kw = reinterpret_cast<const uint2 *>(args.k + (tok * n_qk + hq) * D)[c];
-    const uint2 qw = reinterpret_cast<const uint2 *>(args.q + (tok * n_qk + hq) * D)[c];
     sK[t][c] = make_float4(bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y));
-    sQ[t][c] = make_float4(bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y));
+    if (write_o) {
+      const uint2 qw = reinterpret_cast<const uint2 *>(args.q + (tok * n_qk + hq) * D)[c];
+      sQ[t][c] = make_float4(bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y));
+    }
   }
   for (int x = tid; x < ntok * ROWS; x += 64 * WAVES) {
     const int t = x / ROWS, rr = x % ROWS;
@@ -178,18 +198,20 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
       for (int j = 0; j < NV; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[q][j][e] = fmaf(c, kk[j][e], alpha * s[q][j][e]);
-      // o_i = S[i,:] . q
-      float po = 0.0f;
+      if (write_o) {
+        // o_i = S[i,:] . q
+        float po = 0.0f;
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const float4 qw = sQ[t][sub + LPR * j];
-        po = fmaf(s[q][j][0], qw.x, po);
-        po = fmaf(s[q][j][1], qw.y, po);
-        po = fmaf(s[q][j][2], qw.z, po);
-        po = fmaf(s[q][j][3], qw.w, po);
+        for (int j = 0; j < NV; ++j) {
+          const float4 qw = sQ[t][sub + LPR * j];
+          po = fmaf(s[q][j][0], qw.x, po);
+          po = fmaf(s[q][j][1], qw.y, po);
+          po = fmaf(s[q][j][2], qw.z, po);
+          po = fmaf(s[q][j][3], qw.w, po);
+        }
+        const float oi = group_sum<LPR>(po);
+        if (sub == 0) sO[t][i_local + q] = to_bf16(oi);
       }
-      const float oi = group_sum<LPR>(po);
-      if (sub == 0) sO[t][i_local + q] = to_bf16(oi);
       if (t >= ck_first) {
         float *cp = args.ckpt + ((size_t(ck_row) * args.ck_slots + (t - ck_first)) * n_v + h) * UNIT +
                     size_t(i0 + q) * D;
@@ -198,10 +220,12 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
       }
     }
   }
-  lds_barrier();  // every output of the block is in sO
-  for (int x = tid; x < ntok * ROWS; x += 64 * WAVES) {
-    const int t = x / ROWS, rr = x % ROWS;
-    args.o[((size_t(tok0) + t) * n_v + h) * D + tile * ROWS + rr] = sO[t][rr];
+  if (write_o) {
+    lds_barrier();  // every output of the block is in sO
+    for (int x = tid; x < ntok * ROWS; x += 64 * WAVES) {
+      const int t = x / ROWS, rr = x % ROWS;
+      args.o[((size_t(tok0) + t) * n_v + h) * D + tile * ROWS + rr] = sO[t][rr];
+    }
   }
 
   if (dst >= 0) {

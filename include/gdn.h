@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 1
+#define GDN_VERSION 2
 #define GDN_MAX_K 3 /* largest k_max: at most 4 checkpoint slots per row */
 
 typedef struct gdn_dims {
@@ -98,6 +98,8 @@ int gdn_decode_step(const gdn_dims *dims, int32_t n_rows, const uint16_t *q,
  * for j < T_r; slots j >= T_r are not touched.  The state pool is only read:
  * nothing is published until gdn_commit_accepted (transactional publication, the
  * pull request's "Summary").  ckpt must not overlap state_pool or o (GDN_E_ALIAS).
+ * ckpt may be NULL: then only o is written, and the row is committed with
+ * gdn_commit_replay instead of gdn_commit_accepted.
  */
 int gdn_verify_window(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
                       const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -119,6 +121,29 @@ int gdn_commit_accepted(const gdn_dims *dims, int32_t n_rows, const int32_t *row
                         const float *ckpt, const int32_t *accepted, float *state_pool,
                         int32_t n_slots, const int32_t *dst_slot, uint32_t *status,
                         void *stream);
+
+/*
+ * gdn_commit_replay -- rollback without checkpoints: the pull request thread's
+ * closing note replaces dense recurrent checkpoints with compact fixed-state
+ * replay.  Row r re-runs the first a_r + 1 tokens of its window (row_tokens[r] =
+ * T_r tokens packed as for gdn_verify_window; the bonus token and the a_r accepted
+ * drafts) from the committed state in slot src_slot[r] (-1: zero state) and
+ * writes the resulting state to slot dst_slot[r] (== src_slot[r] commits in
+ * place).  accepted (device int32 [n_rows]) is read on the device.  Decode,
+ * verify and replay run one device routine, so the state written is bit-identical
+ * to checkpoint slot a_r of gdn_verify_window on the same window, i.e. to what
+ * gdn_commit_accepted would publish.  No outputs are written.  A row whose a_r is
+ * outside [0, T_r - 1] is left untouched and bit (r % 32) of status[r / 32] is set
+ * (status: device uint32 [(n_rows + 31) / 32], bits OR-ed in).
+ * Errors: GDN_E_RANGE for a dst slot < 0 or any slot >= n_slots; GDN_E_ALIAS if two
+ * rows share a dst slot or a dst slot is another row's src.
+ */
+int gdn_commit_replay(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                      const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const float *a, const float *b, const float *A_log,
+                      const float *dt_bias, const int32_t *accepted, float *state_pool,
+                      int32_t n_slots, const int32_t *src_slot, const int32_t *dst_slot,
+                      uint32_t *status, void *stream);
 
 /*
  * gdn_chunked_workspace_bytes -- device workspace that gdn_chunked_prefill_with_

@@ -38,7 +38,8 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"gdn_decode_step", "gdn_verify_window", "gdn_commit_accepted",
             "gdn_chunked_prefill_with_checkpoints", "gdn_chunked_workspace_bytes",
-            "gdn_plan_transaction", "gdn_run_transaction", "gdn_status_str", "gdn_version"} <= set(names)
+            "gdn_plan_transaction", "gdn_run_transaction", "gdn_status_str", "gdn_version",
+            "gdn_commit_replay"} <= set(names)
     lib = gb.lib()
     for n in names:
         assert hasattr(lib, n), "libgdn.so does not export %s" % n
@@ -161,6 +162,46 @@ def test_decode_and_commit_validation_codes():
     assert commit([4, 2], [1, 9]) == -3      # slot out of range
     p = b.ptr(1 << 20)
     assert commit([4], [0], pool=p, ckpt=p) == -4  # checkpoint buffer is the pool
+
+
+@no_gpu
+def test_verify_without_checkpoints_and_replay_validation_codes():
+    lib = gb.lib()
+    b = Bufs()
+    d = _dims()
+    NULL = ctypes.c_void_p(0)
+
+    def verify_nock(T, o=None, misalign=0):
+        Ta, Tp = _i32(T)
+        sa, sp = _i32(list(range(len(T))))
+        return lib.gdn_verify_window(ctypes.byref(d), len(Ta), Tp, *[b.ptr() for _ in range(7)], b.ptr(), 8,
+                                     sp, NULL, o if o is not None else b.ptr(misalign=misalign), NULL)
+
+    assert verify_nock([4, 2], o=NULL) == -1          # outputs are still required
+    assert verify_nock([4, 2], misalign=2) == -5      # misaligned o
+    assert verify_nock([4, 5]) == -3                  # T_r > k_max + 1
+    # a valid call passes validation; with no GPU here the launch itself fails
+    assert verify_nock([4, 2]) == -7
+
+    def replay(T, src, dst, accepted=True, status=True, n_slots=8, misalign=0):
+        Ta, Tp = _i32(T)
+        sa, sp = _i32(src)
+        da, dp = _i32(dst)
+        toks = [b.ptr(misalign=misalign)] + [b.ptr() for _ in range(6)]
+        return lib.gdn_commit_replay(ctypes.byref(d), len(Ta), Tp, *toks,
+                                     b.ptr() if accepted else NULL, b.ptr(), n_slots, sp, dp,
+                                     b.ptr() if status else NULL, NULL)
+
+    assert replay([4, 2], [0, 1], [2, 3], accepted=False) == -1   # no accepted counts
+    assert replay([4, 2], [0, 1], [2, 3], status=False) == -1     # no status word
+    assert replay([4, 2], [0, 1], [2, -1]) == -3                  # replay must publish its state
+    assert replay([4, 2], [0, 1], [2, 8]) == -3                   # dst out of range
+    assert replay([4, 5], [0, 1], [2, 3]) == -3                   # T_r > k_max + 1
+    assert replay([4, 2], [0, 1], [2, 2]) == -4                   # two rows write one slot
+    assert replay([4, 2], [0, 1], [1, 3]) == -4                   # row 0 writes row 1's source
+    assert replay([4, 2], [0, 1], [2, 3], misalign=8) == -5       # misaligned q
+    assert replay([4, 2], [0, 1], [0, 1]) == -7                   # in place passes validation
+    assert replay([], [], []) == 0
 
 
 @no_gpu

@@ -45,9 +45,10 @@ def _bf16_bits(t):
 
 # ---------------------------------------------------------------- workload runner
 
-def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: int):
+def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: int, replay: bool = False):
     """Warm every row by decoding its prior tokens, then run n_windows verify windows,
-    each followed by commit of the accepted length; the oracle runs the same chain
+    each followed by commit of the accepted length (replay: verify without
+    checkpoints, then gdn_commit_replay in place); the oracle runs the same chain
     independently from its own states.  Returns the worst errors seen."""
     dims = dims_of(w.shape)
     B, Hv, d = w.n_rows, w.shape.n_v_heads, w.shape.d
@@ -86,10 +87,15 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
     for i in range(n_windows):
         win = w.window_tokens(i)
         acc = w.accepted(i)
-        gb.gdn_verify_window(dims, T, **dev_tokens(win), **P, state_pool=pool, src_slot=rows,
-                             ckpt=ckpt, o=o_win)
-        gb.gdn_commit_accepted(dims, T, ckpt, torch.from_numpy(acc).cuda(), pool, dst_slot=rows,
-                               status=status)
+        wd = dev_tokens(win)
+        if replay:
+            gb.gdn_verify_window(dims, T, **wd, **P, state_pool=pool, src_slot=rows, ckpt=None, o=o_win)
+            gb.gdn_commit_replay(dims, T, **wd, **P, accepted=torch.from_numpy(acc).cuda(), state_pool=pool,
+                                 src_slot=rows, dst_slot=rows, status=status)
+        else:
+            gb.gdn_verify_window(dims, T, **wd, **P, state_pool=pool, src_slot=rows, ckpt=ckpt, o=o_win)
+            gb.gdn_commit_accepted(dims, T, ckpt, torch.from_numpy(acc).cuda(), pool, dst_slot=rows,
+                                   status=status)
         ck_o, o_o = oracle.verify_window(T, win.q, win.k, win.v, win.a, win.b, w.A_log, w.dt_bias,
                                          S_bufs[cur], nan_fill=False, out=out)
         cur = 1 - cur
@@ -97,7 +103,7 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
             S_bufs[cur][r] = ck_o[r, acc[r]]
         mx = assert_o(host(o_win), o_o, "%s window %d outputs" % (w.name, i))
         worst["o_abs"] = max(worst["o_abs"], mx)
-        if i == 0:
+        if i == 0 and not replay:
             for r in range(B):  # every checkpoint of the first window
                 e = assert_state(host(ckpt[r, :T[r]]), ck_o[r, :T[r]], "%s window 0 row %d ckpt" % (w.name, r))
                 worst["state"] = max(worst["state"], e)
