@@ -71,6 +71,21 @@ __device__ __forceinline__ floatx4 mma4(floatx4 acc, float4 a, float4 b) {
   return acc;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// bf16 operand of v_mfma_f32_16x16x32_bf16 for 32-wide k block kb of row t of a
+// row-major bf16 matrix (row pitch ld elements, rows t >= n read as zero): lane
+// (r, g) feeds row element 32 kb + 8 g + e, e = 0..7, one 16-byte load.  Blocks
+// past the row width d (d = 16) are zero.
+template <int D>
+__device__ __forceinline__ bf16x8 frag32_row(const uint16_t *base, int64_t ld, int t, int kb, int n, int g4) {
+  const int c = 32 * kb + 8 * g4;
+  u32x4v w = {0u, 0u, 0u, 0u};
+  if (t < n && c < D) w = *reinterpret_cast<const u32x4v *>(base + int64_t(t) * ld + c);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 // Which row of the launch owns launch-local chunk `c` (rows are few: scalar scan).
 __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
   int row = 0;
@@ -102,7 +117,6 @@ struct Ws {
 
 template <int D>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
-  constexpr int NKB = D / 16;  // 16-wide k blocks over d
   __shared__ double sG[C];
   __shared__ __attribute__((aligned(16))) float sBeta[C];  // beta_m
   __shared__ __attribute__((aligned(16))) float sSK[C];    // beta_m e^{G_m}
@@ -125,9 +139,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   const uint16_t *Vc = args.v + tok_base * ldv + int64_t(h) * D;
   Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * ChunkArgs::ws_unit_floats(D));
 
-  auto row_frag = [&](const uint16_t *base, int64_t ld, int t, int kb) -> float4 {
-    if (t >= n) return zf4();
-    return unpack_bf16x4(*reinterpret_cast<const uint2 *>(base + int64_t(t) * ld + 16 * kb + 4 * g4));
+  auto frag32 = [&](const uint16_t *base, int64_t ld, int t, int kb) {
+    return frag32_row<D>(base, ld, t, kb, n, g4);
   };
 
   // 1. gates and the fp64 inclusive prefix sum of g (tokens t >= n: g = beta = 0);
@@ -184,76 +197,105 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     *reinterpret_cast<uint2 *>(ws.Kt + d * C + m4) = *reinterpret_cast<const uint2 *>(sKt + d * LDB + m4);
   }
 
-  // 2. K K^T -> A (strictly lower, scaled) and Q K^T -> P (lower with diagonal).
-  //    The 10 lower 16x16 tiles (ti >= tj) are dealt round-robin to the 4 waves.
-  for (int tile = w; tile < 10; tile += 4) {
-    int ti = 0;
-    while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
-    const int tj = tile - ti * (ti + 1) / 2;
-    float4 ak[NKB], aq[NKB], bk[NKB];
+  // 2. K K^T -> A (strictly lower, scaled) and Q K^T -> P (lower with diagonal) on
+  //    the bf16 matrix cores: K and Q are bf16, so every product is exact in fp32 and
+  //    only the fp32 accumulation rounds.  Wave w owns row block w: it loads the
+  //    fragments once (its Q rows, the K rows of all four blocks), computes tiles
+  //    (w, tj <= w) and writes zeros to the tiles right of the diagonal.
+  {
+    constexpr int NK32 = (D + 31) / 32;  // 32-wide k blocks over d (D = 16: half of one)
+    bf16x8 fk[4][NK32], fa[NK32], fq[NK32];  // fa: this wave's K rows (register arrays
+#pragma unroll                                 // are indexed by constants only)
+    for (int kb = 0; kb < NK32; ++kb) {
+      fq[kb] = frag32(Qc, ldqk, 16 * w + r16, kb);
+      fa[kb] = frag32(Kc, ldqk, 16 * w + r16, kb);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      ak[kb] = row_frag(Kc, ldqk, 16 * ti + r16, kb);
-      aq[kb] = row_frag(Qc, ldqk, 16 * ti + r16, kb);
-      bk[kb] = row_frag(Kc, ldqk, 16 * tj + r16, kb);
-    }
-    floatx4 kk = zero4(), qk = zero4();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      kk = mma4(kk, ak[kb], bk[kb]);
-      qk = mma4(qk, aq[kb], bk[kb]);
+      for (int tj = 0; tj < 4; ++tj) fk[tj][kb] = frag32(Kc, ldqk, 16 * tj + r16, kb);
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = 16 * ti + 4 * g4 + v, s = 16 * tj + r16;
-      float av = 0.0f, pv = 0.0f;
-      if (s <= t) {
-        const float dec = expf(float(sG[t] - sG[s]));
-        pv = dec * qk[v];
-        if (s < t) av = sBeta[t] * dec * kk[v];
+    for (int tj = 0; tj < 4; ++tj) {
+      floatx4 kk = zero4(), qk = zero4();
+      if (tj <= w) {
+#pragma unroll
+        for (int kb = 0; kb < NK32; ++kb) {
+          kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kb], fk[tj][kb], kk, 0, 0, 0);
+          qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fq[kb], fk[tj][kb], qk, 0, 0, 0);
+        }
       }
-      sA[t * LDC + s] = av;
-      ws.P[t * C + s] = pv;
-    }
-  }
-  for (int tile = w; tile < 6; tile += 4) {  // the 6 upper tiles are zero
-    int ti = 0, tj = 1;
-    for (int q = 0; q < tile; ++q) {
-      if (++tj == 4) { ++ti; tj = ti + 1; }
-    }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = 16 * ti + 4 * g4 + v, s = 16 * tj + r16;
-      sA[t * LDC + s] = 0.0f;
-      ws.P[t * C + s] = 0.0f;
+      for (int v = 0; v < 4; ++v) {
+        const int t = 16 * w + 4 * g4 + v, s = 16 * tj + r16;
+        float av = 0.0f, pv = 0.0f;
+        if (s <= t) {
+          const float dec = expf(float(sG[t] - sG[s]));
+          pv = dec * qk[v];
+          if (s < t) av = sBeta[t] * dec * kk[v];
+        }
+        if (tj <= w) sA[t * LDC + s] = av;  // the upper blocks of sA hold T below
+        ws.P[t * C + s] = pv;
+      }
     }
   }
   lds_barrier();
 
-  // 3. T = (I + A)^{-1} by forward substitution on one wave: lane j holds column j,
-  //    T[t][j] = [t == j] - sum_{m<t} A[t][m] T[m][j]; A row t is read as broadcast
-  //    float4s and summed in four interleaved partial sums.
-  if (w == 0) {
-    float Tc[C];  // T[t][lane], starting from the identity column
+  // 3. T = (I + A)^{-1}, A strictly lower triangular, by 16x16 blocks:
+  //    T_ii = (I + A_ii)^{-1}, then T_ij = -T_ii (sum_{j<=k<i} A_ik T_kj) for i > j,
+  //    one sub-diagonal at a time.  T_ii overwrites A_ii (no longer needed); T_ij
+  //    (i > j) is stored at block (j, i) of sA, right of the diagonal, so A's lower
+  //    blocks stay intact until the last product.
+  {
+    // diagonal blocks, one per wave: lane j < 16 holds column j of T_ww and runs the
+    // forward substitution T[t][j] = [t == j] - sum_{m<t} A[t][m] T[m][j]
+    float* Aw = sA + (16 * w) * LDC + 16 * w;
+    if (lane < 16) {
+      float Tc[16];
 #pragma unroll
-    for (int t = 0; t < C; ++t) Tc[t] = (t == lane) ? 1.0f : 0.0f;
+      for (int t = 0; t < 16; ++t) Tc[t] = (t == lane) ? 1.0f : 0.0f;
 #pragma unroll
-    for (int t = 1; t < C; ++t) {
-      float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+      for (int t = 1; t < 16; ++t) {
+        float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-      for (int m = 0; m < t; m += 4) {
-        const float4 ar = *reinterpret_cast<const float4 *>(sA + t * LDC + m);
-        p0 = fmaf(ar.x, Tc[m + 0], p0);
-        p1 = fmaf(ar.y, Tc[m + 1], p1);
-        p2 = fmaf(ar.z, Tc[m + 2], p2);
-        p3 = fmaf(ar.w, Tc[m + 3], p3);
+        for (int m = 0; m < t; m += 4) {
+          const float4 ar = *reinterpret_cast<const float4 *>(Aw + t * LDC + m);
+          p0 = fmaf(ar.x, Tc[m + 0], p0);
+          p1 = fmaf(ar.y, Tc[m + 1], p1);
+          p0 = fmaf(ar.z, Tc[m + 2], p0);
+          p1 = fmaf(ar.w, Tc[m + 3], p1);
+        }
+        Tc[t] -= p0 + p1;  // A[t][m] = 0 for m >= t within the block
       }
-      Tc[t] -= (p0 + p1) + (p2 + p3);  // A[t][m] = 0 for m >= t, so the tail terms vanish
-    }
 #pragma unroll
-    for (int t = 0; t < C; ++t) sA[t * LDC + lane] = Tc[t];
+      for (int t = 0; t < 16; ++t) Aw[t * LDC + lane] = Tc[t];
+    }
+    lds_barrier();
+    // T_ij block (i > j) lives at rows 16 j.., columns 16 i.. of sA
+    auto tblk = [&](int i, int j) -> float * {
+      return i == j ? sA + (16 * i) * LDC + 16 * i : sA + (16 * j) * LDC + 16 * i;
+    };
+    // B fragment of a 16x16 block X (lane (r, g) feeds X[4g + e][r], e = 0..3)
+    auto bfrag = [&](const float *X) {
+      return make_float4(X[(4 * g4 + 0) * LDC + r16], X[(4 * g4 + 1) * LDC + r16],
+                         X[(4 * g4 + 2) * LDC + r16], X[(4 * g4 + 3) * LDC + r16]);
+    };
+    auto afrag = [&](const float *X) {  // A fragment: X[r][4g + e]
+      return *reinterpret_cast<const float4 *>(X + r16 * LDC + 4 * g4);
+    };
+    for (int lvl = 1; lvl < 4; ++lvl) {
+      const int i = w, j = w - lvl;
+      if (j >= 0) {
+        // X = sum_{k=j}^{i-1} A_ik T_kj, then T_ij = -T_ii X (X's result layout is the
+        // B-operand layout of the second product)
+        floatx4 x = zero4();
+        for (int k = j; k < i; ++k)
+          x = mma4(x, afrag(sA + (16 * i) * LDC + 16 * k), bfrag(tblk(k, j)));
+        floatx4 y = mma4(zero4(), afrag(tblk(i, i)), make_float4(x[0], x[1], x[2], x[3]));
+        float *dstb = tblk(i, j);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dstb[(4 * g4 + v) * LDC + r16] = -y[v];
+      }
+      lds_barrier();
+    }
   }
-  lds_barrier();
 
   // 4. W = T diag(beta e^G) K and U' = T diag(beta) V.  Wave w owns column tiles
   //    {2w, 2w+1} of every row tile (T is lower triangular: k < 16(ti+1)).
@@ -262,7 +304,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
       floatx4 wa = zero4(), ua = zero4();
       for (int kb = 0; kb <= ti; ++kb) {
         const int k0 = 16 * kb + 4 * g4;
-        const float4 tr = *reinterpret_cast<const float4 *>(sA + (16 * ti + r16) * LDC + k0);
+        // block (ti, kb) of T: the diagonal block in place, the others right of it
+        const float *tb = kb == ti ? sA + (16 * ti) * LDC + 16 * ti : sA + (16 * kb) * LDC + 16 * ti;
+        const float4 tr = *reinterpret_cast<const float4 *>(tb + r16 * LDC + 4 * g4);
         const float4 sk = *reinterpret_cast<const float4 *>(sSK + k0);
         const float4 sb = *reinterpret_cast<const float4 *>(sBeta + k0);
         const int d = 16 * nt + r16;
