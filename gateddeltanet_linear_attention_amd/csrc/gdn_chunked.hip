@@ -484,15 +484,20 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
   }
 }
 
-// Outputs of one (chunk, value head, half of the value channels), from the chunk's
-// start state S_c and U recorded by the scan: O = diag(e^G) Q S_c^T + P U (wave w:
-// tokens 16w..16w+15).
+// Outputs of one (chunk, value head, half of the value channels) from the chunk's
+// start state S_c and U recorded by the scan: O = diag(e^G) Q S_c^T + P U.  The
+// block stages its half of S_c and of U^T in LDS once; wave w computes tokens
+// 16w..16w+15 (Q and P rows in registers) against every 16-channel tile of the half.
 template <int D>
 __global__ __launch_bounds__(256) void chunk_out_kernel(ChunkArgs args) {
   constexpr int NKB = D / 16;
   constexpr int NH = D / 16 >= 2 ? 2 : 1;  // value-channel parts per chunk
-  constexpr int NTP = D / 16 / NH;        // 16-wide column tiles per part
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int DH = D / NH;              // value channels per part
+  constexpr int NTP = DH / 16;            // 16-wide column tiles per part
+  constexpr int LDS_ = D + 4;
+  __shared__ __attribute__((aligned(16))) float sSc[DH * LDS_];  // S_c rows of this part
+  __shared__ __attribute__((aligned(16))) float sU[DH * LDC];    // U^T rows of this part
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int cl = blockIdx.x, h = blockIdx.y, part = blockIdx.z;
   const int row = row_of_chunk(args, cl);
@@ -503,43 +508,48 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(ChunkArgs args) {
   const int n_v = args.n_v, n_qk = args.n_qk, hq = h / args.group;
   const int64_t ldqk = int64_t(n_qk) * D;
   const Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * ChunkArgs::ws_unit_floats(D));
+  const int i_base = part * DH;
 
+  for (int idx = tid; idx < DH * (D / 4); idx += 256) {
+    const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+    *reinterpret_cast<float4 *>(sSc + i * LDS_ + d4) =
+        *reinterpret_cast<const float4 *>(ws.Sc + int64_t(i_base + i) * D + d4);
+  }
+  for (int idx = tid; idx < DH * (C / 4); idx += 256) {
+    const int i = idx / (C / 4), s4 = (idx % (C / 4)) * 4;
+    *reinterpret_cast<float4 *>(sU + i * LDC + s4) =
+        *reinterpret_cast<const float4 *>(ws.Ut + (i_base + i) * C + s4);
+  }
   const int t_me = 16 * w + r16;
   const uint16_t *Qc = args.q + tok_base * ldqk + int64_t(hq) * D;
+  const uint16_t *qrow = Qc + int64_t(min(t_me, n - 1)) * ldqk;  // rows past the end: never stored
   float4 qf[NKB], pf[4];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-    qf[kb] = t_me < n ? unpack_bf16x4(*reinterpret_cast<const uint2 *>(Qc + int64_t(t_me) * ldqk + 16 * kb + 4 * g4))
-                      : zf4();
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    pf[kb] = kb <= w ? *reinterpret_cast<const float4 *>(ws.P + t_me * C + 16 * kb + 4 * g4) : zf4();
   float eg[4];
 #pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+    qf[kb] = unpack_bf16x4(*reinterpret_cast<const uint2 *>(qrow + 16 * kb + 4 * g4));
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) pf[kb] = *reinterpret_cast<const float4 *>(ws.P + t_me * C + 16 * kb + 4 * g4);
+#pragma unroll
   for (int v = 0; v < 4; ++v) eg[v] = ws.eG[16 * w + 4 * g4 + v];
-  // B fragments of column tile nt (S_c rows and U^T rows), all loaded up front
-  float4 sf[NTP][NKB], uf[NTP][4];
+  lds_barrier();
+
 #pragma unroll
   for (int q = 0; q < NTP; ++q) {
-    const int i = 16 * (part * NTP + q) + r16;
+    const float *srow = sSc + (16 * q + r16) * LDS_;
+    const float *urow = sU + (16 * q + r16) * LDC;
+    floatx4 oa = zero4(), ob = zero4();
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      sf[q][kb] = *reinterpret_cast<const float4 *>(ws.Sc + int64_t(i) * D + 16 * kb + 4 * g4);
+    for (int kb = 0; kb < NKB; kb += 2) {
+      oa = mma4(oa, qf[kb], *reinterpret_cast<const float4 *>(srow + 16 * kb + 4 * g4));
+      if (kb + 1 < NKB) ob = mma4(ob, qf[kb + 1], *reinterpret_cast<const float4 *>(srow + 16 * (kb + 1) + 4 * g4));
+    }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      uf[q][kb] = kb <= w ? *reinterpret_cast<const float4 *>(ws.Ut + i * C + 16 * kb + 4 * g4) : zf4();
-  }
+    for (int v = 0; v < 4; ++v) oa[v] = eg[v] * (oa[v] + ob[v]);
 #pragma unroll
-  for (int q = 0; q < NTP; ++q) {
-    const int i = 16 * (part * NTP + q) + r16;
-    floatx4 oa = zero4();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) oa = mma4(oa, qf[kb], sf[q][kb]);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) oa[v] *= eg[v];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      if (kb <= w) oa = mma4(oa, pf[kb], uf[q][kb]);
+    for (int kb = 0; kb < 4; ++kb)  // P is zero right of the diagonal block
+      if (kb <= w) oa = mma4(oa, pf[kb], *reinterpret_cast<const float4 *>(urow + 16 * kb + 4 * g4));
+    const int i = i_base + 16 * q + r16;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int t = 16 * w + 4 * g4 + v;
@@ -548,10 +558,6 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(ChunkArgs args) {
   }
 }
 
-// Tail checkpoint j of a row, 16 value rows (tile mi) of one head per block, from
-// the start state S_c and U of the chunk that holds its position p (j' = p - c0):
-// S_p = e^{G_j'} S_c + U^T diag(e^{G_j' - G_s} [s <= j']) K.  Wave w computes the
-// column tiles {2w, 2w+1}.
 template <int D>
 __global__ __launch_bounds__(256) void chunk_ckpt_kernel(ChunkArgs args) {
   constexpr size_t UNIT = size_t(D) * D;
