@@ -89,7 +89,10 @@ __device__ __forceinline__ void store_nt(float *p, const float (&x)[4]) {
   __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
 }
 
-template <int D, int LPR, int RPL, int WAVES>
+// REPLAY: the instantiation behind gdn_commit_replay (accepted counts on the
+// device, no outputs, no checkpoints).  Both instantiations compile the same
+// per-row arithmetic, so they round identically.
+template <int D, int LPR, int RPL, int WAVES, bool REPLAY>
 __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs args) {
   constexpr int NV = D / LPR / 4;                  // float4 per lane per state row
   constexpr int ROWS = WAVES * 64 / LPR * RPL;     // state rows per block
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   const int src = args.src[r], dst = args.dst[r], ck_first = args.ck_first[r];
   const int ck_row = args.ck_row[r];
   const int n_v = args.n_v, n_qk = args.n_qk;
-  if (args.accepted) {
+  if (REPLAY) {
     // Replay of the accepted prefix: the bonus token and a_r drafts, the same
     // sequence of operations as the first a_r + 1 tokens of the window, so the
     // state it leaves is bit-identical to that window's checkpoint slot a_r.
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     }
     ntok = acc + 1;
   }
-  const bool write_o = args.o != nullptr;
+  constexpr bool write_o = !REPLAY;
 
   float s[RPL][NV][4];
 #pragma unroll
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
         const float oi = group_sum<LPR>(po);
         if (sub == 0) sO[t][i_local + q] = to_bf16(oi);
       }
-      if (t >= ck_first) {
+      if (!REPLAY && t >= ck_first) {
         float *cp = args.ckpt + ((size_t(ck_row) * args.ck_slots + (t - ck_first)) * n_v + h) * UNIT +
                     size_t(i0 + q) * D;
 #pragma unroll
@@ -242,24 +245,29 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 
 }  // namespace
 
+template <int D, int LPR, int RPL, int WAVES>
+static void launch_d(const RecurrentArgs &args, hipStream_t stream) {
+  constexpr int TILES = D / (WAVES * 64 / LPR * RPL);
+  const dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * TILES);
+  if (args.accepted)
+    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, true>), grid, dim3(64 * WAVES), 0, stream, args);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, false>), grid, dim3(64 * WAVES), 0, stream, args);
+}
+
 hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream) {
   if (args.n_rows <= 0) return hipSuccess;
   if (args.n_rows > kRowsPerLaunch) return hipErrorInvalidValue;
   for (int r = 0; r < args.n_rows; ++r)  // the kernel stages a row's tokens in fixed LDS arrays
     if (args.ntok[r] < 1 || args.ntok[r] > kMaxWindow) return hipErrorInvalidValue;
-  if (d == 128) {
-    constexpr int D = 128, LPR = 16, RPL = 1, WAVES = 8;
-    constexpr int TILES = D / (WAVES * 64 / LPR * RPL);
-    dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * TILES);
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES>), grid, dim3(64 * WAVES), 0, stream, args);
-  } else if (d == 16) {
-    constexpr int D = 16, LPR = 4, RPL = 1, WAVES = 1;
-    constexpr int TILES = D / (WAVES * 64 / LPR * RPL);
-    dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * TILES);
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES>), grid, dim3(64 * WAVES), 0, stream, args);
-  } else {
+  // replay writes neither outputs nor checkpoints; every other call writes outputs
+  if (args.accepted ? (args.o || args.ckpt || !args.status) : !args.o) return hipErrorInvalidValue;
+  if (d == 128)
+    launch_d<128, 16, 1, 8>(args, stream);
+  else if (d == 16)
+    launch_d<16, 4, 1, 1>(args, stream);
+  else
     return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 
