@@ -124,8 +124,8 @@ int gdn_commit_accepted(const gdn_dims *dims, int32_t n_rows, const int32_t *row
 
 /*
  * gdn_commit_replay -- rollback without checkpoints: the pull request thread's
- * closing note replaces dense recurrent checkpoints with compact fixed-state
- * replay.  Row r re-runs the first a_r + 1 tokens of its window (row_tokens[r] =
+ * closing note replaces dense recurrent checkpoints with a replay of the
+ * recurrent state.  Row r re-runs the first a_r + 1 tokens of its window (row_tokens[r] =
  * T_r tokens packed as for gdn_verify_window; the bonus token and the a_r accepted
  * drafts) from the committed state in slot src_slot[r] (-1: zero state) and
  * writes the resulting state to slot dst_slot[r] (== src_slot[r] commits in

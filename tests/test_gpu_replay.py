@@ -2,7 +2,7 @@
 gdn_commit_replay), through the C ABI.
 
 The pull request thread "Run chained MTP drafting in the batch Engine" closes by
-replacing dense recurrent checkpoints with compact fixed-state replay; the reading
+replacing dense recurrent checkpoints with a replay of the state; the reading
 taken here: verification computes the window's outputs from the committed state
 and stores no checkpoint, and commit re-runs the accepted prefix (the previous
 bonus token and a_r drafts) from the committed state.  Checked:
