@@ -162,6 +162,39 @@ def run_steps(layers, steps, warmup, stream, torch):
     return wall, verify_ms, commit_ms
 
 
+def measure_graph(gb, synth, torch, Ts, steps, warmup, n_layers, seed0, replay=False):
+    """The same step captured once as a HIP graph on a side stream and replayed:
+    wall time per step (launch costs of the 2 L calls removed from the host side)."""
+    dims = gb.Dims(16, 32, 128, 128, 3)
+    cap = torch.cuda.Stream()
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, cap, replay) for i in range(n_layers)]
+
+    def step():
+        for s in sets:
+            s.verify()
+        for s in sets:
+            s.commit()
+    with torch.cuda.stream(cap):
+        for _ in range(3):
+            step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for s in sets:
+        assert int(s.status.abs().sum()) == 0
+    upd = int(sum(Ts)) * V_HEADS * n_layers * steps
+    return {"ms_per_layer": 1e3 * wall / steps / n_layers, "head_token_updates_per_s": upd / wall}
+
+
 def cpu_baseline(s: "VerifySet", seconds: float, seconds_1thread: float):
     """The fp64 oracle on the host, on the same window as the GPU step (a bounded
     sample: repeated windows for about `seconds` of work), with every host core the
@@ -299,6 +332,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-replay", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replays of the batch-1 step")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the 2048-token chunked prefill and print its figures")
     ap.add_argument("--prefill-reps", type=int, default=20)
@@ -337,6 +372,10 @@ def main():
     if not args.no_batch1:
         _, r1 = measure(gb, synth, torch, [4], args.steps, args.warmup, args.layers, stream, 600)
         out_b1 = side(r1, [4])
+        if not args.no_graph:
+            out_b1["graph"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup, args.layers, 600)
+            out_b1["graph_replay_mode"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup,
+                                                        args.layers, 600, replay=True)
     if not args.no_mixed:
         Ts = (synth.verify_workload("conc16").draft_lens + 1).astype(np.int32)
         _, rm = measure(gb, synth, torch, Ts, args.steps, args.warmup, args.layers, stream, 700)

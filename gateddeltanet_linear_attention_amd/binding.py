@@ -235,7 +235,7 @@ def _replay_args(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted
     cd = dims.c()
     args = (ctypes.byref(cd), n_rows, _ip(T), *toks, ap, pp, n_slots, _ip(src), _ip(dst), sp,
             _stream(stream))
-    return args, (cd, T, src, dst)
+    return args, (cd, T, src, dst, q, k, v, a, b, A_log, dt_bias, accepted, state_pool, status)
 
 
 def gdn_commit_replay(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted, state_pool,
@@ -315,13 +315,16 @@ def gdn_run_transaction(dims: Dims, row_tokens, n_ckpt, q, k, v, a, b, A_log, dt
 class PreparedCall:
     """One entry-point call with its arguments checked and marshalled once; calling it
     re-issues the same C call (same buffers, same stream).  For tight loops where the
-    per-call Python checks would dominate the host time."""
+    per-call Python checks would dominate the host time, and for capture into a HIP
+    graph.  It holds a reference to every host array and device tensor its pointers
+    refer to, so none of them can be freed (and its memory reused) while the call
+    exists."""
 
     def __init__(self, name: str, args: tuple, keep: tuple):
         self.name = name
         self._fn = getattr(lib(), name)
         self._args = args
-        self._keep = keep  # host arrays the pointers refer to
+        self._keep = keep  # host arrays and tensors the pointers refer to
 
     def __call__(self) -> None:
         rc = self._fn(*self._args)
@@ -339,7 +342,8 @@ def prepare_verify_window(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias,
     cp = _ckpt(dims, ckpt, n_rows, optional=True)
     cd = dims.c()
     args = (ctypes.byref(cd), n_rows, _ip(T), *toks, pp, n_slots, _ip(src), cp, op, _stream(stream))
-    return PreparedCall("gdn_verify_window", args, (cd, T, src))
+    return PreparedCall("gdn_verify_window", args,
+                        (cd, T, src, q, k, v, a, b, A_log, dt_bias, state_pool, ckpt, o))
 
 
 def prepare_commit_replay(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted, state_pool,
@@ -360,4 +364,4 @@ def prepare_commit_accepted(dims: Dims, row_tokens, ckpt, accepted, state_pool, 
     pp, n_slots = _pool(dims, state_pool)
     cd = dims.c()
     args = (ctypes.byref(cd), n_rows, _ip(T), cp, ap, pp, n_slots, _ip(dst), sp, _stream(stream))
-    return PreparedCall("gdn_commit_accepted", args, (cd, T, dst))
+    return PreparedCall("gdn_commit_accepted", args, (cd, T, dst, ckpt, accepted, state_pool, status))
