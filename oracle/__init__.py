@@ -17,7 +17,10 @@ expresses the verify / commit / decode calls through it:
 * commit(a) -- the committed state becomes the state after a+1 window tokens
   (the previous bonus token plus a accepted drafts), same page, sections
   "Correctness fix" and "Rollback fix and corrected quality disposition";
-* decode -- one token; the verify window is, by definition, repeated decode.
+* decode -- one token; the verify window is, by definition, repeated decode;
+* verify tree -- a draft tree instead of a chain: each node runs from its
+  parent's state (the pages run chains only and refuse tree shapes, "Occamy 1.0
+  MTP", section "MTP1 runtime"; built as an extension, checked against brute force).
 """
 from __future__ import annotations
 
@@ -168,6 +171,42 @@ def verify_window(row_tokens, q, k, v, a, b, A_log, dt_bias, S_committed, k_max=
     assert np.all((T >= 1) & (T <= k_max + 1))
     _, ckpt, o = run_sequential(T, q, k, v, a, b, A_log, dt_bias, S_committed, n_tail=T,
                                 n_slot=k_max + 1, n_threads=n_threads, nan_fill=nan_fill, out=out)
+    return ckpt, o
+
+
+def verify_tree(row_tokens, parents, q, k, v, a, b, A_log, dt_bias, S_committed, k_max=3):
+    """Token-tree windows, by the plain definition: node t of row r is its root path
+    (its ancestors in order, then t itself; parents[cu_r + t] = -1 means the
+    committed state) run token by token from the committed state -- one sequential
+    run per node.  A chain (parent t - 1) is the verify window.
+
+    Returns (ckpt [B][k_max+1][H_v][d_v][d_k] with slot t = node t's state, NaN past
+    T_r, o [N][H_v][d_v] with o_t = S_t q_t)."""
+    T = np.asarray(row_tokens, np.int64)
+    par = np.asarray(parents, np.int64).ravel()
+    q, k, v, a, b = map(_f64, (q, k, v, a, b))
+    S_committed = _f64(S_committed)
+    B, Hv, dv, dk = S_committed.shape
+    assert np.all((T >= 1) & (T <= k_max + 1)) and par.size == int(T.sum())
+    cu = np.concatenate([[0], np.cumsum(T)])
+    ckpt = np.full((B, k_max + 1, Hv, dv, dk), np.nan)
+    o = np.zeros((int(T.sum()), Hv, dv))
+    for r in range(B):
+        if par[cu[r]] != -1:
+            raise ValueError("row %d: the first window token must follow the committed state" % r)
+        for t in range(int(T[r])):
+            p = int(par[cu[r] + t])
+            if not -1 <= p < t:
+                raise ValueError("row %d token %d: parent %d is not an earlier node" % (r, t, p))
+            path, x = [], t
+            while x >= 0:
+                path.append(x)
+                x = int(par[cu[r] + x])
+            idx = cu[r] + np.array(path[::-1])
+            S_fin, _, o_path = run_sequential([len(idx)], q[idx], k[idx], v[idx], a[idx], b[idx], A_log,
+                                              dt_bias, S_committed[r:r + 1])
+            ckpt[r, t] = S_fin[0]
+            o[cu[r] + t] = o_path[-1]
     return ckpt, o
 
 

@@ -357,3 +357,64 @@ def test_oracle_rejects_bad_arguments():
     with pytest.raises(ValueError):  # n_tail larger than the row
         oracle.run_sequential([3], c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"], c["dt_bias"],
                               c["S0"], n_tail=[4], n_slot=4)
+
+
+# ---------------------------------------------------------------- token trees
+
+TREES = [[-1, 0, 0, 1], [-1, -1, 1, 0], [-1, 0, 1, 2], [-1, -1, -1, -1], [-1, 0, 0], [-1]]
+
+
+def test_tree_nodes_match_brute_force_on_their_paths():
+    """Node states and outputs against the explicit transition-matrix evaluation of
+    each node's root path, on grouped heads with d_k != d_v."""
+    Hqk, Hv, dk, dv = 1, 2, 6, 5
+    T = [len(p) for p in TREES]
+    parents = np.concatenate([np.array(p) for p in TREES])
+    c = rand_case(91, T, Hqk, Hv, dk, dv)
+    ckpt, o = oracle.verify_tree(T, parents, c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"],
+                                 c["dt_bias"], c["S0"])
+    cu = np.concatenate([[0], np.cumsum(T)])
+    for r, par in enumerate(TREES):
+        for t in range(len(par)):
+            path, x = [], t
+            while x >= 0:
+                path.append(x)
+                x = par[x]
+            idx = cu[r] + np.array(path[::-1])
+            for h in range(Hv):
+                alpha, beta = lib_gates(c["a"][idx, h], c["b"][idx, h], c["A_log"][h], c["dt_bias"][h])
+                states, outs = brute_force_unit(c["S0"][r, h], c["q"][idx, 0], c["k"][idx, 0], c["v"][idx, h],
+                                                alpha, beta)
+                assert rel(ckpt[r, t, h], states[-1]) < 1e-12
+                assert np.max(np.abs(o[cu[r] + t, h] - outs[-1])) < 1e-12 * max(1.0, np.abs(outs).max())
+        assert np.all(np.isnan(ckpt[r, len(par):]))
+
+
+def test_chain_tree_is_the_verify_window():
+    T = [4, 2, 3]
+    parents = np.concatenate([np.arange(t) - 1 for t in T])
+    c = rand_case(92, T, 2, 4, 16, 16)
+    ck_t, o_t = oracle.verify_tree(T, parents, c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"],
+                                   c["dt_bias"], c["S0"])
+    ck_w, o_w = oracle.verify_window(T, c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"], c["dt_bias"], c["S0"])
+    for r, t in enumerate(T):
+        assert np.array_equal(ck_t[r, :t], ck_w[r, :t])
+    assert np.array_equal(o_t, o_w)
+
+
+def test_star_tree_is_independent_single_steps():
+    T = [4]
+    c = rand_case(93, T, 1, 2, 8, 8)
+    ck, o = oracle.verify_tree(T, [-1, -1, -1, -1], c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"],
+                               c["dt_bias"], c["S0"])
+    for t in range(4):
+        S1, o1 = oracle.decode_step(c["q"][t:t + 1], c["k"][t:t + 1], c["v"][t:t + 1], c["a"][t:t + 1],
+                                    c["b"][t:t + 1], c["A_log"], c["dt_bias"], c["S0"])
+        assert np.array_equal(ck[0, t], S1[0]) and np.array_equal(o[t], o1[0])
+
+
+def test_tree_rejects_bad_parents():
+    c = rand_case(94, [3], 1, 1, 4, 4)
+    for bad in ([0, 0, 1], [-1, 1, 0], [-1, 0, 2], [-1, -2, 0]):
+        with pytest.raises(ValueError):
+            oracle.verify_tree([3], bad, c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"], c["dt_bias"], c["S0"])
