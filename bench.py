@@ -52,6 +52,7 @@ def commit_bytes(n_units: int) -> int:
     return n_units * 2 * STATE_BYTES
 
 
+TREE4 = [-1, 0, 0, 1]      # draft tree of the tree line: the bonus token, two children, one grandchild
 REPLAY_TOKEN_BYTES = 392  # per head-token replayed: k (shared by 2 v-heads) 128 + v 256 + a,b 8
 
 
@@ -90,7 +91,7 @@ class VerifySet:
     """One buffer set: state pool, checkpoints, a window of tokens, accepted counts,
     and the two prepared C-ABI calls of a step."""
 
-    def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False):
+    def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False, parents=None):
         import numpy as np
         import torch
         shape = synth.FULL
@@ -122,6 +123,11 @@ class VerifySet:
             self.commit = gb.prepare_commit_replay(dims, Ts, **tin, accepted=self.acc, state_pool=self.pool,
                                                    src_slot=rows, dst_slot=rows, status=self.status,
                                                    stream=stream)
+        elif parents is not None:  # a draft tree per row; commit the accepted path's last node
+            self.verify = gb.prepare_verify_tree(dims, Ts, np.tile(parents, B), **self.t, state_pool=self.pool,
+                                                 src_slot=rows, ckpt=self.ckpt, o=self.o, stream=stream)
+            self.commit = gb.prepare_commit_accepted(dims, Ts, self.ckpt, self.acc, self.pool, dst_slot=rows,
+                                                     status=self.status, stream=stream)
         else:
             self.verify = gb.prepare_verify_window(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
                                                    ckpt=self.ckpt, o=self.o, stream=stream)
@@ -286,11 +292,11 @@ def measure_prefill(gb, synth, torch, stream, reps):
             "algorithmic_flops_per_call": fl}
 
 
-def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay=False):
+def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay=False, parents=None):
     """Steps over n_layers layers of windows with per-row token counts Ts (replay:
-    verify without checkpoints, commit by replay)."""
+    verify without checkpoints, commit by replay; parents: one draft tree per row)."""
     dims = gb.Dims(16, 32, 128, 128, 3)
-    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay) for i in range(n_layers)]
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents) for i in range(n_layers)]
     wall, verify_ms, commit_ms = run_steps(sets, steps, warmup, stream, torch)
     for s in sets:
         assert int(s.status.abs().sum()) == 0
@@ -332,6 +338,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-replay", action="store_true")
+    ap.add_argument("--no-tree", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replays of the batch-1 step")
     ap.add_argument("--prefill-only", action="store_true",
@@ -391,6 +398,13 @@ def main():
                       "replay_us_mean": 1e3 * rr["commit_ms_mean"], "replay_gbps": rr["commit_gbps"],
                       "step_gbps": rr["step_gbps"],
                       "step_algorithmic_bytes_per_layer": rr["verify_bytes"] + rr["commit_bytes"]}
+    out_tree = None
+    if not args.no_tree:
+        tree = np.array(TREE4, np.int32)
+        _, rt = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 800,
+                        parents=tree)
+        out_tree = side(rt, [4] * 16)
+        out_tree["parents"] = TREE4
     prefill = None if args.no_prefill else measure_prefill(gb, synth, torch, stream, args.prefill_reps)
     cpu = None
     if not args.no_cpu_baseline:
@@ -429,6 +443,7 @@ def main():
         "batch1": out_b1,
         "conc16_mixed_k": out_mixed,
         "conc16_k3_replay": out_replay,
+        "conc16_tree4": out_tree,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

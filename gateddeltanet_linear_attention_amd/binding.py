@@ -59,6 +59,8 @@ _SIGS = {
                          [ctypes.c_int32, _I32P, _VP, _VP, _VP],
     "gdn_commit_accepted": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _VP, _VP, _VP,
                             ctypes.c_int32, _I32P, _VP, _VP],
+    "gdn_verify_tree": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _I32P] + [_VP] * 8 +
+                       [ctypes.c_int32, _I32P, _VP, _VP, _VP],
     "gdn_commit_replay": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
                          [_VP, ctypes.c_int32, _I32P, _I32P, _VP, _VP],
     "gdn_chunked_workspace_bytes": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, ctypes.c_int32],
@@ -204,6 +206,25 @@ def gdn_verify_window(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, sta
     _check("gdn_verify_window", rc)
 
 
+def gdn_verify_tree(dims: Dims, row_tokens, parents, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot,
+                    ckpt, o, stream=None) -> None:
+    """Token-tree windows: token t of a row runs from its parent's state (parents per
+    packed token, -1 = the committed state); checkpoint slot t = node t's state."""
+    T, par, src = _i32(row_tokens), _i32(parents), _i32(src_slot)
+    n_rows = T.size
+    if src.size != n_rows:
+        raise ValueError("row_tokens and src_slot lengths differ")
+    N = int(T.sum())
+    if par.size != N:
+        raise ValueError("parents must hold one entry per packed token")
+    toks, op = _token_ptrs(dims, N, q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    cp = _ckpt(dims, ckpt, n_rows)
+    rc = lib().gdn_verify_tree(ctypes.byref(dims.c()), n_rows, _ip(T), _ip(par), *toks, pp, n_slots,
+                               _ip(src), cp, op, _stream(stream))
+    _check("gdn_verify_tree", rc)
+
+
 def gdn_commit_accepted(dims: Dims, row_tokens, ckpt, accepted, state_pool, dst_slot, status,
                         stream=None) -> None:
     """Copy checkpoint slot accepted[r] (device int32) of each row to slot dst_slot[r]."""
@@ -344,6 +365,22 @@ def prepare_verify_window(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias,
     args = (ctypes.byref(cd), n_rows, _ip(T), *toks, pp, n_slots, _ip(src), cp, op, _stream(stream))
     return PreparedCall("gdn_verify_window", args,
                         (cd, T, src, q, k, v, a, b, A_log, dt_bias, state_pool, ckpt, o))
+
+
+def prepare_verify_tree(dims: Dims, row_tokens, parents, q, k, v, a, b, A_log, dt_bias, state_pool,
+                        src_slot, ckpt, o, stream=None) -> PreparedCall:
+    T, par, src = _i32(row_tokens), _i32(parents), _i32(src_slot)
+    n_rows = T.size
+    N = int(T.sum())
+    if par.size != N:
+        raise ValueError("parents must hold one entry per packed token")
+    toks, op = _token_ptrs(dims, N, q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    cp = _ckpt(dims, ckpt, n_rows)
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, _ip(T), _ip(par), *toks, pp, n_slots, _ip(src), cp, op, _stream(stream))
+    return PreparedCall("gdn_verify_tree", args,
+                        (cd, T, par, src, q, k, v, a, b, A_log, dt_bias, state_pool, ckpt, o))
 
 
 def prepare_commit_replay(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted, state_pool,

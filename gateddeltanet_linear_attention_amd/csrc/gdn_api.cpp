@@ -98,7 +98,8 @@ void fill_common(gdn::RecurrentArgs &ra, const gdn_dims *d, const uint16_t *q,
 int launch_recurrent_rows(const gdn_dims *d, const gdn::RecurrentArgs &proto,
                           const std::vector<int32_t> &rows, const std::vector<int64_t> &cu,
                           const int32_t *ntok, const int32_t *src, const int32_t *dst,
-                          const int32_t *n_ck, hipStream_t stream) {
+                          const int32_t *n_ck, hipStream_t stream,
+                          const int32_t *parents = nullptr) {
   for (size_t base = 0; base < rows.size(); base += kRowsPerLaunch) {
     gdn::RecurrentArgs ra = proto;
     const size_t n = std::min<size_t>(kRowsPerLaunch, rows.size() - base);
@@ -111,7 +112,13 @@ int launch_recurrent_rows(const gdn_dims *d, const gdn::RecurrentArgs &proto,
       ra.dst[j] = dst ? dst[r] : -1;
       ra.ck_first[j] = n_ck ? ntok[r] - n_ck[r] : ntok[r];
       ra.ck_row[j] = r;
+      if (parents) {  // byte t: parent of window token t, plus one
+        uint32_t packed = 0;
+        for (int32_t t = 0; t < ntok[r]; ++t) packed |= uint32_t(parents[cu[r] + t] + 1) << (8 * t);
+        ra.tree[j] = packed;
+      }
     }
+    ra.tree_mode = parents ? 1 : 0;
     if (gdn::launch_recurrent(ra, d->d_k, stream) != hipSuccess) return GDN_E_HIP;
   }
   return GDN_OK;
@@ -297,6 +304,44 @@ int gdn_verify_window(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
   fill_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, nullptr, ckpt, o);
   return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, src_slot, nullptr,
                                ckpt ? row_tokens : nullptr, static_cast<hipStream_t>(stream));
+}
+
+int gdn_verify_tree(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                    const int32_t *parents, const uint16_t *q, const uint16_t *k,
+                    const uint16_t *v, const float *a, const float *b, const float *A_log,
+                    const float *dt_bias, const float *state_pool, int32_t n_slots,
+                    const int32_t *src_slot, float *ckpt, uint16_t *o, void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if (!row_tokens || !parents) return GDN_E_NULL;
+  if ((rc = check_tokens(q, k, v, a, b, A_log, dt_bias, o))) return rc;
+  if (!state_pool || !src_slot || !ckpt) return GDN_E_NULL;
+  if (!aligned(state_pool, 16) || !aligned(ckpt, 16)) return GDN_E_ALIGN;
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+  const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  for (int32_t r = 0; r < n_rows; ++r) {
+    if (parents[cu[r]] != -1) return GDN_E_RANGE;  // the window's first token follows the committed state
+    for (int32_t t = 1; t < row_tokens[r]; ++t)
+      if (parents[cu[r] + t] < -1 || parents[cu[r] + t] >= t) return GDN_E_RANGE;
+  }
+  if ((rc = check_slots(n_rows, n_slots, src_slot, nullptr))) return rc;
+  const Sizes s = sizes_of(dims);
+  const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
+  const size_t ck_b = size_t(n_rows) * s.ck_row_floats * 4;
+  const size_t o_b = size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2;
+  if (overlap(ckpt, ck_b, state_pool, pool_b) || overlap(o, o_b, ckpt, ck_b) ||
+      overlap(o, o_b, state_pool, pool_b))
+    return GDN_E_ALIAS;
+
+  std::vector<int32_t> rows(static_cast<size_t>(n_rows));
+  for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
+  gdn::RecurrentArgs proto;
+  fill_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, nullptr, ckpt, o);
+  return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, src_slot, nullptr, row_tokens,
+                               static_cast<hipStream_t>(stream), parents);
 }
 
 int gdn_commit_replay(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,

@@ -35,6 +35,10 @@ struct RecurrentArgs {
   // sets bit ck_row[r] of status.
   const int32_t *accepted;
   uint32_t *status;
+  // Tree windows (tree_mode != 0): byte t of tree[r] is the parent of window token t
+  // plus one (0: the committed state); token t then runs from its parent's state.
+  int32_t tree_mode;
+  uint32_t tree[kRowsPerLaunch];
   int32_t n_qk, n_v, group;         // heads; group = n_v / n_qk
   int32_t ck_slots;                 // k_max + 1
   int32_t n_rows;                   // rows in this launch

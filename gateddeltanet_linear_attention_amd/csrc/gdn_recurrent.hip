@@ -89,11 +89,15 @@ __device__ __forceinline__ void store_nt(float *p, const float (&x)[4]) {
   __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
 }
 
-// REPLAY: the instantiation behind gdn_commit_replay (accepted counts on the
-// device, no outputs, no checkpoints).  Both instantiations compile the same
-// per-row arithmetic, so they round identically.
-template <int D, int LPR, int RPL, int WAVES, bool REPLAY>
+// Instantiations: kChain (decode, verify windows, short transaction rows), kReplay
+// (gdn_commit_replay: accepted counts on the device, no outputs, no checkpoints) and
+// kTree (gdn_verify_tree: every window token runs from its parent's state).  All
+// compile the same per-token arithmetic, so they round identically.
+enum Mode { kChain = 0, kReplay = 1, kTree = 2 };
+
+template <int D, int LPR, int RPL, int WAVES, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs args) {
+  constexpr bool REPLAY = MODE == kReplay, TREE = MODE == kTree;
   constexpr int NV = D / LPR / 4;                  // float4 per lane per state row
   constexpr int ROWS = WAVES * 64 / LPR * RPL;     // state rows per block
   constexpr int TILES = D / ROWS;                  // blocks per (row, head)
@@ -176,8 +180,8 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   }
   lds_barrier();
 
-#pragma unroll 1
-  for (int t = 0; t < ntok; ++t) {
+  // Token t of the window applied to state rows st, with its output and checkpoint.
+  auto step = [&](int t, float (&st)[RPL][NV][4]) {
     const float alpha = sAlpha[t], beta = sBeta[t];
     float kk[NV][4];
 #pragma unroll
@@ -193,24 +197,24 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 #pragma unroll
       for (int j = 0; j < NV; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p = fmaf(s[q][j][e], kk[j][e], p);
+        for (int e = 0; e < 4; ++e) p = fmaf(st[q][j][e], kk[j][e], p);
       const float u = group_sum<LPR>(p);
       // S[i,:] <- alpha S[i,:] + beta (v_i - alpha u) k
       const float c = beta * (vi - alpha * u);
 #pragma unroll
       for (int j = 0; j < NV; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[q][j][e] = fmaf(c, kk[j][e], alpha * s[q][j][e]);
+        for (int e = 0; e < 4; ++e) st[q][j][e] = fmaf(c, kk[j][e], alpha * st[q][j][e]);
       if (write_o) {
         // o_i = S[i,:] . q
         float po = 0.0f;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
           const float4 qw = sQ[t][sub + LPR * j];
-          po = fmaf(s[q][j][0], qw.x, po);
-          po = fmaf(s[q][j][1], qw.y, po);
-          po = fmaf(s[q][j][2], qw.z, po);
-          po = fmaf(s[q][j][3], qw.w, po);
+          po = fmaf(st[q][j][0], qw.x, po);
+          po = fmaf(st[q][j][1], qw.y, po);
+          po = fmaf(st[q][j][2], qw.z, po);
+          po = fmaf(st[q][j][3], qw.w, po);
         }
         const float oi = group_sum<LPR>(po);
         if (sub == 0) sO[t][i_local + q] = to_bf16(oi);
@@ -219,9 +223,39 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
         float *cp = args.ckpt + ((size_t(ck_row) * args.ck_slots + (t - ck_first)) * n_v + h) * UNIT +
                     size_t(i0 + q) * D;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) store_nt(cp + 4 * (sub + LPR * j), s[q][j]);
+        for (int j = 0; j < NV; ++j) store_nt(cp + 4 * (sub + LPR * j), st[q][j]);
       }
     }
+  };
+  auto copy_state = [&](float (&to)[RPL][NV][4], const float (&from)[RPL][NV][4]) {
+#pragma unroll
+    for (int q = 0; q < RPL; ++q)
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) to[q][j][e] = from[q][j][e];
+  };
+
+  if constexpr (TREE) {
+    // node states stay in registers (indexed by constants only); token t starts
+    // from its parent's state, or from the committed state s
+    float node[TB][RPL][NV][4];
+    const uint32_t tree = args.tree[r];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      if (t >= ntok) break;
+      const int par = int((tree >> (8 * t)) & 0xFFu) - 1;
+      float cur[RPL][NV][4];
+      copy_state(cur, s);
+#pragma unroll
+      for (int k = 0; k < t; ++k)
+        if (par == k) copy_state(cur, node[k]);
+      step(t, cur);
+      copy_state(node[t], cur);
+    }
+  } else {
+#pragma unroll 1
+    for (int t = 0; t < ntok; ++t) step(t, s);
   }
   if (write_o) {
     lds_barrier();  // every output of the block is in sO
@@ -250,9 +284,11 @@ static void launch_d(const RecurrentArgs &args, hipStream_t stream) {
   constexpr int TILES = D / (WAVES * 64 / LPR * RPL);
   const dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * TILES);
   if (args.accepted)
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, true>), grid, dim3(64 * WAVES), 0, stream, args);
+    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kReplay>), grid, dim3(64 * WAVES), 0, stream, args);
+  else if (args.tree_mode)
+    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kTree>), grid, dim3(64 * WAVES), 0, stream, args);
   else
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, false>), grid, dim3(64 * WAVES), 0, stream, args);
+    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kChain>), grid, dim3(64 * WAVES), 0, stream, args);
 }
 
 hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream) {
@@ -261,7 +297,11 @@ hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream
   for (int r = 0; r < args.n_rows; ++r)  // the kernel stages a row's tokens in fixed LDS arrays
     if (args.ntok[r] < 1 || args.ntok[r] > kMaxWindow) return hipErrorInvalidValue;
   // replay writes neither outputs nor checkpoints; every other call writes outputs
-  if (args.accepted ? (args.o || args.ckpt || !args.status) : !args.o) return hipErrorInvalidValue;
+  if (args.accepted ? (args.o || args.ckpt || !args.status || args.tree_mode) : !args.o) return hipErrorInvalidValue;
+  if (args.tree_mode)  // parents precede their children; byte 0 is the committed state
+    for (int r = 0; r < args.n_rows; ++r)
+      for (int t = 0; t < args.ntok[r]; ++t)
+        if (int((args.tree[r] >> (8 * t)) & 0xFFu) > t) return hipErrorInvalidValue;
   if (d == 128)
     launch_d<128, 16, 1, 8>(args, stream);
   else if (d == 16)

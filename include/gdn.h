@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 2
+#define GDN_VERSION 3
 #define GDN_MAX_K 3 /* largest k_max: at most 4 checkpoint slots per row */
 
 typedef struct gdn_dims {
@@ -121,6 +121,24 @@ int gdn_commit_accepted(const gdn_dims *dims, int32_t n_rows, const int32_t *row
                         const float *ckpt, const int32_t *accepted, float *state_pool,
                         int32_t n_slots, const int32_t *dst_slot, uint32_t *status,
                         void *stream);
+
+/*
+ * gdn_verify_tree -- draft verification of a token tree (topk > 1 drafting; the
+ * pages verify chains only and refuse tree shapes, "Occamy 1.0 MTP", section "MTP1
+ * runtime").  As gdn_verify_window, except that window token t of row r runs from
+ * the state of its parent p = parents[cu_r + t] (host int32, one per packed token;
+ * p = -1: the committed state in slot src_slot[r]) instead of from token t - 1:
+ * checkpoint slot t of row r = the state of node t (its root path applied to the
+ * committed state) and o_t = S_t q_t.  Nodes are in topological order: parents[cu_r]
+ * = -1 and -1 <= p < t, else GDN_E_RANGE.  A chain (p = t - 1) gives bit for bit
+ * the result of gdn_verify_window.  Commit the accepted path's last node n_r with
+ * gdn_commit_accepted(accepted[r] = n_r).  ckpt is required.
+ */
+int gdn_verify_tree(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                    const int32_t *parents, const uint16_t *q, const uint16_t *k,
+                    const uint16_t *v, const float *a, const float *b, const float *A_log,
+                    const float *dt_bias, const float *state_pool, int32_t n_slots,
+                    const int32_t *src_slot, float *ckpt, uint16_t *o, void *stream);
 
 /*
  * gdn_commit_replay -- rollback without checkpoints: the pull request thread's

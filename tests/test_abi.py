@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
     assert {"gdn_decode_step", "gdn_verify_window", "gdn_commit_accepted",
             "gdn_chunked_prefill_with_checkpoints", "gdn_chunked_workspace_bytes",
             "gdn_plan_transaction", "gdn_run_transaction", "gdn_status_str", "gdn_version",
-            "gdn_commit_replay"} <= set(names)
+            "gdn_commit_replay", "gdn_verify_tree"} <= set(names)
     lib = gb.lib()
     for n in names:
         assert hasattr(lib, n), "libgdn.so does not export %s" % n
@@ -202,6 +202,32 @@ def test_verify_without_checkpoints_and_replay_validation_codes():
     assert replay([4, 2], [0, 1], [2, 3], misalign=8) == -5       # misaligned q
     assert replay([4, 2], [0, 1], [0, 1]) == -7                   # in place passes validation
     assert replay([], [], []) == 0
+
+
+@no_gpu
+def test_verify_tree_validation_codes():
+    lib = gb.lib()
+    b = Bufs()
+    d = _dims()
+    NULL = ctypes.c_void_p(0)
+
+    def tree(T, parents, ckpt=True, par_null=False):
+        Ta, Tp = _i32(T)
+        pa, pp = _i32(parents)
+        sa, sp = _i32(list(range(len(T))))
+        return lib.gdn_verify_tree(ctypes.byref(d), len(Ta), Tp, None if par_null else pp,
+                                   *[b.ptr() for _ in range(7)], b.ptr(), 8, sp,
+                                   b.ptr() if ckpt else NULL, b.ptr(), NULL)
+
+    assert tree([4], [-1, 0, 0, 1], par_null=True) == -1   # parents required
+    assert tree([4], [-1, 0, 0, 1], ckpt=False) == -1      # checkpoints required
+    assert tree([4], [0, 0, 0, 1]) == -3                   # first token must follow the committed state
+    assert tree([4], [-1, 1, 0, 1]) == -3                  # a parent must be an earlier node
+    assert tree([4], [-1, 0, 3, 1]) == -3
+    assert tree([4], [-1, -2, 0, 1]) == -3                 # below -1
+    assert tree([5], [-1, 0, 1, 2, 3]) == -3               # T_r > k_max + 1
+    assert tree([2, 2], [-1, 0, -1, 1]) == -3              # second row: parent 1 of node 1
+    assert tree([4, 2], [-1, 0, 0, 1, -1, -1]) == -7       # valid: passes validation, no GPU here
 
 
 @no_gpu
