@@ -368,7 +368,10 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
   constexpr int NKB = D / 16;
   constexpr int NT_W = (D / 16 + 3) / 4;  // state column tiles per wave
   constexpr size_t UNIT = size_t(D) * D;
-  __shared__ __attribute__((aligned(16))) float sS[VT * LDS_];  // state tile: row i, column d
+  // state tile (row i, column d), double-buffered: chunk c reads sSb[c & 1] and writes
+  // the next state to sSb[(c + 1) & 1], so no barrier is needed between the last read
+  // of a state and the write of the next one
+  __shared__ __attribute__((aligned(16))) float sSb[2][VT * LDS_];
   __shared__ __attribute__((aligned(16))) float sUt[VT * LDC];  // U^T of this tile: row i, token s
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -398,20 +401,16 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
     if (src >= 0)
       x = *reinterpret_cast<const float4 *>(args.state_in + (int64_t(src) * n_v + h) * UNIT +
                                             int64_t(i0 + i) * D + d4);
-    *reinterpret_cast<float4 *>(sS + i * LDS_ + d4) = x;
+    *reinterpret_cast<float4 *>(sSb[0] + i * LDS_ + d4) = x;
   }
 
   // One chunk of the recurrence with its operand fragments f.
   auto body = [&](int c, const ScanFrag<D> &f) {
     const Ws<D> ws = ws_of(c);
-    lds_barrier();  // the state tile of this chunk is in place
+    const float *sS = sSb[c & 1];
+    float *sS_next = sSb[(c + 1) & 1];
+    lds_barrier();  // the state tile of this chunk is in place; the last chunk's reads of sUt are done
 
-    // record S_c for the output and checkpoint kernels
-    for (int idx = tid; idx < VT * (D / 4); idx += 256) {
-      const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-      *reinterpret_cast<float4 *>(ws.Sc + int64_t(i0 + i) * D + d4) =
-          *reinterpret_cast<const float4 *>(sS + i * LDS_ + d4);
-    }
     // U = U' - W S_c^T for tokens 16w..16w+15 of this tile's 16 value channels,
     // in two interleaved partial chains
     floatx4 ua = zero4(), ub = zero4();
@@ -420,6 +419,13 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
       ua = mma4(ua, f.wf[kb], *reinterpret_cast<const float4 *>(sS + r16 * LDS_ + 16 * kb + 4 * g4));
       if (kb + 1 < NKB)
         ub = mma4(ub, f.wf[kb + 1], *reinterpret_cast<const float4 *>(sS + r16 * LDS_ + 16 * (kb + 1) + 4 * g4));
+    }
+    // record S_c for the output and checkpoint kernels (issued behind the products)
+#pragma unroll
+    for (int idx = tid; idx < VT * (D / 4); idx += 256) {
+      const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+      *reinterpret_cast<float4 *>(ws.Sc + int64_t(i0 + i) * D + d4) =
+          *reinterpret_cast<const float4 *>(sS + i * LDS_ + d4);
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -448,13 +454,12 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
       }
       snew[q] = acc;
     }
-    lds_barrier();  // every read of sS / sUt for this chunk is done
 #pragma unroll
     for (int q = 0; q < NT_W; ++q) {
       const int nt = w + 4 * q;
       if (nt < D / 16)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sS[(4 * g4 + v) * LDS_ + 16 * nt + r16] = snew[q][v];
+        for (int v = 0; v < 4; ++v) sS_next[(4 * g4 + v) * LDS_ + 16 * nt + r16] = snew[q][v];
     }
   };
   auto frag_load = [&](ScanFrag<D> &f, int c) {
@@ -475,6 +480,7 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
   }
   lds_barrier();
   if (dst >= 0) {
+    const float *sS = sSb[nch & 1];
     for (int idx = tid; idx < VT * (D / 4); idx += 256) {
       const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
       *reinterpret_cast<float4 *>(args.state_out + (int64_t(dst) * n_v + h) * UNIT +
