@@ -61,6 +61,20 @@ def verify_nockpt_bytes(row_tokens) -> int:
     return sum(V_HEADS * (STATE_BYTES + TOKEN_BYTES * int(T)) for T in row_tokens)
 
 
+DELTA_TOKEN_BYTES = (128 + 4) * 4   # delta checkpoint per (token, v-head): c (d_v floats) + alpha + pad
+
+
+def verify_delta_bytes(row_tokens) -> int:
+    """Verify with delta checkpoints: read the state, token I/O, write the factors."""
+    return sum(V_HEADS * (STATE_BYTES + (TOKEN_BYTES + DELTA_TOKEN_BYTES) * int(T)) for T in row_tokens)
+
+
+def fold_bytes(accepted) -> int:
+    """Fold commit: read and write the state, read a_r + 1 tokens' keys (128 B per v-head)
+    and delta checkpoints."""
+    return sum(V_HEADS * (2 * STATE_BYTES + (128 + DELTA_TOKEN_BYTES) * (int(a) + 1)) for a in accepted)
+
+
 def replay_bytes(accepted) -> int:
     """Replay commit: read and write the state, re-read a_r + 1 tokens' inputs."""
     return sum(V_HEADS * (2 * STATE_BYTES + REPLAY_TOKEN_BYTES * (int(a) + 1)) for a in accepted)
@@ -91,7 +105,7 @@ class VerifySet:
     """One buffer set: state pool, checkpoints, a window of tokens, accepted counts,
     and the two prepared C-ABI calls of a step."""
 
-    def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False, parents=None):
+    def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False, parents=None, delta=False):
         import numpy as np
         import torch
         shape = synth.FULL
@@ -110,12 +124,18 @@ class VerifySet:
                       A_log=torch.from_numpy(A_log).to(dev), dt_bias=torch.from_numpy(dt_bias).to(dev))
         gen = torch.Generator(device="cpu").manual_seed(seed)
         self.pool = (0.05 * torch.randn(B, Hv, d, d, generator=gen)).to(dev)
-        self.ckpt = None if replay else torch.empty(B, 4, Hv, d, d, device=dev)
+        self.ckpt = None if (replay or delta) else torch.empty(B, 4, Hv, d, d, device=dev)
         self.o = torch.empty(N, Hv, d, dtype=torch.bfloat16, device=dev)
         self.acc = torch.from_numpy(acc).to(dev)
         self.status = torch.zeros((B + 31) // 32, dtype=torch.int32, device=dev)
         rows = np.arange(B, dtype=np.int32)
-        if replay:  # no checkpoints: commit re-runs the accepted prefix in place
+        if delta:  # delta checkpoints: commit folds the accepted prefix in place
+            self.delta = torch.empty(gb.delta_shape(dims, B), device=dev)
+            self.verify = gb.prepare_verify_window_delta(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
+                                                         delta=self.delta, o=self.o, stream=stream)
+            self.commit = gb.prepare_commit_delta(dims, Ts, self.t["k"], self.delta, self.acc, self.pool,
+                                                  src_slot=rows, dst_slot=rows, status=self.status, stream=stream)
+        elif replay:  # no checkpoints: commit re-runs the accepted prefix in place
             self.ckpt = None
             self.verify = gb.prepare_verify_window(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
                                                    ckpt=None, o=self.o, stream=stream)
@@ -292,18 +312,26 @@ def measure_prefill(gb, synth, torch, stream, reps):
             "algorithmic_flops_per_call": fl}
 
 
-def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay=False, parents=None):
+def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay=False, parents=None,
+            delta=False):
     """Steps over n_layers layers of windows with per-row token counts Ts (replay:
     verify without checkpoints, commit by replay; parents: one draft tree per row)."""
     dims = gb.Dims(16, 32, 128, 128, 3)
-    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents) for i in range(n_layers)]
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents, delta) for i in range(n_layers)]
     wall, verify_ms, commit_ms = run_steps(sets, steps, warmup, stream, torch)
     for s in sets:
         assert int(s.status.abs().sum()) == 0
     units = len(Ts) * V_HEADS
     upd_per_layer = int(sum(Ts)) * V_HEADS
-    vb = verify_nockpt_bytes(Ts) if replay else verify_bytes(Ts)
-    cb = (sum(replay_bytes(s.acc_host) for s in sets) / len(sets)) if replay else commit_bytes(units)
+    if delta:
+        vb = verify_delta_bytes(Ts)
+        cb = sum(fold_bytes(s.acc_host) for s in sets) / len(sets)
+    elif replay:
+        vb = verify_nockpt_bytes(Ts)
+        cb = sum(replay_bytes(s.acc_host) for s in sets) / len(sets)
+    else:
+        vb = verify_bytes(Ts)
+        cb = commit_bytes(units)
     vms = sum(verify_ms) / len(verify_ms)
     cms = sum(commit_ms) / len(commit_ms)
     srt = sorted(verify_ms)
@@ -398,6 +426,16 @@ def main():
                       "replay_us_mean": 1e3 * rr["commit_ms_mean"], "replay_gbps": rr["commit_gbps"],
                       "step_gbps": rr["step_gbps"],
                       "step_algorithmic_bytes_per_layer": rr["verify_bytes"] + rr["commit_bytes"]}
+    out_delta = None
+    if not args.no_replay:
+        _, rd = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500, delta=True)
+        out_delta = {"mode": "verify storing each step's rank-1 factors + commit by folding them",
+                     "head_token_updates_per_s": rd["updates_per_s"],
+                     "ms_per_layer": rd["ms_per_step"] / args.layers,
+                     "verify_us_mean": 1e3 * rd["verify_ms_mean"], "verify_gbps": rd["verify_gbps"],
+                     "fold_us_mean": 1e3 * rd["commit_ms_mean"], "fold_gbps": rd["commit_gbps"],
+                     "step_gbps": rd["step_gbps"],
+                     "step_algorithmic_bytes_per_layer": rd["verify_bytes"] + rd["commit_bytes"]}
     out_tree = None
     if not args.no_tree:
         tree = np.array(TREE4, np.int32)
@@ -444,6 +482,7 @@ def main():
         "conc16_mixed_k": out_mixed,
         "conc16_k3_replay": out_replay,
         "conc16_tree4": out_tree,
+        "conc16_k3_delta": out_delta,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

@@ -61,6 +61,10 @@ _SIGS = {
                             ctypes.c_int32, _I32P, _VP, _VP],
     "gdn_verify_tree": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _I32P] + [_VP] * 8 +
                        [ctypes.c_int32, _I32P, _VP, _VP, _VP],
+    "gdn_verify_window_delta": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
+                               [ctypes.c_int32, _I32P, _VP, _VP, _VP],
+    "gdn_commit_delta": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _VP, _VP, _VP, _VP,
+                         ctypes.c_int32, _I32P, _I32P, _VP, _VP],
     "gdn_commit_replay": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
                          [_VP, ctypes.c_int32, _I32P, _I32P, _VP, _VP],
     "gdn_chunked_workspace_bytes": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, ctypes.c_int32],
@@ -240,6 +244,72 @@ def gdn_commit_accepted(dims: Dims, row_tokens, ckpt, accepted, state_pool, dst_
     rc = lib().gdn_commit_accepted(ctypes.byref(dims.c()), n_rows, _ip(T), cp, ap, pp, n_slots,
                                    _ip(dst), sp, _stream(stream))
     _check("gdn_commit_accepted", rc)
+
+
+def delta_shape(dims: Dims, n_rows: int) -> tuple:
+    """Shape of the fp32 delta-checkpoint buffer of gdn_verify_window_delta."""
+    return (n_rows, dims.k_max + 1, dims.n_v_heads, dims.d_v + 4)
+
+
+def _verify_delta_args(dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot, delta, o,
+                       stream):
+    import torch
+    T, src = _i32(row_tokens), _i32(src_slot)
+    n_rows = T.size
+    if src.size != n_rows:
+        raise ValueError("row_tokens and src_slot lengths differ")
+    toks, op = _token_ptrs(dims, int(T.sum()), q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    dp = _dev(delta, "delta", torch.float32, delta_shape(dims, n_rows))
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, _ip(T), *toks, pp, n_slots, _ip(src), dp, op, _stream(stream))
+    return args, (cd, T, src, q, k, v, a, b, A_log, dt_bias, state_pool, delta, o)
+
+
+def _commit_delta_args(dims, row_tokens, k, delta, accepted, state_pool, src_slot, dst_slot, status, stream):
+    import torch
+    T, src, dst = _i32(row_tokens), _i32(src_slot), _i32(dst_slot)
+    n_rows = T.size
+    if not (src.size == dst.size == n_rows):
+        raise ValueError("per-row arrays differ in length")
+    kp = _dev(k, "k", torch.bfloat16, (int(T.sum()), dims.n_qk_heads, dims.d_k))
+    dp = _dev(delta, "delta", torch.float32, delta_shape(dims, n_rows))
+    ap = _dev(accepted, "accepted", torch.int32, (n_rows,))
+    sp = _dev(status, "status", torch.int32, ((n_rows + 31) // 32,))
+    pp, n_slots = _pool(dims, state_pool)
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, _ip(T), kp, dp, ap, pp, n_slots, _ip(src), _ip(dst), sp, _stream(stream))
+    return args, (cd, T, src, dst, k, delta, accepted, state_pool, status)
+
+
+def gdn_verify_window_delta(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot,
+                            delta, o, stream=None) -> None:
+    """Verify windows storing each step's rank-1 factors (delta checkpoints)."""
+    args, _keep = _verify_delta_args(dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot,
+                                     delta, o, stream)
+    _check("gdn_verify_window_delta", lib().gdn_verify_window_delta(*args))
+
+
+def gdn_commit_delta(dims: Dims, row_tokens, k, delta, accepted, state_pool, src_slot, dst_slot, status,
+                     stream=None) -> None:
+    """Fold tokens 0..accepted[r] of each row's delta checkpoints into slot src_slot[r]."""
+    args, _keep = _commit_delta_args(dims, row_tokens, k, delta, accepted, state_pool, src_slot, dst_slot,
+                                     status, stream)
+    _check("gdn_commit_delta", lib().gdn_commit_delta(*args))
+
+
+def prepare_verify_window_delta(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot,
+                                delta, o, stream=None) -> PreparedCall:
+    args, keep = _verify_delta_args(dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot,
+                                    delta, o, stream)
+    return PreparedCall("gdn_verify_window_delta", args, keep)
+
+
+def prepare_commit_delta(dims: Dims, row_tokens, k, delta, accepted, state_pool, src_slot, dst_slot, status,
+                         stream=None) -> PreparedCall:
+    args, keep = _commit_delta_args(dims, row_tokens, k, delta, accepted, state_pool, src_slot, dst_slot,
+                                    status, stream)
+    return PreparedCall("gdn_commit_delta", args, keep)
 
 
 def _replay_args(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted, state_pool,

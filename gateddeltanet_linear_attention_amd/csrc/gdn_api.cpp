@@ -344,6 +344,90 @@ int gdn_verify_tree(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tok
                                static_cast<hipStream_t>(stream), parents);
 }
 
+int gdn_verify_window_delta(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                            const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                            const float *b, const float *A_log, const float *dt_bias,
+                            const float *state_pool, int32_t n_slots, const int32_t *src_slot,
+                            float *delta, uint16_t *o, void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if (!row_tokens) return GDN_E_NULL;
+  if ((rc = check_tokens(q, k, v, a, b, A_log, dt_bias, o))) return rc;
+  if (!state_pool || !src_slot || !delta) return GDN_E_NULL;
+  if (!aligned(state_pool, 16) || !aligned(delta, 16)) return GDN_E_ALIGN;
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+  if ((rc = check_slots(n_rows, n_slots, src_slot, nullptr))) return rc;
+  const Sizes s = sizes_of(dims);
+  const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
+  const size_t dl_b = size_t(n_rows) * size_t(dims->k_max + 1) * size_t(dims->n_v_heads) *
+                      size_t(gdn::delta_row_floats(dims->d_v)) * 4;
+  const size_t o_b = size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2;
+  if (overlap(delta, dl_b, state_pool, pool_b) || overlap(o, o_b, delta, dl_b) ||
+      overlap(o, o_b, state_pool, pool_b))
+    return GDN_E_ALIAS;
+  std::vector<int32_t> rows(static_cast<size_t>(n_rows));
+  for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
+  gdn::RecurrentArgs proto;
+  fill_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, nullptr, nullptr, o);
+  proto.delta = delta;
+  return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, src_slot, nullptr, nullptr,
+                               static_cast<hipStream_t>(stream));
+}
+
+int gdn_commit_delta(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                     const uint16_t *k, const float *delta, const int32_t *accepted,
+                     float *state_pool, int32_t n_slots, const int32_t *src_slot,
+                     const int32_t *dst_slot, uint32_t *status, void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if (!row_tokens || !k || !delta || !accepted || !state_pool || !src_slot || !dst_slot || !status)
+    return GDN_E_NULL;
+  if (!aligned(k, 16) || !aligned(delta, 16) || !aligned(state_pool, 16) || !aligned(accepted, 4) ||
+      !aligned(status, 4))
+    return GDN_E_ALIGN;
+  for (int32_t r = 0; r < n_rows; ++r) {
+    if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+    if (dst_slot[r] < 0) return GDN_E_RANGE;
+  }
+  if ((rc = check_slots(n_rows, n_slots, src_slot, dst_slot))) return rc;
+  const Sizes s = sizes_of(dims);
+  const size_t dl_b = size_t(n_rows) * size_t(dims->k_max + 1) * size_t(dims->n_v_heads) *
+                      size_t(gdn::delta_row_floats(dims->d_v)) * 4;
+  if (overlap(delta, dl_b, state_pool, size_t(n_slots) * s.row_floats * 4)) return GDN_E_ALIAS;
+  const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  for (int32_t r0 = 0; r0 < n_rows; r0 += kRowsPerLaunch) {
+    gdn::FoldArgs fa;
+    memset(&fa, 0, sizeof(fa));
+    const int32_t n = std::min<int32_t>(kRowsPerLaunch, n_rows - r0);
+    fa.k = k;
+    fa.delta = delta;
+    fa.pool_in = state_pool;
+    fa.pool_out = state_pool;
+    fa.accepted = accepted;
+    fa.status = status;
+    fa.n_qk = dims->n_qk_heads;
+    fa.n_v = dims->n_v_heads;
+    fa.group = dims->n_v_heads / dims->n_qk_heads;
+    fa.ck_slots = dims->k_max + 1;
+    fa.n_rows = n;
+    fa.row_base = r0;
+    for (int32_t j = 0; j < n; ++j) {
+      fa.tok0[j] = int32_t(cu[r0 + j]);
+      fa.ntok[j] = row_tokens[r0 + j];
+      fa.src[j] = src_slot[r0 + j];
+      fa.dst[j] = dst_slot[r0 + j];
+    }
+    if (gdn::launch_fold(fa, dims->d_k, static_cast<hipStream_t>(stream)) != hipSuccess) return GDN_E_HIP;
+  }
+  return GDN_OK;
+}
+
 int gdn_commit_replay(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
                       const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
                       const float *b, const float *A_log, const float *dt_bias,

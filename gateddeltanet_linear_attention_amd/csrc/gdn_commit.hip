@@ -56,7 +56,92 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs args, int b
   }
 }
 
+// Fold commit of delta checkpoints: the committed state becomes the accepted prefix
+// of the window applied to the source state, S <- fmaf(c_i, k_t[d], alpha_t S) per
+// element and token -- the verify kernel's own update, operation for operation, so the
+// result is bit-identical to the state the window reached after that prefix.  A block
+// streams 16 KiB of one (row, head) state: four float4 per thread, each inside one
+// state row i.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs args, int blocks_per_unit) {
+  constexpr int N4 = D * D / 4;  // float4 per (row, head) state
+  const int part = blockIdx.x % blocks_per_unit;
+  const int unit = blockIdx.x / blocks_per_unit;
+  const int h = unit % args.n_v, r = unit / args.n_v;
+  const int row = args.row_base + r;
+  const int acc = args.accepted[row];
+  if (acc < 0 || acc >= args.ntok[r]) {
+    if (part == 0 && h == 0 && threadIdx.x == 0) atomicOr(args.status + (row >> 5), 1u << (row & 31));
+    return;
+  }
+  const int hq = h / args.group, src = args.src[r], ntok = args.ntok[r];
+  // every token's factors and keys are loaded before the first update (tokens past the
+  // window are clamped to its last one and never applied): one memory round trip
+  float cf[kMaxWindow][kF4PerThread], al[kMaxWindow];
+  uint2 kw[kMaxWindow][kF4PerThread];
+#pragma unroll
+  for (int t = 0; t < kMaxWindow; ++t) {
+    const int tt = min(t, ntok - 1);
+    const float *dl = args.delta + ((size_t(row) * args.ck_slots + tt) * args.n_v + h) * (D + 4);
+    const uint16_t *kr = args.k + ((size_t(args.tok0[r]) + tt) * args.n_qk + hq) * D;
+    al[t] = dl[D];
+#pragma unroll
+    for (int m = 0; m < kF4PerThread; ++m) {
+      const int idx = min(part * kF4PerBlock + m * kThreads + int(threadIdx.x), N4 - 1);
+      cf[t][m] = dl[(4 * idx) / D];
+      kw[t][m] = *reinterpret_cast<const uint2 *>(kr + (4 * idx) % D);
+    }
+  }
+  float4 x[kF4PerThread];
+#pragma unroll
+  for (int m = 0; m < kF4PerThread; ++m) {
+    const int idx = part * kF4PerBlock + m * kThreads + int(threadIdx.x);
+    x[m] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (idx < N4 && src >= 0) {
+      const f32x4 y = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4 *>(args.pool_in + (size_t(src) * args.n_v + h) * D * D) + idx);
+      x[m] = make_float4(y[0], y[1], y[2], y[3]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kMaxWindow; ++t) {
+    if (t > acc) break;
+#pragma unroll
+    for (int m = 0; m < kF4PerThread; ++m) {
+      const float c = cf[t][m], alpha = al[t];
+      x[m].x = fmaf(c, __uint_as_float(kw[t][m].x << 16), alpha * x[m].x);
+      x[m].y = fmaf(c, __uint_as_float(kw[t][m].x & 0xFFFF0000u), alpha * x[m].y);
+      x[m].z = fmaf(c, __uint_as_float(kw[t][m].y << 16), alpha * x[m].z);
+      x[m].w = fmaf(c, __uint_as_float(kw[t][m].y & 0xFFFF0000u), alpha * x[m].w);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kF4PerThread; ++m) {
+    const int idx = part * kF4PerBlock + m * kThreads + int(threadIdx.x);
+    if (idx < N4)
+      __builtin_nontemporal_store(f32x4{x[m].x, x[m].y, x[m].z, x[m].w},
+                                  reinterpret_cast<f32x4 *>(args.pool_out + (size_t(args.dst[r]) * args.n_v + h) * D * D) + idx);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fold(const FoldArgs &args, int d, hipStream_t stream) {
+  if (args.n_rows <= 0) return hipSuccess;
+  if (args.n_rows > kRowsPerLaunch) return hipErrorInvalidValue;
+  for (int r = 0; r < args.n_rows; ++r)  // the kernel holds a whole window's factors in registers
+    if (args.ntok[r] < 1 || args.ntok[r] > kMaxWindow) return hipErrorInvalidValue;
+  const int n4 = d * d / 4;
+  const int bpu = (n4 + kF4PerBlock - 1) / kF4PerBlock;
+  const dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * unsigned(bpu));
+  if (d == 128)
+    hipLaunchKernelGGL(fold_kernel<128>, grid, dim3(kThreads), 0, stream, args, bpu);
+  else if (d == 16)
+    hipLaunchKernelGGL(fold_kernel<16>, grid, dim3(kThreads), 0, stream, args, bpu);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_commit(const CommitArgs &args, hipStream_t stream) {
   if (args.n_rows <= 0) return hipSuccess;

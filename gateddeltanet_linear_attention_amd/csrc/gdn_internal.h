@@ -39,6 +39,9 @@ struct RecurrentArgs {
   // plus one (0: the committed state); token t then runs from its parent's state.
   int32_t tree_mode;
   uint32_t tree[kRowsPerLaunch];
+  // Delta checkpoints (may be null): the rank-1 factors of every window step instead
+  // of the states, laid out as delta_floats below.
+  float *delta;
   int32_t n_qk, n_v, group;         // heads; group = n_v / n_qk
   int32_t ck_slots;                 // k_max + 1
   int32_t n_rows;                   // rows in this launch
@@ -62,6 +65,32 @@ struct CommitArgs {
   int32_t n_rows;
   int32_t row_base;                 // index of this launch's first row in the call
   int32_t ntok[kRowsPerLaunch];
+  int32_t dst[kRowsPerLaunch];
+};
+
+// Delta checkpoint of one (call row r, window token t, value head h): d + 4 floats at
+// ((r * ck_slots + t) * n_v + h) * (d + 4): c[0..d), c_i = beta_t (v_t[i] - alpha_t
+// u_i), then alpha_t at [d] (the last 3 floats pad rows to 16 bytes).  The step is
+// S_t[i][d'] = fmaf(c_i, k_t[d'], alpha_t S_{t-1}[i][d']) for every element.
+constexpr int delta_row_floats(int d) { return d + 4; }
+
+// Fold commit: row r of the launch applies window tokens 0..accepted[row_base + r]
+// of its delta checkpoints to the state of slot src[r] (-1: zero) and writes slot
+// dst[r]; an accepted count outside [0, ntok[r]) leaves the row untouched and sets
+// its status bit.
+struct FoldArgs {
+  const uint16_t *k;                // bf16 bits, packed window tokens
+  const float *delta;               // delta checkpoints of the whole call
+  const float *pool_in;
+  float *pool_out;
+  const int32_t *accepted;          // device, whole call
+  uint32_t *status;                 // device, whole call
+  int32_t n_qk, n_v, group, ck_slots;
+  int32_t n_rows;
+  int32_t row_base;
+  int32_t tok0[kRowsPerLaunch];
+  int32_t ntok[kRowsPerLaunch];
+  int32_t src[kRowsPerLaunch];
   int32_t dst[kRowsPerLaunch];
 };
 
@@ -105,5 +134,6 @@ struct ChunkArgs {
 hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream);
 hipError_t launch_chunked(const ChunkArgs &args, int d, int n_chunks, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &args, hipStream_t stream);
+hipError_t launch_fold(const FoldArgs &args, int d, hipStream_t stream);
 
 }  // namespace gdn

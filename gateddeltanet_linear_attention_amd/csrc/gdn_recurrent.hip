@@ -91,9 +91,10 @@ __device__ __forceinline__ void store_nt(float *p, const float (&x)[4]) {
 
 // Instantiations: kChain (decode, verify windows, short transaction rows), kReplay
 // (gdn_commit_replay: accepted counts on the device, no outputs, no checkpoints) and
-// kTree (gdn_verify_tree: every window token runs from its parent's state).  All
+// kTree (gdn_verify_tree: every window token runs from its parent's state) and
+// kDelta (gdn_verify_window_delta: each step's rank-1 factors instead of the states).  All
 // compile the same per-token arithmetic, so they round identically.
-enum Mode { kChain = 0, kReplay = 1, kTree = 2 };
+enum Mode { kChain = 0, kReplay = 1, kTree = 2, kDelta = 3 };
 
 template <int D, int LPR, int RPL, int WAVES, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs args) {
@@ -183,6 +184,8 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   // Token t of the window applied to state rows st, with its output and checkpoint.
   auto step = [&](int t, float (&st)[RPL][NV][4]) {
     const float alpha = sAlpha[t], beta = sBeta[t];
+    if (MODE == kDelta && tile == 0 && tid == 0)
+      args.delta[((size_t(ck_row) * args.ck_slots + t) * n_v + h) * (D + 4) + D] = alpha;
     float kk[NV][4];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -205,6 +208,8 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
       for (int j = 0; j < NV; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) st[q][j][e] = fmaf(c, kk[j][e], alpha * st[q][j][e]);
+      if (MODE == kDelta && sub == 0)  // the step's factors: c_i, and alpha once per head
+        args.delta[((size_t(ck_row) * args.ck_slots + t) * n_v + h) * (D + 4) + i0 + q] = c;
       if (write_o) {
         // o_i = S[i,:] . q
         float po = 0.0f;
@@ -285,6 +290,8 @@ static void launch_d(const RecurrentArgs &args, hipStream_t stream) {
   const dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * TILES);
   if (args.accepted)
     hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kReplay>), grid, dim3(64 * WAVES), 0, stream, args);
+  else if (args.delta)
+    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kDelta>), grid, dim3(64 * WAVES), 0, stream, args);
   else if (args.tree_mode)
     hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kTree>), grid, dim3(64 * WAVES), 0, stream, args);
   else
@@ -297,7 +304,9 @@ hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream
   for (int r = 0; r < args.n_rows; ++r)  // the kernel stages a row's tokens in fixed LDS arrays
     if (args.ntok[r] < 1 || args.ntok[r] > kMaxWindow) return hipErrorInvalidValue;
   // replay writes neither outputs nor checkpoints; every other call writes outputs
-  if (args.accepted ? (args.o || args.ckpt || !args.status || args.tree_mode) : !args.o) return hipErrorInvalidValue;
+  if (args.accepted ? (args.o || args.ckpt || !args.status || args.tree_mode || args.delta) : !args.o)
+    return hipErrorInvalidValue;
+  if (args.delta && (args.ckpt || args.tree_mode)) return hipErrorInvalidValue;
   if (args.tree_mode)  // parents precede their children; byte 0 is the committed state
     for (int r = 0; r < args.n_rows; ++r)
       for (int t = 0; t < args.ntok[r]; ++t)

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 3
+#define GDN_VERSION 4
 #define GDN_MAX_K 3 /* largest k_max: at most 4 checkpoint slots per row */
 
 typedef struct gdn_dims {
@@ -162,6 +162,34 @@ int gdn_commit_replay(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
                       const float *dt_bias, const int32_t *accepted, float *state_pool,
                       int32_t n_slots, const int32_t *src_slot, const int32_t *dst_slot,
                       uint32_t *status, void *stream);
+
+/*
+ * gdn_verify_window_delta / gdn_commit_delta -- rollback from compact exact
+ * checkpoints.  Each step of the rule is a rank-1 update applied elementwise,
+ * S_t[i][d] = fmaf(c_i, k_t[d], alpha_t S_{t-1}[i][d]) with c_i = beta_t (v_t[i] -
+ * alpha_t (S_{t-1} k_t)_i), so the state after window token j is determined bit for
+ * bit by the committed state, the keys and the factors (c, alpha_t) of tokens 0..j.
+ * gdn_verify_window_delta is gdn_verify_window storing those factors instead of the
+ * states: delta (device fp32 [n_rows][k_max+1][H_v][d_v + 4], 16-byte aligned)
+ * receives, for window token t < T_r of row r and value head h, c at
+ * [r][t][h][0..d_v) and alpha_t at [r][t][h][d_v] (the last 3 floats are padding):
+ * (d_v + 4) * 4 bytes per (token, head) instead of d_v * d_k * 4.
+ * gdn_commit_delta folds tokens 0..a_r of row r (accepted: device int32 [n_rows];
+ * k: the same packed window keys) into the state of slot src_slot[r] (-1: zero) and
+ * writes slot dst_slot[r] (== src_slot[r] commits in place): bit-identical to
+ * checkpoint slot a_r of gdn_verify_window on the same window.  A row whose a_r is
+ * outside [0, T_r - 1] is left untouched and sets bit (r % 32) of status[r / 32].
+ * Errors as gdn_verify_window and gdn_commit_replay.
+ */
+int gdn_verify_window_delta(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                            const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            const float *a, const float *b, const float *A_log,
+                            const float *dt_bias, const float *state_pool, int32_t n_slots,
+                            const int32_t *src_slot, float *delta, uint16_t *o, void *stream);
+int gdn_commit_delta(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                     const uint16_t *k, const float *delta, const int32_t *accepted,
+                     float *state_pool, int32_t n_slots, const int32_t *src_slot,
+                     const int32_t *dst_slot, uint32_t *status, void *stream);
 
 /*
  * gdn_chunked_workspace_bytes -- device workspace that gdn_chunked_prefill_with_

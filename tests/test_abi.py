@@ -39,7 +39,8 @@ def test_library_exports_every_declared_function():
     assert {"gdn_decode_step", "gdn_verify_window", "gdn_commit_accepted",
             "gdn_chunked_prefill_with_checkpoints", "gdn_chunked_workspace_bytes",
             "gdn_plan_transaction", "gdn_run_transaction", "gdn_status_str", "gdn_version",
-            "gdn_commit_replay", "gdn_verify_tree"} <= set(names)
+            "gdn_commit_replay", "gdn_verify_tree", "gdn_verify_window_delta",
+            "gdn_commit_delta"} <= set(names)
     lib = gb.lib()
     for n in names:
         assert hasattr(lib, n), "libgdn.so does not export %s" % n
@@ -228,6 +229,38 @@ def test_verify_tree_validation_codes():
     assert tree([5], [-1, 0, 1, 2, 3]) == -3               # T_r > k_max + 1
     assert tree([2, 2], [-1, 0, -1, 1]) == -3              # second row: parent 1 of node 1
     assert tree([4, 2], [-1, 0, 0, 1, -1, -1]) == -7       # valid: passes validation, no GPU here
+
+
+@no_gpu
+def test_delta_validation_codes():
+    lib = gb.lib()
+    b = Bufs()
+    d = _dims()
+    NULL = ctypes.c_void_p(0)
+
+    def verify(T, delta=True):
+        Ta, Tp = _i32(T)
+        sa, sp = _i32(list(range(len(T))))
+        return lib.gdn_verify_window_delta(ctypes.byref(d), len(Ta), Tp, *[b.ptr() for _ in range(7)], b.ptr(), 8,
+                                           sp, b.ptr() if delta else NULL, b.ptr(), NULL)
+
+    def commit(T, src, dst, k=True, accepted=True, misalign=0):
+        Ta, Tp = _i32(T)
+        sa, sp = _i32(src)
+        da, dp = _i32(dst)
+        return lib.gdn_commit_delta(ctypes.byref(d), len(Ta), Tp, b.ptr() if k else NULL, b.ptr(misalign=misalign),
+                                    b.ptr() if accepted else NULL, b.ptr(), 8, sp, dp, b.ptr(), NULL)
+
+    assert verify([4, 2], delta=False) == -1
+    assert verify([4, 5]) == -3
+    assert verify([4, 2]) == -7                      # valid: passes validation, no GPU here
+    assert commit([4, 2], [0, 1], [2, 3], k=False) == -1
+    assert commit([4, 2], [0, 1], [2, 3], accepted=False) == -1
+    assert commit([4, 2], [0, 1], [2, -1]) == -3
+    assert commit([4, 2], [0, 1], [2, 2]) == -4
+    assert commit([4, 2], [0, 1], [1, 3]) == -4
+    assert commit([4, 2], [0, 1], [2, 3], misalign=4) == -5
+    assert commit([4, 2], [0, 1], [0, 1]) == -7      # in place passes validation
 
 
 @no_gpu

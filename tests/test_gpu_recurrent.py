@@ -45,11 +45,13 @@ def _bf16_bits(t):
 
 # ---------------------------------------------------------------- workload runner
 
-def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: int, replay: bool = False):
+def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: int, mode: str = "checkpoint"):
     """Warm every row by decoding its prior tokens, then run n_windows verify windows,
-    each followed by commit of the accepted length (replay: verify without
-    checkpoints, then gdn_commit_replay in place); the oracle runs the same chain
-    independently from its own states.  Returns the worst errors seen."""
+    each followed by commit of the accepted length -- mode "checkpoint" (dense
+    checkpoints, gdn_commit_accepted), "replay" (verify without checkpoints, then
+    gdn_commit_replay in place) or "delta" (delta checkpoints, gdn_commit_delta in
+    place); the oracle runs the same chain independently from its own states.
+    Returns the worst errors seen."""
     dims = dims_of(w.shape)
     B, Hv, d = w.n_rows, w.shape.n_v_heads, w.shape.d
     P = dev_params(w.A_log, w.dt_bias)
@@ -77,6 +79,7 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
 
     T = w.window_lens
     ckpt = torch.empty(B, 4, Hv, d, d, device="cuda")
+    delta = torch.empty(gb.delta_shape(dims, B), device="cuda")
     o_win = torch.empty(int(T.sum()), Hv, d, dtype=torch.bfloat16, device="cuda")
     status = torch.zeros((B + 31) // 32, dtype=torch.int32, device="cuda")
     # oracle buffers are reused across windows (fresh pages are slow to fault in)
@@ -88,7 +91,11 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
         win = w.window_tokens(i)
         acc = w.accepted(i)
         wd = dev_tokens(win)
-        if replay:
+        if mode == "delta":
+            gb.gdn_verify_window_delta(dims, T, **wd, **P, state_pool=pool, src_slot=rows, delta=delta, o=o_win)
+            gb.gdn_commit_delta(dims, T, wd["k"], delta, torch.from_numpy(acc).cuda(), pool, src_slot=rows,
+                                dst_slot=rows, status=status)
+        elif mode == "replay":
             gb.gdn_verify_window(dims, T, **wd, **P, state_pool=pool, src_slot=rows, ckpt=None, o=o_win)
             gb.gdn_commit_replay(dims, T, **wd, **P, accepted=torch.from_numpy(acc).cuda(), state_pool=pool,
                                  src_slot=rows, dst_slot=rows, status=status)
@@ -103,7 +110,7 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
             S_bufs[cur][r] = ck_o[r, acc[r]]
         mx = assert_o(host(o_win), o_o, "%s window %d outputs" % (w.name, i))
         worst["o_abs"] = max(worst["o_abs"], mx)
-        if i == 0 and not replay:
+        if i == 0 and mode == "checkpoint":
             for r in range(B):  # every checkpoint of the first window
                 e = assert_state(host(ckpt[r, :T[r]]), ck_o[r, :T[r]], "%s window 0 row %d ckpt" % (w.name, r))
                 worst["state"] = max(worst["state"], e)

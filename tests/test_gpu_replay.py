@@ -131,11 +131,11 @@ def test_replay_zero_source_state():
 
 def test_batch1_workload_in_replay_mode():
     w = synth.verify_workload("batch1", n_windows=64)
-    worst = run_verify_workload(w, n_windows=w.n_windows, check_every=16, replay=True)
+    worst = run_verify_workload(w, n_windows=w.n_windows, check_every=16, mode="replay")
     say("batch1 replay worst:", worst)
 
 
 def test_conc16_workload_in_replay_mode():
     w = synth.verify_workload("conc16", n_windows=128)
-    worst = run_verify_workload(w, n_windows=w.n_windows, check_every=32, replay=True)
+    worst = run_verify_workload(w, n_windows=w.n_windows, check_every=32, mode="replay")
     say("conc16 replay worst:", worst)
