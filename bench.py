@@ -75,6 +75,14 @@ def fold_bytes(accepted) -> int:
     return sum(V_HEADS * (2 * STATE_BYTES + (128 + DELTA_TOKEN_BYTES) * (int(a) + 1)) for a in accepted)
 
 
+def folded_verify_bytes(row_tokens, accepted) -> int:
+    """Verify that first folds the previous window: read the state, write the folded
+    state back, read the previous window's a_r + 1 keys and delta checkpoints, token
+    I/O and the new window's delta checkpoints."""
+    return sum(V_HEADS * (2 * STATE_BYTES + (TOKEN_BYTES + DELTA_TOKEN_BYTES) * int(T)
+                          + (128 + DELTA_TOKEN_BYTES) * (int(a) + 1)) for T, a in zip(row_tokens, accepted))
+
+
 def replay_bytes(accepted) -> int:
     """Replay commit: read and write the state, re-read a_r + 1 tokens' inputs."""
     return sum(V_HEADS * (2 * STATE_BYTES + REPLAY_TOKEN_BYTES * (int(a) + 1)) for a in accepted)
@@ -105,7 +113,8 @@ class VerifySet:
     """One buffer set: state pool, checkpoints, a window of tokens, accepted counts,
     and the two prepared C-ABI calls of a step."""
 
-    def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False, parents=None, delta=False):
+    def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False, parents=None, delta=False,
+                 folded=False):
         import numpy as np
         import torch
         shape = synth.FULL
@@ -124,12 +133,32 @@ class VerifySet:
                       A_log=torch.from_numpy(A_log).to(dev), dt_bias=torch.from_numpy(dt_bias).to(dev))
         gen = torch.Generator(device="cpu").manual_seed(seed)
         self.pool = (0.05 * torch.randn(B, Hv, d, d, generator=gen)).to(dev)
-        self.ckpt = None if (replay or delta) else torch.empty(B, 4, Hv, d, d, device=dev)
+        self.ckpt = None if (replay or delta or folded) else torch.empty(B, 4, Hv, d, d, device=dev)
         self.o = torch.empty(N, Hv, d, dtype=torch.bfloat16, device=dev)
         self.acc = torch.from_numpy(acc).to(dev)
         self.status = torch.zeros((B + 31) // 32, dtype=torch.int32, device=dev)
         rows = np.arange(B, dtype=np.int32)
-        if delta:  # delta checkpoints: commit folds the accepted prefix in place
+        if folded:  # each verify first folds the previous window's accepted prefix: no commit launch
+            self.deltas = [torch.empty(gb.delta_shape(dims, B), device=dev) for _ in range(2)]
+            first = gb.prepare_verify_window_delta(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
+                                                   delta=self.deltas[0], o=self.o, stream=stream)
+            fold = [gb.prepare_verify_window_delta_fold(dims, Ts, **self.t, state_pool=self.pool, slot=rows,
+                                                        delta=self.deltas[1 - j], o=self.o, prev_row_tokens=Ts,
+                                                        prev_k=self.t["k"], prev_delta=self.deltas[j],
+                                                        prev_accepted=self.acc, status=self.status,
+                                                        stream=stream) for j in (0, 1)]
+            phase = [None]
+
+            def verify():
+                if phase[0] is None:
+                    first()
+                    phase[0] = 0
+                else:
+                    fold[phase[0]]()
+                    phase[0] ^= 1
+            self.verify = verify
+            self.commit = lambda: None
+        elif delta:  # delta checkpoints: commit folds the accepted prefix in place
             self.delta = torch.empty(gb.delta_shape(dims, B), device=dev)
             self.verify = gb.prepare_verify_window_delta(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
                                                          delta=self.delta, o=self.o, stream=stream)
@@ -313,17 +342,23 @@ def measure_prefill(gb, synth, torch, stream, reps):
 
 
 def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay=False, parents=None,
-            delta=False):
+            delta=False, folded=False):
     """Steps over n_layers layers of windows with per-row token counts Ts (replay:
-    verify without checkpoints, commit by replay; parents: one draft tree per row)."""
+    verify without checkpoints, commit by replay; parents: one draft tree per row;
+    delta: delta checkpoints folded by a commit launch; folded: folded by the next
+    verify, one launch per layer per step)."""
     dims = gb.Dims(16, 32, 128, 128, 3)
-    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents, delta) for i in range(n_layers)]
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents, delta, folded)
+            for i in range(n_layers)]
     wall, verify_ms, commit_ms = run_steps(sets, steps, warmup, stream, torch)
     for s in sets:
         assert int(s.status.abs().sum()) == 0
     units = len(Ts) * V_HEADS
     upd_per_layer = int(sum(Ts)) * V_HEADS
-    if delta:
+    if folded:
+        vb = sum(folded_verify_bytes(Ts, s.acc_host) for s in sets) / len(sets)
+        cb = 0
+    elif delta:
         vb = verify_delta_bytes(Ts)
         cb = sum(fold_bytes(s.acc_host) for s in sets) / len(sets)
     elif replay:
@@ -347,7 +382,7 @@ def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay
         "verify_gbps": vb / (vms * 1e-3) / 1e9,
         "commit_ms_mean": cms,
         "commit_bytes": cb,
-        "commit_gbps": cb / (cms * 1e-3) / 1e9,
+        "commit_gbps": cb / (cms * 1e-3) / 1e9 if cb else None,
         "step_gbps": (vb + cb) * n_layers * steps / wall / 1e9,
     }
 
@@ -436,6 +471,18 @@ def main():
                      "fold_us_mean": 1e3 * rd["commit_ms_mean"], "fold_gbps": rd["commit_gbps"],
                      "step_gbps": rd["step_gbps"],
                      "step_algorithmic_bytes_per_layer": rd["verify_bytes"] + rd["commit_bytes"]}
+    out_folded = None
+    if not args.no_replay:
+        _, rf = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
+                        folded=True)
+        out_folded = {"mode": "delta checkpoints; each verify first folds the previous window's accepted "
+                              "prefix (one launch per layer per step)",
+                      "head_token_updates_per_s": rf["updates_per_s"],
+                      "ms_per_layer": rf["ms_per_step"] / args.layers,
+                      "verify_us_mean": 1e3 * rf["verify_ms_mean"], "verify_us_p50": 1e3 * rf["verify_ms_p50"],
+                      "verify_gbps": rf["verify_gbps"],
+                      "verify_frac_of_hbm_peak": rf["verify_gbps"] / HBM_PEAK_GBPS,
+                      "step_algorithmic_bytes_per_layer": rf["verify_bytes"]}
     out_tree = None
     if not args.no_tree:
         tree = np.array(TREE4, np.int32)
@@ -483,6 +530,7 @@ def main():
         "conc16_k3_replay": out_replay,
         "conc16_tree4": out_tree,
         "conc16_k3_delta": out_delta,
+        "conc16_k3_delta_folded": out_folded,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

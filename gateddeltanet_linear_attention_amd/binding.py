@@ -63,6 +63,8 @@ _SIGS = {
                        [ctypes.c_int32, _I32P, _VP, _VP, _VP],
     "gdn_verify_window_delta": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
                                [ctypes.c_int32, _I32P, _VP, _VP, _VP],
+    "gdn_verify_window_delta_fold": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
+                                    [ctypes.c_int32, _I32P, _VP, _VP, _I32P, _VP, _VP, _VP, _VP, _VP],
     "gdn_commit_delta": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _VP, _VP, _VP, _VP,
                          ctypes.c_int32, _I32P, _I32P, _VP, _VP],
     "gdn_commit_replay": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
@@ -280,6 +282,45 @@ def _commit_delta_args(dims, row_tokens, k, delta, accepted, state_pool, src_slo
     cd = dims.c()
     args = (ctypes.byref(cd), n_rows, _ip(T), kp, dp, ap, pp, n_slots, _ip(src), _ip(dst), sp, _stream(stream))
     return args, (cd, T, src, dst, k, delta, accepted, state_pool, status)
+
+
+def _verify_fold_args(dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot, delta, o,
+                      prev_row_tokens, prev_k, prev_delta, prev_accepted, status, stream):
+    import torch
+    T, sl, pT = _i32(row_tokens), _i32(slot), _i32(prev_row_tokens)
+    n_rows = T.size
+    if not (sl.size == pT.size == n_rows):
+        raise ValueError("per-row arrays differ in length")
+    toks, op = _token_ptrs(dims, int(T.sum()), q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    dp = _dev(delta, "delta", torch.float32, delta_shape(dims, n_rows))
+    pkp = _dev(prev_k, "prev_k", torch.bfloat16, (int(pT.sum()), dims.n_qk_heads, dims.d_k))
+    pdp = _dev(prev_delta, "prev_delta", torch.float32, delta_shape(dims, n_rows))
+    ap = _dev(prev_accepted, "prev_accepted", torch.int32, (n_rows,))
+    sp = _dev(status, "status", torch.int32, ((n_rows + 31) // 32,))
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, _ip(T), *toks, pp, n_slots, _ip(sl), dp, op, _ip(pT), pkp, pdp, ap, sp,
+            _stream(stream))
+    return args, (cd, T, sl, pT, q, k, v, a, b, A_log, dt_bias, state_pool, delta, o, prev_k, prev_delta,
+                  prev_accepted, status)
+
+
+def gdn_verify_window_delta_fold(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot,
+                                 delta, o, prev_row_tokens, prev_k, prev_delta, prev_accepted, status,
+                                 stream=None) -> None:
+    """Commit each row's previous window (fold its delta checkpoints into slot[r]) and
+    verify the new window from the result, storing its delta checkpoints: one launch."""
+    args, _keep = _verify_fold_args(dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot, delta,
+                                    o, prev_row_tokens, prev_k, prev_delta, prev_accepted, status, stream)
+    _check("gdn_verify_window_delta_fold", lib().gdn_verify_window_delta_fold(*args))
+
+
+def prepare_verify_window_delta_fold(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot,
+                                     delta, o, prev_row_tokens, prev_k, prev_delta, prev_accepted, status,
+                                     stream=None) -> PreparedCall:
+    args, keep = _verify_fold_args(dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot, delta,
+                                   o, prev_row_tokens, prev_k, prev_delta, prev_accepted, status, stream)
+    return PreparedCall("gdn_verify_window_delta_fold", args, keep)
 
 
 def gdn_verify_window_delta(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot,

@@ -99,7 +99,8 @@ int launch_recurrent_rows(const gdn_dims *d, const gdn::RecurrentArgs &proto,
                           const std::vector<int32_t> &rows, const std::vector<int64_t> &cu,
                           const int32_t *ntok, const int32_t *src, const int32_t *dst,
                           const int32_t *n_ck, hipStream_t stream,
-                          const int32_t *parents = nullptr) {
+                          const int32_t *parents = nullptr,
+                          const int32_t *fold_ntok = nullptr, const int64_t *fold_cu = nullptr) {
   for (size_t base = 0; base < rows.size(); base += kRowsPerLaunch) {
     gdn::RecurrentArgs ra = proto;
     const size_t n = std::min<size_t>(kRowsPerLaunch, rows.size() - base);
@@ -119,6 +120,11 @@ int launch_recurrent_rows(const gdn_dims *d, const gdn::RecurrentArgs &proto,
       }
     }
     ra.tree_mode = parents ? 1 : 0;
+    if (fold_ntok)
+      for (size_t j = 0; j < n; ++j) {
+        ra.fold_tok0[j] = int32_t(fold_cu[rows[base + j]]);
+        ra.fold_ntok[j] = fold_ntok[rows[base + j]];
+      }
     if (gdn::launch_recurrent(ra, d->d_k, stream) != hipSuccess) return GDN_E_HIP;
   }
   return GDN_OK;
@@ -376,6 +382,54 @@ int gdn_verify_window_delta(const gdn_dims *dims, int32_t n_rows, const int32_t 
   proto.delta = delta;
   return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, src_slot, nullptr, nullptr,
                                static_cast<hipStream_t>(stream));
+}
+
+int gdn_verify_window_delta_fold(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                                 const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 const float *a, const float *b, const float *A_log,
+                                 const float *dt_bias, float *state_pool, int32_t n_slots,
+                                 const int32_t *slot, float *delta, uint16_t *o,
+                                 const int32_t *prev_row_tokens, const uint16_t *prev_k,
+                                 const float *prev_delta, const int32_t *prev_accepted,
+                                 uint32_t *status, void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if (!row_tokens || !prev_row_tokens) return GDN_E_NULL;
+  if ((rc = check_tokens(q, k, v, a, b, A_log, dt_bias, o))) return rc;
+  if (!state_pool || !slot || !delta || !prev_k || !prev_delta || !prev_accepted || !status)
+    return GDN_E_NULL;
+  if (!aligned(state_pool, 16) || !aligned(delta, 16) || !aligned(prev_delta, 16) || !aligned(prev_k, 16) ||
+      !aligned(prev_accepted, 4) || !aligned(status, 4))
+    return GDN_E_ALIGN;
+  for (int32_t r = 0; r < n_rows; ++r) {
+    if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+    if (prev_row_tokens[r] < 1 || prev_row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+    if (slot[r] < 0) return GDN_E_RANGE;  // the folded state is published to it
+  }
+  if ((rc = check_slots(n_rows, n_slots, slot, slot))) return rc;
+  const Sizes s = sizes_of(dims);
+  const std::vector<int64_t> cu = prefix(n_rows, row_tokens), pcu = prefix(n_rows, prev_row_tokens);
+  const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
+  const size_t dl_b = size_t(n_rows) * size_t(dims->k_max + 1) * size_t(dims->n_v_heads) *
+                      size_t(gdn::delta_row_floats(dims->d_v)) * 4;
+  const size_t o_b = size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2;
+  if (overlap(delta, dl_b, state_pool, pool_b) || overlap(o, o_b, delta, dl_b) ||
+      overlap(o, o_b, state_pool, pool_b) || overlap(delta, dl_b, prev_delta, dl_b) ||
+      overlap(prev_delta, dl_b, state_pool, pool_b))
+    return GDN_E_ALIAS;
+  std::vector<int32_t> rows(static_cast<size_t>(n_rows));
+  for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
+  gdn::RecurrentArgs proto;
+  fill_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, state_pool, nullptr, o);
+  proto.delta = delta;
+  proto.fold_k = prev_k;
+  proto.fold_delta = prev_delta;
+  proto.fold_accepted = prev_accepted;
+  proto.status = status;
+  return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, slot, nullptr, nullptr,
+                               static_cast<hipStream_t>(stream), nullptr, prev_row_tokens, pcu.data());
 }
 
 int gdn_commit_delta(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,

@@ -40,8 +40,18 @@ struct RecurrentArgs {
   int32_t tree_mode;
   uint32_t tree[kRowsPerLaunch];
   // Delta checkpoints (may be null): the rank-1 factors of every window step instead
-  // of the states, laid out as delta_floats below.
+  // of the states, laid out as delta_row_floats below.
   float *delta;
+  // Pending fold (delta mode, may be null): before its window, row r folds tokens
+  // 0..fold_accepted[ck_row[r]] of the previous window (fold_ntok[r] tokens at packed
+  // token fold_tok0[r] of fold_k, factors in fold_delta) into its source state and
+  // writes the result back to slot src[r]; a count outside [0, fold_ntok[r]) leaves
+  // the row untouched (no fold, no window) and sets bit ck_row[r] of status.
+  const uint16_t *fold_k;
+  const float *fold_delta;
+  const int32_t *fold_accepted;
+  int32_t fold_tok0[kRowsPerLaunch];
+  int32_t fold_ntok[kRowsPerLaunch];
   int32_t n_qk, n_v, group;         // heads; group = n_v / n_qk
   int32_t ck_slots;                 // k_max + 1
   int32_t n_rows;                   // rows in this launch

@@ -158,6 +158,54 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     }
   }
 
+  if constexpr (MODE == kDelta) {
+    if (args.fold_k) {
+      // commit the previous window first: fold its accepted prefix into the state
+      // (the fold kernel's operation sequence) and publish it in place
+      const int acc = args.fold_accepted[ck_row];
+      if (acc < 0 || acc >= args.fold_ntok[r]) {
+        if (tile == 0 && h == 0 && tid == 0) atomicOr(args.status + (ck_row >> 5), 1u << (ck_row & 31));
+        return;  // the whole block leaves before any barrier
+      }
+      // the whole window's factors and keys in one round of loads (tokens past the
+      // window clamped to its last one, never applied)
+      float fa[TB], fc[TB][RPL];
+      uint2 fk[TB][NV];
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const int tt = min(t, args.fold_ntok[r] - 1);
+        const float *dl = args.fold_delta + ((size_t(ck_row) * args.ck_slots + tt) * n_v + h) * (D + 4);
+        const uint2 *kr = reinterpret_cast<const uint2 *>(
+            args.fold_k + ((size_t(args.fold_tok0[r]) + tt) * n_qk + hq) * D);
+        fa[t] = dl[D];
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) fc[t][q] = dl[i0 + q];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) fk[t][j] = kr[sub + LPR * j];
+      }
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        if (t > acc) break;
+#pragma unroll
+        for (int q = 0; q < RPL; ++q)
+#pragma unroll
+          for (int j = 0; j < NV; ++j) {
+            s[q][j][0] = fmaf(fc[t][q], bf16_lo(fk[t][j].x), fa[t] * s[q][j][0]);
+            s[q][j][1] = fmaf(fc[t][q], bf16_hi(fk[t][j].x), fa[t] * s[q][j][1]);
+            s[q][j][2] = fmaf(fc[t][q], bf16_lo(fk[t][j].y), fa[t] * s[q][j][2]);
+            s[q][j][3] = fmaf(fc[t][q], bf16_hi(fk[t][j].y), fa[t] * s[q][j][3]);
+          }
+      }
+#pragma unroll
+      for (int q = 0; q < RPL; ++q) {
+        float4 *p = reinterpret_cast<float4 *>(args.state_out + (size_t(src) * n_v + h) * UNIT +
+                                               size_t(i0 + q) * D);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) p[sub + LPR * j] = make_float4(s[q][j][0], s[q][j][1], s[q][j][2], s[q][j][3]);
+      }
+    }
+  }
+
   // stage the row's token inputs (issued while the state loads are in flight)
   for (int x = tid; x < ntok * (D / 4); x += 64 * WAVES) {
     const int t = x / (D / 4), c = x % (D / 4);
@@ -307,6 +355,12 @@ hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream
   if (args.accepted ? (args.o || args.ckpt || !args.status || args.tree_mode || args.delta) : !args.o)
     return hipErrorInvalidValue;
   if (args.delta && (args.ckpt || args.tree_mode)) return hipErrorInvalidValue;
+  if (args.fold_k) {
+    if (!args.delta || !args.fold_delta || !args.fold_accepted || !args.status || !args.state_out)
+      return hipErrorInvalidValue;
+    for (int r = 0; r < args.n_rows; ++r)
+      if (args.src[r] < 0 || args.fold_ntok[r] < 1 || args.fold_ntok[r] > kMaxWindow) return hipErrorInvalidValue;
+  }
   if (args.tree_mode)  // parents precede their children; byte 0 is the committed state
     for (int r = 0; r < args.n_rows; ++r)
       for (int t = 0; t < args.ntok[r]; ++t)

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 4
+#define GDN_VERSION 5
 #define GDN_MAX_K 3 /* largest k_max: at most 4 checkpoint slots per row */
 
 typedef struct gdn_dims {
@@ -190,6 +190,26 @@ int gdn_commit_delta(const gdn_dims *dims, int32_t n_rows, const int32_t *row_to
                      const uint16_t *k, const float *delta, const int32_t *accepted,
                      float *state_pool, int32_t n_slots, const int32_t *src_slot,
                      const int32_t *dst_slot, uint32_t *status, void *stream);
+
+/*
+ * gdn_verify_window_delta_fold -- a verification step that first commits the
+ * row's previous window: exactly gdn_commit_delta(prev_row_tokens, prev_k,
+ * prev_delta, prev_accepted, src = dst = slot) followed by gdn_verify_window_delta
+ * from slot[r] into delta, in one launch (the committed state is folded while it is
+ * in registers and written back to slot[r] before the window runs; bit for bit the
+ * same results).  slot[r] >= 0, distinct across rows; delta and prev_delta are two
+ * different buffers (alternate them between steps).  A row whose prev_accepted is
+ * outside [0, prev_row_tokens[r] - 1] is left untouched -- no fold, no outputs, no
+ * factors -- and sets bit (r % 32) of status[r / 32].
+ */
+int gdn_verify_window_delta_fold(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                                 const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 const float *a, const float *b, const float *A_log,
+                                 const float *dt_bias, float *state_pool, int32_t n_slots,
+                                 const int32_t *slot, float *delta, uint16_t *o,
+                                 const int32_t *prev_row_tokens, const uint16_t *prev_k,
+                                 const float *prev_delta, const int32_t *prev_accepted,
+                                 uint32_t *status, void *stream);
 
 /*
  * gdn_chunked_workspace_bytes -- device workspace that gdn_chunked_prefill_with_

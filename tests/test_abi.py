@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function():
             "gdn_chunked_prefill_with_checkpoints", "gdn_chunked_workspace_bytes",
             "gdn_plan_transaction", "gdn_run_transaction", "gdn_status_str", "gdn_version",
             "gdn_commit_replay", "gdn_verify_tree", "gdn_verify_window_delta",
-            "gdn_commit_delta"} <= set(names)
+            "gdn_commit_delta", "gdn_verify_window_delta_fold"} <= set(names)
     lib = gb.lib()
     for n in names:
         assert hasattr(lib, n), "libgdn.so does not export %s" % n
@@ -261,6 +261,31 @@ def test_delta_validation_codes():
     assert commit([4, 2], [0, 1], [1, 3]) == -4
     assert commit([4, 2], [0, 1], [2, 3], misalign=4) == -5
     assert commit([4, 2], [0, 1], [0, 1]) == -7      # in place passes validation
+
+
+@no_gpu
+def test_folded_verify_validation_codes():
+    lib = gb.lib()
+    b = Bufs()
+    d = _dims()
+    NULL = ctypes.c_void_p(0)
+
+    def fold(T, slots, pT, prev_k=True, same_delta=False):
+        Ta, Tp = _i32(T)
+        sa, sp = _i32(slots)
+        pa, pp = _i32(pT)
+        dl = b.ptr()
+        return lib.gdn_verify_window_delta_fold(ctypes.byref(d), len(Ta), Tp, *[b.ptr() for _ in range(7)], b.ptr(), 8,
+                                                sp, dl, b.ptr(), pp, b.ptr() if prev_k else NULL,
+                                                dl if same_delta else b.ptr(), b.ptr(), b.ptr(), NULL)
+
+    assert fold([4, 2], [0, 1], [4, 4], prev_k=False) == -1
+    assert fold([4, 2], [0, -1], [4, 4]) == -3       # the folded state needs a slot
+    assert fold([4, 2], [0, 1], [4, 5]) == -3        # previous window too long
+    assert fold([4, 2], [0, 1], [0, 4]) == -3        # previous window empty
+    assert fold([4, 2], [1, 1], [4, 4]) == -4        # two rows on one slot
+    assert fold([4, 2], [0, 1], [4, 4], same_delta=True) == -4  # new factors would overwrite the pending ones
+    assert fold([4, 2], [0, 1], [4, 4]) == -7        # valid: passes validation, no GPU here
 
 
 @no_gpu
