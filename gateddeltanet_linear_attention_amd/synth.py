@@ -8,7 +8,9 @@ receive exactly the arrays produced here.
 
 Distributions (one draw per element unless stated):
   * q, k ~ N(0, 1), each (token, qk-head) vector L2-normalised; q then scaled by
-    1/sqrt(d_k); rounded to bfloat16 (ties to even).
+    1/sqrt(d_k); rounded to bfloat16 (ties to even).  With raw_qk the normalisation
+    and the scale are left to the consumer (the library's fused input mode): q, k
+    are the N(0, 1) draws themselves, rounded to bfloat16.
   * v ~ N(0, 1), rounded to bfloat16.
   * gate logits a, b ~ N(0, 1), float32, one per (token, v-head).
   * per v-head parameters: A_log ~ U(log 1, log 16), dt_bias ~ N(0, 0.1^2), float32.
@@ -106,12 +108,18 @@ def _unit_rows(rng: np.random.Generator, n: int, h: int, d: int) -> np.ndarray:
     return x / np.linalg.norm(x, axis=-1, keepdims=True)
 
 
-def tokens(rng: np.random.Generator, shape: HeadShape, n: int, gate_shift: float = 0.0) -> Tokens:
+def tokens(rng: np.random.Generator, shape: HeadShape, n: int, gate_shift: float = 0.0,
+           raw_qk: bool = False) -> Tokens:
     """n fresh tokens.  gate_shift is added to the decay logit a (a negative shift makes
-    the decay slow, alpha close to 1: a stress case for long memory)."""
+    the decay slow, alpha close to 1: a stress case for long memory).  raw_qk: q and k
+    are not normalised (same draws, same stream positions)."""
     d = shape.d
-    q = round_to_bf16(_unit_rows(rng, n, shape.n_qk_heads, d) / np.sqrt(d))
-    k = round_to_bf16(_unit_rows(rng, n, shape.n_qk_heads, d))
+    if raw_qk:
+        q = round_to_bf16(rng.standard_normal((n, shape.n_qk_heads, d)))
+        k = round_to_bf16(rng.standard_normal((n, shape.n_qk_heads, d)))
+    else:
+        q = round_to_bf16(_unit_rows(rng, n, shape.n_qk_heads, d) / np.sqrt(d))
+        k = round_to_bf16(_unit_rows(rng, n, shape.n_qk_heads, d))
     v = round_to_bf16(rng.standard_normal((n, shape.n_v_heads, d)))
     a = (rng.standard_normal((n, shape.n_v_heads)) + gate_shift).astype(np.float32)
     b = rng.standard_normal((n, shape.n_v_heads)).astype(np.float32)
@@ -152,6 +160,7 @@ class VerifyWorkload:
     n_windows: int
     accept: str = "binomial"   # "binomial" (p = 0.85) or "uniform" (0..K_r)
     gate_shift: float = 0.0
+    raw_qk: bool = False       # q, k left unnormalised (fused input mode)
 
     @property
     def n_rows(self) -> int:
@@ -163,10 +172,12 @@ class VerifyWorkload:
 
     def warm_tokens(self) -> Tokens:
         """Packed prior tokens, row r owning warm_lens[r] consecutive tokens."""
-        return tokens(_rng(self.seed, _WARM), self.shape, int(self.warm_lens.sum()), self.gate_shift)
+        return tokens(_rng(self.seed, _WARM), self.shape, int(self.warm_lens.sum()), self.gate_shift,
+                      self.raw_qk)
 
     def window_tokens(self, i: int) -> Tokens:
-        return tokens(_rng(self.seed, _WIN, i), self.shape, int(self.window_lens.sum()), self.gate_shift)
+        return tokens(_rng(self.seed, _WIN, i), self.shape, int(self.window_lens.sum()), self.gate_shift,
+                      self.raw_qk)
 
     def accepted(self, i: int) -> np.ndarray:
         g = _rng(self.seed, _ACC, i)
@@ -179,7 +190,7 @@ VERIFY_WORKLOADS = ("tiny", "batch1", "conc16")
 
 
 def verify_workload(name: str, *, seed: int | None = None, all_k3: bool = False,
-                    n_windows: int | None = None) -> VerifyWorkload:
+                    n_windows: int | None = None, raw_qk: bool = False) -> VerifyWorkload:
     """The verify-window workloads.
 
     "tiny":   one request, one head, d = 16; 8 prompt tokens decoded one by one, then
@@ -211,7 +222,7 @@ def verify_workload(name: str, *, seed: int | None = None, all_k3: bool = False,
     return VerifyWorkload(name=name + ("_k3" if all_k3 else ""), seed=seed, shape=shape,
                           A_log=A_log, dt_bias=dt_bias, warm_lens=np.asarray(warm, np.int32),
                           draft_lens=np.asarray(K, np.int32),
-                          n_windows=nw if n_windows is None else n_windows, accept=acc)
+                          n_windows=nw if n_windows is None else n_windows, accept=acc, raw_qk=raw_qk)
 
 
 @dataclass
@@ -227,20 +238,21 @@ class PrefillWorkload:
     n_tail: np.ndarray
     chunk: int = 64
     gate_shift: float = 0.0
+    raw_qk: bool = False
 
     def tokens(self) -> Tokens:
-        return tokens(_rng(self.seed, _WARM), self.shape, int(self.lens.sum()), self.gate_shift)
+        return tokens(_rng(self.seed, _WARM), self.shape, int(self.lens.sum()), self.gate_shift, self.raw_qk)
 
 
 def prefill_workload(*, seed: int = 1004, lens=(2048,), n_tail=None, shape: HeadShape = FULL,
-                     gate_shift: float = 0.0) -> PrefillWorkload:
+                     gate_shift: float = 0.0, raw_qk: bool = False) -> PrefillWorkload:
     """Default: one request, 2048 new tokens, d = 128 heads, chunk 64, checkpoints at
     the last 4 positions (other lengths / tails for tests)."""
     lens = np.asarray(lens, np.int32)
     nt = np.minimum(lens, 4) if n_tail is None else np.asarray(n_tail, np.int32)
     A_log, dt_bias = head_params(_rng(seed, _PARAMS), shape)
     return PrefillWorkload(seed=seed, shape=shape, A_log=A_log, dt_bias=dt_bias, lens=lens,
-                           n_tail=nt.astype(np.int32), gate_shift=gate_shift)
+                           n_tail=nt.astype(np.int32), gate_shift=gate_shift, raw_qk=raw_qk)
 
 
 @dataclass
@@ -257,19 +269,20 @@ class MixedWorkload:
     prefill_lens: np.ndarray   # [16] (0 for verify rows)
     warm_lens: np.ndarray      # [16] (0 for prefill rows)
     n_windows: int = 64
+    raw_qk: bool = False
 
     @property
     def n_rows(self) -> int:
         return int(self.is_prefill.size)
 
     def warm_tokens(self) -> Tokens:
-        return tokens(_rng(self.seed, _WARM), self.shape, int(self.warm_lens.sum()))
+        return tokens(_rng(self.seed, _WARM), self.shape, int(self.warm_lens.sum()), raw_qk=self.raw_qk)
 
     def transaction_lens(self) -> np.ndarray:
         return np.where(self.is_prefill, self.prefill_lens, 4).astype(np.int32)
 
     def transaction_tokens(self) -> Tokens:
-        return tokens(_rng(self.seed, _DECODE), self.shape, int(self.transaction_lens().sum()))
+        return tokens(_rng(self.seed, _DECODE), self.shape, int(self.transaction_lens().sum()), raw_qk=self.raw_qk)
 
     def transaction_accepted(self) -> np.ndarray:
         """Accepted drafts of the verify rows (prefill rows: unused, 0)."""
@@ -277,13 +290,13 @@ class MixedWorkload:
         return np.where(self.is_prefill, 0, acc).astype(np.int32)
 
     def window_tokens(self, i: int) -> Tokens:
-        return tokens(_rng(self.seed, _WIN, i), self.shape, 4 * self.n_rows)
+        return tokens(_rng(self.seed, _WIN, i), self.shape, 4 * self.n_rows, raw_qk=self.raw_qk)
 
     def accepted(self, i: int) -> np.ndarray:
         return accepted_counts(_rng(self.seed, _ACC, i), np.full(self.n_rows, 3))
 
 
-def mixed_workload(*, seed: int = 1005, n_windows: int = 64) -> MixedWorkload:
+def mixed_workload(*, seed: int = 1005, n_windows: int = 64, raw_qk: bool = False) -> MixedWorkload:
     g = _rng(seed, _LENS)
     B = 16
     is_prefill = np.zeros(B, bool)
@@ -292,4 +305,4 @@ def mixed_workload(*, seed: int = 1005, n_windows: int = 64) -> MixedWorkload:
     warm_lens = np.where(is_prefill, 0, g.integers(128, 2049, size=B)).astype(np.int32)
     A_log, dt_bias = head_params(_rng(seed, _PARAMS), FULL)
     return MixedWorkload(seed=seed, shape=FULL, A_log=A_log, dt_bias=dt_bias, is_prefill=is_prefill,
-                         prefill_lens=prefill_lens, warm_lens=warm_lens, n_windows=n_windows)
+                         prefill_lens=prefill_lens, warm_lens=warm_lens, n_windows=n_windows, raw_qk=raw_qk)

@@ -21,6 +21,10 @@ expresses the verify / commit / decode calls through it:
 * verify tree -- a draft tree instead of a chain: each node runs from its
   parent's state (the pages run chains only and refuse tree shapes, "Occamy 1.0
   MTP", section "MTP1 runtime"; built as an extension, checked against brute force).
+* l2norm_qk -- the input step of the rule when q and k arrive unnormalised: unit
+  Euclidean norm per (token, head) vector, q also scaled by 1/sqrt(d_k) (the gated
+  delta rule normalises queries and keys, Yang, Kautz & Hatamizadeh, ICLR 2025; the
+  pages are silent on it).  Plain numpy, fp64.
 """
 from __future__ import annotations
 
@@ -82,6 +86,19 @@ def _f64(x) -> np.ndarray:
 
 def _p(x):
     return None if x is None else x.ctypes.data_as(_D)
+
+
+L2NORM_EPS = 1e-6  # under the square root: a zero vector maps to zero, not NaN
+
+
+def l2norm_qk(q, k) -> tuple[np.ndarray, np.ndarray]:
+    """(q_hat, k_hat) in fp64: k_hat = k / sqrt(sum_j k_j^2 + eps), and
+    q_hat = q / sqrt(sum_j q_j^2 + eps) / sqrt(d_k), over the last axis."""
+    q, k = _f64(q), _f64(k)
+    d = q.shape[-1]
+    k_hat = k / np.sqrt((k * k).sum(axis=-1, keepdims=True) + L2NORM_EPS)
+    q_hat = q / np.sqrt((q * q).sum(axis=-1, keepdims=True) + L2NORM_EPS) / np.sqrt(d)
+    return q_hat, k_hat
 
 
 def gates(a, b, A_log: float, dt_bias: float) -> tuple[np.ndarray, np.ndarray]:

@@ -418,3 +418,64 @@ def test_tree_rejects_bad_parents():
     for bad in ([0, 0, 1], [-1, 1, 0], [-1, 0, 2], [-1, -2, 0]):
         with pytest.raises(ValueError):
             oracle.verify_tree([3], bad, c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"], c["dt_bias"], c["S0"])
+
+
+# ------------------------------------------------------------ fused input normalisation
+
+def test_l2norm_hand_example():
+    """Pythagorean vectors, worked by hand: |(3, 4, 0, 0)| = 5 and |(1, 2, 2, 0)| = 3,
+    d = 4 so the query scale is 1/2.  The eps under the root moves the results by
+    less than eps / (2 |x|^2) relative."""
+    q = np.array([[[1.0, 2.0, 2.0, 0.0]]])
+    k = np.array([[[3.0, 4.0, 0.0, 0.0]]])
+    qh, kh = oracle.l2norm_qk(q, k)
+    np.testing.assert_allclose(kh[0, 0], [0.6, 0.8, 0.0, 0.0], rtol=1e-7, atol=0)
+    np.testing.assert_allclose(qh[0, 0], [1 / 6, 1 / 3, 1 / 3, 0.0], rtol=1e-7, atol=0)
+
+
+def test_l2norm_unit_vectors_per_token_and_head():
+    """Every (token, head) vector of k_hat has norm 1 and of q_hat norm d^-1/2, each
+    pointing the way its input does (a normalisation over the wrong axis, a missing or
+    misplaced 1/sqrt(d) or a sign slip fails here)."""
+    g = np.random.default_rng(7)
+    d = 128
+    q = g.standard_normal((5, 3, d)) * g.uniform(0.1, 10.0, (5, 3, 1))
+    k = g.standard_normal((5, 3, d)) * g.uniform(0.1, 10.0, (5, 3, 1))
+    qh, kh = oracle.l2norm_qk(q, k)
+    np.testing.assert_allclose(np.linalg.norm(kh, axis=-1), 1.0, rtol=1e-6)
+    np.testing.assert_allclose(np.linalg.norm(qh, axis=-1), d ** -0.5, rtol=1e-6)
+    assert np.all((kh * k).sum(-1) > 0) and np.all((qh * q).sum(-1) > 0)
+    # parallel to the input: the cross terms vanish
+    np.testing.assert_allclose(kh * np.linalg.norm(k, axis=-1, keepdims=True), k, rtol=1e-6, atol=1e-12)
+
+
+def test_l2norm_zero_vector_stays_zero():
+    qh, kh = oracle.l2norm_qk(np.zeros((1, 1, 16)), np.zeros((1, 1, 16)))
+    assert np.all(qh == 0) and np.all(kh == 0)
+
+
+def test_rule_on_normalised_inputs_ignores_input_scale():
+    """With the normalisation in front, scaling the raw q and k by any positive
+    factor leaves states and outputs unchanged (up to eps / |x|^2)."""
+    shape = synth.HeadShape(2, 4, 16)
+    g = synth.streams(31, 2)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    tok = synth.tokens(g[1], shape, 12, raw_qk=True)
+    outs = []
+    for c in (1.0, 8.0):
+        qh, kh = oracle.l2norm_qk(c * tok.q.astype(np.float64), c * tok.k.astype(np.float64))
+        S, _, o = oracle.run_sequential(np.array([12]), qh, kh, tok.v, tok.a, tok.b, A_log, dt_bias)
+        outs.append((S, o))
+    np.testing.assert_allclose(outs[1][0], outs[0][0], rtol=1e-6, atol=1e-9)
+    np.testing.assert_allclose(outs[1][1], outs[0][1], rtol=1e-6, atol=1e-9)
+
+
+def test_raw_tokens_share_the_stream_layout():
+    """raw_qk draws the same number of values as the normalised recipe, so v and the
+    gate logits of a workload are the same in both modes."""
+    shape = synth.FULL
+    t0 = synth.tokens(np.random.default_rng(3), shape, 5)
+    t1 = synth.tokens(np.random.default_rng(3), shape, 5, raw_qk=True)
+    assert np.array_equal(t0.v, t1.v) and np.array_equal(t0.a, t1.a) and np.array_equal(t0.b, t1.b)
+    np.testing.assert_allclose(np.linalg.norm(t0.k.astype(np.float64), axis=-1), 1.0, rtol=1e-2)
+    assert np.linalg.norm(t1.k.astype(np.float64), axis=-1).mean() > 5
