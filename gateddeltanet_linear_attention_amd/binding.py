@@ -23,6 +23,7 @@ GDN_OK = 0
 ROUTE_RECURRENT = 0
 ROUTE_CHUNKED = 1
 MAX_K = 3
+QK_L2NORM = 1  # gdn_dims.flags: q and k are raw; the kernels normalise them (q also by 1/sqrt(d_k))
 
 _ERRORS = {-1: "GDN_E_NULL", -2: "GDN_E_UNSUPPORTED", -3: "GDN_E_RANGE", -4: "GDN_E_ALIAS",
            -5: "GDN_E_ALIGN", -6: "GDN_E_WORKSPACE", -7: "GDN_E_HIP"}
@@ -36,7 +37,8 @@ class GdnError(RuntimeError):
 
 class _Dims(ctypes.Structure):
     _fields_ = [("n_qk_heads", ctypes.c_int32), ("n_v_heads", ctypes.c_int32),
-                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("k_max", ctypes.c_int32)]
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("k_max", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
 
 
 @dataclass(frozen=True)
@@ -46,9 +48,10 @@ class Dims:
     d_k: int
     d_v: int
     k_max: int = 3
+    flags: int = 0  # 0 or QK_L2NORM
 
     def c(self) -> _Dims:
-        return _Dims(self.n_qk_heads, self.n_v_heads, self.d_k, self.d_v, self.k_max)
+        return _Dims(self.n_qk_heads, self.n_v_heads, self.d_k, self.d_v, self.k_max, self.flags)
 
 
 _VP = ctypes.c_void_p

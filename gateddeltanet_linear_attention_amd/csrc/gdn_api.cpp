@@ -29,6 +29,7 @@ int check_dims(const gdn_dims *d) {
     return GDN_E_UNSUPPORTED;
   if (d->n_v_heads > (1 << 16)) return GDN_E_UNSUPPORTED;
   if (d->k_max < 0 || d->k_max > GDN_MAX_K) return GDN_E_UNSUPPORTED;
+  if (d->flags & ~GDN_QK_L2NORM) return GDN_E_UNSUPPORTED;
   return GDN_OK;
 }
 
@@ -91,6 +92,7 @@ void fill_common(gdn::RecurrentArgs &ra, const gdn_dims *d, const uint16_t *q,
   ra.n_qk = d->n_qk_heads; ra.n_v = d->n_v_heads;
   ra.group = d->n_v_heads / d->n_qk_heads;
   ra.ck_slots = d->k_max + 1;
+  ra.qk_norm = (d->flags & GDN_QK_L2NORM) ? 1 : 0;
 }
 
 // Runs rows `rows` (indices into the call's rows) through the recurrent kernel,
@@ -178,6 +180,7 @@ void fill_chunk_common(gdn::ChunkArgs &ca, const gdn_dims *d, const uint16_t *q,
   ca.n_qk = d->n_qk_heads; ca.n_v = d->n_v_heads;
   ca.group = d->n_v_heads / d->n_qk_heads;
   ca.ck_slots = d->k_max + 1;
+  ca.qk_norm = (d->flags & GDN_QK_L2NORM) ? 1 : 0;
 }
 
 // Shared checks of a packed batch whose rows run from src to dst slots with some

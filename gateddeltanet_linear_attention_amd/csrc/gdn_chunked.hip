@@ -12,7 +12,10 @@
 //     S_{c+1} = e^{G_n} S_c + U^T diag(e^{G_n - G}) K
 // (Yang et al., "Parallelizing Linear Transformers with the Delta Rule over
 // Sequence Length", NeurIPS 2024, sec. 3, with the decay of the gated delta rule of
-// Yang, Kautz & Hatamizadeh, ICLR 2025).  A checkpoint at in-chunk position j is
+// Yang, Kautz & Hatamizadeh, ICLR 2025).  When q and k arrive unnormalised, K and Q
+// stand for diag(rk) K and diag(rq) Q (rk_t = 1/|k_t|, rq_t = 1/(|q_t| sqrt(d_k))):
+// the factors are applied to the exact bf16 products and folded into the diagonal
+// scalings above, so the matrix cores still see the bf16 inputs.  A checkpoint at in-chunk position j is
 // (1) truncated at s <= j: one more rank-64 product per requested position, so a
 // long prefill in a ragged batch still publishes the intermediate states a draft
 // rollback needs (the gap named in the onnxruntime-genai pull request "Run chained
@@ -95,11 +98,12 @@ __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
 }
 
 // Workspace of one (chunk, value head): W [C][D], U' [C][D], P [C][C], G [C] fp64,
-// eG[t] = e^{G_t}, eL[s] = e^{G_{n-1} - G_s} (s < n, else 0), K^T [D][C] bf16, the
-// chunk's start state Sc [D][D] and U^T [D][C].
+// eG[t] = e^{G_t}, eL[s] = e^{G_{n-1} - G_s} rk_s (s < n, else 0), K^T [D][C] bf16, the
+// chunk's start state Sc [D][D], U^T [D][C], and the factors rk, rq [C] that scale
+// each token's k and q (1 unless q/k are normalised in the kernels).
 template <int D>
 struct Ws {
-  float *W, *U, *P, *eG, *eL, *Sc, *Ut;
+  float *W, *U, *P, *eG, *eL, *Sc, *Ut, *rk, *rq;
   double *G;
   uint16_t *Kt;
   __device__ Ws(float *base) {
@@ -112,8 +116,19 @@ struct Ws {
     Kt = reinterpret_cast<uint16_t *>(eL + C);
     Sc = eL + C + D * C / 2;
     Ut = Sc + D * D;
+    rk = Ut + D * C;
+    rq = rk + C;
   }
 };
+
+// q/k normalisation of the fused input mode: x / sqrt(sum x^2 + eps), q also by
+// 1/sqrt(d_k).
+constexpr float kNormEps = 1e-6f;
+template <int D>
+constexpr float inv_sqrt_d() {
+  static_assert(D == 16 || D == 128, "head width");
+  return D == 16 ? 0.25f : 0.0883883476483184405501f;
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
@@ -123,6 +138,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   __shared__ __attribute__((aligned(16))) float sA[C * LDC];  // strictly lower A, then T = (I + A)^{-1}
   __shared__ __attribute__((aligned(16))) uint16_t sKt[D * LDB];  // K^T (bf16): row d, column token m
   __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDB];  // V^T (bf16)
+  __shared__ float sRk[C], sRq[C];  // per-token k and q scale factors (1: inputs taken as given)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -144,7 +160,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   };
 
   // 1. gates and the fp64 inclusive prefix sum of g (tokens t >= n: g = beta = 0);
-  //    K^T and V^T staged in LDS; K-row fragments of this wave's tiles loaded.
+  //    K^T and V^T staged in LDS, with the k and q norms when normalising.
+  double G = 0.0, Gl = 0.0;  // wave 0: lane t's prefix sum G_t and the chunk's last one
   if (w == 0) {
     float gf = 0.0f, bt = 0.0f;
     if (lane < n) {
@@ -154,7 +171,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
       gf = -(expf(args.A_log[h]) * sp);
       bt = 1.0f / (1.0f + expf(-args.b[tk * n_v + h]));
     }
-    double G = gf;
+    G = gf;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double y = __shfl_up(G, off, 64);
@@ -163,22 +180,31 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     sG[lane] = G;
     sBeta[lane] = bt;
     sSK[lane] = bt * float(exp(G));
-    const double Gl = __shfl(G, n - 1, 64);
+    Gl = __shfl(G, n - 1, 64);
     ws.G[lane] = G;
     ws.eG[lane] = float(exp(G));
-    ws.eL[lane] = lane < n ? float(exp(Gl - G)) : 0.0f;
   }
   // Transposing stage: lane (m_lo, dg) of wave mh loads 4 dims of token
   // m = 16 mh + m_lo, so the 16 lanes of a group write 16 consecutive columns of a
   // K^T row and the 4 groups land on disjoint banks (row pitch 136 B).
   {
     const int m = 16 * w + (lane & 15), dg = lane >> 4;
+    const bool norm = args.qk_norm != 0;
+    float ssk = 0.0f, ssq = 0.0f;  // this lane's D/4 dims of token m
     for (int it = 0; it < D / 16; ++it) {
       const int d4 = (4 * it + dg) * 4;
-      uint2 kw = make_uint2(0u, 0u), vw = kw;
+      uint2 kw = make_uint2(0u, 0u), vw = kw, qw = kw;
       if (m < n) {
         kw = *reinterpret_cast<const uint2 *>(Kc + int64_t(m) * ldqk + d4);
         vw = *reinterpret_cast<const uint2 *>(Vc + int64_t(m) * ldv + d4);
+        if (norm) qw = *reinterpret_cast<const uint2 *>(Qc + int64_t(m) * ldqk + d4);
+      }
+      if (norm) {
+        const float4 kf = unpack_bf16x4(kw), qf = unpack_bf16x4(qw);
+        ssk = fmaf(kf.x, kf.x, ssk); ssk = fmaf(kf.y, kf.y, ssk);
+        ssk = fmaf(kf.z, kf.z, ssk); ssk = fmaf(kf.w, kf.w, ssk);
+        ssq = fmaf(qf.x, qf.x, ssq); ssq = fmaf(qf.y, qf.y, ssq);
+        ssq = fmaf(qf.z, qf.z, ssq); ssq = fmaf(qf.w, qf.w, ssq);
       }
       sKt[(d4 + 0) * LDB + m] = uint16_t(kw.x);
       sKt[(d4 + 1) * LDB + m] = uint16_t(kw.x >> 16);
@@ -189,8 +215,27 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
       sVt[(d4 + 2) * LDB + m] = uint16_t(vw.y);
       sVt[(d4 + 3) * LDB + m] = uint16_t(vw.y >> 16);
     }
+    if (norm) {  // the 4 lanes of token m (lane bits 4 and 5) hold its partial sums
+      ssk += __shfl_xor(ssk, 16, 64);
+      ssk += __shfl_xor(ssk, 32, 64);
+      ssq += __shfl_xor(ssq, 16, 64);
+      ssq += __shfl_xor(ssq, 32, 64);
+    }
+    if (dg == 0) {
+      sRk[m] = !norm ? 1.0f : m < n ? 1.0f / sqrtf(ssk + kNormEps) : 0.0f;
+      sRq[m] = !norm ? 1.0f : m < n ? 1.0f / sqrtf(ssq + kNormEps) * inv_sqrt_d<D>() : 0.0f;
+    }
   }
   lds_barrier();
+  if (w == 0) {
+    // with the k factors known: the carry's decays e^{G_n - G_s} rk_s and the
+    // diagonal beta e^G rk of W (read in step 4, after further barriers)
+    const float rk = sRk[lane];
+    ws.eL[lane] = lane < n ? float(exp(Gl - G)) * rk : 0.0f;
+    sSK[lane] *= rk;
+    ws.rk[lane] = rk;
+    ws.rq[lane] = sRq[lane];
+  }
   // K^T to the workspace for the scan kernel: row d is 64 contiguous bf16
   for (int idx = tid; idx < D * (C / 4); idx += 256) {
     const int d = idx / (C / 4), m4 = (idx % (C / 4)) * 4;
@@ -228,8 +273,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
         float av = 0.0f, pv = 0.0f;
         if (s <= t) {
           const float dec = expf(float(sG[t] - sG[s]));
-          pv = dec * qk[v];
-          if (s < t) av = sBeta[t] * dec * kk[v];
+          pv = dec * (qk[v] * sRq[t] * sRk[s]);
+          if (s < t) av = sBeta[t] * dec * (kk[v] * sRk[t] * sRk[s]);
         }
         if (tj <= w) sA[t * LDC + s] = av;  // the upper blocks of sA hold T below
         ws.P[t * C + s] = pv;
@@ -537,7 +582,7 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(ChunkArgs args) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) pf[kb] = *reinterpret_cast<const float4 *>(ws.P + t_me * C + 16 * kb + 4 * g4);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) eg[v] = ws.eG[16 * w + 4 * g4 + v];
+  for (int v = 0; v < 4; ++v) eg[v] = ws.eG[16 * w + 4 * g4 + v] * ws.rq[16 * w + 4 * g4 + v];
   lds_barrier();
 
 #pragma unroll
@@ -586,11 +631,11 @@ __global__ __launch_bounds__(256) void chunk_ckpt_kernel(ChunkArgs args) {
   const int jj = p - cin * C;
   const int n_v = args.n_v;
   const Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * ChunkArgs::ws_unit_floats(D));
-  // scale_s = e^{G_j' - G_s} for s <= j' (else 0, a select so an overflowed
+  // scale_s = e^{G_j' - G_s} rk_s for s <= j' (else 0, a select so an overflowed
   // exponential on the masked side cannot become a NaN), rounded exactly as the
   // carry's factors, so the checkpoint at a row's last position is bit-identical
   // to the final state the scan publishes
-  if (w == 0) sScale[lane] = lane <= jj ? float(exp(ws.G[jj] - ws.G[lane])) : 0.0f;
+  if (w == 0) sScale[lane] = lane <= jj ? float(exp(ws.G[jj] - ws.G[lane])) * ws.rk[lane] : 0.0f;
   lds_barrier();
   float4 af[4];
 #pragma unroll

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs args, int b
 }
 
 // Fold commit of delta checkpoints: the committed state becomes the accepted prefix
-// of the window applied to the source state, S <- fmaf(c_i, k_t[d], alpha_t S) per
+// of the window applied to the source state, S <- fmaf(c_i, k_t[d] ks_t, alpha_t S) per
 // element and token -- the verify kernel's own update, operation for operation, so the
 // result is bit-identical to the state the window reached after that prefix.  A block
 // streams 16 KiB of one (row, head) state: four float4 per thread, each inside one
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs args, int block
   const int hq = h / args.group, src = args.src[r], ntok = args.ntok[r];
   // every token's factors and keys are loaded before the first update (tokens past the
   // window are clamped to its last one and never applied): one memory round trip
-  float cf[kMaxWindow][kF4PerThread], al[kMaxWindow];
+  float cf[kMaxWindow][kF4PerThread], al[kMaxWindow], ks[kMaxWindow];
   uint2 kw[kMaxWindow][kF4PerThread];
 #pragma unroll
   for (int t = 0; t < kMaxWindow; ++t) {
@@ -85,6 +85,7 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs args, int block
     const float *dl = args.delta + ((size_t(row) * args.ck_slots + tt) * args.n_v + h) * (D + 4);
     const uint16_t *kr = args.k + ((size_t(args.tok0[r]) + tt) * args.n_qk + hq) * D;
     al[t] = dl[D];
+    ks[t] = dl[D + 1];  // the key's scale factor (1 unless normalised in the kernel)
 #pragma unroll
     for (int m = 0; m < kF4PerThread; ++m) {
       const int idx = min(part * kF4PerBlock + m * kThreads + int(threadIdx.x), N4 - 1);
@@ -108,11 +109,11 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs args, int block
     if (t > acc) break;
 #pragma unroll
     for (int m = 0; m < kF4PerThread; ++m) {
-      const float c = cf[t][m], alpha = al[t];
-      x[m].x = fmaf(c, __uint_as_float(kw[t][m].x << 16), alpha * x[m].x);
-      x[m].y = fmaf(c, __uint_as_float(kw[t][m].x & 0xFFFF0000u), alpha * x[m].y);
-      x[m].z = fmaf(c, __uint_as_float(kw[t][m].y << 16), alpha * x[m].z);
-      x[m].w = fmaf(c, __uint_as_float(kw[t][m].y & 0xFFFF0000u), alpha * x[m].w);
+      const float c = cf[t][m], alpha = al[t], f = ks[t];
+      x[m].x = fmaf(c, __uint_as_float(kw[t][m].x << 16) * f, alpha * x[m].x);
+      x[m].y = fmaf(c, __uint_as_float(kw[t][m].x & 0xFFFF0000u) * f, alpha * x[m].y);
+      x[m].z = fmaf(c, __uint_as_float(kw[t][m].y << 16) * f, alpha * x[m].z);
+      x[m].w = fmaf(c, __uint_as_float(kw[t][m].y & 0xFFFF0000u) * f, alpha * x[m].w);
     }
   }
 #pragma unroll

@@ -61,6 +61,7 @@ struct RecurrentArgs {
   int32_t dst[kRowsPerLaunch];
   int32_t ck_first[kRowsPerLaunch];
   int32_t ck_row[kRowsPerLaunch];   // checkpoint row (index of the row in the call)
+  int32_t qk_norm;                  // GDN_QK_L2NORM: normalise q and k in the kernel
 };
 
 // Commit: row r copies checkpoint slot accepted[r] of its ckpt row to pool slot
@@ -80,8 +81,9 @@ struct CommitArgs {
 
 // Delta checkpoint of one (call row r, window token t, value head h): d + 4 floats at
 // ((r * ck_slots + t) * n_v + h) * (d + 4): c[0..d), c_i = beta_t (v_t[i] - alpha_t
-// u_i), then alpha_t at [d] (the last 3 floats pad rows to 16 bytes).  The step is
-// S_t[i][d'] = fmaf(c_i, k_t[d'], alpha_t S_{t-1}[i][d']) for every element.
+// u_i), alpha_t at [d] and the key's scale factor ks_t at [d + 1] (1 unless q/k are
+// normalised in the kernel; the last 2 floats pad rows to 16 bytes).  The step is
+// S_t[i][d'] = fmaf(c_i, k_t[d'] * ks_t, alpha_t S_{t-1}[i][d']) for every element.
 constexpr int delta_row_floats(int d) { return d + 4; }
 
 // Fold commit: row r of the launch applies window tokens 0..accepted[row_base + r]
@@ -113,10 +115,11 @@ constexpr int kChunk = 64;
 
 // Workspace floats per (chunk, value head): W [64][d], U' [64][d], P [64][64],
 // the 64 fp64 prefix sums of the log-decay, two 64-float decay vectors, K^T
-// [d][64] in bf16, the chunk's start state [d][d] and U^T [d][64].
+// [d][64] in bf16, the chunk's start state [d][d], U^T [d][64] and the per-token
+// k and q scale factors [2][64].
 constexpr int64_t chunk_ws_unit_floats(int d) {
   return 2 * int64_t(kChunk) * d + int64_t(kChunk) * kChunk + 4 * kChunk + int64_t(d) * kChunk / 2 +
-         int64_t(d) * d + int64_t(d) * kChunk;
+         int64_t(d) * d + int64_t(d) * kChunk + 2 * kChunk;
 }
 
 struct ChunkArgs {
@@ -138,6 +141,7 @@ struct ChunkArgs {
   int32_t dst[kRowsPerLaunch];
   int32_t n_tail[kRowsPerLaunch];
   int32_t ck_row[kRowsPerLaunch];
+  int32_t qk_norm;                  // GDN_QK_L2NORM: normalise q and k in the kernels
   static constexpr int64_t ws_unit_floats(int d) { return chunk_ws_unit_floats(d); }
 };
 

@@ -82,6 +82,24 @@ __device__ __forceinline__ float group_sum(float p) {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Sum over the 64 lanes of a wave by an xor butterfly: at each step a lane adds its
+// partner's partial sum to its own, and addition is commutative, so every lane
+// ends with the same bits.
+__device__ __forceinline__ float wave_sum(float p) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
+  return p;
+}
+
+// q/k normalisation of the fused input mode: x / sqrt(sum x^2 + eps), q also by
+// 1/sqrt(d_k).
+constexpr float kNormEps = 1e-6f;
+template <int D>
+constexpr float inv_sqrt_d() {
+  static_assert(D == 16 || D == 128, "head width");
+  return D == 16 ? 0.25f : 0.0883883476483184405501f;
+}
+
 // Checkpoints are written once and read at most once (by commit), after the whole
 // window: stream them past the caches.
 __device__ __forceinline__ void store_nt(float *p, const float (&x)[4]) {
@@ -110,6 +128,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   __shared__ float4 sK[TB][D / 4], sQ[TB][D / 4];
   __shared__ float sV[TB][ROWS];
   __shared__ float sAlpha[TB], sBeta[TB];
+  __shared__ float sKs[TB];          // the factor each key was scaled by (1: none)
   __shared__ uint16_t sO[TB][ROWS];  // outputs, written back coalesced at the end
 
   const int tid = threadIdx.x;
@@ -169,7 +188,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
       }
       // the whole window's factors and keys in one round of loads (tokens past the
       // window clamped to its last one, never applied)
-      float fa[TB], fc[TB][RPL];
+      float fa[TB], fs[TB], fc[TB][RPL];
       uint2 fk[TB][NV];
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
@@ -178,6 +197,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
         const uint2 *kr = reinterpret_cast<const uint2 *>(
             args.fold_k + ((size_t(args.fold_tok0[r]) + tt) * n_qk + hq) * D);
         fa[t] = dl[D];
+        fs[t] = dl[D + 1];
 #pragma unroll
         for (int q = 0; q < RPL; ++q) fc[t][q] = dl[i0 + q];
 #pragma unroll
@@ -190,10 +210,10 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
         for (int q = 0; q < RPL; ++q)
 #pragma unroll
           for (int j = 0; j < NV; ++j) {
-            s[q][j][0] = fmaf(fc[t][q], bf16_lo(fk[t][j].x), fa[t] * s[q][j][0]);
-            s[q][j][1] = fmaf(fc[t][q], bf16_hi(fk[t][j].x), fa[t] * s[q][j][1]);
-            s[q][j][2] = fmaf(fc[t][q], bf16_lo(fk[t][j].y), fa[t] * s[q][j][2]);
-            s[q][j][3] = fmaf(fc[t][q], bf16_hi(fk[t][j].y), fa[t] * s[q][j][3]);
+            s[q][j][0] = fmaf(fc[t][q], bf16_lo(fk[t][j].x) * fs[t], fa[t] * s[q][j][0]);
+            s[q][j][1] = fmaf(fc[t][q], bf16_hi(fk[t][j].x) * fs[t], fa[t] * s[q][j][1]);
+            s[q][j][2] = fmaf(fc[t][q], bf16_lo(fk[t][j].y) * fs[t], fa[t] * s[q][j][2]);
+            s[q][j][3] = fmaf(fc[t][q], bf16_hi(fk[t][j].y) * fs[t], fa[t] * s[q][j][3]);
           }
       }
 #pragma unroll
@@ -226,14 +246,39 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     const size_t tok = size_t(tok0) + tid;
     eval_gates(args.a[tok * n_v + h], args.b[tok * n_v + h], args.A_log[h], args.dt_bias[h],
                sAlpha[tid], sBeta[tid]);
+    sKs[tid] = 1.0f;
   }
   lds_barrier();
+  if (args.qk_norm) {
+    // raw q and k: one wave per staged vector computes its norm and scales it in
+    // place.  The result depends only on the token's own values, never on its window
+    // position, the tile or the launch, so every instantiation normalises alike.
+    const int wave = tid / 64, lane = tid % 64;
+    const int nvec = write_o ? 2 * ntok : ntok;
+    for (int vi = wave; vi < nvec; vi += WAVES) {
+      const int t = write_o ? vi >> 1 : vi;
+      const bool isq = write_o && (vi & 1);
+      float4 *vec = isq ? sQ[t] : sK[t];
+      const float4 x = lane < D / 4 ? vec[lane] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      float ss = x.x * x.x;
+      ss = fmaf(x.y, x.y, ss);
+      ss = fmaf(x.z, x.z, ss);
+      ss = fmaf(x.w, x.w, ss);
+      ss = wave_sum(ss);
+      float f = 1.0f / sqrtf(ss + kNormEps);
+      if (isq) f *= inv_sqrt_d<D>();
+      if (lane < D / 4) vec[lane] = make_float4(x.x * f, x.y * f, x.z * f, x.w * f);
+      if (!isq && lane == 0) sKs[t] = f;
+    }
+    lds_barrier();
+  }
 
   // Token t of the window applied to state rows st, with its output and checkpoint.
   auto step = [&](int t, float (&st)[RPL][NV][4]) {
     const float alpha = sAlpha[t], beta = sBeta[t];
     if (MODE == kDelta && tile == 0 && tid == 0)
-      args.delta[((size_t(ck_row) * args.ck_slots + t) * n_v + h) * (D + 4) + D] = alpha;
+      *reinterpret_cast<float2 *>(args.delta + ((size_t(ck_row) * args.ck_slots + t) * n_v + h) * (D + 4) + D) =
+          make_float2(alpha, sKs[t]);
     float kk[NV][4];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {

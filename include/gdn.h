@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 5
+#define GDN_VERSION 6
 #define GDN_MAX_K 3 /* largest k_max: at most 4 checkpoint slots per row */
 
 typedef struct gdn_dims {
@@ -59,7 +59,22 @@ typedef struct gdn_dims {
   int32_t d_k;        /* key / query width */
   int32_t d_v;        /* value width (== d_k) */
   int32_t k_max;      /* largest draft count per row; checkpoint slots per row = k_max + 1 */
+  uint32_t flags;     /* 0, or GDN_QK_L2NORM; other bits: GDN_E_UNSUPPORTED */
 } gdn_dims;
+
+/*
+ * GDN_QK_L2NORM -- fused input side.  q and k arrive as raw projections; every
+ * call that reads them (decode, verification in every mode, replay, chunked
+ * prefill, transactions) first normalises each (token, q/k head) vector:
+ *     k_hat = k / sqrt(sum_j k_j^2 + 1e-6),  q_hat = q / sqrt(sum_j q_j^2 + 1e-6) / sqrt(d_k)
+ * in fp32 from the bf16 inputs (the normalised values are not rounded back to
+ * bf16), and runs the rule on k_hat, q_hat (the gated delta rule normalises its
+ * queries and keys, Yang, Kautz & Hatamizadeh, ICLR 2025; the pages are silent).
+ * The recurrent calls normalise a token identically whatever its window position,
+ * so the decode/verify bit-consistency holds in this mode too.  Without the flag q
+ * and k are taken as already normalised and scaled.
+ */
+#define GDN_QK_L2NORM 1u
 
 enum {
   GDN_OK = 0,
@@ -172,7 +187,8 @@ int gdn_commit_replay(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
  * gdn_verify_window_delta is gdn_verify_window storing those factors instead of the
  * states: delta (device fp32 [n_rows][k_max+1][H_v][d_v + 4], 16-byte aligned)
  * receives, for window token t < T_r of row r and value head h, c at
- * [r][t][h][0..d_v) and alpha_t at [r][t][h][d_v] (the last 3 floats are padding):
+ * [r][t][h][0..d_v), alpha_t at [r][t][h][d_v] and the factor the step's key was
+ * scaled by at [r][t][h][d_v + 1] (1 unless GDN_QK_L2NORM; 2 floats of padding):
  * (d_v + 4) * 4 bytes per (token, head) instead of d_v * d_k * 4.
  * gdn_commit_delta folds tokens 0..a_r of row r (accepted: device int32 [n_rows];
  * k: the same packed window keys) into the state of slot src_slot[r] (-1: zero) and

@@ -29,8 +29,16 @@ def say(*args):
     sys.stdout.flush()
 
 
-def dims_of(shape: synth.HeadShape, k_max: int = 3) -> gb.Dims:
-    return gb.Dims(shape.n_qk_heads, shape.n_v_heads, shape.d, shape.d, k_max)
+def dims_of(shape: synth.HeadShape, k_max: int = 3, raw_qk: bool = False) -> gb.Dims:
+    """raw_qk: q and k are unnormalised and the library normalises them (GDN_QK_L2NORM)."""
+    return gb.Dims(shape.n_qk_heads, shape.n_v_heads, shape.d, shape.d, k_max,
+                   gb.QK_L2NORM if raw_qk else 0)
+
+
+def ref_qk(tok: synth.Tokens, raw_qk: bool):
+    """The q and k the oracle runs on: normalised by the oracle when the inputs are raw."""
+    import oracle
+    return oracle.l2norm_qk(tok.q, tok.k) if raw_qk else (tok.q, tok.k)
 
 
 def dev_tokens(tok: synth.Tokens) -> dict:

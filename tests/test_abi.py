@@ -264,6 +264,19 @@ def test_delta_validation_codes():
 
 
 @no_gpu
+def test_unknown_dims_flags_are_refused():
+    lib = gb.lib()
+    b = Bufs()
+    src, src_p = _i32([0])
+    dst, dst_p = _i32([1])
+    for flags, expect in ((2, -2), (0x80000000, -2), (gb.QK_L2NORM, -7)):
+        d = gb._Dims(16, 32, 128, 128, 3, flags)
+        rc = lib.gdn_decode_step(ctypes.byref(d), 1, *[b.ptr() for _ in range(7)], b.ptr(), 4,
+                                 src_p, dst_p, b.ptr(), None)
+        assert rc == expect, (flags, rc)  # -7: valid, refused only for want of a GPU
+
+
+@no_gpu
 def test_folded_verify_validation_codes():
     lib = gb.lib()
     b = Bufs()
@@ -304,7 +317,7 @@ def test_chunked_and_transaction_validation_codes():
     b = Bufs()
     d = _dims()
     need = gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100, 64, 1])
-    assert need == (2 + 1 + 1) * 32 * (2 * 64 * 128 + 64 * 64 + 256 + 128 * 32 + 128 * 128 + 128 * 64) * 4
+    assert need == (2 + 1 + 1) * 32 * (2 * 64 * 128 + 64 * 64 + 256 + 128 * 32 + 128 * 128 + 128 * 64 + 128) * 4
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100], chunk=32) == 0
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [0]) == 0
 

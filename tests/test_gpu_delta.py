@@ -32,10 +32,13 @@ def _pool(n_slots, Hv, d, seed, scale=0.3):
     return (scale * torch.randn(n_slots, Hv, d, d, generator=g)).cuda()
 
 
+@pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
 @pytest.mark.parametrize("shape", [synth.FULL, synth.TINY, synth.HeadShape(2, 6, 128)],
                          ids=["h16x32_d128", "h1_d16", "h2x6_d128"])
-def test_delta_commit_equals_checkpoint_commit_bitwise(shape):
-    dims = dims_of(shape)
+def test_delta_commit_equals_checkpoint_commit_bitwise(shape, raw_qk):
+    """With GDN_QK_L2NORM the fold re-scales each raw key by the factor the verify
+    stored, so the bits still agree."""
+    dims = dims_of(shape, raw_qk=raw_qk)
     Hv, d = shape.n_v_heads, shape.d
     pairs = [(t, a) for t in range(1, 5) for a in range(t)]
     T = np.array([t for t, _ in pairs], np.int32)
@@ -43,7 +46,7 @@ def test_delta_commit_equals_checkpoint_commit_bitwise(shape):
     g = synth.streams(51, 2)
     A_log, dt_bias = synth.head_params(g[0], shape)
     P = dev_params(A_log, dt_bias)
-    td = dev_tokens(synth.tokens(g[1], shape, int(T.sum())))
+    td = dev_tokens(synth.tokens(g[1], shape, int(T.sum()), raw_qk=raw_qk))
     acc = torch.tensor([a for _, a in pairs], dtype=torch.int32, device="cuda")
     rows = np.arange(B, dtype=np.int32)
     pool = _pool(3 * B, Hv, d, 11)
@@ -116,12 +119,13 @@ def test_conc16_workload_in_delta_mode():
 
 # ---------------------------------------------------------------- fold into the next verify
 
-def test_folded_verify_equals_commit_then_verify_bitwise():
+@pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
+def test_folded_verify_equals_commit_then_verify_bitwise(raw_qk):
     """gdn_verify_window_delta_fold == gdn_commit_delta(previous window) followed by
     gdn_verify_window_delta (new window), bit for bit: pool, outputs and factors;
     a row with a bad previous accepted count is left untouched and flagged."""
     shape = synth.FULL
-    dims = dims_of(shape)
+    dims = dims_of(shape, raw_qk=raw_qk)
     Hv, d = shape.n_v_heads, shape.d
     B = 6
     T1 = np.array([4, 3, 2, 4, 1, 4], np.int32)
@@ -129,8 +133,8 @@ def test_folded_verify_equals_commit_then_verify_bitwise():
     g = synth.streams(55, 4)
     A_log, dt_bias = synth.head_params(g[0], shape)
     P = dev_params(A_log, dt_bias)
-    w1 = dev_tokens(synth.tokens(g[1], shape, int(T1.sum())))
-    w2 = dev_tokens(synth.tokens(g[2], shape, int(T2.sum())))
+    w1 = dev_tokens(synth.tokens(g[1], shape, int(T1.sum()), raw_qk=raw_qk))
+    w2 = dev_tokens(synth.tokens(g[2], shape, int(T2.sum()), raw_qk=raw_qk))
     acc_np = np.array([g[3].integers(0, t) for t in T1], np.int32)
     acc_np[4] = 1  # out of range for a 1-token window: row 4 must stay untouched
     acc = torch.from_numpy(acc_np).cuda()

@@ -21,7 +21,7 @@ import oracle
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
 from tests.gpu_common import (assert_o, assert_state, bits, dev_params, dev_tokens, dims_of, host,
-                              index_tokens, o_err, say, state_err)
+                              index_tokens, o_err, ref_qk, say, state_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,9 +50,10 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
     each followed by commit of the accepted length -- mode "checkpoint" (dense
     checkpoints, gdn_commit_accepted), "replay" (verify without checkpoints, then
     gdn_commit_replay in place) or "delta" (delta checkpoints, gdn_commit_delta in
-    place); the oracle runs the same chain independently from its own states.
+    place); the oracle runs the same chain independently from its own states.  A workload
+    with raw q/k runs with GDN_QK_L2NORM, the oracle on its own normalisation.
     Returns the worst errors seen."""
-    dims = dims_of(w.shape)
+    dims = dims_of(w.shape, raw_qk=w.raw_qk)
     B, Hv, d = w.n_rows, w.shape.n_v_heads, w.shape.d
     P = dev_params(w.A_log, w.dt_bias)
     rows = np.arange(B, dtype=np.int32)
@@ -70,7 +71,7 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
         src = act if t > 0 else np.full(len(act), -1, np.int32)
         gb.gdn_decode_step(dims, **tok, **P, state_pool=pool, src_slot=src, dst_slot=act, o=o_step)
         o_warm[torch.as_tensor(idx, device="cuda")] = o_step
-    S_ref, _, o_ref = oracle.run_sequential(w.warm_lens, warm.q, warm.k, warm.v, warm.a, warm.b,
+    S_ref, _, o_ref = oracle.run_sequential(w.warm_lens, *ref_qk(warm, w.raw_qk), warm.v, warm.a, warm.b,
                                             w.A_log, w.dt_bias)
     torch.cuda.synchronize()
     worst = {"o_abs": assert_o(host(o_warm), o_ref, w.name + " warm-up outputs"),
@@ -103,7 +104,7 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
             gb.gdn_verify_window(dims, T, **wd, **P, state_pool=pool, src_slot=rows, ckpt=ckpt, o=o_win)
             gb.gdn_commit_accepted(dims, T, ckpt, torch.from_numpy(acc).cuda(), pool, dst_slot=rows,
                                    status=status)
-        ck_o, o_o = oracle.verify_window(T, win.q, win.k, win.v, win.a, win.b, w.A_log, w.dt_bias,
+        ck_o, o_o = oracle.verify_window(T, *ref_qk(win, w.raw_qk), win.v, win.a, win.b, w.A_log, w.dt_bias,
                                          S_bufs[cur], nan_fill=False, out=out)
         cur = 1 - cur
         for r in range(B):  # commit(a_r): the state after a_r + 1 window tokens
@@ -203,16 +204,17 @@ def _random_pool(n_slots, Hv, d, seed, scale=0.3):
     return (scale * torch.randn(n_slots, Hv, d, d, generator=g)).cuda()
 
 
+@pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
 @pytest.mark.parametrize("shape", [synth.FULL, synth.TINY, synth.HeadShape(2, 6, 128)],
                          ids=["h16x32_d128", "h1_d16", "h2x6_d128"])
-def test_verify_checkpoint_j_bit_identical_to_decode_chain(shape):
-    dims = dims_of(shape)
+def test_verify_checkpoint_j_bit_identical_to_decode_chain(shape, raw_qk):
+    dims = dims_of(shape, raw_qk=raw_qk)
     B, Hv, d = 16, shape.n_v_heads, shape.d
     T = np.array([1, 2, 3, 4] * (B // 4), np.int32)
     g = synth.streams(17, 2)
     A_log, dt_bias = synth.head_params(g[0], shape)
     P = dev_params(A_log, dt_bias)
-    tok = synth.tokens(g[1], shape, int(T.sum()))
+    tok = synth.tokens(g[1], shape, int(T.sum()), raw_qk=raw_qk)
     td = dev_tokens(tok)
     pool = _random_pool(B, Hv, d, 5)
     ref_pool = pool.clone()
@@ -239,7 +241,7 @@ def test_verify_checkpoint_j_bit_identical_to_decode_chain(shape):
     for r in range(B):
         assert bool((bits(ckpt[r, T[r]:]) == POISON).all()), "row %d: slot >= T_r written" % r
     # and the values are right
-    ck_o, o_o = oracle.verify_window(T, tok.q, tok.k, tok.v, tok.a, tok.b, A_log, dt_bias, host(ref_pool))
+    ck_o, o_o = oracle.verify_window(T, *ref_qk(tok, raw_qk), tok.v, tok.a, tok.b, A_log, dt_bias, host(ref_pool))
     assert_o(host(o_win), o_o, "verify outputs")
     for r in range(B):
         assert_state(host(ckpt[r, :T[r]]), ck_o[r, :T[r]], "row %d checkpoints" % r)

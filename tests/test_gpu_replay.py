@@ -34,24 +34,25 @@ def _pool(n_slots, Hv, d, seed, scale=0.3):
     return (scale * torch.randn(n_slots, Hv, d, d, generator=g)).cuda()
 
 
-def _case(shape, T, seed):
+def _case(shape, T, seed, raw_qk=False):
     g = synth.streams(seed, 3)
     A_log, dt_bias = synth.head_params(g[0], shape)
-    tok = synth.tokens(g[1], shape, int(np.sum(T)))
+    tok = synth.tokens(g[1], shape, int(np.sum(T)), raw_qk=raw_qk)
     acc = np.array([g[2].integers(0, t) for t in T], np.int32)
     return dev_params(A_log, dt_bias), dev_tokens(tok), acc
 
 
+@pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
 @pytest.mark.parametrize("shape", [synth.FULL, synth.TINY, synth.HeadShape(2, 6, 128)],
                          ids=["h16x32_d128", "h1_d16", "h2x6_d128"])
-def test_replay_equals_checkpoint_commit_bitwise(shape):
-    dims = dims_of(shape)
+def test_replay_equals_checkpoint_commit_bitwise(shape, raw_qk):
+    dims = dims_of(shape, raw_qk=raw_qk)
     Hv, d = shape.n_v_heads, shape.d
     # every (T, a) pair with 1 <= T <= 4, 0 <= a < T
     pairs = [(t, a) for t in range(1, 5) for a in range(t)]
     T = np.array([t for t, _ in pairs], np.int32)
     B = T.size
-    P, td, _ = _case(shape, T, 41)
+    P, td, _ = _case(shape, T, 41, raw_qk)
     acc = torch.tensor([a for _, a in pairs], dtype=torch.int32, device="cuda")
     rows = np.arange(B, dtype=np.int32)
     pool = _pool(3 * B, Hv, d, 7)

@@ -30,17 +30,17 @@ torch = pytest.importorskip("torch")
 POISON = 0x7FC0DEAD
 
 
-def _case(shape, parents_by_row, seed):
+def _case(shape, parents_by_row, seed, raw_qk=False):
     T = np.array([len(p) for p in parents_by_row], np.int32)
     g = synth.streams(seed, 2)
     A_log, dt_bias = synth.head_params(g[0], shape)
-    tok = synth.tokens(g[1], shape, int(T.sum()))
+    tok = synth.tokens(g[1], shape, int(T.sum()), raw_qk=raw_qk)
     parents = np.concatenate([np.asarray(p, np.int32) for p in parents_by_row])
     return T, parents, tok, A_log, dt_bias
 
 
-def _run_tree(shape, T, parents, tok, A_log, dt_bias, pool):
-    dims = dims_of(shape)
+def _run_tree(shape, T, parents, tok, A_log, dt_bias, pool, raw_qk=False):
+    dims = dims_of(shape, raw_qk=raw_qk)
     B, Hv, d = len(T), shape.n_v_heads, shape.d
     ckpt = torch.empty(B, 4, Hv, d, d, device="cuda")
     ckpt.view(torch.int32).fill_(POISON)
@@ -89,15 +89,16 @@ def test_random_trees_full_shape_against_the_oracle():
         assert bool((bits(ckpt[r, t:]) == POISON).all()), "row %d: slot >= T_r written" % r
 
 
+@pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
 @pytest.mark.parametrize("shape", [synth.FULL, synth.TINY], ids=["h16x32_d128", "h1_d16"])
-def test_chain_shaped_tree_is_bit_identical_to_the_window(shape):
-    dims = dims_of(shape)
+def test_chain_shaped_tree_is_bit_identical_to_the_window(shape, raw_qk):
+    dims = dims_of(shape, raw_qk=raw_qk)
     T = np.array([4, 3, 1, 2, 4], np.int32)
     parents = np.concatenate([np.arange(t) - 1 for t in T]).astype(np.int32)
-    _, _, tok, A_log, dt_bias = _case(shape, [list(range(-1, t - 1)) for t in T], 74)
+    _, _, tok, A_log, dt_bias = _case(shape, [list(range(-1, t - 1)) for t in T], 74, raw_qk)
     g = torch.Generator(device="cpu").manual_seed(5)
     pool = (0.2 * torch.randn(len(T), shape.n_v_heads, shape.d, shape.d, generator=g)).cuda()
-    ck_t, o_t = _run_tree(shape, T, parents, tok, A_log, dt_bias, pool)
+    ck_t, o_t = _run_tree(shape, T, parents, tok, A_log, dt_bias, pool, raw_qk)
     ck_w = torch.empty_like(ck_t)
     ck_w.view(torch.int32).fill_(POISON)
     o_w = torch.empty_like(o_t)
