@@ -115,6 +115,7 @@ class VerifySet:
 
     def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False, parents=None, delta=False,
                  folded=False):
+        raw_qk = bool(dims.flags & gb.QK_L2NORM)
         import numpy as np
         import torch
         shape = synth.FULL
@@ -123,7 +124,7 @@ class VerifySet:
         B, N = int(Ts.size), int(Ts.sum())
         g = synth.streams(seed, 3)
         A_log, dt_bias = synth.head_params(g[0], shape)
-        tok = synth.tokens(g[1], shape, N)
+        tok = synth.tokens(g[1], shape, N, raw_qk=raw_qk)
         acc = synth.accepted_counts(g[2], Ts - 1)
         dev = "cuda"
         self.t = dict(q=torch.from_numpy(tok.q).to(torch.bfloat16).to(dev),
@@ -302,11 +303,12 @@ def prefill_flops(L: int, n_heads: int = 32, d: int = 128, C: int = 64) -> float
     return float((L + C - 1) // C) * n_heads * per_chunk
 
 
-def measure_prefill(gb, synth, torch, stream, reps):
+def measure_prefill(gb, synth, torch, stream, reps, raw_qk=False):
     """The 2048-token chunked prefill (1 row, 32 value heads, chunk 64, checkpoints at
-    the last 4 positions), timed with events on the launch stream."""
-    w = synth.prefill_workload()
-    dims = gb.Dims(16, 32, 128, 128, 3)
+    the last 4 positions), timed with events on the launch stream.  raw_qk: q and k
+    unnormalised, normalised inside the kernels (GDN_QK_L2NORM)."""
+    w = synth.prefill_workload(raw_qk=raw_qk)
+    dims = gb.Dims(16, 32, 128, 128, 3, gb.QK_L2NORM if raw_qk else 0)
     tok = w.tokens()
     dev = "cuda"
     t = dict(q=torch.from_numpy(tok.q).to(torch.bfloat16).to(dev),
@@ -342,12 +344,12 @@ def measure_prefill(gb, synth, torch, stream, reps):
 
 
 def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay=False, parents=None,
-            delta=False, folded=False):
+            delta=False, folded=False, raw_qk=False):
     """Steps over n_layers layers of windows with per-row token counts Ts (replay:
     verify without checkpoints, commit by replay; parents: one draft tree per row;
     delta: delta checkpoints folded by a commit launch; folded: folded by the next
-    verify, one launch per layer per step)."""
-    dims = gb.Dims(16, 32, 128, 128, 3)
+    verify, one launch per layer per step; raw_qk: q and k normalised inside the kernels)."""
+    dims = gb.Dims(16, 32, 128, 128, 3, gb.QK_L2NORM if raw_qk else 0)
     sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents, delta, folded)
             for i in range(n_layers)]
     wall, verify_ms, commit_ms = run_steps(sets, steps, warmup, stream, torch)
@@ -402,6 +404,8 @@ def main():
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-replay", action="store_true")
     ap.add_argument("--no-tree", action="store_true")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the line with q/k normalised inside the kernels")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replays of the batch-1 step")
     ap.add_argument("--prefill-only", action="store_true",
@@ -483,6 +487,19 @@ def main():
                       "verify_gbps": rf["verify_gbps"],
                       "verify_frac_of_hbm_peak": rf["verify_gbps"] / HBM_PEAK_GBPS,
                       "step_algorithmic_bytes_per_layer": rf["verify_bytes"]}
+    out_fused = None
+    if not args.no_fused:
+        _, rq = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
+                        raw_qk=True)
+        out_fused = side(rq, [4] * 16)
+        out_fused["mode"] = ("raw q/k normalised inside the kernels (GDN_QK_L2NORM), checkpoint verify + "
+                             "commit; same algorithmic bytes as the headline")
+        # what the fusion removes: a separate pass reading raw bf16 q and k and writing
+        # them back normalised, per layer-step
+        out_fused["saved_pass_bytes_per_layer"] = 2 * 2 * 16 * 4 * 16 * 128 * 2
+        if not args.no_prefill:
+            out_fused["prefill_us_per_call"] = measure_prefill(gb, synth, torch, stream, args.prefill_reps,
+                                                               raw_qk=True)["us_per_call"]
     out_tree = None
     if not args.no_tree:
         tree = np.array(TREE4, np.int32)
@@ -531,6 +548,7 @@ def main():
         "conc16_tree4": out_tree,
         "conc16_k3_delta": out_delta,
         "conc16_k3_delta_folded": out_folded,
+        "conc16_k3_fused_qk_norm": out_fused,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

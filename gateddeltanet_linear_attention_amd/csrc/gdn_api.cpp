@@ -62,6 +62,7 @@ int check_tokens(const uint16_t *q, const uint16_t *k, const uint16_t *v, const 
 // Source slots may be -1 (zero state); destination slots must be distinct and
 // must not be read by another row of the same launch set.
 int check_slots(int32_t n_rows, int32_t n_slots, const int32_t *src, const int32_t *dst) {
+  if (n_rows > 0 && n_slots < 1) return GDN_E_RANGE;  // kernels read slot 0 for source -1
   for (int32_t r = 0; r < n_rows; ++r) {
     if (src && (src[r] < -1 || src[r] >= n_slots)) return GDN_E_RANGE;
     if (dst && (dst[r] < -1 || dst[r] >= n_slots)) return GDN_E_RANGE;

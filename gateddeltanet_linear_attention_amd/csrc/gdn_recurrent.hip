@@ -82,15 +82,6 @@ __device__ __forceinline__ float group_sum(float p) {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Sum over the 64 lanes of a wave by an xor butterfly: at each step a lane adds its
-// partner's partial sum to its own, and addition is commutative, so every lane
-// ends with the same bits.
-__device__ __forceinline__ float wave_sum(float p) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
-  return p;
-}
-
 // q/k normalisation of the fused input mode: x / sqrt(sum x^2 + eps), q also by
 // 1/sqrt(d_k).
 constexpr float kNormEps = 1e-6f;
@@ -98,6 +89,26 @@ template <int D>
 constexpr float inv_sqrt_d() {
   static_assert(D == 16 || D == 128, "head width");
   return D == 16 ? 0.25f : 0.0883883476483184405501f;
+}
+
+// Squared norm of a D-vector held as one float4 by each of D/4 consecutive lanes
+// (a quad at D = 16, half a wave at D = 128): in-lane chain, DPP butterfly over the
+// lane group, then at D = 128 the two 16-lane halves swapped and added.  Every lane
+// of the group ends with the same bits, and the result does not depend on where in
+// the wave the group sits.
+template <int D>
+__device__ __forceinline__ float sq_norm(const float4 &x) {
+  float p = x.x * x.x;
+  p = fmaf(x.y, x.y, p);
+  p = fmaf(x.z, x.z, p);
+  p = fmaf(x.w, x.w, p);
+  if constexpr (D == 16) {
+    return group_sum<4>(p);
+  } else {
+    static_assert(D == 128, "head width");
+    p = group_sum<16>(p);
+    return p + __shfl_xor(p, 16, 64);
+  }
 }
 
 // Checkpoints are written once and read at most once (by commit), after the whole
@@ -160,20 +171,41 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   }
   constexpr bool write_o = !REPLAY;
 
+  // The row's token inputs are loaded before the state: one counter tracks loads in
+  // issue order, so the waits that staging needs then leave the state loads in
+  // flight, and staging (gates, q/k normalisation, LDS writes) overlaps their latency.
+  // Thread x holds float4 column group x % (D/4) of token x / (D/4) of k (and q), the
+  // v value at x / ROWS, x % ROWS of the block's slice, and the gate logits of token
+  // x.  Every load is issued unconditionally (indexes past the window clamped to its
+  // last token, results unused): with a fixed number of loads after each one, the
+  // compiler can wait for exactly the ones it needs.
+  static_assert(kMaxWindow * (D / 4) <= 64 * WAVES && kMaxWindow * ROWS <= 64 * WAVES,
+                "one pass stages a window");
+  const int kt = tid / (D / 4), kc = tid % (D / 4);
+  const int vt = tid / ROWS, vr = tid % ROWS;
+  uint2 kw, qw = make_uint2(0u, 0u);
+  {
+    const size_t tk = size_t(tok0) + min(kt, ntok - 1);
+    kw = reinterpret_cast<const uint2 *>(args.k + (tk * n_qk + hq) * D)[kc];
+    if (write_o) qw = reinterpret_cast<const uint2 *>(args.q + (tk * n_qk + hq) * D)[kc];
+  }
+  const uint32_t vw = args.v[((size_t(tok0) + min(vt, ntok - 1)) * n_v + h) * D + tile * ROWS + vr];
+  const size_t tg = size_t(tok0) + min(tid, ntok - 1);
+  const float ga = args.a[tg * n_v + h], gb = args.b[tg * n_v + h];
+  const float A_log_h = args.A_log[h], dt_bias_h = args.dt_bias[h];
+  __builtin_amdgcn_sched_barrier(0);  // keep every token load ahead of the state loads
+
+  // the committed state (slot -1: zero; slot 0, which every pool has, is read and
+  // discarded, keeping the load unconditional)
   float s[RPL][NV][4];
 #pragma unroll
   for (int q = 0; q < RPL; ++q) {
-    if (src >= 0) {
-      const float4 *p = reinterpret_cast<const float4 *>(
-          args.state_in + (size_t(src) * n_v + h) * UNIT + size_t(i0 + q) * D);
+    const float4 *p = reinterpret_cast<const float4 *>(
+        args.state_in + (size_t(max(src, 0)) * n_v + h) * UNIT + size_t(i0 + q) * D);
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const float4 x = p[sub + LPR * j];
-        s[q][j][0] = x.x; s[q][j][1] = x.y; s[q][j][2] = x.z; s[q][j][3] = x.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NV; ++j) s[q][j][0] = s[q][j][1] = s[q][j][2] = s[q][j][3] = 0.0f;
+    for (int j = 0; j < NV; ++j) {
+      const float4 x = p[sub + LPR * j];
+      s[q][j][0] = x.x; s[q][j][1] = x.y; s[q][j][2] = x.z; s[q][j][3] = x.w;
     }
   }
 
@@ -226,51 +258,35 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     }
   }
 
-  // stage the row's token inputs (issued while the state loads are in flight)
-  for (int x = tid; x < ntok * (D / 4); x += 64 * WAVES) {
-    const int t = x / (D / 4), c = x % (D / 4);
-    const size_t tok = size_t(tok0) + t;
-    const uint2 kw = reinterpret_cast<const uint2 *>(args.k + (tok * n_qk + hq) * D)[c];
-    sK[t][c] = make_float4(bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y));
-    if (write_o) {
-      const uint2 qw = reinterpret_cast<const uint2 *>(args.q + (tok * n_qk + hq) * D)[c];
-      sQ[t][c] = make_float4(bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y));
+  // stage the window in LDS; with raw q/k the D/4 threads of a token first reduce its
+  // squared norm among themselves and scale (every lane takes part, those past the
+  // window with zeros)
+  {
+    float4 kf = make_float4(bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y));
+    float4 qf = make_float4(bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y));
+    float fk = 1.0f;
+    if (args.qk_norm) {
+      fk = 1.0f / sqrtf(sq_norm<D>(kf) + kNormEps);
+      kf = make_float4(kf.x * fk, kf.y * fk, kf.z * fk, kf.w * fk);
+      if (write_o) {
+        const float fq = (1.0f / sqrtf(sq_norm<D>(qf) + kNormEps)) * inv_sqrt_d<D>();
+        qf = make_float4(qf.x * fq, qf.y * fq, qf.z * fq, qf.w * fq);
+      }
+    }
+    if (kt < ntok) {
+      sK[kt][kc] = kf;
+      if (write_o) sQ[kt][kc] = qf;
+      if (kc == 0) sKs[kt] = fk;
     }
   }
-  for (int x = tid; x < ntok * ROWS; x += 64 * WAVES) {
-    const int t = x / ROWS, rr = x % ROWS;
-    const size_t tok = size_t(tok0) + t;
-    sV[t][rr] = __uint_as_float(uint32_t(args.v[(tok * n_v + h) * D + tile * ROWS + rr]) << 16);
-  }
-  if (tid < ntok) {
-    const size_t tok = size_t(tok0) + tid;
-    eval_gates(args.a[tok * n_v + h], args.b[tok * n_v + h], args.A_log[h], args.dt_bias[h],
-               sAlpha[tid], sBeta[tid]);
-    sKs[tid] = 1.0f;
-  }
+  if (vt < ntok) sV[vt][vr] = __uint_as_float(vw << 16);
+  if (tid < ntok) eval_gates(ga, gb, A_log_h, dt_bias_h, sAlpha[tid], sBeta[tid]);
   lds_barrier();
-  if (args.qk_norm) {
-    // raw q and k: one wave per staged vector computes its norm and scales it in
-    // place.  The result depends only on the token's own values, never on its window
-    // position, the tile or the launch, so every instantiation normalises alike.
-    const int wave = tid / 64, lane = tid % 64;
-    const int nvec = write_o ? 2 * ntok : ntok;
-    for (int vi = wave; vi < nvec; vi += WAVES) {
-      const int t = write_o ? vi >> 1 : vi;
-      const bool isq = write_o && (vi & 1);
-      float4 *vec = isq ? sQ[t] : sK[t];
-      const float4 x = lane < D / 4 ? vec[lane] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      float ss = x.x * x.x;
-      ss = fmaf(x.y, x.y, ss);
-      ss = fmaf(x.z, x.z, ss);
-      ss = fmaf(x.w, x.w, ss);
-      ss = wave_sum(ss);
-      float f = 1.0f / sqrtf(ss + kNormEps);
-      if (isq) f *= inv_sqrt_d<D>();
-      if (lane < D / 4) vec[lane] = make_float4(x.x * f, x.y * f, x.z * f, x.w * f);
-      if (!isq && lane == 0) sKs[t] = f;
-    }
-    lds_barrier();
+  if (src < 0) {  // after staging: replacing a register whose load is in flight would wait for it
+#pragma unroll
+    for (int q = 0; q < RPL; ++q)
+#pragma unroll
+      for (int j = 0; j < NV; ++j) s[q][j][0] = s[q][j][1] = s[q][j][2] = s[q][j][3] = 0.0f;
   }
 
   // Token t of the window applied to state rows st, with its output and checkpoint.

@@ -31,6 +31,8 @@
  *      ckpt   fp32 [n_rows][k_max+1][H_v][d_v][d_k]  checkpoint slot j of row r
  *  - Host arrays (validated before anything is launched): per-row token counts,
  *    slot indices and checkpoint counts.  A source slot of -1 means the zero state.
+ *    A call with rows needs n_slots >= 1 (GDN_E_RANGE otherwise): the kernels read
+ *    slot 0 in place of a zero source and discard it.
  *  - Alignment: q, k, v, o, state_pool, ckpt and the workspace 16 B; a, b, A_log,
  *    dt_bias 4 B.  Otherwise GDN_E_ALIGN.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
