@@ -401,9 +401,12 @@ static void launch_d(const RecurrentArgs &args, hipStream_t stream) {
     hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kReplay>), grid, dim3(64 * WAVES), 0, stream, args);
   else if (args.delta)
     hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kDelta>), grid, dim3(64 * WAVES), 0, stream, args);
-  else if (args.tree_mode)
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kTree>), grid, dim3(64 * WAVES), 0, stream, args);
-  else
+  else if constexpr (RPL == 1) {  // trees always store checkpoints: one lane layout
+    if (args.tree_mode)
+      hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kTree>), grid, dim3(64 * WAVES), 0, stream, args);
+    else
+      hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kChain>), grid, dim3(64 * WAVES), 0, stream, args);
+  } else
     hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kChain>), grid, dim3(64 * WAVES), 0, stream, args);
 }
 
@@ -426,9 +429,17 @@ hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream
     for (int r = 0; r < args.n_rows; ++r)
       for (int t = 0; t < args.ntok[r]; ++t)
         if (int((args.tree[r] >> (8 * t)) & 0xFFu) > t) return hipErrorInvalidValue;
-  if (d == 128)
-    launch_d<128, 16, 1, 8>(args, stream);
-  else if (d == 16)
+  if (d == 128) {
+    // A launch that stores no dense checkpoints moves little data per block and waits
+    // mostly on its state loads; when it has two rounds of blocks or more, two state
+    // rows per lane halve the block count and double the loads each lane has in
+    // flight.  Each state row keeps its 16 lanes, columns and butterfly, so every
+    // result is bit-identical in both layouts.
+    if (!args.ckpt && !args.tree_mode && int64_t(args.n_rows) * args.n_v >= 512)
+      launch_d<128, 16, 2, 8>(args, stream);
+    else
+      launch_d<128, 16, 1, 8>(args, stream);
+  } else if (d == 16)
     launch_d<16, 4, 1, 1>(args, stream);
   else
     return hipErrorInvalidValue;
