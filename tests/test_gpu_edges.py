@@ -1,0 +1,110 @@
+"""Edge cases through the C ABI on the GPU.
+
+* Zero rows: every entry point returns without launching or writing anything.
+* Degenerate gates and vectors, against the oracle: write strength beta -> 1 (the
+  delta-rule overwrite) and -> 0 (pure decay), decay alpha -> 0 (state reset) and
+  -> 1 (no decay), zero keys, zero values and zero queries, with q/k given or
+  normalised in the kernels (a zero raw vector stays zero), through the recurrent
+  kernel and the chunked form.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gateddeltanet_linear_attention_amd import binding as gb
+from gateddeltanet_linear_attention_amd import synth
+from tests.gpu_common import assert_o, assert_state, bits, dev_params, dev_tokens, dims_of, host, ref_qk
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+POISON = 0x7FC0DEAD
+
+
+def test_zero_row_calls_write_nothing():
+    shape = synth.FULL
+    dims = dims_of(shape)
+    Hv, d, Hq = shape.n_v_heads, shape.d, shape.n_qk_heads
+    pool = torch.empty(2, Hv, d, d, device="cuda")
+    pool.view(torch.int32).fill_(POISON)
+    before = pool.clone()
+    e16 = lambda h: torch.empty(0, h, d, dtype=torch.bfloat16, device="cuda")
+    ef = torch.empty(0, Hv, device="cuda")
+    P = dev_params(np.zeros(Hv, np.float32), np.zeros(Hv, np.float32))
+    tok = dict(q=e16(Hq), k=e16(Hq), v=e16(Hv), a=ef, b=ef.clone())
+    none = np.zeros(0, np.int32)
+    ckpt = torch.empty(0, 4, Hv, d, d, device="cuda")
+    o = e16(Hv)
+    acc = torch.empty(0, dtype=torch.int32, device="cuda")
+    st = torch.zeros(0, dtype=torch.int32, device="cuda")  # status words for zero rows
+    delta = torch.empty(gb.delta_shape(dims, 0), device="cuda")
+    gb.gdn_decode_step(dims, **tok, **P, state_pool=pool, src_slot=none, dst_slot=none, o=o)
+    gb.gdn_verify_window(dims, none, **tok, **P, state_pool=pool, src_slot=none, ckpt=ckpt, o=o)
+    gb.gdn_verify_window(dims, none, **tok, **P, state_pool=pool, src_slot=none, ckpt=None, o=o)
+    gb.gdn_verify_tree(dims, none, none, **tok, **P, state_pool=pool, src_slot=none, ckpt=ckpt, o=o)
+    gb.gdn_commit_accepted(dims, none, ckpt, acc, pool, dst_slot=none, status=st)
+    gb.gdn_commit_replay(dims, none, **tok, **P, accepted=acc, state_pool=pool, src_slot=none, dst_slot=none,
+                         status=st)
+    gb.gdn_verify_window_delta(dims, none, **tok, **P, state_pool=pool, src_slot=none, delta=delta, o=o)
+    gb.gdn_commit_delta(dims, none, tok["k"], delta, acc, pool, src_slot=none, dst_slot=none, status=st)
+    gb.gdn_verify_window_delta_fold(dims, none, **tok, **P, state_pool=pool, slot=none, delta=delta, o=o,
+                                    prev_row_tokens=none, prev_k=tok["k"], prev_delta=delta.clone(),
+                                    prev_accepted=acc, status=st)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    assert gb.gdn_chunked_workspace_bytes(dims, none) == 0
+    gb.gdn_chunked_prefill_with_checkpoints(dims, none, none, **tok, **P, state_pool=pool, src_slot=none,
+                                            dst_slot=none, ckpt=ckpt, o=o, workspace=ws)
+    gb.gdn_run_transaction(dims, none, none, **tok, **P, state_pool=pool, src_slot=none, dst_slot=none,
+                           ckpt=ckpt, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(pool), bits(before))
+
+
+def _degenerate_tokens(shape, raw_qk, seed):
+    """8 rows x 4 tokens; row r carries one extreme case on every token."""
+    g = synth.streams(seed, 2)
+    tok = synth.tokens(g[0], shape, 32, raw_qk=raw_qk)
+    q, k, v, a, b = (x.copy() for x in (tok.q, tok.k, tok.v, tok.a, tok.b))
+    rows = lambda r: slice(4 * r, 4 * r + 4)
+    b[rows(0)] = 60.0    # beta = 1: the key's old value is overwritten
+    b[rows(1)] = -60.0   # beta ~ 1e-26: pure decay
+    a[rows(2)] = 60.0    # alpha = exp(-exp(A_log) * 60) ~ 0: the state is reset
+    a[rows(3)] = -60.0   # alpha ~ 1: no decay
+    k[rows(4)] = 0.0     # zero keys
+    v[rows(5)] = 0.0     # zero values
+    q[rows(6)] = 0.0     # zero queries: zero outputs
+    a[rows(7)] = 88.0    # both gates saturated at once
+    b[rows(7)] = 88.0
+    return synth.Tokens(q, k, v, a, b), *synth.head_params(g[1], shape)
+
+
+@pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
+def test_degenerate_gates_and_vectors_match_the_oracle(raw_qk):
+    shape = synth.HeadShape(2, 4, 128)
+    dims = dims_of(shape, raw_qk=raw_qk)
+    Hv, d = shape.n_v_heads, shape.d
+    tok, A_log, dt_bias = _degenerate_tokens(shape, raw_qk, 95)
+    B, T = 8, np.full(8, 4, np.int32)
+    gen = torch.Generator(device="cpu").manual_seed(95)
+    pool = (0.3 * torch.randn(B, Hv, d, d, generator=gen)).cuda()
+    td, P = dev_tokens(tok), dev_params(A_log, dt_bias)
+    ckpt = torch.empty(B, 4, Hv, d, d, device="cuda")
+    o = torch.empty(32, Hv, d, dtype=torch.bfloat16, device="cuda")
+    gb.gdn_verify_window(dims, T, **td, **P, state_pool=pool, src_slot=np.arange(B), ckpt=ckpt, o=o)
+    # the same rows through the chunked form, from the same states, into fresh slots
+    pool2 = torch.cat([pool, torch.zeros_like(pool)])
+    ck_c = torch.empty_like(ckpt)
+    o_c = torch.empty_like(o)
+    ws = torch.empty(gb.gdn_chunked_workspace_bytes(dims, T), dtype=torch.uint8, device="cuda")
+    gb.gdn_chunked_prefill_with_checkpoints(dims, T, T, **td, **P, state_pool=pool2, src_slot=np.arange(B),
+                                            dst_slot=np.arange(B, 2 * B), ckpt=ck_c, o=o_c, workspace=ws)
+    qo, ko = ref_qk(tok, raw_qk)
+    ck_o, o_o = oracle.verify_window(T, qo, ko, tok.v, tok.a, tok.b, A_log, dt_bias, host(pool))
+    torch.cuda.synchronize()
+    for name, oo, cc in (("recurrent", o, ckpt), ("chunked", o_c, ck_c)):
+        assert bool(torch.isfinite(cc).all()) and bool(torch.isfinite(oo.float()).all()), name
+        assert_o(host(oo), o_o, name + " outputs")
+        for r in range(B):
+            assert_state(host(cc[r]), ck_o[r], "%s row %d checkpoints" % (name, r))
+    assert not bool(o[24:28].view(torch.int16).any()), "zero queries must give zero outputs"
