@@ -135,7 +135,7 @@ int launch_recurrent_rows(const gdn_dims *d, const gdn::RecurrentArgs &proto,
 
 int64_t chunks_of(int32_t len) { return (int64_t(len) + gdn::kChunk - 1) / gdn::kChunk; }
 
-// Runs rows `rows` through the two chunked kernels, kRowsPerLaunch at a time;
+// Runs rows `rows` through the chunked kernels, kRowsPerLaunch at a time;
 // workspace chunks are numbered over all of `rows`.
 int launch_chunked_rows(const gdn_dims *d, const gdn::ChunkArgs &proto,
                         const std::vector<int32_t> &rows, const std::vector<int64_t> &cu,

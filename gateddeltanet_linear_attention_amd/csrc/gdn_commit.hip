@@ -6,7 +6,9 @@
 // in the batch Engine", sections "Correctness fix" and "Rollback fix and
 // corrected quality disposition").  a_r is read on the device, never on the
 // host.  The copy is a plain bit copy with 16-byte coalesced accesses; an a_r
-// outside [0, T_r) leaves the row untouched and raises the row's status bit.
+// outside [0, T_r) leaves the row untouched and raises the row's status bit.  The
+// fold kernel below commits delta checkpoints the same way by re-applying the
+// accepted steps' rank-1 factors.
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"

@@ -20,20 +20,24 @@
 // non-temporal stores: the traffic is one state read to T checkpoint writes, and
 // streaming the writes past the caches is what lets it approach the HBM peak.
 //
-// Replay.  With a device array of accepted counts the kernel runs only each row's
-// accepted prefix (bonus token + a_r drafts) from the committed state and writes
-// the resulting state, no outputs and no checkpoints: rollback by re-running the
-// accepted tokens instead of storing a state per window token.
+// Modes (one instantiation each, same per-token code): chain (decode, verify windows
+// with or without checkpoints, short transaction rows), replay (each row's accepted
+// prefix re-run from the committed state, the result written back: rollback without
+// stored states), tree (each window token runs from its parent's state) and delta
+// (each step's rank-1 factors stored instead of the state, optionally after folding
+// the previous window's accepted prefix into the state).  Raw q/k are normalised in
+// the staging lanes when the caller asks for it.
 //
-// Bit-exactness.  Decode, verify, replay and transaction rows all run this one kernel
-// instantiation per d; the per-row arithmetic (element ownership, FMA order,
-// butterfly, gate code) does not depend on the row's token count, the launch's
-// row count or the grid.  So the checkpoint after j+1 verify tokens is
-// bit-identical to j+1 decode launches: both compute the same sequence of fp32
-// operations on the same values, and fp32 state round-trips through memory
-// exactly ("Native three-step MTP", section "What changed": state-update
-// rounding consistent between decode and verification).  Built with
-// -ffp-contract=off; every fused multiply-add is an explicit fmaf.
+// Bit-exactness.  The per-row arithmetic (element ownership within the row's LPR
+// lanes, FMA order, butterfly, gate and normalisation code) is the same in every
+// mode and both lane layouts (one or two state rows per lane), and does not depend
+// on the row's token count, the launch's row count or the grid.  So the checkpoint
+// after j+1 verify tokens is bit-identical to j+1 decode launches, a replayed or
+// folded commit to the checkpoint it replaces: each computes the same sequence of
+// fp32 operations on the same values, and fp32 state round-trips through memory
+// exactly ("Native three-step MTP", section "What changed": state-update rounding
+// consistent between decode and verification).  Built with -ffp-contract=off;
+// every fused multiply-add is an explicit fmaf.
 #include <hip/hip_runtime.h>
 
 #include "gdn_device.h"
