@@ -97,10 +97,15 @@ __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
   return row;
 }
 
-// Workspace of one (chunk, value head): W [C][D], U' [C][D], P [C][C], G [C] fp64,
-// eG[t] = e^{G_t}, eL[s] = e^{G_{n-1} - G_s} rk_s (s < n, else 0), K^T [D][C] bf16, the
-// chunk's start state Sc [D][D], U^T [D][C], and the factors rk, rq [C] that scale
-// each token's k and q (1 unless q/k are normalised in the kernels).
+// Workspace of one (chunk, value head): W [C][D], U'^T [D][C], P [C][C], G [C] fp64,
+// eG[t] = e^{G_t}, eL[s] = e^{G_{n-1} - G_s} rk_s (s < n, else 0), K^T [D][C] bf16 with
+// each row's tokens in kt_pos order (below), the chunk's start state Sc [D][D], U^T
+// [D][C], and the factors rk, rq [C] that scale each token's k and q (1 unless q/k
+// are normalised in the kernels).
+// Token m = 16 kb + 4 g + e of a chunk sits at 16 g + 4 kb + e of a stored K^T row, so
+// the MFMA lane group g finds its four 4-token pieces (kb = 0..3) in 32 contiguous bytes.
+__device__ __forceinline__ int kt_pos(int m) { return 16 * ((m >> 2) & 3) + 4 * (m >> 4) + (m & 3); }
+
 template <int D>
 struct Ws {
   float *W, *U, *P, *eG, *eL, *Sc, *Ut, *rk, *rq;
@@ -236,10 +241,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     ws.rk[lane] = rk;
     ws.rq[lane] = sRq[lane];
   }
-  // K^T to the workspace for the scan kernel: row d is 64 contiguous bf16
+  // K^T to the workspace for the scan and checkpoint kernels: row d is 64 contiguous
+  // bf16, 4-token pieces placed by kt_pos
   for (int idx = tid; idx < D * (C / 4); idx += 256) {
     const int d = idx / (C / 4), m4 = (idx % (C / 4)) * 4;
-    *reinterpret_cast<uint2 *>(ws.Kt + d * C + m4) = *reinterpret_cast<const uint2 *>(sKt + d * LDB + m4);
+    *reinterpret_cast<uint2 *>(ws.Kt + d * C + kt_pos(m4)) = *reinterpret_cast<const uint2 *>(sKt + d * LDB + m4);
   }
 
   // 2. K K^T -> A (strictly lower, scaled) and Q K^T -> P (lower with diagonal) on
@@ -360,12 +366,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
         wa = mma4(wa, mul4(tr, sk), kt);
         ua = mma4(ua, mul4(tr, sb), vt);
       }
+      const int d = 16 * nt + r16;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = 16 * ti + 4 * g4 + v, d = 16 * nt + r16;
-        ws.W[t * D + d] = wa[v];
-        ws.U[t * D + d] = ua[v];
-      }
+      for (int v = 0; v < 4; ++v) ws.W[(16 * ti + 4 * g4 + v) * D + d] = wa[v];
+      // U'^T: the lane's 4 tokens are contiguous
+      *reinterpret_cast<float4 *>(ws.U + d * C + 16 * ti + 4 * g4) = make_float4(ua[0], ua[1], ua[2], ua[3]);
     }
   }
 }
@@ -376,29 +381,30 @@ template <int D>
 struct ScanFrag {
   static constexpr int NKB = D / 16;
   static constexpr int NT_W = (D / 16 + 3) / 4;
-  float4 wf[NKB], el[4], kf[NT_W][4];
-  float up[4];
+  float4 wf[NKB], el, kf[NT_W][4];
+  float4 up;
   float e_last;
   __device__ void load(const Ws<D> &ws, int n, int w, int r16, int g4, int i0) {
     const int t_me = 16 * w + r16;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
       wf[kb] = *reinterpret_cast<const float4 *>(ws.W + t_me * D + 16 * kb + 4 * g4);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) el[kb] = *reinterpret_cast<const float4 *>(ws.eL + 16 * kb + 4 * g4);
+    // the carry's decay factors of the 4 tokens whose U this lane writes
+    el = *reinterpret_cast<const float4 *>(ws.eL + 16 * w + 4 * g4);
 #pragma unroll
     for (int q = 0; q < NT_W; ++q) {
       // a wave without a q-th column tile loads the last tile and never uses it:
       // unconditional loads keep the prefetch free of branches, whose waits would
       // expose its latency
       const int nt = min(w + 4 * q, D / 16 - 1);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        kf[q][kb] = unpack_bf16x4(
-            *reinterpret_cast<const uint2 *>(ws.Kt + (16 * nt + r16) * C + 16 * kb + 4 * g4));
+      const uint4 *kr = reinterpret_cast<const uint4 *>(ws.Kt + (16 * nt + r16) * C + 16 * g4);
+      const uint4 k01 = kr[0], k23 = kr[1];  // pieces kb = 0, 1 and 2, 3 (kt_pos order)
+      kf[q][0] = unpack_bf16x4(make_uint2(k01.x, k01.y));
+      kf[q][1] = unpack_bf16x4(make_uint2(k01.z, k01.w));
+      kf[q][2] = unpack_bf16x4(make_uint2(k23.x, k23.y));
+      kf[q][3] = unpack_bf16x4(make_uint2(k23.z, k23.w));
     }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) up[v] = ws.U[(16 * w + 4 * g4 + v) * D + i0 + r16];
+    up = *reinterpret_cast<const float4 *>(ws.U + (i0 + r16) * C + 16 * w + 4 * g4);
     e_last = ws.eG[n - 1];
   }
 };
@@ -472,12 +478,13 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
       *reinterpret_cast<float4 *>(ws.Sc + int64_t(i0 + i) * D + d4) =
           *reinterpret_cast<const float4 *>(sS + i * LDS_ + d4);
     }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = 16 * w + 4 * g4 + v;
-      const float u = f.up[v] - (ua[v] + ub[v]);
-      sUt[r16 * LDC + t] = u;
-      ws.Ut[(i0 + r16) * C + t] = u;
+    {
+      // this lane's tokens 16w + 4g4 + (0..3) of value channel i0 + r16: contiguous in
+      // both U^T buffers; LDS gets U^T diag(e^{G_n - G}), as the carry uses it
+      const float4 u = make_float4(f.up.x - (ua[0] + ub[0]), f.up.y - (ua[1] + ub[1]),
+                                   f.up.z - (ua[2] + ub[2]), f.up.w - (ua[3] + ub[3]));
+      *reinterpret_cast<float4 *>(sUt + r16 * LDC + 16 * w + 4 * g4) = mul4(u, f.el);
+      *reinterpret_cast<float4 *>(ws.Ut + (i0 + r16) * C + 16 * w + 4 * g4) = u;
     }
     lds_barrier();  // U^T of the tile complete
 
@@ -485,7 +492,7 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
     float4 af[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      af[kb] = mul4(*reinterpret_cast<const float4 *>(sUt + r16 * LDC + 16 * kb + 4 * g4), f.el[kb]);
+      af[kb] = *reinterpret_cast<const float4 *>(sUt + r16 * LDC + 16 * kb + 4 * g4);
     floatx4 snew[NT_W];
 #pragma unroll
     for (int q = 0; q < NT_W; ++q) {
@@ -513,7 +520,7 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
   };
 
   // Chunks in pairs with two fragment sets: the next chunk's operands are in flight
-  // while this chunk's products run.
+  // while this chunk's products run (fetching two chunks ahead was measured slower).
   ScanFrag<D> fa, fb;
   frag_load(fa, 0);
   for (int c = 0; c < nch; c += 2) {
@@ -649,7 +656,7 @@ __global__ __launch_bounds__(256) void chunk_ckpt_kernel(ChunkArgs args) {
     float sc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      kf[kb] = unpack_bf16x4(*reinterpret_cast<const uint2 *>(ws.Kt + (16 * nt + r16) * C + 16 * kb + 4 * g4));
+      kf[kb] = unpack_bf16x4(*reinterpret_cast<const uint2 *>(ws.Kt + (16 * nt + r16) * C + 16 * g4 + 4 * kb));
 #pragma unroll
     for (int v = 0; v < 4; ++v) sc[v] = ws.Sc[int64_t(16 * mi + 4 * g4 + v) * D + 16 * nt + r16];
     floatx4 acc;
