@@ -218,12 +218,16 @@ def run_steps(layers, steps, warmup, stream, torch):
     return wall, verify_ms, commit_ms
 
 
-def measure_graph(gb, synth, torch, Ts, steps, warmup, n_layers, seed0, replay=False):
+def measure_graph(gb, synth, torch, Ts, steps, warmup, n_layers, seed0, replay=False, folded=False):
     """The same step captured once as a HIP graph on a side stream and replayed:
-    wall time per step (launch costs of the 2 L calls removed from the host side)."""
+    wall time per step (launch costs of the 2 L calls removed from the host side).
+    folded: one launch per layer and step (the previous window's commit inside the
+    next verify); the graph holds two steps, so the two factor buffers alternate as
+    they do in a real decode loop."""
     dims = gb.Dims(16, 32, 128, 128, 3)
     cap = torch.cuda.Stream()
-    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, cap, replay) for i in range(n_layers)]
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, cap, replay, folded=folded) for i in range(n_layers)]
+    per_replay = 2 if folded else 1
 
     def step():
         for s in sets:
@@ -236,7 +240,8 @@ def measure_graph(gb, synth, torch, Ts, steps, warmup, n_layers, seed0, replay=F
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=cap):
-        step()
+        for _ in range(per_replay):
+            step()
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -247,8 +252,8 @@ def measure_graph(gb, synth, torch, Ts, steps, warmup, n_layers, seed0, replay=F
     wall = time.perf_counter() - t0
     for s in sets:
         assert int(s.status.abs().sum()) == 0
-    upd = int(sum(Ts)) * V_HEADS * n_layers * steps
-    return {"ms_per_layer": 1e3 * wall / steps / n_layers, "head_token_updates_per_s": upd / wall}
+    upd = int(sum(Ts)) * V_HEADS * n_layers * steps * per_replay
+    return {"ms_per_layer": 1e3 * wall / (steps * per_replay) / n_layers, "head_token_updates_per_s": upd / wall}
 
 
 def cpu_baseline(s: "VerifySet", seconds: float, seconds_1thread: float):
@@ -450,6 +455,9 @@ def main():
             out_b1["graph"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup, args.layers, 600)
             out_b1["graph_replay_mode"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup,
                                                         args.layers, 600, replay=True)
+            if not args.no_replay:
+                out_b1["graph_folded_delta_mode"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup,
+                                                                  args.layers, 600, folded=True)
     if not args.no_mixed:
         Ts = (synth.verify_workload("conc16").draft_lens + 1).astype(np.int32)
         _, rm = measure(gb, synth, torch, Ts, args.steps, args.warmup, args.layers, stream, 700)
