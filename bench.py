@@ -114,7 +114,7 @@ class VerifySet:
     and the two prepared C-ABI calls of a step."""
 
     def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False, parents=None, delta=False,
-                 folded=False):
+                 folded=False, select=False):
         raw_qk = bool(dims.flags & gb.QK_L2NORM)
         import numpy as np
         import torch
@@ -134,12 +134,32 @@ class VerifySet:
                       A_log=torch.from_numpy(A_log).to(dev), dt_bias=torch.from_numpy(dt_bias).to(dev))
         gen = torch.Generator(device="cpu").manual_seed(seed)
         self.pool = (0.05 * torch.randn(B, Hv, d, d, generator=gen)).to(dev)
-        self.ckpt = None if (replay or delta or folded) else torch.empty(B, 4, Hv, d, d, device=dev)
+        self.ckpt = None if (replay or delta or folded or select) else torch.empty(B, 4, Hv, d, d, device=dev)
         self.o = torch.empty(N, Hv, d, dtype=torch.bfloat16, device=dev)
         self.acc = torch.from_numpy(acc).to(dev)
         self.status = torch.zeros((B + 31) // 32, dtype=torch.int32, device=dev)
         rows = np.arange(B, dtype=np.int32)
-        if folded:  # each verify first folds the previous window's accepted prefix: no commit launch
+        if select:  # checkpoints into two pool banks per row, used alternately; commit selects
+            start = self.pool
+            self.pool = torch.empty(9 * B, Hv, d, d, device=dev)
+            self.pool[8 * B:] = start
+            self.table = torch.arange(8 * B, 9 * B, dtype=torch.int32, device=dev)
+            banks = [2 * rows + j for j in (0, 1)]
+            sv = [gb.prepare_verify_window_select(dims, Ts, **self.t, state_pool=self.pool, slot_table=self.table,
+                                                  bank=banks[j], o=self.o, status=self.status, stream=stream)
+                  for j in (0, 1)]
+            sc = [gb.prepare_commit_select(dims, Ts, self.acc, banks[j], self.pool, self.table, self.status,
+                                           stream=stream) for j in (0, 1)]
+            phase = [0]
+
+            def verify():
+                sv[phase[0]]()
+
+            def commit():
+                sc[phase[0]]()
+                phase[0] ^= 1
+            self.verify, self.commit = verify, commit
+        elif folded:  # each verify first folds the previous window's accepted prefix: no commit launch
             self.deltas = [torch.empty(gb.delta_shape(dims, B), device=dev) for _ in range(2)]
             first = gb.prepare_verify_window_delta(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
                                                    delta=self.deltas[0], o=self.o, stream=stream)
@@ -349,13 +369,13 @@ def measure_prefill(gb, synth, torch, stream, reps, raw_qk=False):
 
 
 def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay=False, parents=None,
-            delta=False, folded=False, raw_qk=False):
+            delta=False, folded=False, raw_qk=False, select=False):
     """Steps over n_layers layers of windows with per-row token counts Ts (replay:
     verify without checkpoints, commit by replay; parents: one draft tree per row;
     delta: delta checkpoints folded by a commit launch; folded: folded by the next
     verify, one launch per layer per step; raw_qk: q and k normalised inside the kernels)."""
     dims = gb.Dims(16, 32, 128, 128, 3, gb.QK_L2NORM if raw_qk else 0)
-    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents, delta, folded)
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents, delta, folded, select)
             for i in range(n_layers)]
     wall, verify_ms, commit_ms = run_steps(sets, steps, warmup, stream, torch)
     for s in sets:
@@ -364,6 +384,9 @@ def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay
     upd_per_layer = int(sum(Ts)) * V_HEADS
     if folded:
         vb = sum(folded_verify_bytes(Ts, s.acc_host) for s in sets) / len(sets)
+        cb = 0
+    elif select:  # same verify traffic; the commit moves no state
+        vb = verify_bytes(Ts)
         cb = 0
     elif delta:
         vb = verify_delta_bytes(Ts)
@@ -508,6 +531,13 @@ def main():
         if not args.no_prefill:
             out_fused["prefill_us_per_call"] = measure_prefill(gb, synth, torch, stream, args.prefill_reps,
                                                                raw_qk=True)["us_per_call"]
+    out_select = None
+    if not args.no_replay:
+        _, rs = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
+                        select=True)
+        out_select = side(rs, [4] * 16)
+        out_select["mode"] = ("dense checkpoints written into two pool banks per row, used alternately; commit "
+                              "selects the accepted one in a device slot table (nothing copied)")
     out_tree = None
     if not args.no_tree:
         tree = np.array(TREE4, np.int32)
@@ -557,6 +587,7 @@ def main():
         "conc16_k3_delta": out_delta,
         "conc16_k3_delta_folded": out_folded,
         "conc16_k3_fused_qk_norm": out_fused,
+        "conc16_k3_select": out_select,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

@@ -70,6 +70,10 @@ _SIGS = {
                                     [ctypes.c_int32, _I32P, _VP, _VP, _I32P, _VP, _VP, _VP, _VP, _VP],
     "gdn_commit_delta": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _VP, _VP, _VP, _VP,
                          ctypes.c_int32, _I32P, _I32P, _VP, _VP],
+    "gdn_verify_window_select": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
+                                [ctypes.c_int32, _VP, _I32P, _VP, _VP, _VP],
+    "gdn_commit_select": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _VP, _I32P, ctypes.c_int32, _VP, _VP,
+                          _VP],
     "gdn_commit_replay": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
                          [_VP, ctypes.c_int32, _I32P, _I32P, _VP, _VP],
     "gdn_chunked_workspace_bytes": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, ctypes.c_int32],
@@ -90,6 +94,9 @@ def lib() -> ctypes.CDLL:
     """The loaded libgdn.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # torch first: the library's HIP runtime dependency then resolves to the one
+        # torch loaded, so both share one runtime (streams, device memory)
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise ImportError("libgdn.so is not built (%s); run "
                               "`python -m gateddeltanet_linear_attention_amd.build`" % LIB_PATH)
@@ -354,6 +361,66 @@ def prepare_commit_delta(dims: Dims, row_tokens, k, delta, accepted, state_pool,
     args, keep = _commit_delta_args(dims, row_tokens, k, delta, accepted, state_pool, src_slot, dst_slot,
                                     status, stream)
     return PreparedCall("gdn_commit_delta", args, keep)
+
+
+def _verify_select_args(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot_table, bank, o,
+                        status, stream):
+    import torch
+    T, bk = _i32(row_tokens), _i32(bank)
+    n_rows = T.size
+    if bk.size != n_rows:
+        raise ValueError("per-row arrays differ in length")
+    toks, op = _token_ptrs(dims, int(T.sum()), q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    tp = _dev(slot_table, "slot_table", torch.int32, (n_rows,))
+    sp = _dev(status, "status", torch.int32, ((n_rows + 31) // 32,))
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, _ip(T), *toks, pp, n_slots, tp, _ip(bk), op, sp, _stream(stream))
+    return args, (cd, T, bk, q, k, v, a, b, A_log, dt_bias, state_pool, slot_table, o, status)
+
+
+def _commit_select_args(dims: Dims, row_tokens, accepted, bank, state_pool, slot_table, status, stream):
+    import torch
+    T, bk = _i32(row_tokens), _i32(bank)
+    n_rows = T.size
+    if bk.size != n_rows:
+        raise ValueError("per-row arrays differ in length")
+    _, n_slots = _pool(dims, state_pool)
+    ap = _dev(accepted, "accepted", torch.int32, (n_rows,))
+    tp = _dev(slot_table, "slot_table", torch.int32, (n_rows,))
+    sp = _dev(status, "status", torch.int32, ((n_rows + 31) // 32,))
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, _ip(T), ap, _ip(bk), n_slots, tp, sp, _stream(stream))
+    return args, (cd, T, bk, accepted, slot_table, status)
+
+
+def gdn_verify_window_select(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot_table, bank,
+                             o, status, stream=None) -> None:
+    """Verify windows writing their checkpoints into the pool, row r into slots
+    bank[r] * (k_max + 1) + j, from the source slot slot_table[r] (device int32)."""
+    args, _keep = _verify_select_args(dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot_table,
+                                      bank, o, status, stream)
+    _check("gdn_verify_window_select", lib().gdn_verify_window_select(*args))
+
+
+def gdn_commit_select(dims: Dims, row_tokens, accepted, bank, state_pool, slot_table, status, stream=None) -> None:
+    """slot_table[r] = bank[r] * (k_max + 1) + accepted[r] (device): select, not copy.
+    state_pool is passed for its slot count only; nothing in it is read or written."""
+    args, _keep = _commit_select_args(dims, row_tokens, accepted, bank, state_pool, slot_table, status, stream)
+    _check("gdn_commit_select", lib().gdn_commit_select(*args))
+
+
+def prepare_verify_window_select(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot_table,
+                                 bank, o, status, stream=None) -> PreparedCall:
+    args, keep = _verify_select_args(dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot_table,
+                                     bank, o, status, stream)
+    return PreparedCall("gdn_verify_window_select", args, keep)
+
+
+def prepare_commit_select(dims: Dims, row_tokens, accepted, bank, state_pool, slot_table, status,
+                          stream=None) -> PreparedCall:
+    args, keep = _commit_select_args(dims, row_tokens, accepted, bank, state_pool, slot_table, status, stream)
+    return PreparedCall("gdn_commit_select", args, keep)
 
 
 def _replay_args(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, accepted, state_pool,

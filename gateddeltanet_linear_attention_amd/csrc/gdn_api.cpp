@@ -103,7 +103,8 @@ int launch_recurrent_rows(const gdn_dims *d, const gdn::RecurrentArgs &proto,
                           const int32_t *ntok, const int32_t *src, const int32_t *dst,
                           const int32_t *n_ck, hipStream_t stream,
                           const int32_t *parents = nullptr,
-                          const int32_t *fold_ntok = nullptr, const int64_t *fold_cu = nullptr) {
+                          const int32_t *fold_ntok = nullptr, const int64_t *fold_cu = nullptr,
+                          const int32_t *ck_rows = nullptr) {
   for (size_t base = 0; base < rows.size(); base += kRowsPerLaunch) {
     gdn::RecurrentArgs ra = proto;
     const size_t n = std::min<size_t>(kRowsPerLaunch, rows.size() - base);
@@ -115,7 +116,7 @@ int launch_recurrent_rows(const gdn_dims *d, const gdn::RecurrentArgs &proto,
       ra.src[j] = src ? src[r] : -1;
       ra.dst[j] = dst ? dst[r] : -1;
       ra.ck_first[j] = n_ck ? ntok[r] - n_ck[r] : ntok[r];
-      ra.ck_row[j] = r;
+      ra.ck_row[j] = ck_rows ? ck_rows[r] : r;
       if (parents) {  // byte t: parent of window token t, plus one
         uint32_t packed = 0;
         for (int32_t t = 0; t < ntok[r]; ++t) packed |= uint32_t(parents[cu[r] + t] + 1) << (8 * t);
@@ -515,6 +516,79 @@ int gdn_commit_replay(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
   proto.status = status;
   return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, src_slot, dst_slot, nullptr,
                                static_cast<hipStream_t>(stream));
+}
+
+// Banks of a checkpoint-select call: inside the pool, distinct, one launch of rows.
+int check_banks(const gdn_dims *dims, int32_t n_rows, int32_t n_slots, const int32_t *bank) {
+  if (n_rows > kRowsPerLaunch) return GDN_E_RANGE;
+  const int64_t per_bank = dims->k_max + 1;
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (bank[r] < 0 || (int64_t(bank[r]) + 1) * per_bank > n_slots) return GDN_E_RANGE;
+  std::vector<int32_t> sorted(bank, bank + n_rows);
+  std::sort(sorted.begin(), sorted.end());
+  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return GDN_E_ALIAS;
+  return GDN_OK;
+}
+
+int gdn_verify_window_select(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                             const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                             const float *b, const float *A_log, const float *dt_bias, float *state_pool,
+                             int32_t n_slots, const int32_t *slot_table, const int32_t *bank, uint16_t *o,
+                             uint32_t *status, void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if (!row_tokens || !slot_table || !bank || !status) return GDN_E_NULL;
+  if ((rc = check_tokens(q, k, v, a, b, A_log, dt_bias, o))) return rc;
+  if (!state_pool) return GDN_E_NULL;
+  if (!aligned(state_pool, 16) || !aligned(slot_table, 4) || !aligned(status, 4)) return GDN_E_ALIGN;
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+  if ((rc = check_banks(dims, n_rows, n_slots, bank))) return rc;
+  const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  const Sizes s = sizes_of(dims);
+  const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
+  const size_t o_b = size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2;
+  if (overlap(o, o_b, state_pool, pool_b) || overlap(slot_table, size_t(n_rows) * 4, state_pool, pool_b) ||
+      overlap(status, size_t((n_rows + 31) / 32) * 4, state_pool, pool_b))
+    return GDN_E_ALIAS;
+
+  std::vector<int32_t> rows(static_cast<size_t>(n_rows));
+  for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
+  gdn::RecurrentArgs proto;
+  fill_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, state_pool, state_pool, o);
+  proto.src_table = slot_table;
+  proto.status = status;
+  proto.n_slots = n_slots;
+  return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, nullptr, nullptr, row_tokens,
+                               static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, bank);
+}
+
+int gdn_commit_select(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                      const int32_t *accepted, const int32_t *bank, int32_t n_slots, int32_t *slot_table,
+                      uint32_t *status, void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  if (!row_tokens || !accepted || !bank || !slot_table || !status) return GDN_E_NULL;
+  if (!aligned(accepted, 4) || !aligned(slot_table, 4) || !aligned(status, 4)) return GDN_E_ALIGN;
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+  if ((rc = check_banks(dims, n_rows, n_slots, bank))) return rc;
+  gdn::SelectArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.accepted = accepted;
+  sa.slot_table = slot_table;
+  sa.status = status;
+  sa.ck_slots = dims->k_max + 1;
+  sa.n_rows = n_rows;
+  for (int32_t r = 0; r < n_rows; ++r) {
+    sa.ntok[r] = row_tokens[r];
+    sa.bank[r] = bank[r];
+  }
+  return gdn::launch_select(sa, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK : GDN_E_HIP;
 }
 
 int gdn_commit_accepted(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,

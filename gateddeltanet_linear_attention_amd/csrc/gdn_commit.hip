@@ -127,7 +127,27 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs args, int block
   }
 }
 
+// Checkpoint select: the accepted checkpoint becomes the committed state where it is.
+// One thread per row; the table entry is written with an ordinary vector store.
+__global__ __launch_bounds__(kRowsPerLaunch) void select_kernel(SelectArgs args) {
+  const int r = threadIdx.x;
+  if (r >= args.n_rows) return;
+  const int acc = args.accepted[r];
+  if (acc < 0 || acc >= args.ntok[r]) {
+    atomicOr(args.status + (r >> 5), 1u << (r & 31));
+    return;
+  }
+  args.slot_table[r] = args.bank[r] * args.ck_slots + acc;
+}
+
 }  // namespace
+
+hipError_t launch_select(const SelectArgs &args, hipStream_t stream) {
+  if (args.n_rows <= 0) return hipSuccess;
+  if (args.n_rows > kRowsPerLaunch) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kRowsPerLaunch), 0, stream, args);
+  return hipGetLastError();
+}
 
 hipError_t launch_fold(const FoldArgs &args, int d, hipStream_t stream) {
   if (args.n_rows <= 0) return hipSuccess;

@@ -62,6 +62,13 @@ struct RecurrentArgs {
   int32_t ck_first[kRowsPerLaunch];
   int32_t ck_row[kRowsPerLaunch];   // checkpoint row (index of the row in the call)
   int32_t qk_norm;                  // GDN_QK_L2NORM: normalise q and k in the kernel
+  // Checkpoint select (may be null): the launch holds every row of the call (row r of
+  // the launch is row r of the call), checkpoints go to pool slots ck_row[r] * ck_slots
+  // + j (ckpt == state_out == the pool, ck_row = the bank), and row r's source slot is
+  // src_table[r] on the device.  A source outside [-1, n_slots) or inside any row's bank
+  // leaves the row untouched and sets bit r of status.
+  const int32_t *src_table;
+  int32_t n_slots;
 };
 
 // Commit: row r copies checkpoint slot accepted[r] of its ckpt row to pool slot
@@ -145,7 +152,20 @@ struct ChunkArgs {
   static constexpr int64_t ws_unit_floats(int d) { return chunk_ws_unit_floats(d); }
 };
 
+// Checkpoint select commit: slot_table[r] = bank[r] * ck_slots + accepted[r] when
+// 0 <= accepted[r] < ntok[r], else the entry is left and bit r of status is set.
+struct SelectArgs {
+  const int32_t *accepted;          // device
+  int32_t *slot_table;              // device
+  uint32_t *status;                 // device
+  int32_t ck_slots;
+  int32_t n_rows;                   // <= kRowsPerLaunch
+  int32_t ntok[kRowsPerLaunch];
+  int32_t bank[kRowsPerLaunch];
+};
+
 hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream);
+hipError_t launch_select(const SelectArgs &args, hipStream_t stream);
 hipError_t launch_chunked(const ChunkArgs &args, int d, int n_chunks, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &args, hipStream_t stream);
 hipError_t launch_fold(const FoldArgs &args, int d, hipStream_t stream);

@@ -123,11 +123,12 @@ __device__ __forceinline__ void store_nt(float *p, const float (&x)[4]) {
 }
 
 // Instantiations: kChain (decode, verify windows, short transaction rows), kReplay
-// (gdn_commit_replay: accepted counts on the device, no outputs, no checkpoints) and
-// kTree (gdn_verify_tree: every window token runs from its parent's state) and
-// kDelta (gdn_verify_window_delta: each step's rank-1 factors instead of the states).  All
-// compile the same per-token arithmetic, so they round identically.
-enum Mode { kChain = 0, kReplay = 1, kTree = 2, kDelta = 3 };
+// (gdn_commit_replay: accepted counts on the device, no outputs, no checkpoints), kTree
+// (gdn_verify_tree: every window token runs from its parent's state), kDelta
+// (gdn_verify_window_delta: each step's rank-1 factors instead of the states) and kSelect
+// (gdn_verify_window_select: checkpoints into pool banks, the source slot from a device
+// table).  All compile the same per-token arithmetic, so they round identically.
+enum Mode { kChain = 0, kReplay = 1, kTree = 2, kDelta = 3, kSelect = 4 };
 
 template <int D, int LPR, int RPL, int WAVES, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs args) {
@@ -159,7 +160,8 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 
   int ntok = args.ntok[r];
   const int tok0 = args.tok0[r];
-  const int src = args.src[r], dst = args.dst[r], ck_first = args.ck_first[r];
+  int src = args.src[r];
+  const int dst = args.dst[r], ck_first = args.ck_first[r];
   const int ck_row = args.ck_row[r];
   const int n_v = args.n_v, n_qk = args.n_qk;
   if (REPLAY) {
@@ -174,6 +176,16 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     ntok = acc + 1;
   }
   constexpr bool write_o = !REPLAY;
+
+  // checkpoint select: the row's source slot is read first, as a vector load (the
+  // index is hidden from the compiler's uniformity analysis), so waiting for it later
+  // leaves the token loads issued after it in flight
+  int sel_raw = 0;
+  if constexpr (MODE == kSelect) {
+    int idx = r;
+    asm volatile("" : "+v"(idx));
+    sel_raw = args.src_table[idx];
+  }
 
   // The row's token inputs are loaded before the state: one counter tracks loads in
   // issue order, so the waits that staging needs then leave the state loads in
@@ -198,6 +210,12 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   const float ga = args.a[tg * n_v + h], gb = args.b[tg * n_v + h];
   const float A_log_h = args.A_log[h], dt_bias_h = args.dt_bias[h];
   __builtin_amdgcn_sched_barrier(0);  // keep every token load ahead of the state loads
+  // the state is loaded from the selected slot clamped into the pool, and the check
+  // that it lies outside every bank this launch writes runs while those loads are in
+  // flight -- a refused row leaves before any store or barrier
+  constexpr bool select = MODE == kSelect;
+  const int sel_src = select ? __builtin_amdgcn_readfirstlane(sel_raw) : 0;
+  if (select) src = min(max(sel_src, -1), args.n_slots - 1);
 
   // the committed state (slot -1: zero; slot 0, which every pool has, is read and
   // discarded, keeping the load unconditional)
@@ -210,6 +228,18 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     for (int j = 0; j < NV; ++j) {
       const float4 x = p[sub + LPR * j];
       s[q][j][0] = x.x; s[q][j][1] = x.y; s[q][j][2] = x.z; s[q][j][3] = x.w;
+    }
+  }
+  if (select) {
+    bool bad = sel_src < -1 || sel_src >= args.n_slots;
+#pragma unroll
+    for (int j = 0; j < kRowsPerLaunch; ++j) {
+      const int lo = args.ck_row[j] * args.ck_slots;
+      bad |= j < args.n_rows && sel_src >= lo && sel_src < lo + args.ck_slots;
+    }
+    if (bad) {
+      if (tile == 0 && h == 0 && tid == 0) atomicOr(args.status + (r >> 5), 1u << (r & 31));
+      return;  // the whole block leaves before any store or barrier
     }
   }
 
@@ -408,9 +438,13 @@ static void launch_d(const RecurrentArgs &args, hipStream_t stream) {
   else if constexpr (RPL == 1) {  // trees always store checkpoints: one lane layout
     if (args.tree_mode)
       hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kTree>), grid, dim3(64 * WAVES), 0, stream, args);
+    else if (args.src_table)
+      hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kSelect>), grid, dim3(64 * WAVES), 0, stream, args);
     else
       hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kChain>), grid, dim3(64 * WAVES), 0, stream, args);
-  } else
+  } else if (args.src_table)
+    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kSelect>), grid, dim3(64 * WAVES), 0, stream, args);
+  else
     hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kChain>), grid, dim3(64 * WAVES), 0, stream, args);
 }
 
@@ -423,6 +457,10 @@ hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream
   if (args.accepted ? (args.o || args.ckpt || !args.status || args.tree_mode || args.delta) : !args.o)
     return hipErrorInvalidValue;
   if (args.delta && (args.ckpt || args.tree_mode)) return hipErrorInvalidValue;
+  // checkpoint select: chain windows into the pool, all rows of the call in this launch
+  if (args.src_table && (args.accepted || args.delta || args.tree_mode || !args.status || !args.ckpt ||
+                         args.n_slots < 1))
+    return hipErrorInvalidValue;
   if (args.fold_k) {
     if (!args.delta || !args.fold_delta || !args.fold_accepted || !args.status || !args.state_out)
       return hipErrorInvalidValue;
@@ -435,11 +473,12 @@ hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream
         if (int((args.tree[r] >> (8 * t)) & 0xFFu) > t) return hipErrorInvalidValue;
   if (d == 128) {
     // A launch that stores no dense checkpoints moves little data per block and waits
-    // mostly on its state loads; when it has two rounds of blocks or more, two state
-    // rows per lane halve the block count and double the loads each lane has in
-    // flight.  Each state row keeps its 16 lanes, columns and butterfly, so every
-    // result is bit-identical in both layouts.
-    if (!args.ckpt && !args.tree_mode && int64_t(args.n_rows) * args.n_v >= 512)
+    // mostly on its state loads, and a checkpoint-select launch first waits for each
+    // row's slot from the device table; with two rounds of blocks or more, two state
+    // rows per lane halve the block count (those waits are paid once) and double the
+    // loads each lane has in flight.  Each state row keeps its 16 lanes, columns and
+    // butterfly, so every result is bit-identical in both layouts.
+    if ((!args.ckpt || args.src_table) && !args.tree_mode && int64_t(args.n_rows) * args.n_v >= 512)
       launch_d<128, 16, 2, 8>(args, stream);
     else
       launch_d<128, 16, 1, 8>(args, stream);

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 6
+#define GDN_VERSION 7
 #define GDN_MAX_K 3 /* largest k_max: at most 4 checkpoint slots per row */
 
 typedef struct gdn_dims {
@@ -228,6 +228,33 @@ int gdn_verify_window_delta_fold(const gdn_dims *dims, int32_t n_rows, const int
                                  const int32_t *prev_row_tokens, const uint16_t *prev_k,
                                  const float *prev_delta, const int32_t *prev_accepted,
                                  uint32_t *status, void *stream);
+
+/*
+ * gdn_verify_window_select / gdn_commit_select -- rollback by selecting the accepted
+ * checkpoint instead of copying it (the checkpoint-select form of the commit).  The
+ * checkpoints live in the state pool: row r writes pool slots bank[r] * (k_max + 1) + j
+ * for j < T_r (bank: host int32 [n_rows], >= 0, distinct across rows, (bank[r] + 1) *
+ * (k_max + 1) <= n_slots).  Its source slot is read on the device from slot_table[r]
+ * (device int32 [n_rows]; -1: zero state), so accepted counts never visit the host
+ * (the pull request keeps draft data on the device, "Summary").  gdn_commit_select sets
+ * slot_table[r] = bank[r] * (k_max + 1) + accepted[r]: the state after the accepted
+ * prefix becomes the committed state where it already is, bit-identical to what
+ * gdn_commit_accepted would copy.  A caller alternates each row between two banks, so a
+ * window never writes over the state it starts from.  Checked on the device: a source
+ * slot outside [-1, n_slots) or inside any bank of the call leaves the row untouched (no
+ * outputs, no checkpoints); an accepted count outside [0, T_r) leaves slot_table[r]
+ * unchanged; either sets bit (r % 32) of status[r / 32].  n_rows <= 64 per call
+ * (GDN_E_RANGE otherwise): the banks of a call are checked in one launch.
+ */
+int gdn_verify_window_select(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                             const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const float *a, const float *b, const float *A_log,
+                             const float *dt_bias, float *state_pool, int32_t n_slots,
+                             const int32_t *slot_table, const int32_t *bank, uint16_t *o,
+                             uint32_t *status, void *stream);
+int gdn_commit_select(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                      const int32_t *accepted, const int32_t *bank, int32_t n_slots,
+                      int32_t *slot_table, uint32_t *status, void *stream);
 
 /*
  * gdn_chunked_workspace_bytes -- device workspace that gdn_chunked_prefill_with_

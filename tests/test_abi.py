@@ -40,7 +40,8 @@ def test_library_exports_every_declared_function():
             "gdn_chunked_prefill_with_checkpoints", "gdn_chunked_workspace_bytes",
             "gdn_plan_transaction", "gdn_run_transaction", "gdn_status_str", "gdn_version",
             "gdn_commit_replay", "gdn_verify_tree", "gdn_verify_window_delta",
-            "gdn_commit_delta", "gdn_verify_window_delta_fold"} <= set(names)
+            "gdn_commit_delta", "gdn_verify_window_delta_fold", "gdn_verify_window_select",
+            "gdn_commit_select"} <= set(names)
     lib = gb.lib()
     for n in names:
         assert hasattr(lib, n), "libgdn.so does not export %s" % n
@@ -261,6 +262,39 @@ def test_delta_validation_codes():
     assert commit([4, 2], [0, 1], [1, 3]) == -4
     assert commit([4, 2], [0, 1], [2, 3], misalign=4) == -5
     assert commit([4, 2], [0, 1], [0, 1]) == -7      # in place passes validation
+
+
+@no_gpu
+def test_select_validation_codes():
+    lib = gb.lib()
+    b = Bufs()
+    d = _dims()
+    NULL = ctypes.c_void_p(0)
+
+    def verify(T, bank, n_slots=16, table=True, status=True):
+        Ta, Tp = _i32(T)
+        ba, bp = _i32(bank)
+        return lib.gdn_verify_window_select(ctypes.byref(d), len(Ta), Tp, *[b.ptr() for _ in range(7)], b.ptr(),
+                                            n_slots, b.ptr() if table else NULL, bp, b.ptr(),
+                                            b.ptr() if status else NULL, NULL)
+
+    def commit(T, bank, n_slots=16):
+        Ta, Tp = _i32(T)
+        ba, bp = _i32(bank)
+        return lib.gdn_commit_select(ctypes.byref(d), len(Ta), Tp, b.ptr(), bp, n_slots, b.ptr(), b.ptr(), NULL)
+
+    assert verify([4, 2], [0, 1], table=False) == -1
+    assert verify([4, 2], [0, 1], status=False) == -1
+    assert verify([4, 5], [0, 1]) == -3               # window too long
+    assert verify([4, 2], [0, 4]) == -3               # bank 4 ends past 16 slots
+    assert verify([4, 2], [-1, 1]) == -3
+    assert verify([4, 2], [1, 1]) == -4               # two rows on one bank
+    assert verify([1] * 65, list(range(65)), n_slots=4 * 65) == -3  # more rows than one launch
+    assert verify([4, 2], [0, 3]) == -7               # valid: passes validation, no GPU here
+    assert commit([4, 2], [0, 1]) == -7
+    assert commit([4, 2], [2, 2]) == -4
+    assert commit([4, 0], [0, 1]) == -3
+    assert verify([], []) == 0 and commit([], []) == 0
 
 
 @no_gpu

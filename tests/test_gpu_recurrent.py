@@ -49,8 +49,9 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
     """Warm every row by decoding its prior tokens, then run n_windows verify windows,
     each followed by commit of the accepted length -- mode "checkpoint" (dense
     checkpoints, gdn_commit_accepted), "replay" (verify without checkpoints, then
-    gdn_commit_replay in place) or "delta" (delta checkpoints, gdn_commit_delta in
-    place); the oracle runs the same chain independently from its own states.  A workload
+    gdn_commit_replay in place), "delta" (delta checkpoints, gdn_commit_delta in
+    place) or "select" (checkpoints into two pool banks per row used alternately,
+    gdn_commit_select updating the device slot table); the oracle runs the same chain independently from its own states.  A workload
     with raw q/k runs with GDN_QK_L2NORM, the oracle on its own normalisation.
     Returns the worst errors seen."""
     dims = dims_of(w.shape, raw_qk=w.raw_qk)
@@ -79,6 +80,10 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
     say("%s: warm-up ok (o %.2e, state %.2e)" % (w.name, worst["o_abs"], worst["state"]))
 
     T = w.window_lens
+    if mode == "select":  # banks 2r, 2r + 1 per row; the warmed states in the slots after them
+        sel_pool = torch.zeros(9 * B, Hv, d, d, device="cuda")
+        sel_pool[8 * B:] = pool
+        table = torch.arange(8 * B, 9 * B, dtype=torch.int32, device="cuda")
     ckpt = torch.empty(B, 4, Hv, d, d, device="cuda")
     delta = torch.empty(gb.delta_shape(dims, B), device="cuda")
     o_win = torch.empty(int(T.sum()), Hv, d, dtype=torch.bfloat16, device="cuda")
@@ -92,7 +97,12 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
         win = w.window_tokens(i)
         acc = w.accepted(i)
         wd = dev_tokens(win)
-        if mode == "delta":
+        if mode == "select":
+            bank = 2 * rows + (i % 2)
+            gb.gdn_verify_window_select(dims, T, **wd, **P, state_pool=sel_pool, slot_table=table, bank=bank,
+                                        o=o_win, status=status)
+            gb.gdn_commit_select(dims, T, torch.from_numpy(acc).cuda(), bank, sel_pool, table, status)
+        elif mode == "delta":
             gb.gdn_verify_window_delta(dims, T, **wd, **P, state_pool=pool, src_slot=rows, delta=delta, o=o_win)
             gb.gdn_commit_delta(dims, T, wd["k"], delta, torch.from_numpy(acc).cuda(), pool, src_slot=rows,
                                 dst_slot=rows, status=status)
@@ -116,7 +126,8 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
                 e = assert_state(host(ckpt[r, :T[r]]), ck_o[r, :T[r]], "%s window 0 row %d ckpt" % (w.name, r))
                 worst["state"] = max(worst["state"], e)
         if (i + 1) % check_every == 0 or i == n_windows - 1:
-            e = assert_state(host(pool), S_bufs[cur], "%s committed state after window %d" % (w.name, i))
+            committed = pool if mode != "select" else sel_pool[table.long()]
+            e = assert_state(host(committed), S_bufs[cur], "%s committed state after window %d" % (w.name, i))
             worst["state"] = max(worst["state"], e)
             say("%s: window %d ok (o %.2e, state %.2e)" % (w.name, i, worst["o_abs"], worst["state"]))
     torch.cuda.synchronize()
