@@ -57,21 +57,6 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint32).view(np.float32).reshape(f.shape)
 
 
-def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """The upper 16 bits of float32 values that are exactly bfloat16-representable."""
-    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = f.view(np.uint32)
-    if np.any(u & np.uint32(0xFFFF)):
-        raise ValueError("values are not bfloat16-representable")
-    return (u >> np.uint32(16)).astype(np.uint16)
-
-
-def bf16_from_bits(bits: np.ndarray) -> np.ndarray:
-    """Widen raw bfloat16 bit patterns (uint16) to float32 (exact)."""
-    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
-    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
-
-
 def head_params(rng: np.random.Generator, shape: HeadShape) -> tuple[np.ndarray, np.ndarray]:
     """Per v-head A_log ~ U(log 1, log 16) and dt_bias ~ N(0, 0.1^2), float32."""
     A_log = rng.uniform(np.log(1.0), np.log(16.0), size=shape.n_v_heads).astype(np.float32)
