@@ -15,8 +15,16 @@ Workload of the headline line: 16 concurrent requests, every row K=3 (4 tokens p
 window): 16 x 32 x 4 = 2048 head-token updates per layer, L = 12 layers per step
 by default.  Every layer has its own state pool, checkpoints and tokens (160 MiB),
 so a step touches 1.9 GB and the state a verify reads was written a whole step
-earlier: it streams from HBM, not from the 256 MB last-level cache.  The batch-1
-K=3 figures are reported alongside.
+earlier: it streams from HBM, not from the 256 MB last-level cache.  `roofline` is
+the verify launch's algorithmic bytes over its mean duration (HIP events on the
+launch stream), with the calibrated HBM traffic from the committed rocprofv3
+counter summary when it was taken on the current kernel sources.
+
+Reported beside the headline, on the same synthetic data: batch 1 (eager and
+HIP-graph steps), mixed draft lengths, the other rollback forms (replay, delta
+checkpoints with a fold commit or folded into the next verify, checkpoint select),
+token trees, raw q/k normalised in the kernels, the 2048-token chunked prefill, and
+the fp64 oracle timed on the host cores.
 
 Prints one JSON line (see --help).  --gpus N>1 is refused: the path runs on one GPU.
 """
