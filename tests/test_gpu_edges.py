@@ -108,3 +108,22 @@ def test_degenerate_gates_and_vectors_match_the_oracle(raw_qk):
         for r in range(B):
             assert_state(host(cc[r]), ck_o[r], "%s row %d checkpoints" % (name, r))
     assert not bool(o[24:28].view(torch.int16).any()), "zero queries must give zero outputs"
+
+
+def test_readme_example_runs_and_matches_the_oracle():
+    """The usage example of the README, as written, against the oracle."""
+    import re
+    import os
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "README.md")).read()
+    code = re.search(r"```python\n(.*?)```", src, re.S).group(1)
+    env = {}
+    torch.manual_seed(0)
+    exec(compile(code, "README.md", "exec"), env)
+    torch.cuda.synchronize()
+    host_ = lambda t: t.float().cpu().numpy().astype(np.float64)
+    qh, kh = host_(env["q"]), host_(env["k"])
+    ck_o, o_o = oracle.verify_window(env["T"], qh, kh, host_(env["v"]), host_(env["a"]), host_(env["b"]),
+                                     host_(env["A_log"]), host_(env["dt_bias"]), np.zeros((16, 32, 128, 128)))
+    assert_o(host(env["o"]), o_o, "README example outputs")
+    assert_state(host(env["pool"]), oracle.commit(ck_o, env["T"], np.full(16, 3)), "README example commit")
+    assert int(env["status"][0]) == 0
