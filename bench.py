@@ -284,6 +284,52 @@ def measure_graph(gb, synth, torch, Ts, steps, warmup, n_layers, seed0, replay=F
     return {"ms_per_layer": 1e3 * wall / (steps * per_replay) / n_layers, "head_token_updates_per_s": upd / wall}
 
 
+def decode_bytes(n_rows: int) -> int:
+    """One decode launch: read and write each (row, head) state once, 776 B of token I/O."""
+    return n_rows * V_HEADS * (2 * STATE_BYTES + TOKEN_BYTES)
+
+
+def measure_decode(gb, synth, torch, B, steps, warmup, n_layers, stream, seed0):
+    """In-place decode of one token per row through n_layers layers (each with its own
+    state pool and tokens), HIP events around each step's run of launches."""
+    import numpy as np
+    dims = gb.Dims(16, 32, 128, 128, 3)
+    rows = np.arange(B, dtype=np.int32)
+    calls, keep = [], []
+    for li in range(n_layers):
+        g = synth.streams(seed0 + li, 2)
+        A_log, dt_bias = synth.head_params(g[0], synth.FULL)
+        tok = synth.tokens(g[1], synth.FULL, B)
+        t = dict(q=torch.from_numpy(tok.q).to(torch.bfloat16).cuda(), k=torch.from_numpy(tok.k).to(torch.bfloat16).cuda(),
+                 v=torch.from_numpy(tok.v).to(torch.bfloat16).cuda(), a=torch.from_numpy(tok.a).cuda(),
+                 b=torch.from_numpy(tok.b).cuda(), A_log=torch.from_numpy(A_log).cuda(),
+                 dt_bias=torch.from_numpy(dt_bias).cuda())
+        gen = torch.Generator(device="cpu").manual_seed(seed0 + li)
+        pool = (0.05 * torch.randn(B, 32, 128, 128, generator=gen)).cuda()
+        o = torch.empty(B, 32, 128, dtype=torch.bfloat16, device="cuda")
+        calls.append(gb.prepare_decode_step(dims, **t, state_pool=pool, src_slot=rows, dst_slot=rows, o=o,
+                                            stream=stream))
+        keep.append((t, pool, o))
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for c in calls:
+            c()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / (steps * n_layers)
+    nb = decode_bytes(B)
+    return {"rows": B, "decode_us_mean": us, "algorithmic_bytes_per_launch": nb,
+            "gbps": nb / (us * 1e-6) / 1e9, "frac_of_hbm_peak": nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "head_token_updates_per_s": B * V_HEADS * n_layers * steps / wall}
+
+
 def cpu_baseline(s: "VerifySet", seconds: float, seconds_1thread: float):
     """The fp64 oracle on the host, on the same window as the GPU step (a bounded
     sample: repeated windows for about `seconds` of work), with every host core the
@@ -539,6 +585,8 @@ def main():
         if not args.no_prefill:
             out_fused["prefill_us_per_call"] = measure_prefill(gb, synth, torch, stream, args.prefill_reps,
                                                                raw_qk=True)["us_per_call"]
+    decode = {"conc16": measure_decode(gb, synth, torch, 16, args.steps, args.warmup, args.layers, stream, 900),
+              "batch1": measure_decode(gb, synth, torch, 1, args.steps, args.warmup, args.layers, stream, 950)}
     out_select = None
     if not args.no_replay:
         _, rs = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
@@ -596,6 +644,7 @@ def main():
         "conc16_k3_delta_folded": out_folded,
         "conc16_k3_fused_qk_norm": out_fused,
         "conc16_k3_select": out_select,
+        "decode": decode,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

@@ -191,18 +191,29 @@ def gdn_status_str(code: int) -> str:
     return lib().gdn_status_str(code).decode()
 
 
-def gdn_decode_step(dims: Dims, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot, dst_slot, o,
-                    stream=None) -> None:
-    """One token per row; new state of row r to slot dst_slot[r]."""
+def _decode_args(dims: Dims, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot, dst_slot, o, stream):
     src, dst = _i32(src_slot), _i32(dst_slot)
     n_rows = src.size
     if dst.size != n_rows:
         raise ValueError("src_slot and dst_slot lengths differ")
     toks, op = _token_ptrs(dims, n_rows, q, k, v, a, b, A_log, dt_bias, o)
     pp, n_slots = _pool(dims, state_pool)
-    rc = lib().gdn_decode_step(ctypes.byref(dims.c()), n_rows, *toks, pp, n_slots, _ip(src), _ip(dst),
-                               op, _stream(stream))
-    _check("gdn_decode_step", rc)
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, *toks, pp, n_slots, _ip(src), _ip(dst), op, _stream(stream))
+    return args, (cd, src, dst, q, k, v, a, b, A_log, dt_bias, state_pool, o)
+
+
+def gdn_decode_step(dims: Dims, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot, dst_slot, o,
+                    stream=None) -> None:
+    """One token per row; new state of row r to slot dst_slot[r]."""
+    args, _keep = _decode_args(dims, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot, dst_slot, o, stream)
+    _check("gdn_decode_step", lib().gdn_decode_step(*args))
+
+
+def prepare_decode_step(dims: Dims, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot, dst_slot, o,
+                        stream=None) -> "PreparedCall":
+    args, keep = _decode_args(dims, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot, dst_slot, o, stream)
+    return PreparedCall("gdn_decode_step", args, keep)
 
 
 def gdn_verify_window(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, src_slot,
