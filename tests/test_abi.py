@@ -387,3 +387,36 @@ def test_chunked_and_transaction_validation_codes():
     assert tx([4, 100], [4, 0], [0, -1], [-1, 1], ws_bytes=100) == -6  # the long row needs workspace
     assert tx([4, 100], [5, 0], [0, -1], [-1, 1]) == -3                # checkpoints > k_max + 1
     assert tx([4, 100], [4, 0], [0, -1], [-1, 0]) == -4                # prefill row overwrites a verify source
+
+
+@no_gpu
+def test_header_compiles_as_c_and_a_c_program_links_the_library(tmp_path):
+    """include/gdn.h is a C header: a C11 program includes it, links libgdn.so and
+    calls it (validation paths only: no GPU here)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi_c.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include "gdn.h"
+int main(void) {
+  gdn_dims d = {16, 32, 128, 128, 3, 0};
+  gdn_dims bad = {16, 32, 64, 64, 3, 0};
+  int32_t T[1] = {4}, src[1] = {0};
+  if (gdn_version() != GDN_VERSION) return 1;
+  if (gdn_verify_window(&d, 0, T, 0, 0, 0, 0, 0, 0, 0, 0, 1, src, 0, 0, 0) != GDN_OK) return 2;
+  if (gdn_verify_window(&bad, 1, T, 0, 0, 0, 0, 0, 0, 0, 0, 1, src, 0, 0, 0) != GDN_E_UNSUPPORTED) return 3;
+  if (gdn_verify_window(&d, 1, T, 0, 0, 0, 0, 0, 0, 0, 0, 1, src, 0, 0, 0) != GDN_E_NULL) return 4;
+  printf("%s\n", gdn_status_str(GDN_E_ALIAS));
+  return 0;
+}
+""")
+    exe = tmp_path / "abi_c"
+    lib_dir = os.path.dirname(gb.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe),
+                    "-L", lib_dir, "-lgdn", "-Wl,-rpath," + lib_dir], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert r.stdout.strip()
