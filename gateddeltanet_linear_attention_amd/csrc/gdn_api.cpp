@@ -27,7 +27,8 @@ int check_dims(const gdn_dims *d) {
   if (d->d_k != d->d_v || (d->d_k != 16 && d->d_k != 128)) return GDN_E_UNSUPPORTED;
   if (d->n_qk_heads <= 0 || d->n_v_heads <= 0 || d->n_v_heads % d->n_qk_heads)
     return GDN_E_UNSUPPORTED;
-  if (d->n_v_heads > (1 << 16)) return GDN_E_UNSUPPORTED;
+  // keeps every launch's grid (rows x heads x blocks per head x threads) far below 2^32
+  if (d->n_v_heads > GDN_MAX_V_HEADS) return GDN_E_UNSUPPORTED;
   if (d->k_max < 0 || d->k_max > GDN_MAX_K) return GDN_E_UNSUPPORTED;
   if (d->flags & ~GDN_QK_L2NORM) return GDN_E_UNSUPPORTED;
   return GDN_OK;
@@ -302,6 +303,7 @@ int gdn_verify_window(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
   if ((rc = check_slots(n_rows, n_slots, src_slot, nullptr))) return rc;
   const Sizes s = sizes_of(dims);
   const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  if (cu.back() > INT32_MAX) return GDN_E_RANGE;  // token offsets are int32
   const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
   const size_t ck_b = ckpt ? size_t(n_rows) * s.ck_row_floats * 4 : 0;
   const size_t o_b = size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2;
@@ -333,6 +335,7 @@ int gdn_verify_tree(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tok
   for (int32_t r = 0; r < n_rows; ++r)
     if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
   const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  if (cu.back() > INT32_MAX) return GDN_E_RANGE;  // token offsets are int32
   for (int32_t r = 0; r < n_rows; ++r) {
     if (parents[cu[r]] != -1) return GDN_E_RANGE;  // the window's first token follows the committed state
     for (int32_t t = 1; t < row_tokens[r]; ++t)
@@ -373,6 +376,7 @@ int gdn_verify_window_delta(const gdn_dims *dims, int32_t n_rows, const int32_t 
   if ((rc = check_slots(n_rows, n_slots, src_slot, nullptr))) return rc;
   const Sizes s = sizes_of(dims);
   const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  if (cu.back() > INT32_MAX) return GDN_E_RANGE;  // token offsets are int32
   const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
   const size_t dl_b = size_t(n_rows) * size_t(dims->k_max + 1) * size_t(dims->n_v_heads) *
                       size_t(gdn::delta_row_floats(dims->d_v)) * 4;
@@ -416,6 +420,7 @@ int gdn_verify_window_delta_fold(const gdn_dims *dims, int32_t n_rows, const int
   if ((rc = check_slots(n_rows, n_slots, slot, slot))) return rc;
   const Sizes s = sizes_of(dims);
   const std::vector<int64_t> cu = prefix(n_rows, row_tokens), pcu = prefix(n_rows, prev_row_tokens);
+  if (cu.back() > INT32_MAX || pcu.back() > INT32_MAX) return GDN_E_RANGE;  // token offsets are int32
   const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
   const size_t dl_b = size_t(n_rows) * size_t(dims->k_max + 1) * size_t(dims->n_v_heads) *
                       size_t(gdn::delta_row_floats(dims->d_v)) * 4;
@@ -460,6 +465,7 @@ int gdn_commit_delta(const gdn_dims *dims, int32_t n_rows, const int32_t *row_to
                       size_t(gdn::delta_row_floats(dims->d_v)) * 4;
   if (overlap(delta, dl_b, state_pool, size_t(n_slots) * s.row_floats * 4)) return GDN_E_ALIAS;
   const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  if (cu.back() > INT32_MAX) return GDN_E_RANGE;  // token offsets are int32
   for (int32_t r0 = 0; r0 < n_rows; r0 += kRowsPerLaunch) {
     gdn::FoldArgs fa;
     memset(&fa, 0, sizeof(fa));
@@ -510,6 +516,7 @@ int gdn_commit_replay(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
   std::vector<int32_t> rows(static_cast<size_t>(n_rows));
   for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
   const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  if (cu.back() > INT32_MAX) return GDN_E_RANGE;  // token offsets are int32
   gdn::RecurrentArgs proto;
   fill_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, state_pool, nullptr, nullptr);
   proto.accepted = accepted;
@@ -547,6 +554,7 @@ int gdn_verify_window_select(const gdn_dims *dims, int32_t n_rows, const int32_t
     if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
   if ((rc = check_banks(dims, n_rows, n_slots, bank))) return rc;
   const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
+  if (cu.back() > INT32_MAX) return GDN_E_RANGE;  // token offsets are int32
   const Sizes s = sizes_of(dims);
   const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
   const size_t o_b = size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2;

@@ -19,8 +19,8 @@
  * sections "Correctness fix" and "Rollback fix and corrected quality disposition").
  *
  * Conventions shared by every call.
- *  - Supported shapes: d_k == d_v in {16, 128}; H_v a multiple of H_qk; 0 <= k_max <= 3.
- *    Anything else returns GDN_E_UNSUPPORTED.
+ *  - Supported shapes: d_k == d_v in {16, 128}; H_v a multiple of H_qk and at most
+ *    GDN_MAX_V_HEADS; 0 <= k_max <= 3.  Anything else returns GDN_E_UNSUPPORTED.
  *  - Rows are packed in order; row r owns tokens [cu_r, cu_r + L_r) of the packed
  *    token dimension N, cu_r = L_0 + ... + L_{r-1}; a row's tokens are in time order.
  *  - Device arrays (caller-allocated, caller-owned; the library allocates nothing):
@@ -39,7 +39,10 @@
  *    stream) and never synchronises the host.  Ordering across streams (publish a
  *    prefill before a dependent verify, "Native three-step MTP", section "What
  *    changed") is the caller's, through events.
- *  - Fail closed: on any error code nothing is launched and nothing is written.
+ *  - Fail closed: every argument is checked before the first launch, so on any error
+ *    code but GDN_E_HIP nothing is launched and nothing is written.  GDN_E_HIP is the
+ *    runtime refusing a launch; a call that launches several kernels (more than 64
+ *    rows, or a chunked prefill) may have run the launches before it.
  *  - The library holds no mutable global state; calls are thread-safe.
  */
 #ifndef GDN_H_
@@ -54,6 +57,7 @@ extern "C" {
 
 #define GDN_VERSION 7
 #define GDN_MAX_K 3 /* largest k_max: at most 4 checkpoint slots per row */
+#define GDN_MAX_V_HEADS 1024 /* largest H_v */
 
 typedef struct gdn_dims {
   int32_t n_qk_heads; /* H_qk */

@@ -116,6 +116,8 @@ def test_verify_validation_codes():
     assert _verify(_dims(d_k=64, d_v=64), [1], [0]) == -2          # unsupported width
     assert _verify(_dims(d_k=128, d_v=16), [1], [0]) == -2         # d_k != d_v
     assert _verify(_dims(n_v_heads=30), [1], [0]) == -2            # H_v % H_qk != 0
+    assert _verify(_dims(n_v_heads=2048), [1], [0]) == -2          # H_v > GDN_MAX_V_HEADS
+    assert _verify(_dims(n_qk_heads=1024, n_v_heads=1024), [5], [0]) == -3  # H_v 1024 passes the shape check
     assert _verify(_dims(k_max=4), [1], [0]) == -2                 # k_max > 3
     assert _verify(d, [1, 5], [0, 1]) == -3                        # T_r > k_max + 1
     assert _verify(d, [1, 0], [0, 1]) == -3                        # T_r < 1
