@@ -18,11 +18,20 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kF4PerThread = 4;
-constexpr int kF4PerBlock = kThreads * kF4PerThread;  // 16 KiB per block
+// Copy blocks move THREADS * F4 float4, every load of a thread issued before its
+// first store.  Large commits take 64 KiB blocks (with 16 KiB blocks the 32 MiB
+// commit of 16 rows took 10 % longer); small ones take 16 KiB blocks, so that one
+// row's 2 MiB still spreads over 128 compute units.
+constexpr int kCopyBigThreads = 512, kCopyBigF4 = 8;
+constexpr int kCopySmallThreads = 256, kCopySmallF4 = 4;
+constexpr int64_t kCopyBigMinBlocks = 512;  // big blocks once a launch has at least this many
+// fold blocks: 16 KiB of state each
+constexpr int kFoldThreads = 256;
+constexpr int kFoldF4 = 4;
+constexpr int kFoldF4PerBlock = kFoldThreads * kFoldF4;
 
-__global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs args, int blocks_per_row) {
+template <int THREADS, int F4>
+__global__ __launch_bounds__(THREADS) void commit_kernel(CommitArgs args, int blocks_per_row) {
   const int r = blockIdx.x / blocks_per_row;
   const int part = blockIdx.x % blocks_per_row;
   const int acc = args.accepted[r];
@@ -37,19 +46,19 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs args, int b
   const float4 *src = reinterpret_cast<const float4 *>(
       args.ckpt + (int64_t(r) * args.ck_slots + acc) * args.row_floats);
   float4 *dst = reinterpret_cast<float4 *>(args.pool + int64_t(args.dst[r]) * args.row_floats);
-  const int64_t base = int64_t(part) * kF4PerBlock + threadIdx.x;
-  float4 x[kF4PerThread];
+  const int64_t base = int64_t(part) * (THREADS * F4) + threadIdx.x;
+  float4 x[F4];
 #pragma unroll
-  for (int m = 0; m < kF4PerThread; ++m) {
-    const int64_t idx = base + int64_t(m) * kThreads;
+  for (int m = 0; m < F4; ++m) {
+    const int64_t idx = base + int64_t(m) * THREADS;
     if (idx < n4) {  // each checkpoint is read once: keep it out of the caches
       const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + idx));
       x[m] = make_float4(y[0], y[1], y[2], y[3]);
     }
   }
 #pragma unroll
-  for (int m = 0; m < kF4PerThread; ++m) {
-    const int64_t idx = base + int64_t(m) * kThreads;
+  for (int m = 0; m < F4; ++m) {
+    const int64_t idx = base + int64_t(m) * THREADS;
     // the committed state is read again only by the row's next call, a whole model
     // step later: write it through, leaving no dirty lines to be evicted later
     if (idx < n4)
@@ -65,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs args, int b
 // streams 16 KiB of one (row, head) state: four float4 per thread, each inside one
 // state row i.
 template <int D>
-__global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs args, int blocks_per_unit) {
+__global__ __launch_bounds__(kFoldThreads) void fold_kernel(FoldArgs args, int blocks_per_unit) {
   constexpr int N4 = D * D / 4;  // float4 per (row, head) state
   const int part = blockIdx.x % blocks_per_unit;
   const int unit = blockIdx.x / blocks_per_unit;
@@ -79,8 +88,8 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs args, int block
   const int hq = h / args.group, src = args.src[r], ntok = args.ntok[r];
   // every token's factors and keys are loaded before the first update (tokens past the
   // window are clamped to its last one and never applied): one memory round trip
-  float cf[kMaxWindow][kF4PerThread], al[kMaxWindow], ks[kMaxWindow];
-  uint2 kw[kMaxWindow][kF4PerThread];
+  float cf[kMaxWindow][kFoldF4], al[kMaxWindow], ks[kMaxWindow];
+  uint2 kw[kMaxWindow][kFoldF4];
 #pragma unroll
   for (int t = 0; t < kMaxWindow; ++t) {
     const int tt = min(t, ntok - 1);
@@ -89,16 +98,16 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs args, int block
     al[t] = dl[D];
     ks[t] = dl[D + 1];  // the key's scale factor (1 unless normalised in the kernel)
 #pragma unroll
-    for (int m = 0; m < kF4PerThread; ++m) {
-      const int idx = min(part * kF4PerBlock + m * kThreads + int(threadIdx.x), N4 - 1);
+    for (int m = 0; m < kFoldF4; ++m) {
+      const int idx = min(part * kFoldF4PerBlock + m * kFoldThreads + int(threadIdx.x), N4 - 1);
       cf[t][m] = dl[(4 * idx) / D];
       kw[t][m] = *reinterpret_cast<const uint2 *>(kr + (4 * idx) % D);
     }
   }
-  float4 x[kF4PerThread];
+  float4 x[kFoldF4];
 #pragma unroll
-  for (int m = 0; m < kF4PerThread; ++m) {
-    const int idx = part * kF4PerBlock + m * kThreads + int(threadIdx.x);
+  for (int m = 0; m < kFoldF4; ++m) {
+    const int idx = part * kFoldF4PerBlock + m * kFoldThreads + int(threadIdx.x);
     x[m] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (idx < N4 && src >= 0) {
       const f32x4 y = __builtin_nontemporal_load(
@@ -110,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs args, int block
   for (int t = 0; t < kMaxWindow; ++t) {
     if (t > acc) break;
 #pragma unroll
-    for (int m = 0; m < kF4PerThread; ++m) {
+    for (int m = 0; m < kFoldF4; ++m) {
       const float c = cf[t][m], alpha = al[t], f = ks[t];
       x[m].x = fmaf(c, __uint_as_float(kw[t][m].x << 16) * f, alpha * x[m].x);
       x[m].y = fmaf(c, __uint_as_float(kw[t][m].x & 0xFFFF0000u) * f, alpha * x[m].y);
@@ -119,8 +128,8 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs args, int block
     }
   }
 #pragma unroll
-  for (int m = 0; m < kF4PerThread; ++m) {
-    const int idx = part * kF4PerBlock + m * kThreads + int(threadIdx.x);
+  for (int m = 0; m < kFoldF4; ++m) {
+    const int idx = part * kFoldF4PerBlock + m * kFoldThreads + int(threadIdx.x);
     if (idx < N4)
       __builtin_nontemporal_store(f32x4{x[m].x, x[m].y, x[m].z, x[m].w},
                                   reinterpret_cast<f32x4 *>(args.pool_out + (size_t(args.dst[r]) * args.n_v + h) * D * D) + idx);
@@ -155,12 +164,12 @@ hipError_t launch_fold(const FoldArgs &args, int d, hipStream_t stream) {
   for (int r = 0; r < args.n_rows; ++r)  // the kernel holds a whole window's factors in registers
     if (args.ntok[r] < 1 || args.ntok[r] > kMaxWindow) return hipErrorInvalidValue;
   const int n4 = d * d / 4;
-  const int bpu = (n4 + kF4PerBlock - 1) / kF4PerBlock;
+  const int bpu = (n4 + kFoldF4PerBlock - 1) / kFoldF4PerBlock;
   const dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * unsigned(bpu));
   if (d == 128)
-    hipLaunchKernelGGL(fold_kernel<128>, grid, dim3(kThreads), 0, stream, args, bpu);
+    hipLaunchKernelGGL(fold_kernel<128>, grid, dim3(kFoldThreads), 0, stream, args, bpu);
   else if (d == 16)
-    hipLaunchKernelGGL(fold_kernel<16>, grid, dim3(kThreads), 0, stream, args, bpu);
+    hipLaunchKernelGGL(fold_kernel<16>, grid, dim3(kFoldThreads), 0, stream, args, bpu);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -169,9 +178,16 @@ hipError_t launch_fold(const FoldArgs &args, int d, hipStream_t stream) {
 hipError_t launch_commit(const CommitArgs &args, hipStream_t stream) {
   if (args.n_rows <= 0) return hipSuccess;
   const int64_t n4 = args.row_floats / 4;
-  const int blocks_per_row = int((n4 + kF4PerBlock - 1) / kF4PerBlock);
-  dim3 grid(unsigned(args.n_rows) * unsigned(blocks_per_row));
-  hipLaunchKernelGGL(commit_kernel, grid, dim3(kThreads), 0, stream, args, blocks_per_row);
+  constexpr int64_t big = kCopyBigThreads * kCopyBigF4, small = kCopySmallThreads * kCopySmallF4;
+  const int64_t big_blocks = (n4 + big - 1) / big;
+  if (big_blocks * args.n_rows >= kCopyBigMinBlocks) {
+    hipLaunchKernelGGL((commit_kernel<kCopyBigThreads, kCopyBigF4>), dim3(unsigned(args.n_rows * big_blocks)),
+                       dim3(kCopyBigThreads), 0, stream, args, int(big_blocks));
+  } else {
+    const int64_t blocks = (n4 + small - 1) / small;
+    hipLaunchKernelGGL((commit_kernel<kCopySmallThreads, kCopySmallF4>), dim3(unsigned(args.n_rows * blocks)),
+                       dim3(kCopySmallThreads), 0, stream, args, int(blocks));
+  }
   return hipGetLastError();
 }
 
