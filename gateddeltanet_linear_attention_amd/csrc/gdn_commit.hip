@@ -80,11 +80,12 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(FoldArgs args, int b
   const int unit = blockIdx.x / blocks_per_unit;
   const int h = unit % args.n_v, r = unit / args.n_v;
   const int row = args.row_base + r;
-  const int acc = args.accepted[row];
-  if (acc < 0 || acc >= args.ntok[r]) {
-    if (part == 0 && h == 0 && threadIdx.x == 0) atomicOr(args.status + (row >> 5), 1u << (row & 31));
-    return;
-  }
+  // a_r is read first, as a vector load (a scalar load would share one out-of-order
+  // counter with the arguments the addresses below need), and checked once every
+  // load is in flight
+  int acc_idx = row;
+  asm volatile("" : "+v"(acc_idx));
+  const int acc_raw = args.accepted[acc_idx];
   const int hq = h / args.group, src = args.src[r], ntok = args.ntok[r];
   // every token's factors and keys are loaded before the first update (tokens past the
   // window are clamped to its last one and never applied): one memory round trip
@@ -114,6 +115,12 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(FoldArgs args, int b
           reinterpret_cast<const f32x4 *>(args.pool_in + (size_t(src) * args.n_v + h) * D * D) + idx);
       x[m] = make_float4(y[0], y[1], y[2], y[3]);
     }
+  }
+  asm volatile("" ::: "memory");  // keeps the loads above from sinking below the exit
+  const int acc = __builtin_amdgcn_readfirstlane(acc_raw);
+  if (acc < 0 || acc >= ntok) {
+    if (part == 0 && h == 0 && threadIdx.x == 0) atomicOr(args.status + (row >> 5), 1u << (row & 31));
+    return;
   }
 #pragma unroll
   for (int t = 0; t < kMaxWindow; ++t) {

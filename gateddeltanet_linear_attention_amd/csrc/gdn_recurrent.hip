@@ -164,18 +164,15 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   const int dst = args.dst[r], ck_first = args.ck_first[r];
   const int ck_row = args.ck_row[r];
   const int n_v = args.n_v, n_qk = args.n_qk;
-  if (REPLAY) {
-    // Replay of the accepted prefix: the bonus token and a_r drafts, the same
-    // sequence of operations as the first a_r + 1 tokens of the window, so the
-    // state it leaves is bit-identical to that window's checkpoint slot a_r.
-    const int acc = args.accepted[ck_row];
-    if (acc < 0 || acc >= ntok) {
-      if (tile == 0 && h == 0 && tid == 0) atomicOr(args.status + (ck_row >> 5), 1u << (ck_row & 31));
-      return;  // the whole block leaves before any barrier
-    }
-    ntok = acc + 1;
-  }
   constexpr bool write_o = !REPLAY;
+  // replay: a_r is read first, as a vector load like the select table below, and
+  // checked once the state loads are in flight
+  int acc_raw = 0;
+  if constexpr (REPLAY) {
+    int idx = ck_row;
+    asm volatile("" : "+v"(idx));
+    acc_raw = args.accepted[idx];
+  }
 
   // checkpoint select: the row's source slot is read first, as a vector load (the
   // index is hidden from the compiler's uniformity analysis), so waiting for it later
@@ -229,6 +226,20 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
       const float4 x = p[sub + LPR * j];
       s[q][j][0] = x.x; s[q][j][1] = x.y; s[q][j][2] = x.z; s[q][j][3] = x.w;
     }
+  }
+  if constexpr (REPLAY) {
+    // Replay of the accepted prefix: the bonus token and a_r drafts, the same
+    // sequence of operations as the first a_r + 1 tokens of the window, so the
+    // state it leaves is bit-identical to that window's checkpoint slot a_r.  The
+    // token loads above are clamped to the whole window; the empty asm keeps the
+    // compiler from sinking the state loads below this exit (4 % on the commit).
+    asm volatile("" ::: "memory");
+    const int acc = __builtin_amdgcn_readfirstlane(acc_raw);
+    if (acc < 0 || acc >= ntok) {
+      if (tile == 0 && h == 0 && tid == 0) atomicOr(args.status + (ck_row >> 5), 1u << (ck_row & 31));
+      return;  // the whole block leaves before any store or barrier
+    }
+    ntok = acc + 1;
   }
   if (select) {
     bool bad = sel_src < -1 || sel_src >= args.n_slots;
