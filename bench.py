@@ -625,7 +625,7 @@ def main():
                    "state": "fp32", "io": "bf16", "layers_per_step": args.layers},
         "roofline": {"bound": "hbm", "achieved": r16["verify_gbps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": r16["verify_gbps"] / HBM_PEAK_GBPS,
-                     "traffic": traffic, "kernel": "recurrent_kernel<128,16,1,8> (gdn_verify_window)",
+                     "traffic": traffic, "kernel": "recurrent_kernel<128,16,1,4,chain,stream> (gdn_verify_window)",
                      "algorithmic_bytes_per_launch": r16["verify_bytes"],
                      "launch_us_mean": 1e3 * r16["verify_ms_mean"],
                      "launch_us_p10": 1e3 * r16["verify_ms_p10"],

@@ -130,8 +130,16 @@ __device__ __forceinline__ void store_nt(float *p, const float (&x)[4]) {
 // table).  All compile the same per-token arithmetic, so they round identically.
 enum Mode { kChain = 0, kReplay = 1, kTree = 2, kDelta = 3, kSelect = 4 };
 
-template <int D, int LPR, int RPL, int WAVES, int MODE>
+// STREAM: the launch streams dense states out (checkpoints, or a written state) and its
+// blocks run in several rounds per CU.  A block that has just started then issues its
+// token and state loads at raised wave priority, ahead of the older blocks' arithmetic
+// and stores on the same SIMDs, so the memory system always holds the next round's
+// reads; and each output goes straight to memory from the lane that reduced it, so a
+// block retires as soon as its last store is issued.  (Launches that write no dense
+// state measured slower in this form.)
+template <int D, int LPR, int RPL, int WAVES, int MODE, bool STREAM>
 __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs args) {
+  if constexpr (STREAM) __builtin_amdgcn_s_setprio(3);
   constexpr bool REPLAY = MODE == kReplay, TREE = MODE == kTree;
   constexpr int NV = D / LPR / 4;                  // float4 per lane per state row
   constexpr int ROWS = WAVES * 64 / LPR * RPL;     // state rows per block
@@ -145,7 +153,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   __shared__ float sV[TB][ROWS];
   __shared__ float sAlpha[TB], sBeta[TB];
   __shared__ float sKs[TB];          // the factor each key was scaled by (1: none)
-  __shared__ uint16_t sO[TB][ROWS];  // outputs, written back coalesced at the end
+  __shared__ uint16_t sO[TB][ROWS];  // outputs, written back coalesced at the end (launches without STREAM)
 
   const int tid = threadIdx.x;
   const int sub = tid % LPR;
@@ -227,6 +235,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
       s[q][j][0] = x.x; s[q][j][1] = x.y; s[q][j][2] = x.z; s[q][j][3] = x.w;
     }
   }
+  if constexpr (STREAM) __builtin_amdgcn_s_setprio(0);  // every load of the block is issued
   if constexpr (REPLAY) {
     // Replay of the accepted prefix: the bonus token and a_r drafts, the same
     // sequence of operations as the first a_r + 1 tokens of the window, so the
@@ -376,7 +385,12 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
           po = fmaf(st[q][j][3], qw.w, po);
         }
         const float oi = group_sum<LPR>(po);
-        if (sub == 0) sO[t][i_local + q] = to_bf16(oi);
+        if (sub == 0) {
+          if constexpr (STREAM)
+            args.o[((size_t(tok0) + t) * n_v + h) * D + i0 + q] = to_bf16(oi);
+          else
+            sO[t][i_local + q] = to_bf16(oi);
+        }
       }
       if (!REPLAY && t >= ck_first) {
         float *cp = args.ckpt + ((size_t(ck_row) * args.ck_slots + (t - ck_first)) * n_v + h) * UNIT +
@@ -416,7 +430,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 #pragma unroll 1
     for (int t = 0; t < ntok; ++t) step(t, s);
   }
-  if (write_o) {
+  if (write_o && !STREAM) {
     lds_barrier();  // every output of the block is in sO
     for (int x = tid; x < ntok * ROWS; x += 64 * WAVES) {
       const int t = x / ROWS, rr = x % ROWS;
@@ -438,25 +452,37 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 
 }  // namespace
 
-template <int D, int LPR, int RPL, int WAVES>
-static void launch_d(const RecurrentArgs &args, hipStream_t stream) {
+template <int D, int LPR, int RPL, int WAVES, int MODE, bool STREAM>
+static void launch_one(const RecurrentArgs &args, hipStream_t stream) {
   constexpr int TILES = D / (WAVES * 64 / LPR * RPL);
   const dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * TILES);
+  hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, MODE, STREAM>), grid, dim3(64 * WAVES), 0, stream, args);
+}
+
+template <int D, int LPR, int RPL, int WAVES>
+static void launch_d(const RecurrentArgs &args, hipStream_t stream) {
+  // dense states streamed out: checkpoints, or a row's new state written to its slot
+  bool writes_state = args.ckpt != nullptr;
+  for (int r = 0; r < args.n_rows; ++r) writes_state |= args.dst[r] >= 0;
   if (args.accepted)
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kReplay>), grid, dim3(64 * WAVES), 0, stream, args);
+    launch_one<D, LPR, RPL, WAVES, kReplay, true>(args, stream);
   else if (args.delta)
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kDelta>), grid, dim3(64 * WAVES), 0, stream, args);
+    launch_one<D, LPR, RPL, WAVES, kDelta, false>(args, stream);
   else if constexpr (RPL == 1) {  // trees always store checkpoints: one lane layout
     if (args.tree_mode)
-      hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kTree>), grid, dim3(64 * WAVES), 0, stream, args);
+      launch_one<D, LPR, RPL, WAVES, kTree, true>(args, stream);
     else if (args.src_table)
-      hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kSelect>), grid, dim3(64 * WAVES), 0, stream, args);
+      launch_one<D, LPR, RPL, WAVES, kSelect, true>(args, stream);
+    else if (writes_state)
+      launch_one<D, LPR, RPL, WAVES, kChain, true>(args, stream);
     else
-      hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kChain>), grid, dim3(64 * WAVES), 0, stream, args);
+      launch_one<D, LPR, RPL, WAVES, kChain, false>(args, stream);
   } else if (args.src_table)
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kSelect>), grid, dim3(64 * WAVES), 0, stream, args);
+    launch_one<D, LPR, RPL, WAVES, kSelect, true>(args, stream);
+  else if (writes_state)
+    launch_one<D, LPR, RPL, WAVES, kChain, true>(args, stream);
   else
-    hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, kChain>), grid, dim3(64 * WAVES), 0, stream, args);
+    launch_one<D, LPR, RPL, WAVES, kChain, false>(args, stream);
 }
 
 hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream) {
@@ -489,10 +515,12 @@ hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream
     // rows per lane halve the block count (those waits are paid once) and double the
     // loads each lane has in flight.  Each state row keeps its 16 lanes, columns and
     // butterfly, so every result is bit-identical in both layouts.
+    // Otherwise one row per lane in 4-wave blocks: with checkpoints, smaller blocks
+    // turn over more often, which keeps each CU's loads and stores interleaved.
     if ((!args.ckpt || args.src_table) && !args.tree_mode && int64_t(args.n_rows) * args.n_v >= 512)
       launch_d<128, 16, 2, 8>(args, stream);
     else
-      launch_d<128, 16, 1, 8>(args, stream);
+      launch_d<128, 16, 1, 4>(args, stream);
   } else if (d == 16)
     launch_d<16, 4, 1, 1>(args, stream);
   else
