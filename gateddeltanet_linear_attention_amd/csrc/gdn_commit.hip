@@ -20,10 +20,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Copy blocks move THREADS * F4 float4, every load of a thread issued before its
 // first store.  Large commits take 64 KiB blocks (with 16 KiB blocks the 32 MiB
-// commit of 16 rows took 10 % longer); small ones take 16 KiB blocks, so that one
-// row's 2 MiB still spreads over 128 compute units.
+// commit of 16 rows took 10 % longer); small ones take 8 KiB blocks, so that one
+// row's 2 MiB spreads over 256 compute units (against 16 KiB blocks, a batch-1
+// verify + commit step replayed from a graph took 8.37 instead of 7.97 us per layer;
+// 4 and 16 KiB blocks, and 64-thread blocks, were slower).
 constexpr int kCopyBigThreads = 512, kCopyBigF4 = 8;
-constexpr int kCopySmallThreads = 256, kCopySmallF4 = 4;
+constexpr int kCopySmallThreads = 128, kCopySmallF4 = 4;
 constexpr int64_t kCopyBigMinBlocks = 512;  // big blocks once a launch has at least this many
 // fold blocks: 16 KiB of state each
 constexpr int kFoldThreads = 256;
