@@ -130,13 +130,13 @@ __device__ __forceinline__ void store_nt(float *p, const float (&x)[4]) {
 // table).  All compile the same per-token arithmetic, so they round identically.
 enum Mode { kChain = 0, kReplay = 1, kTree = 2, kDelta = 3, kSelect = 4 };
 
-// STREAM: the launch streams dense states out (checkpoints, or a written state) and its
-// blocks run in several rounds per CU.  A block that has just started then issues its
-// token and state loads at raised wave priority, ahead of the older blocks' arithmetic
-// and stores on the same SIMDs, so the memory system always holds the next round's
-// reads; and each output goes straight to memory from the lane that reduced it, so a
-// block retires as soon as its last store is issued.  (Launches that write no dense
-// state measured slower in this form.)
+// STREAM: the launch streams dense states out (checkpoints, a decode's new state, a
+// replayed commit).  A block issues its token and state loads at raised wave priority,
+// ahead of the arithmetic and stores of older blocks on the same SIMDs, so with several
+// rounds of blocks per CU the memory system always holds the next round's reads; and
+// each output goes straight to memory from the lane that reduced it, so a block retires
+// as soon as its last store is issued.  (Launches that write no dense state measured
+// slower in this form.)
 template <int D, int LPR, int RPL, int WAVES, int MODE, bool STREAM>
 __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs args) {
   if constexpr (STREAM) __builtin_amdgcn_s_setprio(3);
