@@ -23,8 +23,10 @@ counter summary when it was taken on the current kernel sources.
 Reported beside the headline, on the same synthetic data: batch 1 (eager and
 HIP-graph steps), mixed draft lengths, the other rollback forms (replay, delta
 checkpoints with a fold commit or folded into the next verify, checkpoint select),
-token trees, raw q/k normalised in the kernels, the 2048-token chunked prefill, and
-the fp64 oracle timed on the host cores.
+token trees, raw q/k normalised in the kernels, the in-place decode step, the
+2048-token chunked prefill, the mixed ragged transaction (4 prefill rows and 12
+verify rows planned per row in one call), and the fp64 oracle timed on the host
+cores.
 
 Prints one JSON line (see --help).  --gpus N>1 is refused: the path runs on one GPU.
 """
@@ -330,6 +332,59 @@ def measure_decode(gb, synth, torch, B, steps, warmup, n_layers, stream, seed0):
             "head_token_updates_per_s": B * V_HEADS * n_layers * steps / wall}
 
 
+def measure_transaction(gb, synth, torch, stream, reps):
+    """The mixed ragged transaction (16 rows in one packed batch: 4 prefills of
+    U{256..4096} tokens from the zero state, 12 K=3 verify windows with all four
+    checkpoints), planned per row and launched by gdn_run_transaction on both routes;
+    events on the launch stream around `reps` back-to-back transactions.  Also the
+    host planner's own time per call."""
+    import numpy as np
+    m = synth.mixed_workload()
+    dims = gb.Dims(16, 32, 128, 128, 3)
+    B, Hv, d = m.n_rows, 32, 128
+    lens = m.transaction_lens()
+    rows = np.arange(B, dtype=np.int32)
+    is_pf = m.is_prefill
+    n_ck = np.where(is_pf, 0, 4).astype(np.int32)
+    src = np.where(is_pf, -1, rows).astype(np.int32)
+    dst = np.where(is_pf, rows, -1).astype(np.int32)
+    tx = m.transaction_tokens()
+    dev = "cuda"
+    t = dict(q=torch.from_numpy(tx.q).to(torch.bfloat16).to(dev), k=torch.from_numpy(tx.k).to(torch.bfloat16).to(dev),
+             v=torch.from_numpy(tx.v).to(torch.bfloat16).to(dev), a=torch.from_numpy(tx.a).to(dev),
+             b=torch.from_numpy(tx.b).to(dev), A_log=torch.from_numpy(m.A_log).to(dev),
+             dt_bias=torch.from_numpy(m.dt_bias).to(dev))
+    gen = torch.Generator(device="cpu").manual_seed(1005)
+    pool = (0.05 * torch.randn(B, Hv, d, d, generator=gen)).to(dev)
+    ckpt = torch.empty(B, 4, Hv, d, d, device=dev)
+    o = torch.empty(int(lens.sum()), Hv, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gb.gdn_chunked_workspace_bytes(dims, lens), dtype=torch.uint8, device=dev)
+
+    def call():
+        gb.gdn_run_transaction(dims, lens, n_ck, **t, state_pool=pool, src_slot=src, dst_slot=dst, ckpt=ckpt,
+                               o=o, workspace=ws, stream=stream)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * ev[0].elapsed_time(ev[1]) / reps
+    n_plan = 2000
+    t0 = time.perf_counter()
+    for _ in range(n_plan):
+        gb.gdn_plan_transaction(dims, lens)
+    plan_us = 1e6 * (time.perf_counter() - t0) / n_plan
+    n_tok = int(lens.sum())
+    return {"workload": "mixed_transaction_4_prefills_12_verify_rows", "row_tokens": [int(x) for x in lens],
+            "us_per_transaction": us, "tokens": n_tok, "head_token_updates_per_s": n_tok * Hv / (us * 1e-6),
+            "planner_host_us_per_call": plan_us,
+            "planner_note": "host time of the Python binding call (marshalling included)"}
+
+
 def cpu_baseline(s: "VerifySet", seconds: float, seconds_1thread: float):
     """The fp64 oracle on the host, on the same window as the GPU step (a bounded
     sample: repeated windows for about `seconds` of work), with every host core the
@@ -493,6 +548,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the 2048-token chunked prefill and print its figures")
     ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--no-transaction", action="store_true",
+                    help="skip the mixed ragged transaction (4 prefills + 12 verify rows); --no-prefill skips it too")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this path runs on one GPU; --gpus %d is not supported "
@@ -602,6 +659,9 @@ def main():
         out_tree = side(rt, [4] * 16)
         out_tree["parents"] = TREE4
     prefill = None if args.no_prefill else measure_prefill(gb, synth, torch, stream, args.prefill_reps)
+    transaction = None
+    if not (args.no_prefill or args.no_transaction):
+        transaction = measure_transaction(gb, synth, torch, stream, args.prefill_reps)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(sets16[0], args.cpu_seconds, args.cpu_seconds_1thread)
@@ -646,6 +706,7 @@ def main():
         "conc16_k3_select": out_select,
         "decode": decode,
         "prefill": prefill,
+        "mixed_transaction": transaction,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

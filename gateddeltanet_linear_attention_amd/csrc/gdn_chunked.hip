@@ -409,10 +409,13 @@ struct ScanFrag {
   }
 };
 
-// One block per CU at the sizes this serves (a few hundred (unit, tile) chains), so
-// a wave may use the whole register file: two chunks' operands stay live.
+// A wave keeps two chunks' operands live (170 VGPRs), capped so that two blocks share
+// a CU: one 2048-token row has 256 (unit, tile) chains, one per CU, but a transaction
+// with several long prefill rows has more chains than CUs, and two of them then run
+// on each CU at once (the 16-row mixed transaction with 4 prefills of 883-3702 tokens
+// took 1012-1025 instead of 1075-1090 us; the single row is unchanged).
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void chunk_scan_kernel(ChunkArgs args, int n_units) {
   constexpr int LDS_ = D + 4;
   constexpr int TILES = D / VT;
