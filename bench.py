@@ -25,8 +25,9 @@ HIP-graph steps), mixed draft lengths, the other rollback forms (replay, delta
 checkpoints with a fold commit or folded into the next verify, checkpoint select),
 token trees, raw q/k normalised in the kernels, the in-place decode step, the
 2048-token chunked prefill, the mixed ragged transaction (4 prefill rows and 12
-verify rows planned per row in one call), and the fp64 oracle timed on the host
-cores.
+verify rows planned per row in one call), the streaming-bandwidth ceilings of a plain
+kernel with the verify's and the commit's traffic (context; the roofline's peak stays
+8 TB/s), and the fp64 oracle timed on the host cores.
 
 Prints one JSON line (see --help).  --gpus N>1 is refused: the path runs on one GPU.
 """
@@ -385,6 +386,52 @@ def measure_transaction(gb, synth, torch, stream, reps):
             "planner_note": "host time of the Python binding call (marshalling included)"}
 
 
+def measure_ceilings(torch, stream, sets: int = 12, reps: int = 240):
+    """Streaming ceilings for context, in the same process: a plain kernel that reads
+    32 MiB once and writes it to 4 copies (the verify's 1 read : 4 writes of state, none
+    of its work) and to 1 copy (a plain copy, the commit's traffic), over `sets` rotating
+    buffer sets so that every launch streams from HBM; HIP events on the launch stream."""
+    import ctypes
+    path = os.path.join(ROOT, "gateddeltanet_linear_attention_amd", "libgdn_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError("%s is missing: run python -m gateddeltanet_linear_attention_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    lib.gdn_probe_stream.restype = ctypes.c_int
+    lib.gdn_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_void_p]
+    n = 32 << 20
+    src = [torch.zeros(n // 4, device="cuda") for _ in range(sets)]
+    dst = [torch.empty(4 * n // 4, device="cuda") for _ in range(sets)]
+    shapes = {0: "512x2", 1: "256x2_prio", 2: "256x4_prio"}
+    out = {}
+    for n_out, name in ((4, "stream_1r4w_32MiB"), (1, "copy_1r1w_32MiB")):
+        per = {}
+        for shape, sname in shapes.items():
+            def launch(i):
+                rc = lib.gdn_probe_stream(src[i % sets].data_ptr(), dst[i % sets].data_ptr(), n, n_out, shape,
+                                          ctypes.c_void_p(stream.cuda_stream))
+                if rc != 0:
+                    raise RuntimeError("gdn_probe_stream returned %d" % rc)
+            for i in range(2 * sets):
+                launch(i)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for i in range(reps):
+                launch(i)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            per[sname] = 1e3 * ev[0].elapsed_time(ev[1]) / reps
+        best = min(per, key=per.get)
+        us = per[best]
+        gbps = (1 + n_out) * n / (us * 1e-6) / 1e9
+        out[name] = {"us": us, "gbps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS, "schedule": best,
+                     "us_per_schedule": per}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(s: "VerifySet", seconds: float, seconds_1thread: float):
     """The fp64 oracle on the host, on the same window as the GPU step (a bounded
     sample: repeated windows for about `seconds` of work), with every host core the
@@ -548,6 +595,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the 2048-token chunked prefill and print its figures")
     ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the streaming-bandwidth ceilings (plain 1:4 and 1:1 streams) reported for context")
     ap.add_argument("--no-transaction", action="store_true",
                     help="skip the mixed ragged transaction (4 prefills + 12 verify rows); --no-prefill skips it too")
     args = ap.parse_args()
@@ -659,6 +708,12 @@ def main():
         out_tree = side(rt, [4] * 16)
         out_tree["parents"] = TREE4
     prefill = None if args.no_prefill else measure_prefill(gb, synth, torch, stream, args.prefill_reps)
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = measure_ceilings(torch, stream)
+        # ceiling time / kernel time: 1 means the kernel runs as fast as the best plain stream
+        ceilings["verify_frac_of_1r4w_ceiling"] = ceilings["stream_1r4w_32MiB"]["us"] / (1e3 * r16["verify_ms_mean"])
+        ceilings["commit_frac_of_copy_ceiling"] = ceilings["copy_1r1w_32MiB"]["us"] / (1e3 * r16["commit_ms_mean"])
     transaction = None
     if not (args.no_prefill or args.no_transaction):
         transaction = measure_transaction(gb, synth, torch, stream, args.prefill_reps)
@@ -707,6 +762,7 @@ def main():
         "decode": decode,
         "prefill": prefill,
         "mixed_transaction": transaction,
+        "streaming_ceilings": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

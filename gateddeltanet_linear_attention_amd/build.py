@@ -1,4 +1,5 @@
-"""Build libgdn.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Build libgdn.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and beside it
+libgdn_probe.so (the streaming-bandwidth probe the benchmark reports as context).
 
     python -m gateddeltanet_linear_attention_amd.build
 
@@ -20,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
+PROBE_SRC = os.path.join(PKG, "probe", "bw_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libgdn_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -57,7 +60,22 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """libgdn_probe.so: the streaming-bandwidth probe the benchmark reports as context."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe build failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print("built", PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

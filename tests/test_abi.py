@@ -47,6 +47,25 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), "libgdn.so does not export %s" % n
 
 
+def test_bandwidth_probe_library_loads_and_refuses_bad_arguments():
+    """The benchmark's streaming-ceiling probe is a library of its own beside libgdn.so;
+    its argument checks run on the host, so bad calls return -1 without a GPU."""
+    path = os.path.join(os.path.dirname(gb.LIB_PATH), "libgdn_probe.so")
+    lib = ctypes.CDLL(path)
+    f = lib.gdn_probe_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p]
+    a, b = 1 << 40, 2 << 40  # never dereferenced: every call below fails its checks first
+    assert f(None, b, 1024, 4, 0, None) == -1
+    assert f(a, b, 0, 4, 0, None) == -1
+    assert f(a, b, 1000, 4, 0, None) == -1   # not a multiple of 16
+    assert f(a, b, 1024, 0, 0, None) == -1
+    assert f(a, b, 1024, 9, 0, None) == -1
+    assert f(a + 4, b, 1024, 4, 0, None) == -1  # misaligned
+    assert f(a, b, 1024, 4, 3, None) == -1   # no such schedule
+
+
 def test_version_and_status_strings():
     m = re.search(r"#define GDN_VERSION (\d+)", open(HEADER).read())
     assert gb.gdn_version() == int(m.group(1))
