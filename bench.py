@@ -595,6 +595,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the 2048-token chunked prefill and print its figures")
     ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--transaction-only", action="store_true",
+                    help="time only the mixed ragged transaction and print its figures")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the streaming-bandwidth ceilings (plain 1:4 and 1:1 streams) reported for context")
     ap.add_argument("--no-transaction", action="store_true",
@@ -618,6 +620,9 @@ def main():
 
     if args.prefill_only:
         print(json.dumps(measure_prefill(gb, synth, torch, stream, args.prefill_reps)), flush=True)
+        return
+    if args.transaction_only:
+        print(json.dumps(measure_transaction(gb, synth, torch, stream, args.prefill_reps)), flush=True)
         return
 
     import numpy as np
