@@ -399,9 +399,9 @@ def measure_ceilings(torch, stream, sets: int = 12, reps: int = 240):
     lib.gdn_probe_stream.restype = ctypes.c_int
     lib.gdn_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_void_p]
-    n = 32 << 20
-    src = [torch.zeros(n // 4, device="cuda") for _ in range(sets)]
-    dst = [torch.empty(4 * n // 4, device="cuda") for _ in range(sets)]
+    n = 32 << 20  # bytes read per launch
+    src = [torch.zeros(n // 4, device="cuda") for _ in range(sets)]          # 32 MiB of fp32
+    dst = [torch.empty(4 * (n // 4), device="cuda") for _ in range(sets)]    # room for 4 copies
     shapes = {0: "512x2", 1: "256x2_prio", 2: "256x4_prio"}
     out = {}
     for n_out, name in ((4, "stream_1r4w_32MiB"), (1, "copy_1r1w_32MiB")):
