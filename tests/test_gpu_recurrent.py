@@ -208,6 +208,15 @@ def test_conc16_all_k3_short():
     run_verify_workload(w, n_windows=w.n_windows, check_every=8)
 
 
+def test_conc16_all_k3_full_workload():
+    """The benchmark's configuration (16 rows, every row K=3, the launch layout bench.py
+    times) over the workload's full 512 windows, each committed, against the oracle."""
+    w = synth.verify_workload("conc16", all_k3=True)
+    assert w.n_windows == 512 and set(w.draft_lens.tolist()) == {3}
+    worst = run_verify_workload(w, n_windows=w.n_windows, check_every=64)
+    say("conc16 all-K3 worst:", worst)
+
+
 # ---------------------------------------------------------------- bit-exact properties
 
 def _random_pool(n_slots, Hv, d, seed, scale=0.3):
