@@ -33,9 +33,12 @@
 //       channels), all in parallel: the outputs O.
 //   chunk_ckpt_kernel  one block per (row, tail checkpoint, value head, 16 value
 //       rows): the requested checkpoints, from the recorded chunk state.
-// Every contraction runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, 157 TF
-// dense on MI355X): the state tolerance (relative 1e-4) rules out rounding the fp32
-// operands T, W, U, S to bf16.  A wave loads all operand fragments of a product
+// The contractions run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, 157 TF dense
+// on MI355X): the state tolerance (relative 1e-4) rules out rounding the fp32 operands
+// T, W, U, S to bf16.  Two products run on the bf16 cores at fp32 accuracy: K K^T and
+// Q K^T (bf16 inputs, exact products), and the carry's U^T diag(.) K, whose K is bf16
+// and whose fp32 factor is split into three bf16 parts that sum to it to within a unit
+// in its last place.  A wave loads all operand fragments of a product
 // before its first matrix instruction and interleaves independent accumulation
 // chains, so global-memory latency is paid once per phase, not once per k step.
 // Decays are formed only as differences G_t - G_s with s <= t, from an fp64 prefix
@@ -76,6 +79,55 @@ __device__ __forceinline__ floatx4 mma4(floatx4 acc, float4 a, float4 b) {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// x = hi + mid + lo to fp32 precision in three bf16 parts, each the round to nearest of
+// what the parts before it leave (every subtraction is exact), written as the bits of
+// the lane's four values per part.  A bf16 matrix product of these parts against an
+// exactly-bf16 operand then reproduces the fp32 product to fp32 accuracy (the bf16x3
+// split: Henry, Tang & Heinecke, "Leveraging the bfloat16 Artificial Intelligence
+// Datatype for Higher-Precision Computations", ARITH 2019).
+struct Parts4 {  // one 4-token piece in three parts, bf16 bits
+  uint2 h, m, l;
+};
+// the three parts of one value, packed at bit 16 * `hi` of the three words
+__device__ __forceinline__ void split3_into(float v, int hi, uint32_t &h, uint32_t &m, uint32_t &l) {
+  const uint32_t bh = to_bf16(v);
+  const float r1 = v - __uint_as_float(bh << 16);
+  const uint32_t bm = to_bf16(r1);
+  const uint32_t bl = to_bf16(r1 - __uint_as_float(bm << 16));
+  h |= bh << (16 * hi);
+  m |= bm << (16 * hi);
+  l |= bl << (16 * hi);
+}
+__device__ __forceinline__ Parts4 split3x4(float4 x) {
+  uint32_t h0 = 0, m0 = 0, l0 = 0, h1 = 0, m1 = 0, l1 = 0;
+  split3_into(x.x, 0, h0, m0, l0);
+  split3_into(x.y, 1, h0, m0, l0);
+  split3_into(x.z, 0, h1, m1, l1);
+  split3_into(x.w, 1, h1, m1, l1);
+  return Parts4{make_uint2(h0, h1), make_uint2(m0, m1), make_uint2(l0, l1)};
+}
+
+// Two 4-token pieces (bf16 bits) as one 8-wide operand of v_mfma_f32_16x16x32_bf16.
+__device__ __forceinline__ bf16x8 pieces8(uint2 a, uint2 b) {
+  return __builtin_bit_cast(bf16x8, u32x4v{a.x, a.y, b.x, b.y});
+}
+
+// acc(16x16) += A(16 x 64 tokens) * B(64 tokens x 16) with A given as the bf16x3 parts of
+// its four 4-token pieces (lane (r, g): A[r][16 kb + 4 g + e]) and B exactly bf16 in
+// the same pieces (B[16 kb + 4 g + e][r]): each 32-wide matrix instruction takes pieces
+// kb = 2 m, 2 m + 1 (a permutation of the token index, the same on both sides), parts
+// hi, mid, lo in that order.  Output layout as mma4's.
+__device__ __forceinline__ floatx4 mma_bf16x3_32(floatx4 acc, Parts4 a0, Parts4 a1, uint2 b0, uint2 b1) {
+  const bf16x8 b = pieces8(b0, b1);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pieces8(a0.h, a1.h), b, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pieces8(a0.m, a1.m), b, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(pieces8(a0.l, a1.l), b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma_bf16x3_64(floatx4 acc, Parts4 a0, Parts4 a1, Parts4 a2, Parts4 a3,
+                                                 uint2 b0, uint2 b1, uint2 b2, uint2 b3) {
+  return mma_bf16x3_32(mma_bf16x3_32(acc, a0, a1, b0, b1), a2, a3, b2, b3);
+}
 
 // bf16 operand of v_mfma_f32_16x16x32_bf16 for 32-wide k block kb of row t of a
 // row-major bf16 matrix (row pitch ld elements, rows t >= n read as zero): lane
@@ -381,7 +433,8 @@ template <int D>
 struct ScanFrag {
   static constexpr int NKB = D / 16;
   static constexpr int NT_W = (D / 16 + 3) / 4;
-  float4 wf[NKB], el, kf[NT_W][4];
+  float4 wf[NKB], el;
+  uint2 kp[NT_W][4];  // K^T pieces kb = 0..3 of each column tile, bf16 bits
   float4 up;
   float e_last;
   __device__ void load(const Ws<D> &ws, int n, int w, int r16, int g4, int i0) {
@@ -399,10 +452,10 @@ struct ScanFrag {
       const int nt = min(w + 4 * q, D / 16 - 1);
       const uint4 *kr = reinterpret_cast<const uint4 *>(ws.Kt + (16 * nt + r16) * C + 16 * g4);
       const uint4 k01 = kr[0], k23 = kr[1];  // pieces kb = 0, 1 and 2, 3 (kt_pos order)
-      kf[q][0] = unpack_bf16x4(make_uint2(k01.x, k01.y));
-      kf[q][1] = unpack_bf16x4(make_uint2(k01.z, k01.w));
-      kf[q][2] = unpack_bf16x4(make_uint2(k23.x, k23.y));
-      kf[q][3] = unpack_bf16x4(make_uint2(k23.z, k23.w));
+      kp[q][0] = make_uint2(k01.x, k01.y);
+      kp[q][1] = make_uint2(k01.z, k01.w);
+      kp[q][2] = make_uint2(k23.x, k23.y);
+      kp[q][3] = make_uint2(k23.z, k23.w);
     }
     up = *reinterpret_cast<const float4 *>(ws.U + (i0 + r16) * C + 16 * w + 4 * g4);
     e_last = ws.eG[n - 1];
@@ -426,7 +479,8 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
   // the next state to sSb[(c + 1) & 1], so no barrier is needed between the last read
   // of a state and the write of the next one
   __shared__ __attribute__((aligned(16))) float sSb[2][VT * LDS_];
-  __shared__ __attribute__((aligned(16))) float sUt[VT * LDC];  // U^T of this tile: row i, token s
+  // U^T diag(e^{G_n - G}) of this tile (row i, token s) as its three bf16x3 parts
+  __shared__ __attribute__((aligned(16))) uint16_t sUp[3][VT * LDB];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -463,7 +517,7 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
     const Ws<D> ws = ws_of(c);
     const float *sS = sSb[c & 1];
     float *sS_next = sSb[(c + 1) & 1];
-    lds_barrier();  // the state tile of this chunk is in place; the last chunk's reads of sUt are done
+    lds_barrier();  // the state tile of this chunk is in place; the last chunk's reads of sUp are done
 
     // U = U' - W S_c^T for tokens 16w..16w+15 of this tile's 16 value channels,
     // in two interleaved partial chains
@@ -483,19 +537,30 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
     }
     {
       // this lane's tokens 16w + 4g4 + (0..3) of value channel i0 + r16: contiguous in
-      // both U^T buffers; LDS gets U^T diag(e^{G_n - G}), as the carry uses it
+      // both U^T buffers; LDS gets U^T diag(e^{G_n - G}), as the carry uses it, split
+      // into bf16x3 parts once here (K is bf16, so the carry runs on the bf16 matrix
+      // cores at fp32 accuracy)
       const float4 u = make_float4(f.up.x - (ua[0] + ub[0]), f.up.y - (ua[1] + ub[1]),
                                    f.up.z - (ua[2] + ub[2]), f.up.w - (ua[3] + ub[3]));
-      *reinterpret_cast<float4 *>(sUt + r16 * LDC + 16 * w + 4 * g4) = mul4(u, f.el);
+      const Parts4 part = split3x4(mul4(u, f.el));
+      const int o = r16 * LDB + 16 * w + 4 * g4;
+      *reinterpret_cast<uint2 *>(sUp[0] + o) = part.h;
+      *reinterpret_cast<uint2 *>(sUp[1] + o) = part.m;
+      *reinterpret_cast<uint2 *>(sUp[2] + o) = part.l;
       *reinterpret_cast<float4 *>(ws.Ut + (i0 + r16) * C + 16 * w + 4 * g4) = u;
     }
     lds_barrier();  // U^T of the tile complete
 
     // S_{c+1} = e^{G_n} S_c + U^T diag(e^{G_n - G}) K on this wave's column tiles
-    float4 af[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      af[kb] = *reinterpret_cast<const float4 *>(sUt + r16 * LDC + 16 * kb + 4 * g4);
+    auto lds_parts = [&](int kb) {
+      const int o = r16 * LDB + 16 * kb + 4 * g4;
+      Parts4 r;
+      r.h = *reinterpret_cast<const uint2 *>(sUp[0] + o);
+      r.m = *reinterpret_cast<const uint2 *>(sUp[1] + o);
+      r.l = *reinterpret_cast<const uint2 *>(sUp[2] + o);
+      return r;
+    };
+    const Parts4 a0 = lds_parts(0), a1 = lds_parts(1), a2 = lds_parts(2), a3 = lds_parts(3);
     floatx4 snew[NT_W];
 #pragma unroll
     for (int q = 0; q < NT_W; ++q) {
@@ -504,8 +569,7 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
       if (nt < D / 16) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[v] = f.e_last * sS[(4 * g4 + v) * LDS_ + 16 * nt + r16];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = mma4(acc, af[kb], f.kf[q][kb]);
+        acc = mma_bf16x3_64(acc, a0, a1, a2, a3, f.kp[q][0], f.kp[q][1], f.kp[q][2], f.kp[q][3]);
       }
       snew[q] = acc;
     }
@@ -647,26 +711,24 @@ __global__ __launch_bounds__(256) void chunk_ckpt_kernel(ChunkArgs args) {
   // to the final state the scan publishes
   if (w == 0) sScale[lane] = lane <= jj ? float(exp(ws.G[jj] - ws.G[lane])) * ws.rk[lane] : 0.0f;
   lds_barrier();
-  float4 af[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    af[kb] = mul4(*reinterpret_cast<const float4 *>(ws.Ut + (16 * mi + r16) * C + 16 * kb + 4 * g4),
-                  *reinterpret_cast<const float4 *>(sScale + 16 * kb + 4 * g4));
+  // the scan's carry operation, part for part: at a row's last position the scaled U
+  // values, their bf16x3 split and the matrix-instruction sequence are the scan's own
+  auto scaled_parts = [&](int kb) {
+    return split3x4(mul4(*reinterpret_cast<const float4 *>(ws.Ut + (16 * mi + r16) * C + 16 * kb + 4 * g4),
+                         *reinterpret_cast<const float4 *>(sScale + 16 * kb + 4 * g4)));
+  };
+  const Parts4 a0 = scaled_parts(0), a1 = scaled_parts(1), a2 = scaled_parts(2), a3 = scaled_parts(3);
   const float ej = ws.eG[jj];
   float *cdst = args.ckpt + ((int64_t(args.ck_row[row]) * args.ck_slots + j) * n_v + h) * UNIT;
   for (int nt = 2 * w; nt < 2 * w + 2 && nt < D / 16; ++nt) {
-    float4 kf[4];
+    const uint2 *kr = reinterpret_cast<const uint2 *>(ws.Kt + (16 * nt + r16) * C + 16 * g4);  // pieces 0..3
     float sc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      kf[kb] = unpack_bf16x4(*reinterpret_cast<const uint2 *>(ws.Kt + (16 * nt + r16) * C + 16 * g4 + 4 * kb));
 #pragma unroll
     for (int v = 0; v < 4; ++v) sc[v] = ws.Sc[int64_t(16 * mi + 4 * g4 + v) * D + 16 * nt + r16];
     floatx4 acc;
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] = ej * sc[v];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) acc = mma4(acc, af[kb], kf[kb]);
+    acc = mma_bf16x3_64(acc, a0, a1, a2, a3, kr[0], kr[1], kr[2], kr[3]);
 #pragma unroll
     for (int v = 0; v < 4; ++v) cdst[int64_t(16 * mi + 4 * g4 + v) * D + 16 * nt + r16] = acc[v];
   }
