@@ -292,9 +292,11 @@ def decode_bytes(n_rows: int) -> int:
     return n_rows * V_HEADS * (2 * STATE_BYTES + TOKEN_BYTES)
 
 
-def measure_decode(gb, synth, torch, B, steps, warmup, n_layers, stream, seed0):
-    """In-place decode of one token per row through n_layers layers (each with its own
-    state pool and tokens), HIP events around each step's run of launches."""
+def measure_decode(gb, synth, torch, B, steps, warmup, n_layers, stream, seed0, two_sets=False):
+    """Decode of one token per row through n_layers layers (each with its own state
+    pool and tokens), HIP events around each step's run of launches.  In place by
+    default; two_sets: each layer's pool holds two slot sets and the steps alternate
+    between them (new state to the other set, twice the state memory)."""
     import numpy as np
     dims = gb.Dims(16, 32, 128, 128, 3)
     rows = np.arange(B, dtype=np.int32)
@@ -308,27 +310,31 @@ def measure_decode(gb, synth, torch, B, steps, warmup, n_layers, stream, seed0):
                  b=torch.from_numpy(tok.b).cuda(), A_log=torch.from_numpy(A_log).cuda(),
                  dt_bias=torch.from_numpy(dt_bias).cuda())
         gen = torch.Generator(device="cpu").manual_seed(seed0 + li)
-        pool = (0.05 * torch.randn(B, 32, 128, 128, generator=gen)).cuda()
+        pool = (0.05 * torch.randn((2 if two_sets else 1) * B, 32, 128, 128, generator=gen)).cuda()
         o = torch.empty(B, 32, 128, dtype=torch.bfloat16, device="cuda")
-        calls.append(gb.prepare_decode_step(dims, **t, state_pool=pool, src_slot=rows, dst_slot=rows, o=o,
-                                            stream=stream))
+        if two_sets:
+            calls.append([gb.prepare_decode_step(dims, **t, state_pool=pool, src_slot=rows + B * j,
+                                                 dst_slot=rows + B * (1 - j), o=o, stream=stream) for j in (0, 1)])
+        else:
+            c = gb.prepare_decode_step(dims, **t, state_pool=pool, src_slot=rows, dst_slot=rows, o=o, stream=stream)
+            calls.append([c, c])
         keep.append((t, pool, o))
-    for _ in range(warmup):
+    for i in range(warmup):
         for c in calls:
-            c()
+            c[i % 2]()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
         for c in calls:
-            c()
+            c[(warmup + i) % 2]()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / (steps * n_layers)
     nb = decode_bytes(B)
-    return {"rows": B, "decode_us_mean": us, "algorithmic_bytes_per_launch": nb,
+    return {"rows": B, "in_place": not two_sets, "decode_us_mean": us, "algorithmic_bytes_per_launch": nb,
             "gbps": nb / (us * 1e-6) / 1e9, "frac_of_hbm_peak": nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
             "head_token_updates_per_s": B * V_HEADS * n_layers * steps / wall}
 
@@ -697,6 +703,8 @@ def main():
             out_fused["prefill_us_per_call"] = measure_prefill(gb, synth, torch, stream, args.prefill_reps,
                                                                raw_qk=True)["us_per_call"]
     decode = {"conc16": measure_decode(gb, synth, torch, 16, args.steps, args.warmup, args.layers, stream, 900),
+              "conc16_two_slot_sets": measure_decode(gb, synth, torch, 16, args.steps, args.warmup, args.layers,
+                                                     stream, 900, two_sets=True),
               "batch1": measure_decode(gb, synth, torch, 1, args.steps, args.warmup, args.layers, stream, 950)}
     out_select = None
     if not args.no_replay:

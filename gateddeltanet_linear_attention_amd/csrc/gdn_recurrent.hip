@@ -439,13 +439,22 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   }
 
   if (dst >= 0) {
+    // A new state bound for another slot is streamed past the caches like a checkpoint;
+    // one written over the state just read is stored plainly (measured on the 16-row
+    // decode: out of place 12.95 -> 11.95 us with non-temporal stores, in place 15.25
+    // plain against 15.9 non-temporal).
+    const bool stream_out = dst != src;
 #pragma unroll
     for (int q = 0; q < RPL; ++q) {
-      float4 *p = reinterpret_cast<float4 *>(args.state_out + (size_t(dst) * n_v + h) * UNIT +
-                                             size_t(i0 + q) * D);
+      float *p = args.state_out + (size_t(dst) * n_v + h) * UNIT + size_t(i0 + q) * D;
+      if (stream_out) {
 #pragma unroll
-      for (int j = 0; j < NV; ++j)
-        p[sub + LPR * j] = make_float4(s[q][j][0], s[q][j][1], s[q][j][2], s[q][j][3]);
+        for (int j = 0; j < NV; ++j) store_nt(p + 4 * (sub + LPR * j), s[q][j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+          reinterpret_cast<float4 *>(p)[sub + LPR * j] = make_float4(s[q][j][0], s[q][j][1], s[q][j][2], s[q][j][3]);
+      }
     }
   }
 }

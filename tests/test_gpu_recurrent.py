@@ -267,6 +267,34 @@ def test_verify_checkpoint_j_bit_identical_to_decode_chain(shape, raw_qk):
         assert_state(host(ckpt[r, :T[r]]), ck_o[r, :T[r]], "row %d checkpoints" % r)
 
 
+@pytest.mark.parametrize("B", [16, 2], ids=["rows16", "rows2"])
+def test_decode_to_another_slot_equals_decode_in_place(B):
+    """A decode whose new state goes to another slot (streamed with non-temporal stores)
+    and one that overwrites its source slot give the same bits, states and outputs."""
+    shape = synth.FULL
+    dims = dims_of(shape)
+    Hv, d = shape.n_v_heads, shape.d
+    g = synth.streams(23, 2)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    P = dev_params(A_log, dt_bias)
+    td = dev_tokens(synth.tokens(g[1], shape, B))
+    rows = np.arange(B, dtype=np.int32)
+    pool = _random_pool(2 * B, Hv, d, 9)
+    pool[B:] = pool[:B]
+    before = pool[:B].clone()
+    o_in = torch.empty(B, Hv, d, dtype=torch.bfloat16, device="cuda")
+    o_out = torch.empty_like(o_in)
+    # in place on slots B..2B-1; from slots 0..B-1 into a third set
+    out = torch.empty(3 * B, Hv, d, d, device="cuda")
+    out[:2 * B] = pool
+    gb.gdn_decode_step(dims, **td, **P, state_pool=out, src_slot=rows + B, dst_slot=rows + B, o=o_in)
+    gb.gdn_decode_step(dims, **td, **P, state_pool=out, src_slot=rows, dst_slot=rows + 2 * B, o=o_out)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out[2 * B:]), bits(out[B:2 * B]))
+    assert torch.equal(o_in.view(torch.int16), o_out.view(torch.int16))
+    assert torch.equal(bits(out[:B]), bits(before)), "the source slots were written"
+
+
 @pytest.mark.parametrize("accepted", [0, 1, 2, 3])
 def test_rollback_leaves_no_trace(accepted):
     """verify(K=3) + commit(a) + 3 more decode steps == decode of the previous bonus
