@@ -102,6 +102,9 @@ enum { GDN_ROUTE_RECURRENT = 0, GDN_ROUTE_CHUNKED = 1 };
  * writes o[r] and the new state to slot dst_slot[r] (== src_slot[r] updates in
  * place).  Decode is the single-token case of the verify window below: both run
  * one device routine, so verify checkpoint j is bit-identical to j+1 decode calls.
+ * Both forms give the same bits; a new state bound for another slot is streamed
+ * past the caches, which measured faster than updating in place (a caller with two
+ * slot sets per request can alternate between them).
  * Errors: GDN_E_RANGE for a slot outside [0, n_slots) (src may be -1);
  * GDN_E_ALIAS if two rows share a dst slot or a dst slot is another row's src.
  */
