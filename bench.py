@@ -125,7 +125,7 @@ class VerifySet:
     and the two prepared C-ABI calls of a step."""
 
     def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False, parents=None, delta=False,
-                 folded=False, select=False):
+                 folded=False, select=False, two_sets=False):
         raw_qk = bool(dims.flags & gb.QK_L2NORM)
         import numpy as np
         import torch
@@ -196,6 +196,26 @@ class VerifySet:
                                                          delta=self.delta, o=self.o, stream=stream)
             self.commit = gb.prepare_commit_delta(dims, Ts, self.t["k"], self.delta, self.acc, self.pool,
                                                   src_slot=rows, dst_slot=rows, status=self.status, stream=stream)
+        elif replay and two_sets:  # replay from one slot set into the other, the sets alternating
+            self.ckpt = None
+            start = self.pool
+            self.pool = torch.empty(2 * B, Hv, d, d, device=dev)
+            self.pool[:B] = start
+            tin = {k: v for k, v in self.t.items()}
+            sv = [gb.prepare_verify_window(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows + B * j,
+                                           ckpt=None, o=self.o, stream=stream) for j in (0, 1)]
+            sc = [gb.prepare_commit_replay(dims, Ts, **tin, accepted=self.acc, state_pool=self.pool,
+                                           src_slot=rows + B * j, dst_slot=rows + B * (1 - j), status=self.status,
+                                           stream=stream) for j in (0, 1)]
+            phase = [0]
+
+            def verify():
+                sv[phase[0]]()
+
+            def commit():
+                sc[phase[0]]()
+                phase[0] ^= 1
+            self.verify, self.commit = verify, commit
         elif replay:  # no checkpoints: commit re-runs the accepted prefix in place
             self.ckpt = None
             self.verify = gb.prepare_verify_window(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
@@ -531,13 +551,13 @@ def measure_prefill(gb, synth, torch, stream, reps, raw_qk=False):
 
 
 def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay=False, parents=None,
-            delta=False, folded=False, raw_qk=False, select=False):
+            delta=False, folded=False, raw_qk=False, select=False, two_sets=False):
     """Steps over n_layers layers of windows with per-row token counts Ts (replay:
     verify without checkpoints, commit by replay; parents: one draft tree per row;
     delta: delta checkpoints folded by a commit launch; folded: folded by the next
     verify, one launch per layer per step; raw_qk: q and k normalised inside the kernels)."""
     dims = gb.Dims(16, 32, 128, 128, 3, gb.QK_L2NORM if raw_qk else 0)
-    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents, delta, folded, select)
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents, delta, folded, select, two_sets)
             for i in range(n_layers)]
     wall, verify_ms, commit_ms = run_steps(sets, steps, warmup, stream, torch)
     for s in sets:
@@ -667,6 +687,13 @@ def main():
                       "replay_us_mean": 1e3 * rr["commit_ms_mean"], "replay_gbps": rr["commit_gbps"],
                       "step_gbps": rr["step_gbps"],
                       "step_algorithmic_bytes_per_layer": rr["verify_bytes"] + rr["commit_bytes"]}
+        _, rr2 = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
+                         replay=True, two_sets=True)
+        out_replay["two_slot_sets"] = {
+            "mode": "the replay writes into a second slot set, the two sets used alternately (twice the state memory)",
+            "head_token_updates_per_s": rr2["updates_per_s"], "ms_per_layer": rr2["ms_per_step"] / args.layers,
+            "verify_us_mean": 1e3 * rr2["verify_ms_mean"], "replay_us_mean": 1e3 * rr2["commit_ms_mean"],
+            "replay_gbps": rr2["commit_gbps"]}
     out_delta = None
     if not args.no_replay:
         _, rd = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500, delta=True)
