@@ -126,6 +126,64 @@ def test_slow_decay_long_memory():
                      what="slow decay")
 
 
+def test_more_than_64_chunked_rows_span_launches():
+    """70 rows: the library splits a call into launches of at most 64 rows and numbers
+    workspace chunks across them; tails straddle chunk boundaries, sources are mixed."""
+    rng = np.random.default_rng(68)
+    lens = rng.integers(65, 201, size=70).astype(np.int32)
+    lens[:6] = [65, 127, 128, 129, 191, 200]
+    n_tail = np.minimum(rng.integers(0, 5, size=70), lens).astype(np.int32)
+    run_chunked_case(synth.HeadShape(1, 2, 128), lens, n_tail, "mixed", 68, what="70 rows")
+
+
+def test_transaction_of_140_rows_mixing_routes():
+    """140 rows alternating K<=3 verify windows and 65-300-token prefills: both routes
+    take two launches each; every row's outputs, checkpoints and final state vs the
+    oracle, verify rows' pool slots untouched."""
+    shape = synth.HeadShape(1, 2, 128)
+    dims = dims_of(shape)
+    B, Hv, d = 140, shape.n_v_heads, shape.d
+    rng = np.random.default_rng(69)
+    is_pf = np.arange(B) % 2 == 1
+    lens = np.where(is_pf, rng.integers(65, 301, size=B), rng.integers(1, 5, size=B)).astype(np.int32)
+    n_ck = np.where(is_pf, rng.integers(0, 5, size=B), lens).astype(np.int32)
+    n_ck = np.minimum(n_ck, lens).astype(np.int32)
+    assert np.array_equal(gb.gdn_plan_transaction(dims, lens),
+                          np.where(is_pf, gb.ROUTE_CHUNKED, gb.ROUTE_RECURRENT))
+    g = synth.streams(69, 3)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    tok = synth.tokens(g[1], shape, int(lens.sum()))
+    gen = torch.Generator(device="cpu").manual_seed(69)
+    pool = (0.3 * torch.randn(2 * B, Hv, d, d, generator=gen)).cuda()
+    src = np.arange(B, dtype=np.int32)
+    src[is_pf & (np.arange(B) % 4 == 1)] = -1
+    dst = np.where(is_pf, B + np.arange(B), -1).astype(np.int32)
+    before = pool.clone()
+    ckpt = _poison((B, 4, Hv, d, d))
+    o = torch.empty(int(lens.sum()), Hv, d, dtype=torch.bfloat16, device="cuda")
+    say("transaction of 140 rows: %d chunked, %d recurrent" % (is_pf.sum(), (~is_pf).sum()))
+    gb.gdn_run_transaction(dims, lens, n_ck, **dev_tokens(tok), **dev_params(A_log, dt_bias), state_pool=pool,
+                           src_slot=src, dst_slot=dst, ckpt=ckpt, o=o, workspace=_ws(dims, lens[is_pf]))
+    S0 = host(before[:B])
+    S0[src < 0] = 0.0
+    S_ref, ck_ref, o_ref = oracle.run_sequential(lens, tok.q, tok.k, tok.v, tok.a, tok.b, A_log, dt_bias, S0,
+                                                 n_tail=n_ck, n_slot=4)
+    torch.cuda.synchronize()
+    mo = assert_o(host(o), o_ref, "140-row transaction outputs")
+    pf_i = torch.as_tensor(np.nonzero(is_pf)[0], device="cuda")
+    vf_i = torch.as_tensor(np.nonzero(~is_pf)[0], device="cuda")
+    ms = assert_state(host(pool[B:].index_select(0, pf_i)), S_ref[is_pf], "140-row transaction final states")
+    ck_h = host(ckpt)
+    for r in range(B):
+        if n_ck[r]:
+            ms = max(ms, assert_state(ck_h[r, :n_ck[r]], ck_ref[r, :n_ck[r]], "row %d checkpoints" % r))
+        assert bool((bits(ckpt[r, n_ck[r]:]) == POISON).all()), "row %d: extra checkpoint slot written" % r
+    assert torch.equal(bits(pool[:B]), bits(before[:B])), "a source slot was written"
+    assert torch.equal(bits(pool[B:].index_select(0, vf_i)), bits(before[B:].index_select(0, vf_i))), \
+        "a verify row published a state"
+    say("140-row transaction: max |do| %.2e, state rel %.2e" % (mo, ms))
+
+
 def test_chunked_matches_verify_within_tolerance_and_commit_works_on_it():
     """Commit is path-agnostic: tail slots of a chunked row mean what verify slots mean."""
     shape = synth.FULL
