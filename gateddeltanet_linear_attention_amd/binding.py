@@ -81,6 +81,9 @@ _SIGS = {
                                              ctypes.c_int32, _I32P] + [_VP] * 8 +
                                             [ctypes.c_int32, _I32P, _I32P, _VP, _VP, _VP,
                                              ctypes.c_size_t, _VP],
+    "gdn_chunked_prefill_with_checkpoints_static": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P,
+                                                    ctypes.c_int32, _I32P] + [_VP] * 8 +
+                                                   [ctypes.c_int32, _I32P, _I32P, _VP, _VP, _VP],
     "gdn_plan_transaction": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _I32P],
     "gdn_run_transaction": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _I32P] + [_VP] * 8 +
                            [ctypes.c_int32, _I32P, _I32P, _VP, _VP, _VP, ctypes.c_size_t, _VP],
@@ -490,6 +493,29 @@ def gdn_chunked_prefill_with_checkpoints(dims: Dims, row_tokens, n_tail, q, k, v
         ctypes.byref(dims.c()), n_rows, _ip(T), chunk, _ip(nt), *toks, pp, n_slots, _ip(src), _ip(dst),
         cp, op, wp, wb, _stream(stream))
     _check("gdn_chunked_prefill_with_checkpoints", rc)
+
+
+STATIC_WS_BYTES = 128 << 20  # GDN_STATIC_WS_BYTES
+
+
+def gdn_chunked_prefill_with_checkpoints_static(dims: Dims, row_tokens, n_tail, q, k, v, a, b, A_log,
+                                                dt_bias, state_pool, src_slot, dst_slot, ckpt, o,
+                                                chunk: int = 64, stream=None) -> None:
+    """gdn_chunked_prefill_with_checkpoints on the library's own per-GPU workspace
+    (STATIC_WS_BYTES): the call allocates no device memory.  Calls that overlap on one
+    GPU share that workspace and must be ordered by the caller."""
+    T, nt, src, dst = _i32(row_tokens), _i32(n_tail), _i32(src_slot), _i32(dst_slot)
+    n_rows = T.size
+    if not (nt.size == src.size == dst.size == n_rows):
+        raise ValueError("per-row arrays differ in length")
+    N = int(T.sum())
+    toks, op = _token_ptrs(dims, N, q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    cp = _ckpt(dims, ckpt, n_rows)
+    rc = lib().gdn_chunked_prefill_with_checkpoints_static(
+        ctypes.byref(dims.c()), n_rows, _ip(T), chunk, _ip(nt), *toks, pp, n_slots, _ip(src), _ip(dst),
+        cp, op, _stream(stream))
+    _check("gdn_chunked_prefill_with_checkpoints_static", rc)
 
 
 def gdn_plan_transaction(dims: Dims, row_tokens) -> np.ndarray:

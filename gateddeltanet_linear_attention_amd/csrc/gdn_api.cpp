@@ -236,6 +236,40 @@ std::vector<int64_t> prefix(int32_t n_rows, const int32_t *ntok) {
   return cu;
 }
 
+// Chunked prefill with a caller workspace, or (use_static) with the library's static
+// per-GPU array; every argument is checked before the array is looked up.
+int chunked_prefill(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens, int32_t chunk,
+                    const int32_t *n_tail, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const float *a, const float *b, const float *A_log, const float *dt_bias,
+                    float *state_pool, int32_t n_slots, const int32_t *src_slot, const int32_t *dst_slot,
+                    float *ckpt, uint16_t *o, void *workspace, size_t ws_bytes, bool use_static,
+                    hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (chunk != gdn::kChunk) return GDN_E_UNSUPPORTED;
+  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
+  if (n_rows == 0) return GDN_OK;
+  std::vector<int64_t> cu;
+  if ((rc = check_packed(dims, n_rows, row_tokens, n_tail, q, k, v, a, b, A_log, dt_bias,
+                         state_pool, n_slots, src_slot, dst_slot, ckpt, o, cu)))
+    return rc;
+  std::vector<int32_t> rows(static_cast<size_t>(n_rows));
+  for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
+  const Sizes s = sizes_of(dims);
+  const size_t need = chunked_ws_bytes(dims, rows, row_tokens);
+  if (use_static) {
+    if (need > GDN_STATIC_WS_BYTES) return GDN_E_WORKSPACE;
+    if (gdn::static_workspace(&workspace, &ws_bytes) != hipSuccess) return GDN_E_HIP;
+  }
+  if ((rc = check_workspace(workspace, ws_bytes, need, state_pool, size_t(n_slots) * s.row_floats * 4,
+                            ckpt, ckpt ? size_t(n_rows) * s.ck_row_floats * 4 : 0, o,
+                            size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2)))
+    return rc;
+  gdn::ChunkArgs proto;
+  fill_chunk_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, ckpt, o, workspace);
+  return launch_chunked_rows(dims, proto, rows, cu, row_tokens, n_tail, src_slot, dst_slot, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -675,27 +709,20 @@ int gdn_chunked_prefill_with_checkpoints(
     const float *a, const float *b, const float *A_log, const float *dt_bias,
     float *state_pool, int32_t n_slots, const int32_t *src_slot, const int32_t *dst_slot,
     float *ckpt, uint16_t *o, void *workspace, size_t ws_bytes, void *stream) {
-  int rc = check_dims(dims);
-  if (rc) return rc;
-  if (chunk != gdn::kChunk) return GDN_E_UNSUPPORTED;
-  if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
-  if (n_rows == 0) return GDN_OK;
-  std::vector<int64_t> cu;
-  if ((rc = check_packed(dims, n_rows, row_tokens, n_tail, q, k, v, a, b, A_log, dt_bias,
-                         state_pool, n_slots, src_slot, dst_slot, ckpt, o, cu)))
-    return rc;
-  std::vector<int32_t> rows(static_cast<size_t>(n_rows));
-  for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
-  const Sizes s = sizes_of(dims);
-  const size_t need = chunked_ws_bytes(dims, rows, row_tokens);
-  if ((rc = check_workspace(workspace, ws_bytes, need, state_pool, size_t(n_slots) * s.row_floats * 4,
-                            ckpt, ckpt ? size_t(n_rows) * s.ck_row_floats * 4 : 0, o,
-                            size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2)))
-    return rc;
-  gdn::ChunkArgs proto;
-  fill_chunk_common(proto, dims, q, k, v, a, b, A_log, dt_bias, state_pool, ckpt, o, workspace);
-  return launch_chunked_rows(dims, proto, rows, cu, row_tokens, n_tail, src_slot, dst_slot,
-                             static_cast<hipStream_t>(stream));
+  return chunked_prefill(dims, n_rows, row_tokens, chunk, n_tail, q, k, v, a, b, A_log, dt_bias,
+                         state_pool, n_slots, src_slot, dst_slot, ckpt, o, workspace, ws_bytes, false,
+                         static_cast<hipStream_t>(stream));
+}
+
+int gdn_chunked_prefill_with_checkpoints_static(
+    const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens, int32_t chunk,
+    const int32_t *n_tail, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+    const float *a, const float *b, const float *A_log, const float *dt_bias,
+    float *state_pool, int32_t n_slots, const int32_t *src_slot, const int32_t *dst_slot,
+    float *ckpt, uint16_t *o, void *stream) {
+  return chunked_prefill(dims, n_rows, row_tokens, chunk, n_tail, q, k, v, a, b, A_log, dt_bias,
+                         state_pool, n_slots, src_slot, dst_slot, ckpt, o, nullptr, 0, true,
+                         static_cast<hipStream_t>(stream));
 }
 
 int gdn_run_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,

@@ -46,6 +46,10 @@
 // fp32 sums would lose ~1e-5 relative).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
+#include "gdn.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -753,6 +757,39 @@ hipError_t launch_d(const ChunkArgs &args, int n_chunks, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Workspace of gdn_chunked_prefill_with_checkpoints_static: a file-scope device array,
+// one copy per GPU, resident from the library's load until the process ends.  In host
+// code its name is only a stand-in for the symbol: kernels get the address that
+// hipGetSymbolAddress returns for the current GPU, never the name.
+__device__ __align__(256) float scratch[GDN_STATIC_WS_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];  // per GPU, filled on first use
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t static_workspace(void **ptr, size_t *bytes) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  *bytes = GDN_STATIC_WS_BYTES;
+  return hipSuccess;
+}
 
 hipError_t launch_chunked(const ChunkArgs &args, int d, int n_chunks, hipStream_t stream) {
   if (args.n_rows <= 0 || n_chunks <= 0) return hipSuccess;

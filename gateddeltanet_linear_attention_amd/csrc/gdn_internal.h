@@ -167,6 +167,9 @@ struct SelectArgs {
 hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream);
 hipError_t launch_select(const SelectArgs &args, hipStream_t stream);
 hipError_t launch_chunked(const ChunkArgs &args, int d, int n_chunks, hipStream_t stream);
+// The current GPU's copy of the static chunked workspace (GDN_STATIC_WS_BYTES): its
+// device address, looked up once per GPU and kept.
+hipError_t static_workspace(void **ptr, size_t *bytes);
 hipError_t launch_commit(const CommitArgs &args, hipStream_t stream);
 hipError_t launch_fold(const FoldArgs &args, int d, hipStream_t stream);
 

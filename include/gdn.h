@@ -43,7 +43,10 @@
  *    code but GDN_E_HIP nothing is launched and nothing is written.  GDN_E_HIP is the
  *    runtime refusing a launch; a call that launches several kernels (more than 64
  *    rows, or a chunked prefill) may have run the launches before it.
- *  - The library holds no mutable global state; calls are thread-safe.
+ *  - The library holds no mutable global state but one table: the per-GPU address of
+ *    the static workspace of gdn_chunked_prefill_with_checkpoints_static, filled once
+ *    per GPU under a lock.  Calls are thread-safe, except that calls of that entry point
+ *    overlapping on one GPU share its workspace (see there).
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -290,6 +293,30 @@ int gdn_chunked_prefill_with_checkpoints(
     float *state_pool, int32_t n_slots, const int32_t *src_slot,
     const int32_t *dst_slot, float *ckpt, uint16_t *o, void *workspace,
     size_t ws_bytes, void *stream);
+
+/*
+ * gdn_chunked_prefill_with_checkpoints_static -- gdn_chunked_prefill_with_checkpoints
+ * for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The caller still passes every input
+ * and output; the workspace is a device array that the library itself holds, one per
+ * GPU, GDN_STATIC_WS_BYTES long, resident from the library's load until the process
+ * ends.  The call allocates and frees nothing: on its first use on a GPU it looks up
+ * that GPU's copy of the array (hipGetSymbolAddress) and keeps the address.
+ * Same arguments, results and errors as gdn_chunked_prefill_with_checkpoints without
+ * workspace/ws_bytes, plus: GDN_E_WORKSPACE when gdn_chunked_workspace_bytes(...)
+ * exceeds GDN_STATIC_WS_BYTES (the call is refused, nothing runs), GDN_E_HIP if the
+ * lookup fails.  Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (two streams, two host threads) race and must be ordered by the
+ * caller.  Nothing in the array has to start at zero: each call writes every
+ * workspace value before it reads it.
+ */
+#define GDN_STATIC_WS_BYTES ((size_t)128 << 20) /* 128 MiB per GPU */
+int gdn_chunked_prefill_with_checkpoints_static(
+    const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens, int32_t chunk,
+    const int32_t *n_tail, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+    const float *a, const float *b, const float *A_log, const float *dt_bias,
+    float *state_pool, int32_t n_slots, const int32_t *src_slot,
+    const int32_t *dst_slot, float *ckpt, uint16_t *o, void *stream);
 
 /*
  * gdn_plan_transaction -- the per-row execution plan of a packed ragged batch

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function():
             "gdn_plan_transaction", "gdn_run_transaction", "gdn_status_str", "gdn_version",
             "gdn_commit_replay", "gdn_verify_tree", "gdn_verify_window_delta",
             "gdn_commit_delta", "gdn_verify_window_delta_fold", "gdn_verify_window_select",
-            "gdn_commit_select"} <= set(names)
+            "gdn_commit_select", "gdn_chunked_prefill_with_checkpoints_static"} <= set(names)
     lib = gb.lib()
     for n in names:
         assert hasattr(lib, n), "libgdn.so does not export %s" % n
@@ -404,6 +404,27 @@ def test_chunked_and_transaction_validation_codes():
         return lib.gdn_run_transaction(ctypes.byref(d), len(La), Lp, np_, *[b.ptr() for _ in range(7)], b.ptr(), 8,
                                        sp, dp, b.ptr(), b.ptr(), ws if ws is not None else b.ptr(), ws_bytes,
                                        ctypes.c_void_p(0))
+
+    def static(L, nt, src, dst, chunk=64):
+        La, Lp = _i32(L)
+        na, np_ = _i32(nt)
+        sa, sp = _i32(src)
+        da, dp = _i32(dst)
+        return lib.gdn_chunked_prefill_with_checkpoints_static(
+            ctypes.byref(d), len(La), Lp, chunk, np_, *[b.ptr() for _ in range(7)], b.ptr(), 8, sp, dp,
+            b.ptr(), b.ptr(), ctypes.c_void_p(0))
+
+    # the no-allocation form: the same checks, then a hard cap at the static array's size
+    # (refused before the array is looked up, so nothing here needs a GPU)
+    m = re.search(r"#define GDN_STATIC_WS_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    cap = int(m.group(1)) << int(m.group(2))
+    assert cap == gb.STATIC_WS_BYTES
+    assert static([100], [4], [0], [1], chunk=32) == -2
+    assert static([100], [5], [0], [1]) == -3
+    assert static([100, 50], [0, 0], [0, 1], [3, 3]) == -4
+    big = [2048] * 4
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), big) > cap
+    assert static(big, [0] * 4, [0, 1, 2, 3], [4, 5, 6, 7]) == -6
 
     assert tx([4, 100], [4, 0], [0, -1], [-1, 1], ws_bytes=100) == -6  # the long row needs workspace
     assert tx([4, 100], [5, 0], [0, -1], [-1, 1]) == -3                # checkpoints > k_max + 1

@@ -1,0 +1,74 @@
+"""GPU test of gdn_chunked_prefill_with_checkpoints_static, the chunked prefill that
+allocates nothing (its workspace is the library's own per-GPU device array), through
+the C ABI: two calls in a row, the second smaller, each bit-identical to
+gdn_chunked_prefill_with_checkpoints on a caller workspace (the same kernels) and
+within the oracle's tolerances.  The second call runs on whatever the first left in
+the shared array, so a value read before it is written would show up here.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gateddeltanet_linear_attention_amd import binding as gb
+from gateddeltanet_linear_attention_amd import synth
+from tests.gpu_common import (assert_o, assert_state, bits, dev_params, dev_tokens, dims_of, host,
+                              ref_qk, say)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+POISON = 0x7FC0DEAD
+
+
+def _case(lens, n_tail, src_rows, seed):
+    shape = synth.FULL
+    dims = dims_of(shape)
+    B, Hv, d = len(lens), shape.n_v_heads, shape.d
+    lens = np.asarray(lens, np.int32)
+    n_tail = np.asarray(n_tail, np.int32)
+    assert gb.gdn_chunked_workspace_bytes(dims, lens) <= gb.STATIC_WS_BYTES
+    g = synth.streams(seed, 3)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    tok = synth.tokens(g[1], shape, int(lens.sum()))
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    pool0 = (0.3 * torch.randn(2 * B, Hv, d, d, generator=gen)).cuda()
+    src = np.where(np.asarray(src_rows, bool), np.arange(B), -1).astype(np.int32)
+    dst = np.arange(B, 2 * B, dtype=np.int32)
+    t, p = dev_tokens(tok), dev_params(A_log, dt_bias)
+    out = {}
+    for kind in ("workspace", "static"):
+        pool = pool0.clone()
+        ckpt = torch.empty(B, 4, Hv, d, d, device="cuda")
+        ckpt.view(torch.int32).fill_(POISON)
+        o = torch.empty(int(lens.sum()), Hv, d, dtype=torch.bfloat16, device="cuda")
+        say("no-alloc case seed %d lens %s n_tail %s: %s entry point" % (seed, lens.tolist(), n_tail.tolist(), kind))
+        if kind == "workspace":
+            ws = torch.empty(gb.gdn_chunked_workspace_bytes(dims, lens), dtype=torch.uint8, device="cuda")
+            gb.gdn_chunked_prefill_with_checkpoints(dims, lens, n_tail, **t, **p, state_pool=pool, src_slot=src,
+                                                    dst_slot=dst, ckpt=ckpt, o=o, workspace=ws)
+        else:
+            gb.gdn_chunked_prefill_with_checkpoints_static(dims, lens, n_tail, **t, **p, state_pool=pool,
+                                                           src_slot=src, dst_slot=dst, ckpt=ckpt, o=o)
+        torch.cuda.synchronize()
+        out[kind] = (pool, ckpt, o)
+    (pw, cw, ow), (ps, cs, os_) = out["workspace"], out["static"]
+    assert torch.equal(bits(ps), bits(pw)), "states differ from the workspace entry point"
+    assert torch.equal(bits(cs), bits(cw)), "checkpoints differ from the workspace entry point"
+    assert torch.equal(os_.view(torch.int16), ow.view(torch.int16)), "outputs differ from the workspace entry point"
+    S0 = host(pool0[:B])
+    S0[src < 0] = 0.0
+    S_ref, ck_ref, o_ref = oracle.run_sequential(lens, *ref_qk(tok, False), tok.v, tok.a, tok.b, A_log, dt_bias,
+                                                 S0, n_tail=n_tail, n_slot=4)
+    mo = assert_o(host(os_), o_ref, "no-alloc outputs")
+    ms = assert_state(host(ps[B:]), S_ref, "no-alloc final states")
+    for r in range(B):
+        if n_tail[r]:
+            ms = max(ms, assert_state(host(cs[r, :n_tail[r]]), ck_ref[r, :n_tail[r]], "no-alloc checkpoints"))
+        assert bool((bits(cs[r, n_tail[r]:]) == POISON).all()), "row %d: extra checkpoint slot written" % r
+    say("no-alloc: bit-identical to the workspace form; max |do| %.2e, state rel %.2e" % (mo, ms))
+
+
+def test_static_workspace_matches_the_workspace_form_twice_the_second_smaller():
+    _case([300, 129], [4, 2], [True, False], seed=71)
+    _case([70], [3], [False], seed=72)
