@@ -15,35 +15,31 @@
 // Yang, Kautz & Hatamizadeh, ICLR 2025).  When q and k arrive unnormalised, K and Q
 // stand for diag(rk) K and diag(rq) Q (rk_t = 1/|k_t|, rq_t = 1/(|q_t| sqrt(d_k))):
 // the factors are applied to the exact bf16 products and folded into the diagonal
-// scalings above, so the matrix cores still see the bf16 inputs.  A checkpoint at in-chunk position j is
-// (1) truncated at s <= j: one more rank-64 product per requested position, so a
-// long prefill in a ragged batch still publishes the intermediate states a draft
-// rollback needs (the gap named in the onnxruntime-genai pull request "Run chained
-// MTP drafting in the batch Engine", section "Correctness fix").
+// scalings above, so the matrix cores still see the bf16 inputs.  A checkpoint at
+// in-chunk position j is (1) truncated at s <= j: one more rank-64 product per
+// requested position, so a long prefill in a ragged batch still publishes the
+// intermediate states a draft rollback needs (the gap named in the onnxruntime-genai
+// pull request "Run chained MTP drafting in the batch Engine", section "Correctness fix").
 //
-// Four kernels, same stream:
-//   chunk_prep_kernel  one block per (chunk, value head), all chunks in parallel:
+// Two kernels, same stream:
+//   chunk_prep_kernel   one block per (chunk, value head), all chunks in parallel:
 //       gates, fp64 prefix sum of g, K K^T and Q K^T, forward substitution for T,
-//       W, U', K^T and the decay factors -> workspace.
-//   chunk_scan_kernel  one block per (row, value head, 16 state rows), chunks in
-//       order, only the sequential part: U = U' - W S_c^T and the state carry (the
-//       state tile stays in LDS; the next chunk's operands are fetched during the
-//       current one); each chunk's start state and U^T -> workspace.
-//   chunk_out_kernel   one block per (chunk, value head, half of the value
-//       channels), all in parallel: the outputs O.
-//   chunk_ckpt_kernel  one block per (row, tail checkpoint, value head, 16 value
-//       rows): the requested checkpoints, from the recorded chunk state.
-// The contractions run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, 157 TF dense
-// on MI355X): the state tolerance (relative 1e-4) rules out rounding the fp32 operands
-// T, W, U, S to bf16.  Two products run on the bf16 cores at fp32 accuracy: K K^T and
-// Q K^T (bf16 inputs, exact products), and the carry's U^T diag(.) K, whose K is bf16
-// and whose fp32 factor is split into three bf16 parts that sum to it to within a unit
-// in its last place.  A wave loads all operand fragments of a product
-// before its first matrix instruction and interleaves independent accumulation
-// chains, so global-memory latency is paid once per phase, not once per k step.
-// Decays are formed only as differences G_t - G_s with s <= t, from an fp64 prefix
-// sum (|G| reaches hundreds within a chunk under strong decay, where differences of
-// fp32 sums would lose ~1e-5 relative).
+//       W, U', P = Gamma o Q K^T, K^T and the decay factors -> workspace.
+//   chunk_chain_kernel  one block per (row, value head, 16 value channels), chunks in
+//       order: U = U' - W S_c^T, the outputs O of the block's channels, the state
+//       carry, the requested checkpoints and the final state.  The state tile never
+//       leaves the block: each lane keeps its part in registers, and LDS holds the
+//       bf16 parts that the products read.
+// Every product runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, 2.5 PF dense
+// on MI355X) at fp32 accuracy: an fp32 operand enters as three bf16 parts that sum to it
+// to within 2^-24 of its magnitude (hi, the round of what hi leaves, the round of what
+// both leave; every subtraction exact), and the products of the parts that matter are
+// accumulated in fp32 -- three when the other operand is exactly bf16 (K, Q, V), six when
+// both are fp32 (the bf16x3 split: Henry, Tang & Heinecke, "Leveraging the bfloat16
+// Artificial Intelligence Datatype for Higher-Precision Computations", ARITH 2019).  The
+// prep kernel's T products run on the fp32 matrix cores.  Decays are formed only as
+// differences G_t - G_s with s <= t, from an fp64 prefix sum (|G| reaches hundreds within a
+// chunk under strong decay, where differences of fp32 sums would lose ~1e-5 relative).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -57,11 +53,16 @@ namespace gdn {
 namespace {
 
 constexpr int C = 64;       // chunk length
-constexpr int VT = 16;      // state rows per scan block
+constexpr int VT = 16;      // state rows (value channels) per chain block
 constexpr int LDC = C + 4;  // padded LDS row length (floats) for C-wide rows
-constexpr int LDB = C + 4;  // padded LDS row length (bf16) for C-wide rows
+constexpr int LDB = C + 4;  // padded LDS row length (bf16) for C-wide rows (prep)
+constexpr int LDP = C + 8;  // row length (bf16) of C-wide part buffers: 16-B aligned rows
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.0f, 0.0f, 0.0f, 0.0f}; }
 __device__ __forceinline__ float4 zf4() { return make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
@@ -69,7 +70,7 @@ __device__ __forceinline__ float4 mul4(float4 a, float4 b) {
   return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
 }
 
-// One 16-wide k block of acc(16x16) += A(16 x K) * B(K x 16) on the matrix cores.
+// One 16-wide k block of acc(16x16) += A(16 x K) * B(K x 16) on the fp32 matrix cores.
 // Lane l (r = l % 16, g = l / 16) holds a = A[r][kb+4g .. kb+4g+3] and
 // b = B[kb+4g .. kb+4g+3][r]: a permutation of k inside the block, the same on
 // both sides.  After all k blocks, lane l holds C[4g + v][r] in acc[v].
@@ -81,56 +82,78 @@ __device__ __forceinline__ floatx4 mma4(floatx4 acc, float4 a, float4 b) {
   return acc;
 }
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+// acc(16x16) += A(16 x 32) * B(32 x 16) on the bf16 matrix cores: lane (r, g) gives
+// A[r][8g .. 8g+7] and B[8g .. 8g+7][r]; lane (r, g) then holds C[4g + v][r] in acc[v].
+__device__ __forceinline__ floatx4 mfma_bf16(bf16x8 a, bf16x8 b, floatx4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
 
-// x = hi + mid + lo to fp32 precision in three bf16 parts, each the round to nearest of
-// what the parts before it leave (every subtraction is exact), written as the bits of
-// the lane's four values per part.  A bf16 matrix product of these parts against an
-// exactly-bf16 operand then reproduces the fp32 product to fp32 accuracy (the bf16x3
-// split: Henry, Tang & Heinecke, "Leveraging the bfloat16 Artificial Intelligence
-// Datatype for Higher-Precision Computations", ARITH 2019).
-struct Parts4 {  // one 4-token piece in three parts, bf16 bits
+// Two fp32 values to bf16 bits, round to nearest even (v_cvt_pk_bf16_f32), packed
+// low-first.
+__device__ __forceinline__ uint32_t bf16x2_rn(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, bf16x2));
+}
+
+// The three bf16 parts of two values, each part the round of what the parts before it
+// leave; every subtraction is exact, and hi + mid + lo equals the value to within
+// 2^-24 of its magnitude.
+__device__ __forceinline__ void split_pair(float x, float y, uint32_t &h, uint32_t &m, uint32_t &l) {
+  h = bf16x2_rn(x, y);
+  const float rx = x - __uint_as_float(h << 16), ry = y - __uint_as_float(h & 0xFFFF0000u);
+  m = bf16x2_rn(rx, ry);
+  l = bf16x2_rn(rx - __uint_as_float(m << 16), ry - __uint_as_float(m & 0xFFFF0000u));
+}
+
+struct Parts8 {  // eight values as three bf16x8 matrix operands
+  bf16x8 h, m, l;
+};
+struct Parts4 {  // four values as three 8-byte pieces (bf16 bits)
   uint2 h, m, l;
 };
-// the three parts of one value, packed at bit 16 * `hi` of the three words
-__device__ __forceinline__ void split3_into(float v, int hi, uint32_t &h, uint32_t &m, uint32_t &l) {
-  const uint32_t bh = to_bf16(v);
-  const float r1 = v - __uint_as_float(bh << 16);
-  const uint32_t bm = to_bf16(r1);
-  const uint32_t bl = to_bf16(r1 - __uint_as_float(bm << 16));
-  h |= bh << (16 * hi);
-  m |= bm << (16 * hi);
-  l |= bl << (16 * hi);
-}
-__device__ __forceinline__ Parts4 split3x4(float4 x) {
-  uint32_t h0 = 0, m0 = 0, l0 = 0, h1 = 0, m1 = 0, l1 = 0;
-  split3_into(x.x, 0, h0, m0, l0);
-  split3_into(x.y, 1, h0, m0, l0);
-  split3_into(x.z, 0, h1, m1, l1);
-  split3_into(x.w, 1, h1, m1, l1);
+__device__ __forceinline__ Parts4 split4(float4 a) {
+  uint32_t h0, m0, l0, h1, m1, l1;
+  split_pair(a.x, a.y, h0, m0, l0);
+  split_pair(a.z, a.w, h1, m1, l1);
   return Parts4{make_uint2(h0, h1), make_uint2(m0, m1), make_uint2(l0, l1)};
 }
 
-// Two 4-token pieces (bf16 bits) as one 8-wide operand of v_mfma_f32_16x16x32_bf16.
-__device__ __forceinline__ bf16x8 pieces8(uint2 a, uint2 b) {
-  return __builtin_bit_cast(bf16x8, u32x4v{a.x, a.y, b.x, b.y});
+// acc += A B with A in parts and B exactly bf16 (three products, smallest first)
+__device__ __forceinline__ floatx4 mma3a(floatx4 acc, const Parts8 &a, bf16x8 b) {
+  acc = mfma_bf16(a.l, b, acc);
+  acc = mfma_bf16(a.m, b, acc);
+  return mfma_bf16(a.h, b, acc);
+}
+// acc += A B with A exactly bf16 and B in parts
+__device__ __forceinline__ floatx4 mma3b(floatx4 acc, bf16x8 a, const Parts8 &b) {
+  acc = mfma_bf16(a, b.l, acc);
+  acc = mfma_bf16(a, b.m, acc);
+  return mfma_bf16(a, b.h, acc);
+}
+// acc += A B with both in parts: the six products whose parts reach 2^-16 of the
+// leading one (the three below that are dropped: 2^-24 relative)
+__device__ __forceinline__ floatx4 mma6(floatx4 acc, const Parts8 &a, const Parts8 &b) {
+  acc = mfma_bf16(a.l, b.h, acc);
+  acc = mfma_bf16(a.m, b.m, acc);
+  acc = mfma_bf16(a.h, b.l, acc);
+  acc = mfma_bf16(a.m, b.h, acc);
+  acc = mfma_bf16(a.h, b.m, acc);
+  return mfma_bf16(a.h, b.h, acc);
 }
 
-// acc(16x16) += A(16 x 64 tokens) * B(64 tokens x 16) with A given as the bf16x3 parts of
-// its four 4-token pieces (lane (r, g): A[r][16 kb + 4 g + e]) and B exactly bf16 in
-// the same pieces (B[16 kb + 4 g + e][r]): each 32-wide matrix instruction takes pieces
-// kb = 2 m, 2 m + 1 (a permutation of the token index, the same on both sides), parts
-// hi, mid, lo in that order.  Output layout as mma4's.
-__device__ __forceinline__ floatx4 mma_bf16x3_32(floatx4 acc, Parts4 a0, Parts4 a1, uint2 b0, uint2 b1) {
-  const bf16x8 b = pieces8(b0, b1);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pieces8(a0.h, a1.h), b, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pieces8(a0.m, a1.m), b, acc, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(pieces8(a0.l, a1.l), b, acc, 0, 0, 0);
+// Part buffers in LDS: three planes of rows of bf16.  A lane writes four consecutive
+// values of one row (8 B per plane) and reads eight (16 B per plane).
+template <int PITCH>
+__device__ __forceinline__ void lds_put4(uint16_t *buf, int plane_elems, int row, int col, const Parts4 &p) {
+  uint16_t *q = buf + row * PITCH + col;
+  *reinterpret_cast<uint2 *>(q) = p.h;
+  *reinterpret_cast<uint2 *>(q + plane_elems) = p.m;
+  *reinterpret_cast<uint2 *>(q + 2 * plane_elems) = p.l;
 }
-__device__ __forceinline__ floatx4 mma_bf16x3_64(floatx4 acc, Parts4 a0, Parts4 a1, Parts4 a2, Parts4 a3,
-                                                 uint2 b0, uint2 b1, uint2 b2, uint2 b3) {
-  return mma_bf16x3_32(mma_bf16x3_32(acc, a0, a1, b0, b1), a2, a3, b2, b3);
+template <int PITCH>
+__device__ __forceinline__ Parts8 lds_get8(const uint16_t *buf, int plane_elems, int row, int col) {
+  const uint16_t *q = buf + row * PITCH + col;
+  return Parts8{*reinterpret_cast<const bf16x8 *>(q), *reinterpret_cast<const bf16x8 *>(q + plane_elems),
+                *reinterpret_cast<const bf16x8 *>(q + 2 * plane_elems)};
 }
 
 // bf16 operand of v_mfma_f32_16x16x32_bf16 for 32-wide k block kb of row t of a
@@ -153,33 +176,45 @@ __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
   return row;
 }
 
-// Workspace of one (chunk, value head): W [C][D], U'^T [D][C], P [C][C], G [C] fp64,
-// eG[t] = e^{G_t}, eL[s] = e^{G_{n-1} - G_s} rk_s (s < n, else 0), K^T [D][C] bf16 with
-// each row's tokens in kt_pos order (below), the chunk's start state Sc [D][D], U^T
-// [D][C], and the factors rk, rq [C] that scale each token's k and q (1 unless q/k
-// are normalised in the kernels).
-// Token m = 16 kb + 4 g + e of a chunk sits at 16 g + 4 kb + e of a stored K^T row, so
-// the MFMA lane group g finds its four 4-token pieces (kb = 0..3) in 32 contiguous bytes.
-__device__ __forceinline__ int kt_pos(int m) { return 16 * ((m >> 2) & 3) + 4 * (m >> 4) + (m & 3); }
-
+// Workspace of one (chunk, value head).  The chain kernel's operands are stored in
+// fragment order: every 16-byte piece a lane of a wave takes for one matrix instruction
+// sits at piece index lane of a 1 KiB block, so each of the chain kernel's loads reads
+// 1 KiB contiguous (a wave reading 16 rows of 64 bytes instead measured ~3x slower per
+// load, which bounded the chain).  With token tile tt (16 tokens), 32-wide block kb,
+// bf16 part plane p (hi, mid, lo: their sum is the fp32 value to within 2^-24 of it),
+// 16-wide state column tile nt and lane l = r + 16 g:
+//   WF [tt][kb][p][l]  W[16 tt + r][32 kb + 8 g + e]      (e = 0..7, bf16 parts)
+//   QF [tt][kb][l]     Q[16 tt + r][32 kb + 8 g + e]      (bf16, the input q)
+//   KF [nt][kb][l]     K[32 kb + 8 g + e][16 nt + r]      (bf16, kb < 2: tokens)
+//   PF [tt][kb][p][l]  P[16 tt + r][32 kb + 8 g + e]      (bf16 parts, kb < 2)
+//   UF [nt][tt][l]     U'[16 tt + 4 g + v][16 nt + r]     (fp32, v = 0..3)
+// with P[t][s] = e^{G_t - G_s} rq_t rk_s q_t.k_s for s <= t, else 0; then G [C] fp64,
+// eG[t] = e^{G_t}, eL[s] = e^{G_{n-1} - G_s} rk_s (s < n, else 0), rk[s] (the factor
+// token s's key is scaled by) and eGq[t] = e^{G_t} rq_t (the factor of the output's state
+// term); rk = rq = 1 unless q/k are normalised in the kernels.  For d = 16 the pieces of
+// lanes g >= 2 of WF lie past the head width and are not written (the chain kernel reads
+// zeros in their place); QF holds zeros there.
 template <int D>
 struct Ws {
-  float *W, *U, *P, *eG, *eL, *Sc, *Ut, *rk, *rq;
+  static constexpr int NK = D >= 32 ? D / 32 : 1;  // 32-wide blocks over d
+  static constexpr int NT = D / 16;                // 16-wide state column tiles
+  uint16_t *WF, *QF, *KF, *PF;
+  float *UF, *eG, *eL, *rk, *eGq;
   double *G;
-  uint16_t *Kt;
   __device__ Ws(float *base) {
-    W = base;
-    U = base + C * D;
-    P = base + 2 * C * D;
-    G = reinterpret_cast<double *>(base + 2 * C * D + C * C);
-    eG = base + 2 * C * D + C * C + 2 * C;
+    WF = reinterpret_cast<uint16_t *>(base);
+    QF = WF + 4 * NK * 3 * 512;
+    KF = QF + 4 * NK * 512;
+    PF = KF + NT * 2 * 512;
+    UF = reinterpret_cast<float *>(PF + 4 * 2 * 3 * 512);
+    G = reinterpret_cast<double *>(UF + NT * 4 * 256);
+    eG = reinterpret_cast<float *>(G + C);
     eL = eG + C;
-    Kt = reinterpret_cast<uint16_t *>(eL + C);
-    Sc = eL + C + D * C / 2;
-    Ut = Sc + D * D;
-    rk = Ut + D * C;
-    rq = rk + C;
+    rk = eL + C;
+    eGq = rk + C;
   }
+  // element offset of lane l's 16-byte piece in 1-KiB fragment block `blk` of a bf16 array
+  static __device__ __forceinline__ int piece(int blk, int l) { return (blk * 64 + l) * 8; }
 };
 
 // q/k normalisation of the fused input mode: x / sqrt(sum x^2 + eps), q also by
@@ -295,20 +330,25 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     ws.eL[lane] = lane < n ? float(exp(Gl - G)) * rk : 0.0f;
     sSK[lane] *= rk;
     ws.rk[lane] = rk;
-    ws.rq[lane] = sRq[lane];
+    ws.eGq[lane] = float(exp(G)) * sRq[lane];
   }
-  // K^T to the workspace for the scan and checkpoint kernels: row d is 64 contiguous
-  // bf16, 4-token pieces placed by kt_pos
-  for (int idx = tid; idx < D * (C / 4); idx += 256) {
-    const int d = idx / (C / 4), m4 = (idx % (C / 4)) * 4;
-    *reinterpret_cast<uint2 *>(ws.Kt + d * C + kt_pos(m4)) = *reinterpret_cast<const uint2 *>(sKt + d * LDB + m4);
+  // K^T in fragment order for the chain kernel's carry: piece (nt, kb, l = r + 16 g) is
+  // K^T[16 nt + r][32 kb + 8 g .. +7]
+  for (int idx = tid; idx < (D / 16) * 2 * 64; idx += 256) {
+    const int nt = idx >> 7, kb = (idx >> 6) & 1, l = idx & 63;
+    const uint16_t *src = sKt + (16 * nt + (l & 15)) * LDB + 32 * kb + 8 * (l >> 4);  // 8-B aligned rows
+    const uint2 lo = *reinterpret_cast<const uint2 *>(src), hi = *reinterpret_cast<const uint2 *>(src + 4);
+    *reinterpret_cast<uint4 *>(ws.KF + idx * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 
   // 2. K K^T -> A (strictly lower, scaled) and Q K^T -> P (lower with diagonal) on
   //    the bf16 matrix cores: K and Q are bf16, so every product is exact in fp32 and
   //    only the fp32 accumulation rounds.  Wave w owns row block w: it loads the
   //    fragments once (its Q rows, the K rows of all four blocks), computes tiles
-  //    (w, tj <= w) and writes zeros to the tiles right of the diagonal.
+  //    (w, tj <= w) and writes zeros to the tiles right of the diagonal.  Q K^T is
+  //    formed transposed (lane: token 16 w + r16, keys 16 tj + 4 g4 + v), so each lane
+  //    holds 4 consecutive columns of a P row and P goes out in parts, in fragment order.
+  //    The wave's Q fragments are the chain kernel's: stored as they are.
   {
     constexpr int NK32 = (D + 31) / 32;  // 32-wide k blocks over d (D = 16: half of one)
     bf16x8 fk[4][NK32], fa[NK32], fq[NK32];  // fa: this wave's K rows (register arrays
@@ -318,6 +358,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
       fa[kb] = frag32(Kc, ldqk, 16 * w + r16, kb);
 #pragma unroll
       for (int tj = 0; tj < 4; ++tj) fk[tj][kb] = frag32(Kc, ldqk, 16 * tj + r16, kb);
+      *reinterpret_cast<bf16x8 *>(ws.QF + Ws<D>::piece(w * NK32 + kb, lane)) = fq[kb];
     }
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
@@ -326,21 +367,30 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
 #pragma unroll
         for (int kb = 0; kb < NK32; ++kb) {
           kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kb], fk[tj][kb], kk, 0, 0, 0);
-          qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fq[kb], fk[tj][kb], qk, 0, 0, 0);
+          qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[tj][kb], fq[kb], qk, 0, 0, 0);
         }
       }
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int t = 16 * w + 4 * g4 + v, s = 16 * tj + r16;
-        float av = 0.0f, pv = 0.0f;
-        if (s <= t) {
-          const float dec = expf(float(sG[t] - sG[s]));
-          pv = dec * (qk[v] * sRq[t] * sRk[s]);
-          if (s < t) av = sBeta[t] * dec * (kk[v] * sRk[t] * sRk[s]);
-        }
+        float av = 0.0f;
+        if (s < t) av = sBeta[t] * expf(float(sG[t] - sG[s])) * (kk[v] * sRk[t] * sRk[s]);
         if (tj <= w) sA[t * LDC + s] = av;  // the upper blocks of sA hold T below
-        ws.P[t * C + s] = pv;
       }
+      float pv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = 16 * w + r16, s = 16 * tj + 4 * g4 + v;
+        pv[v] = s <= t ? expf(float(sG[t] - sG[s])) * (qk[v] * sRq[t] * sRk[s]) : 0.0f;
+      }
+      // lane (r16, g4) holds P[16 w + r16][16 tj + 4 g4 + 0..3]: half of the 16-byte piece
+      // of lane r16 + 16 (2 (tj & 1) + g4 / 2) in block (w, tj / 2, part)
+      const Parts4 pp = split4(make_float4(pv[0], pv[1], pv[2], pv[3]));
+      const int l2 = r16 + 16 * (2 * (tj & 1) + (g4 >> 1)), half = 4 * (g4 & 1);
+      const int pb = (w * 2 + (tj >> 1)) * 3;
+      *reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 0, l2) + half) = pp.h;
+      *reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 1, l2) + half) = pp.m;
+      *reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 2, l2) + half) = pp.l;
     }
   }
   lds_barrier();
@@ -404,8 +454,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     }
   }
 
-  // 4. W = T diag(beta e^G) K and U' = T diag(beta) V.  Wave w owns column tiles
-  //    {2w, 2w+1} of every row tile (T is lower triangular: k < 16(ti+1)).
+  // 4. W = T diag(beta e^G) K (stored as three bf16 parts) and U' = T diag(beta) V.
+  //    Wave w owns column tiles {2w, 2w+1} of every row tile (T is lower triangular:
+  //    k < 16(ti+1)).
   for (int nt = 2 * w; nt < 2 * w + 2 && nt < D / 16; ++nt) {
     for (int ti = 0; ti < 4; ++ti) {
       floatx4 wa = zero4(), ua = zero4();
@@ -419,78 +470,108 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
         const int d = 16 * nt + r16;
         const float4 kt = unpack_bf16x4(*reinterpret_cast<const uint2 *>(sKt + d * LDB + k0));
         const float4 vt = unpack_bf16x4(*reinterpret_cast<const uint2 *>(sVt + d * LDB + k0));
-        wa = mma4(wa, mul4(tr, sk), kt);
+        wa = mma4(wa, kt, mul4(tr, sk));  // W^T: lane holds W[16 ti + r16][16 nt + 4 g4 + v]
         ua = mma4(ua, mul4(tr, sb), vt);
       }
-      const int d = 16 * nt + r16;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) ws.W[(16 * ti + 4 * g4 + v) * D + d] = wa[v];
-      // U'^T: the lane's 4 tokens are contiguous
-      *reinterpret_cast<float4 *>(ws.U + d * C + 16 * ti + 4 * g4) = make_float4(ua[0], ua[1], ua[2], ua[3]);
+      // W in parts, in fragment order: lane (r16, g4) holds W[16 ti + r16][16 nt + 4 g4 + 0..3],
+      // half of the piece of lane r16 + 16 (2 (nt & 1) + g4 / 2) in block (ti, nt / 2, part)
+      const Parts4 wp = split4(make_float4(wa[0], wa[1], wa[2], wa[3]));
+      const int l2 = r16 + 16 * (2 * (nt & 1) + (g4 >> 1)), half = 4 * (g4 & 1);
+      const int wb = (ti * Ws<D>::NK + (nt >> 1)) * 3;
+      *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 0, l2) + half) = wp.h;
+      *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 1, l2) + half) = wp.m;
+      *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 2, l2) + half) = wp.l;
+      // U': lane (r16, g4) holds U'[16 ti + 4 g4 + v][16 nt + r16], the piece of block (nt, ti)
+      *reinterpret_cast<float4 *>(ws.UF + ((nt * 4 + ti) * 64 + lane) * 4) = make_float4(ua[0], ua[1], ua[2], ua[3]);
     }
   }
 }
 
-// Operands of one chunk that a scan wave needs: its W rows, its U' values, the
-// carry's decay factors and the K^T fragments of its state column tiles.
+// One chunk's operands of a chain wave (w, lane = r16 + 16 g4), fetched a chunk ahead:
+// every load reads one 1-KiB fragment block of the workspace.
 template <int D>
-struct ScanFrag {
-  static constexpr int NKB = D / 16;
-  static constexpr int NT_W = (D / 16 + 3) / 4;
-  float4 wf[NKB], el;
-  uint2 kp[NT_W][4];  // K^T pieces kb = 0..3 of each column tile, bf16 bits
-  float4 up;
-  float e_last;
-  __device__ void load(const Ws<D> &ws, int n, int w, int r16, int g4, int i0) {
-    const int t_me = 16 * w + r16;
+struct ChainOps {
+  static constexpr int NK = Ws<D>::NK;
+  static constexpr int NT = (D / 16 + 3) / 4;  // 16-wide state column tiles per wave
+  Parts8 w[NK];       // W[16 w + r16][32 kb + 8 g4 + 0..7] in parts (zero past d)
+  bf16x8 q[NK];       // Q[16 w + r16][32 kb + 8 g4 + 0..7] (zero past d)
+  bf16x8 kt[NT][2];   // K^T[16 nt + r16][32 kb + 8 g4 + 0..7], nt = w + 4 q
+  Parts8 p[2];        // P[16 w + r16][32 kb + 8 g4 + 0..7] in parts
+  float4 up;          // U'[16 w + 4 g4 + v][i0 + r16], v = 0..3
+  float4 el;          // eL[16 w + 4 g4 + v]
+  float egq;          // eGq[16 w + r16]
+  float e_last;       // e^{G_{n-1}}
+  __device__ void load(const Ws<D> &ws, int n, int wv, int lane, int tile) {
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4v{0u, 0u, 0u, 0u});
+    auto frag = [&](const uint16_t *a, int blk) { return *reinterpret_cast<const bf16x8 *>(a + Ws<D>::piece(blk, lane)); };
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      wf[kb] = *reinterpret_cast<const float4 *>(ws.W + t_me * D + 16 * kb + 4 * g4);
-    // the carry's decay factors of the 4 tokens whose U this lane writes
-    el = *reinterpret_cast<const float4 *>(ws.eL + 16 * w + 4 * g4);
-#pragma unroll
-    for (int q = 0; q < NT_W; ++q) {
-      // a wave without a q-th column tile loads the last tile and never uses it:
-      // unconditional loads keep the prefetch free of branches, whose waits would
-      // expose its latency
-      const int nt = min(w + 4 * q, D / 16 - 1);
-      const uint4 *kr = reinterpret_cast<const uint4 *>(ws.Kt + (16 * nt + r16) * C + 16 * g4);
-      const uint4 k01 = kr[0], k23 = kr[1];  // pieces kb = 0, 1 and 2, 3 (kt_pos order)
-      kp[q][0] = make_uint2(k01.x, k01.y);
-      kp[q][1] = make_uint2(k01.z, k01.w);
-      kp[q][2] = make_uint2(k23.x, k23.y);
-      kp[q][3] = make_uint2(k23.z, k23.w);
+    for (int kb = 0; kb < NK; ++kb) {
+      const int b3 = (wv * NK + kb) * 3;
+      w[kb] = 32 * kb + 8 * g4 < D ? Parts8{frag(ws.WF, b3), frag(ws.WF, b3 + 1), frag(ws.WF, b3 + 2)}
+                                   : Parts8{z, z, z};
+      q[kb] = frag(ws.QF, wv * NK + kb);
     }
-    up = *reinterpret_cast<const float4 *>(ws.U + (i0 + r16) * C + 16 * w + 4 * g4);
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) {
+      // a wave without a qt-th tile loads the last one and never uses it: unconditional
+      // loads keep the prefetch free of branches
+      const int nt = min(wv + 4 * qt, D / 16 - 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kt[qt][kb] = frag(ws.KF, nt * 2 + kb);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int b3 = (wv * 2 + kb) * 3;
+      p[kb] = Parts8{frag(ws.PF, b3), frag(ws.PF, b3 + 1), frag(ws.PF, b3 + 2)};
+    }
+    up = *reinterpret_cast<const float4 *>(ws.UF + ((tile * 4 + wv) * 64 + lane) * 4);
+    el = *reinterpret_cast<const float4 *>(ws.eL + 16 * wv + 4 * g4);
+    egq = ws.eGq[16 * wv + r16];
     e_last = ws.eG[n - 1];
   }
 };
 
-// A wave keeps two chunks' operands live (170 VGPRs), capped so that two blocks share
-// a CU: one 2048-token row has 256 (unit, tile) chains, one per CU, but a transaction
-// with several long prefill rows has more chains than CUs, and two of them then run
-// on each CU at once (the 16-row mixed transaction with 4 prefills of 883-3702 tokens
-// took 1012-1025 instead of 1075-1090 us; the single row is unchanged).
+// A 16-byte store that bypasses the caches on its way to memory (dense states are
+// written once and not read back by this call).
+__device__ __forceinline__ void store_nt(float *dst, float4 x) {
+  __builtin_nontemporal_store(floatx4{x.x, x.y, x.z, x.w}, reinterpret_cast<floatx4 *>(dst));
+}
+__device__ __forceinline__ void store_nt(float *dst, floatx4 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<floatx4 *>(dst));
+}
+
+// The chain of one (row, value head, 16 value channels i0..i0+15): chunks in order.
+// Wave w owns tokens 16w..16w+15 of each chunk (U, outputs) and state column tiles
+// w and w + 4 (the carry).  Per chunk:
+//   A  U = U' - W S_c^T for the wave's tokens (S_c's parts from LDS, W split in
+//      registers); U^T diag(e^{G_n - G}) and U^T in parts -> LDS; barrier.
+//   B  the carry S_{c+1} = e^{G_n} S_c + U^T diag(.) K on the wave's column tiles, the
+//      outputs O = diag(e^G rq) Q S_c^T + P U of its tokens, the checkpoints this
+//      chunk holds, and S_{c+1}'s parts -> LDS; barrier.
+// The state stays in registers in the carry's output layout (lane (r16, g4) of wave w
+// holds S[i0 + r16][16 nt + 4 g4 + v]), which is also where the next carry's
+// accumulator starts from; LDS holds the parts of S_c that the U and output products
+// read, in two buffers used alternately (chunk c reads one while S_{c+1} is written to
+// the other).  Blocks of one (row, head) unit are spaced 8 apart in launch order, which
+// places all its tiles on one of the 8 chiplets and lets them share that L2's copy of
+// the chunk operands (W, K^T, P).
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void chunk_scan_kernel(ChunkArgs args, int n_units) {
-  constexpr int LDS_ = D + 4;
+__global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_units) {
   constexpr int TILES = D / VT;
-  constexpr int NKB = D / 16;
-  constexpr int NT_W = (D / 16 + 3) / 4;  // state column tiles per wave
+  constexpr int NK = ChainOps<D>::NK;
+  constexpr int NT = ChainOps<D>::NT;
+  constexpr int LDS_ = D + 8;     // S part row (bf16): 16-B aligned rows
+  constexpr int SPL = VT * LDS_;  // elements per plane of S parts
+  constexpr int UPL = VT * LDP;   // elements per plane of U parts
   constexpr size_t UNIT = size_t(D) * D;
-  // state tile (row i, column d), double-buffered: chunk c reads sSb[c & 1] and writes
-  // the next state to sSb[(c + 1) & 1], so no barrier is needed between the last read
-  // of a state and the write of the next one
-  __shared__ __attribute__((aligned(16))) float sSb[2][VT * LDS_];
-  // U^T diag(e^{G_n - G}) of this tile (row i, token s) as its three bf16x3 parts
-  __shared__ __attribute__((aligned(16))) uint16_t sUp[3][VT * LDB];
+  __shared__ __attribute__((aligned(16))) uint16_t sS[2][3 * SPL];  // S_c in parts: row i, column d
+  __shared__ __attribute__((aligned(16))) uint16_t sUc[3 * UPL];    // (U^T diag(e^{G_n - G})): row i, token s
+  __shared__ __attribute__((aligned(16))) uint16_t sUr[3 * UPL];    // U^T
+  __shared__ __attribute__((aligned(16))) uint16_t sUt[3 * UPL];    // U^T diag(e^{G_j - G}) of a checkpoint
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  // Blocks of one (row, head) unit are spaced 8 apart in launch order, which places
-  // all its tiles on one of the 8 chiplets and lets them share that L2's copy of the
-  // chunk operands (W, K^T).
   const int b = blockIdx.x;
   const int k8 = b >> 3;
   const int tile = k8 % TILES;
@@ -503,238 +584,149 @@ void chunk_scan_kernel(ChunkArgs args, int n_units) {
   const int nch = (L + C - 1) / C;
   const int n_v = args.n_v;
   const int src = args.src[row], dst = args.dst[row];
+  const int tail0 = L - args.n_tail[row];  // first position with a checkpoint
   auto ws_of = [&](int c) {
     return Ws<D>(args.ws + (int64_t(args.chunk0[row] + c) * n_v + h) * ChunkArgs::ws_unit_floats(D));
   };
+  auto has_tile = [&](int q) { return w + 4 * q < D / 16; };
+  // parts of S_c for 32-wide d block kb (lane (r16, g4): S_c[i0 + r16][32 kb + 8 g4 + e])
+  auto s_parts = [&](const uint16_t *buf, int kb) {
+    const int col = 32 * kb + 8 * g4;
+    if (col < D) return lds_get8<LDS_>(buf, SPL, r16, col);
+    const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4v{0u, 0u, 0u, 0u});
+    return Parts8{z, z, z};
+  };
 
-  for (int idx = tid; idx < VT * (D / 4); idx += 256) {
-    const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-    float4 x = zf4();
-    if (src >= 0)
-      x = *reinterpret_cast<const float4 *>(args.state_in + (int64_t(src) * n_v + h) * UNIT +
-                                            int64_t(i0 + i) * D + d4);
-    *reinterpret_cast<float4 *>(sSb[0] + i * LDS_ + d4) = x;
+  // the start state: registers, and its parts in LDS
+  float4 S[NT];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    S[q] = zf4();
+    if (src >= 0 && has_tile(q))
+      S[q] = *reinterpret_cast<const float4 *>(args.state_in + (int64_t(src) * n_v + h) * UNIT +
+                                               int64_t(i0 + r16) * D + 16 * (w + 4 * q) + 4 * g4);
   }
+  auto put_state = [&](uint16_t *buf) {
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+      if (has_tile(q)) lds_put4<LDS_>(buf, SPL, r16, 16 * (w + 4 * q) + 4 * g4, split4(S[q]));
+  };
+  put_state(sS[0]);
+  lds_barrier();
 
-  // One chunk of the recurrence with its operand fragments f.
-  auto body = [&](int c, const ScanFrag<D> &f) {
+  auto body = [&](int c, const ChainOps<D> &f) {
     const Ws<D> ws = ws_of(c);
-    const float *sS = sSb[c & 1];
-    float *sS_next = sSb[(c + 1) & 1];
-    lds_barrier();  // the state tile of this chunk is in place; the last chunk's reads of sUp are done
+    const int c0 = c * C;
+    const int n = min(C, L - c0);
+    const int64_t tok_base = int64_t(args.tok0[row]) + c0;
+    const uint16_t *sSc = sS[c & 1];
 
-    // U = U' - W S_c^T for tokens 16w..16w+15 of this tile's 16 value channels,
-    // in two interleaved partial chains
-    floatx4 ua = zero4(), ub = zero4();
+    // A. U = U' - W S_c^T and (Q S_c^T)^T for tokens 16w..16w+15, channels i0..i0+15 (one
+    //    read of S_c's parts serves both; two accumulators for U interleave the chains)
+    floatx4 ua = zero4(), ub = zero4(), oq = zero4();
 #pragma unroll
-    for (int kb = 0; kb < NKB; kb += 2) {
-      ua = mma4(ua, f.wf[kb], *reinterpret_cast<const float4 *>(sS + r16 * LDS_ + 16 * kb + 4 * g4));
-      if (kb + 1 < NKB)
-        ub = mma4(ub, f.wf[kb + 1], *reinterpret_cast<const float4 *>(sS + r16 * LDS_ + 16 * (kb + 1) + 4 * g4));
+    for (int kb = 0; kb < NK; ++kb) {
+      const Parts8 sp = s_parts(sSc, kb);
+      if (kb & 1)
+        ub = mma6(ub, f.w[kb], sp);
+      else
+        ua = mma6(ua, f.w[kb], sp);
+      oq = mma3a(oq, sp, f.q[kb]);  // O^T: rows are channels, columns tokens
     }
-    // record S_c for the output and checkpoint kernels (issued behind the products)
-#pragma unroll
-    for (int idx = tid; idx < VT * (D / 4); idx += 256) {
-      const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-      *reinterpret_cast<float4 *>(ws.Sc + int64_t(i0 + i) * D + d4) =
-          *reinterpret_cast<const float4 *>(sS + i * LDS_ + d4);
-    }
-    {
-      // this lane's tokens 16w + 4g4 + (0..3) of value channel i0 + r16: contiguous in
-      // both U^T buffers; LDS gets U^T diag(e^{G_n - G}), as the carry uses it, split
-      // into bf16x3 parts once here (K is bf16, so the carry runs on the bf16 matrix
-      // cores at fp32 accuracy)
-      const float4 u = make_float4(f.up.x - (ua[0] + ub[0]), f.up.y - (ua[1] + ub[1]),
-                                   f.up.z - (ua[2] + ub[2]), f.up.w - (ua[3] + ub[3]));
-      const Parts4 part = split3x4(mul4(u, f.el));
-      const int o = r16 * LDB + 16 * w + 4 * g4;
-      *reinterpret_cast<uint2 *>(sUp[0] + o) = part.h;
-      *reinterpret_cast<uint2 *>(sUp[1] + o) = part.m;
-      *reinterpret_cast<uint2 *>(sUp[2] + o) = part.l;
-      *reinterpret_cast<float4 *>(ws.Ut + (i0 + r16) * C + 16 * w + 4 * g4) = u;
-    }
-    lds_barrier();  // U^T of the tile complete
+    ua += ub;
+    const float4 u = make_float4(f.up.x - ua[0], f.up.y - ua[1], f.up.z - ua[2], f.up.w - ua[3]);
+    lds_put4<LDP>(sUc, UPL, r16, 16 * w + 4 * g4, split4(mul4(u, f.el)));
+    lds_put4<LDP>(sUr, UPL, r16, 16 * w + 4 * g4, split4(u));
+    lds_barrier();  // U of all 64 tokens in LDS
 
-    // S_{c+1} = e^{G_n} S_c + U^T diag(e^{G_n - G}) K on this wave's column tiles
-    auto lds_parts = [&](int kb) {
-      const int o = r16 * LDB + 16 * kb + 4 * g4;
-      Parts4 r;
-      r.h = *reinterpret_cast<const uint2 *>(sUp[0] + o);
-      r.m = *reinterpret_cast<const uint2 *>(sUp[1] + o);
-      r.l = *reinterpret_cast<const uint2 *>(sUp[2] + o);
-      return r;
-    };
-    const Parts4 a0 = lds_parts(0), a1 = lds_parts(1), a2 = lds_parts(2), a3 = lds_parts(3);
-    floatx4 snew[NT_W];
+    // B. the carry on the wave's column tiles
+    float4 Sn[NT];
 #pragma unroll
-    for (int q = 0; q < NT_W; ++q) {
-      const int nt = w + 4 * q;
-      floatx4 acc = zero4();
-      if (nt < D / 16) {
+    for (int q = 0; q < NT; ++q) {
+      floatx4 a = {f.e_last * S[q].x, f.e_last * S[q].y, f.e_last * S[q].z, f.e_last * S[q].w};
+      if (has_tile(q)) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = f.e_last * sS[(4 * g4 + v) * LDS_ + 16 * nt + r16];
-        acc = mma_bf16x3_64(acc, a0, a1, a2, a3, f.kp[q][0], f.kp[q][1], f.kp[q][2], f.kp[q][3]);
+        for (int kb = 0; kb < 2; ++kb) a = mma3b(a, f.kt[q][kb], lds_get8<LDP>(sUc, UPL, r16, 32 * kb + 8 * g4));
       }
-      snew[q] = acc;
+      Sn[q] = make_float4(a[0], a[1], a[2], a[3]);
+    }
+    // the outputs of the wave's tokens, transposed: O^T = S_c Q^T diag(e^G rq) + U^T P^T,
+    // lane (r16, g4) holding O[16 w + r16][i0 + 4 g4 + 0..3] (one 8-byte store)
+    floatx4 op = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)  // P is zero right of the diagonal: tokens >= 32 only for waves 2, 3
+      if (kb == 0 || w >= 2) op = mma6(op, lds_get8<LDP>(sUr, UPL, r16, 32 * kb + 8 * g4), f.p[kb]);
+    if (16 * w + r16 < n) {
+      const uint2 ob = make_uint2(bf16x2_rn(f.egq * oq[0] + op[0], f.egq * oq[1] + op[1]),
+                                  bf16x2_rn(f.egq * oq[2] + op[2], f.egq * oq[3] + op[3]));
+      *reinterpret_cast<uint2 *>(args.o + ((tok_base + 16 * w + r16) * n_v + h) * D + i0 + 4 * g4) = ob;
+    }
+    // checkpoints at the positions p of this chunk with p >= tail0: slot p - tail0
+    const int p_hi = c0 + n;
+    for (int p = max(tail0, c0); p < p_hi; ++p) {  // uniform over the block
+      float *cdst = args.ckpt + ((int64_t(args.ck_row[row]) * args.ck_slots + (p - tail0)) * n_v + h) * UNIT +
+                    int64_t(i0 + r16) * D + 4 * g4;
+      if (p == L - 1) {  // the row's last state is the carry's result
+#pragma unroll
+        for (int q = 0; q < NT; ++q)
+          if (has_tile(q)) store_nt(cdst + 16 * (w + 4 * q), Sn[q]);
+        continue;
+      }
+      const int jj = p - c0;
+      const double Gj = ws.G[jj];
+      float sc[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int s = 16 * w + 4 * g4 + v;
+        sc[v] = s <= jj ? float(exp(Gj - ws.G[s])) * ws.rk[s] : 0.0f;
+      }
+      lds_put4<LDP>(sUt, UPL, r16, 16 * w + 4 * g4, split4(mul4(u, make_float4(sc[0], sc[1], sc[2], sc[3]))));
+      lds_barrier();
+      const float ej = ws.eG[jj];
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+        if (!has_tile(q)) continue;
+        floatx4 a = {ej * S[q].x, ej * S[q].y, ej * S[q].z, ej * S[q].w};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) a = mma3b(a, f.kt[q][kb], lds_get8<LDP>(sUt, UPL, r16, 32 * kb + 8 * g4));
+        store_nt(cdst + 16 * (w + 4 * q), a);
+      }
+      lds_barrier();  // sUt is rewritten by the next position
     }
 #pragma unroll
-    for (int q = 0; q < NT_W; ++q) {
-      const int nt = w + 4 * q;
-      if (nt < D / 16)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sS_next[(4 * g4 + v) * LDS_ + 16 * nt + r16] = snew[q][v];
-    }
+    for (int q = 0; q < NT; ++q) S[q] = Sn[q];
+    put_state(sS[(c + 1) & 1]);
+    lds_barrier();  // S_{c+1}'s parts complete; every read of this chunk's U parts done
   };
-  auto frag_load = [&](ScanFrag<D> &f, int c) {
+  auto frag_load = [&](ChainOps<D> &f, int c) {
     c = min(c, nch - 1);  // past the end: reload the last chunk, never read
-    f.load(ws_of(c), min(C, L - c * C), w, r16, g4, i0);
+    f.load(ws_of(c), min(C, L - c * C), w, lane, tile);
   };
 
-  // Chunks in pairs with two fragment sets: the next chunk's operands are in flight
-  // while this chunk's products run (fetching two chunks ahead was measured slower).
-  ScanFrag<D> fa, fb;
+  // Chunks in pairs with two operand sets: the next chunk's operands are in flight
+  // while this chunk's products run.  Each chunk's operands are fetched as one group at
+  // one point (the compiler may not move memory accesses across the fences), so the
+  // in-order load counter never makes a wait for this chunk's operands wait for the
+  // next chunk's.
+  ChainOps<D> fa, fb;
   frag_load(fa, 0);
   for (int c = 0; c < nch; c += 2) {
+    __asm__ volatile("" ::: "memory");
     frag_load(fb, c + 1);
+    __asm__ volatile("" ::: "memory");
     body(c, fa);
     if (c + 1 >= nch) break;
+    __asm__ volatile("" ::: "memory");
     frag_load(fa, c + 2);
+    __asm__ volatile("" ::: "memory");
     body(c + 1, fb);
   }
-  lds_barrier();
   if (dst >= 0) {
-    const float *sS = sSb[nch & 1];
-    for (int idx = tid; idx < VT * (D / 4); idx += 256) {
-      const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-      *reinterpret_cast<float4 *>(args.state_out + (int64_t(dst) * n_v + h) * UNIT +
-                                  int64_t(i0 + i) * D + d4) =
-          *reinterpret_cast<const float4 *>(sS + i * LDS_ + d4);
-    }
-  }
-}
-
-// Outputs of one (chunk, value head, half of the value channels) from the chunk's
-// start state S_c and U recorded by the scan: O = diag(e^G) Q S_c^T + P U.  The
-// block stages its half of S_c and of U^T in LDS once; wave w computes tokens
-// 16w..16w+15 (Q and P rows in registers) against every 16-channel tile of the half.
-template <int D>
-__global__ __launch_bounds__(256) void chunk_out_kernel(ChunkArgs args) {
-  constexpr int NKB = D / 16;
-  constexpr int NH = D / 16 >= 2 ? 2 : 1;  // value-channel parts per chunk
-  constexpr int DH = D / NH;              // value channels per part
-  constexpr int NTP = DH / 16;            // 16-wide column tiles per part
-  constexpr int LDS_ = D + 4;
-  __shared__ __attribute__((aligned(16))) float sSc[DH * LDS_];  // S_c rows of this part
-  __shared__ __attribute__((aligned(16))) float sU[DH * LDC];    // U^T rows of this part
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int cl = blockIdx.x, h = blockIdx.y, part = blockIdx.z;
-  const int row = row_of_chunk(args, cl);
-  const int cin = cl - args.chunk_start[row];
-  const int c0 = cin * C;
-  const int n = min(C, args.len[row] - c0);
-  const int64_t tok_base = int64_t(args.tok0[row]) + c0;
-  const int n_v = args.n_v, n_qk = args.n_qk, hq = h / args.group;
-  const int64_t ldqk = int64_t(n_qk) * D;
-  const Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * ChunkArgs::ws_unit_floats(D));
-  const int i_base = part * DH;
-
-  for (int idx = tid; idx < DH * (D / 4); idx += 256) {
-    const int i = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-    *reinterpret_cast<float4 *>(sSc + i * LDS_ + d4) =
-        *reinterpret_cast<const float4 *>(ws.Sc + int64_t(i_base + i) * D + d4);
-  }
-  for (int idx = tid; idx < DH * (C / 4); idx += 256) {
-    const int i = idx / (C / 4), s4 = (idx % (C / 4)) * 4;
-    *reinterpret_cast<float4 *>(sU + i * LDC + s4) =
-        *reinterpret_cast<const float4 *>(ws.Ut + (i_base + i) * C + s4);
-  }
-  const int t_me = 16 * w + r16;
-  const uint16_t *Qc = args.q + tok_base * ldqk + int64_t(hq) * D;
-  const uint16_t *qrow = Qc + int64_t(min(t_me, n - 1)) * ldqk;  // rows past the end: never stored
-  float4 qf[NKB], pf[4];
-  float eg[4];
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-    qf[kb] = unpack_bf16x4(*reinterpret_cast<const uint2 *>(qrow + 16 * kb + 4 * g4));
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) pf[kb] = *reinterpret_cast<const float4 *>(ws.P + t_me * C + 16 * kb + 4 * g4);
-#pragma unroll
-  for (int v = 0; v < 4; ++v) eg[v] = ws.eG[16 * w + 4 * g4 + v] * ws.rq[16 * w + 4 * g4 + v];
-  lds_barrier();
-
-#pragma unroll
-  for (int q = 0; q < NTP; ++q) {
-    const float *srow = sSc + (16 * q + r16) * LDS_;
-    const float *urow = sU + (16 * q + r16) * LDC;
-    floatx4 oa = zero4(), ob = zero4();
-#pragma unroll
-    for (int kb = 0; kb < NKB; kb += 2) {
-      oa = mma4(oa, qf[kb], *reinterpret_cast<const float4 *>(srow + 16 * kb + 4 * g4));
-      if (kb + 1 < NKB) ob = mma4(ob, qf[kb + 1], *reinterpret_cast<const float4 *>(srow + 16 * (kb + 1) + 4 * g4));
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) oa[v] = eg[v] * (oa[v] + ob[v]);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)  // P is zero right of the diagonal block
-      if (kb <= w) oa = mma4(oa, pf[kb], *reinterpret_cast<const float4 *>(urow + 16 * kb + 4 * g4));
-    const int i = i_base + 16 * q + r16;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = 16 * w + 4 * g4 + v;
-      if (t < n) args.o[((tok_base + t) * n_v + h) * D + i] = to_bf16(oa[v]);
-    }
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void chunk_ckpt_kernel(ChunkArgs args) {
-  constexpr size_t UNIT = size_t(D) * D;
-  constexpr int MT = D / 16;
-  __shared__ __attribute__((aligned(16))) float sScale[C];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r16 = lane & 15, g4 = lane >> 4;
-  int b = blockIdx.x;
-  const int mi = b % MT;
-  b /= MT;
-  const int h = b % args.n_v;
-  b /= args.n_v;
-  const int j = b % args.ck_slots;
-  const int row = b / args.ck_slots;
-  const int n_tail = args.n_tail[row];
-  if (j >= n_tail) return;
-  const int L = args.len[row];
-  const int p = L - n_tail + j;  // checkpoint slot j: state after p + 1 tokens
-  const int cin = p / C;
-  const int jj = p - cin * C;
-  const int n_v = args.n_v;
-  const Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * ChunkArgs::ws_unit_floats(D));
-  // scale_s = e^{G_j' - G_s} rk_s for s <= j' (else 0, a select so an overflowed
-  // exponential on the masked side cannot become a NaN), rounded exactly as the
-  // carry's factors, so the checkpoint at a row's last position is bit-identical
-  // to the final state the scan publishes
-  if (w == 0) sScale[lane] = lane <= jj ? float(exp(ws.G[jj] - ws.G[lane])) * ws.rk[lane] : 0.0f;
-  lds_barrier();
-  // the scan's carry operation, part for part: at a row's last position the scaled U
-  // values, their bf16x3 split and the matrix-instruction sequence are the scan's own
-  auto scaled_parts = [&](int kb) {
-    return split3x4(mul4(*reinterpret_cast<const float4 *>(ws.Ut + (16 * mi + r16) * C + 16 * kb + 4 * g4),
-                         *reinterpret_cast<const float4 *>(sScale + 16 * kb + 4 * g4)));
-  };
-  const Parts4 a0 = scaled_parts(0), a1 = scaled_parts(1), a2 = scaled_parts(2), a3 = scaled_parts(3);
-  const float ej = ws.eG[jj];
-  float *cdst = args.ckpt + ((int64_t(args.ck_row[row]) * args.ck_slots + j) * n_v + h) * UNIT;
-  for (int nt = 2 * w; nt < 2 * w + 2 && nt < D / 16; ++nt) {
-    const uint2 *kr = reinterpret_cast<const uint2 *>(ws.Kt + (16 * nt + r16) * C + 16 * g4);  // pieces 0..3
-    float sc[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sc[v] = ws.Sc[int64_t(16 * mi + 4 * g4 + v) * D + 16 * nt + r16];
-    floatx4 acc;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = ej * sc[v];
-    acc = mma_bf16x3_64(acc, a0, a1, a2, a3, kr[0], kr[1], kr[2], kr[3]);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) cdst[int64_t(16 * mi + 4 * g4 + v) * D + 16 * nt + r16] = acc[v];
+    for (int q = 0; q < NT; ++q)
+      if (has_tile(q))
+        store_nt(args.state_out + (int64_t(dst) * n_v + h) * UNIT + int64_t(i0 + r16) * D + 16 * (w + 4 * q) + 4 * g4,
+                 S[q]);
   }
 }
 
@@ -744,15 +736,8 @@ hipError_t launch_d(const ChunkArgs &args, int n_chunks, hipStream_t stream) {
                      stream, args);
   const int n_units = args.n_rows * args.n_v;
   const int groups = (n_units + 7) / 8;  // units are dealt to the 8 chiplets in groups of 8
-  hipLaunchKernelGGL(chunk_scan_kernel<D>, dim3(unsigned(groups * 8 * (D / VT))), dim3(256), 0, stream,
+  hipLaunchKernelGGL(chunk_chain_kernel<D>, dim3(unsigned(groups * 8 * (D / VT))), dim3(256), 0, stream,
                      args, n_units);
-  hipLaunchKernelGGL(chunk_out_kernel<D>, dim3(unsigned(n_chunks), unsigned(args.n_v), unsigned(D / 16 >= 2 ? 2 : 1)),
-                     dim3(256), 0, stream, args);
-  int any_tail = 0;
-  for (int r = 0; r < args.n_rows; ++r) any_tail |= args.n_tail[r];
-  if (any_tail)
-    hipLaunchKernelGGL(chunk_ckpt_kernel<D>, dim3(unsigned(args.n_rows * args.ck_slots * args.n_v * (D / 16))),
-                       dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -120,13 +120,13 @@ struct FoldArgs {
 // tokens, stored to checkpoint row ck_row[r].
 constexpr int kChunk = 64;
 
-// Workspace floats per (chunk, value head): W [64][d], U' [64][d], P [64][64],
-// the 64 fp64 prefix sums of the log-decay, two 64-float decay vectors, K^T
-// [d][64] in bf16, the chunk's start state [d][d], U^T [d][64] and the per-token
-// k and q scale factors [2][64].
+// Workspace floats per (chunk, value head), the chain kernel's operands in 1-KiB
+// fragment blocks: W in three bf16 parts [4][d/32][3] blocks, Q [4][d/32], K^T [d/16][2],
+// P in three bf16 parts [4][2][3], U' [d/16][4] blocks of 256 fp32 each, then
+// the 64 fp64 prefix sums of the log-decay and four 64-float factor vectors.
 constexpr int64_t chunk_ws_unit_floats(int d) {
-  return 2 * int64_t(kChunk) * d + int64_t(kChunk) * kChunk + 4 * kChunk + int64_t(d) * kChunk / 2 +
-         int64_t(d) * d + int64_t(d) * kChunk + 2 * kChunk;
+  const int64_t nk = d >= 32 ? d / 32 : 1, nt = d / 16;
+  return 3072 * nk + 1024 * nk + 512 * nt + 6144 + 1024 * nt + 2 * kChunk + 4 * kChunk;
 }
 
 struct ChunkArgs {

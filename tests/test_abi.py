@@ -372,7 +372,8 @@ def test_chunked_and_transaction_validation_codes():
     b = Bufs()
     d = _dims()
     need = gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100, 64, 1])
-    assert need == (2 + 1 + 1) * 32 * (2 * 64 * 128 + 64 * 64 + 256 + 128 * 32 + 128 * 128 + 128 * 64 + 128) * 4
+    # per (chunk, value head): W parts 48 KiB, Q 16, K^T 16, P parts 24, U' 32 KiB, 1.5 KiB of factors
+    assert need == (2 + 1 + 1) * 32 * ((48 + 16 + 16 + 24 + 32) * 1024 + 1536)
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100], chunk=32) == 0
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [0]) == 0
 
