@@ -501,34 +501,48 @@ struct ChainOps {
   float4 el;          // eL[16 w + 4 g4 + v]
   float egq;          // eGq[16 w + r16]
   float e_last;       // e^{G_{n-1}}
-  __device__ void load(const Ws<D> &ws, int n, int wv, int lane, int tile) {
-    const int r16 = lane & 15, g4 = lane >> 4;
+  // The operands arrive in three groups, each loaded where the chunk before has a
+  // stretch of matrix work to hide it behind: (a) W and Q of block kb, used by phase A;
+  // (b) K^T, U', eL, e_last, used by the U exchange and the carry; (c) P and eGq, used by
+  // the outputs.
+  __device__ void load_a(const Ws<D> &ws, int kb, int wv, int lane) {
+    const int g4 = lane >> 4;
     const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4v{0u, 0u, 0u, 0u});
-    auto frag = [&](const uint16_t *a, int blk) { return *reinterpret_cast<const bf16x8 *>(a + Ws<D>::piece(blk, lane)); };
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb) {
-      const int b3 = (wv * NK + kb) * 3;
-      w[kb] = 32 * kb + 8 * g4 < D ? Parts8{frag(ws.WF, b3), frag(ws.WF, b3 + 1), frag(ws.WF, b3 + 2)}
-                                   : Parts8{z, z, z};
-      q[kb] = frag(ws.QF, wv * NK + kb);
-    }
+    const int b3 = (wv * NK + kb) * 3;
+    w[kb] = 32 * kb + 8 * g4 < D ? Parts8{frag(ws.WF, b3, lane), frag(ws.WF, b3 + 1, lane), frag(ws.WF, b3 + 2, lane)}
+                                 : Parts8{z, z, z};
+    q[kb] = frag(ws.QF, wv * NK + kb, lane);
+  }
+  __device__ void load_b(const Ws<D> &ws, int n, int wv, int lane, int tile) {
+    const int g4 = lane >> 4;
 #pragma unroll
     for (int qt = 0; qt < NT; ++qt) {
       // a wave without a qt-th tile loads the last one and never uses it: unconditional
       // loads keep the prefetch free of branches
       const int nt = min(wv + 4 * qt, D / 16 - 1);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) kt[qt][kb] = frag(ws.KF, nt * 2 + kb);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int b3 = (wv * 2 + kb) * 3;
-      p[kb] = Parts8{frag(ws.PF, b3), frag(ws.PF, b3 + 1), frag(ws.PF, b3 + 2)};
+      for (int kb = 0; kb < 2; ++kb) kt[qt][kb] = frag(ws.KF, nt * 2 + kb, lane);
     }
     up = *reinterpret_cast<const float4 *>(ws.UF + ((tile * 4 + wv) * 64 + lane) * 4);
     el = *reinterpret_cast<const float4 *>(ws.eL + 16 * wv + 4 * g4);
-    egq = ws.eGq[16 * wv + r16];
     e_last = ws.eG[n - 1];
+  }
+  __device__ void load_c(const Ws<D> &ws, int wv, int lane) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int b3 = (wv * 2 + kb) * 3;
+      p[kb] = Parts8{frag(ws.PF, b3, lane), frag(ws.PF, b3 + 1, lane), frag(ws.PF, b3 + 2, lane)};
+    }
+    egq = ws.eGq[16 * wv + (lane & 15)];
+  }
+  __device__ void load(const Ws<D> &ws, int n, int wv, int lane, int tile) {
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) load_a(ws, kb, wv, lane);
+    load_b(ws, n, wv, lane, tile);
+    load_c(ws, wv, lane);
+  }
+  static __device__ __forceinline__ bf16x8 frag(const uint16_t *a, int blk, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(a + Ws<D>::piece(blk, lane));
   }
 };
 
@@ -614,8 +628,12 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
   put_state(sS[0]);
   lds_barrier();
 
-  auto body = [&](int c, const ChainOps<D> &f) {
+  auto body = [&](int c, const ChainOps<D> &f, ChainOps<D> &nx) {
     const Ws<D> ws = ws_of(c);
+    // the next chunk's operands (past the end: the last chunk again, never read)
+    const int cn = min(c + 1, nch - 1);
+    const Ws<D> wsn = ws_of(cn);
+    const int nn = min(C, L - cn * C);
     const int c0 = c * C;
     const int n = min(C, L - c0);
     const int64_t tok_base = int64_t(args.tok0[row]) + c0;
@@ -627,6 +645,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) {
       const Parts8 sp = s_parts(sSc, kb);
+      nx.load_a(wsn, kb, w, lane);
       if (kb & 1)
         ub = mma6(ub, f.w[kb], sp);
       else
@@ -637,6 +656,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
     const float4 u = make_float4(f.up.x - ua[0], f.up.y - ua[1], f.up.z - ua[2], f.up.w - ua[3]);
     lds_put4<LDP>(sUc, UPL, r16, 16 * w + 4 * g4, split4(mul4(u, f.el)));
     lds_put4<LDP>(sUr, UPL, r16, 16 * w + 4 * g4, split4(u));
+    nx.load_b(wsn, nn, w, lane, tile);
     lds_barrier();  // U of all 64 tokens in LDS
 
     // B. the carry on the wave's column tiles
@@ -650,6 +670,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
       }
       Sn[q] = make_float4(a[0], a[1], a[2], a[3]);
     }
+    nx.load_c(wsn, w, lane);
     // the outputs of the wave's tokens, transposed: O^T = S_c Q^T diag(e^G rq) + U^T P^T,
     // lane (r16, g4) holding O[16 w + r16][i0 + 4 g4 + 0..3] (one 8-byte store)
     floatx4 op = zero4();
@@ -698,28 +719,16 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
     put_state(sS[(c + 1) & 1]);
     lds_barrier();  // S_{c+1}'s parts complete; every read of this chunk's U parts done
   };
-  auto frag_load = [&](ChainOps<D> &f, int c) {
-    c = min(c, nch - 1);  // past the end: reload the last chunk, never read
-    f.load(ws_of(c), min(C, L - c * C), w, lane, tile);
-  };
-
-  // Chunks in pairs with two operand sets: the next chunk's operands are in flight
-  // while this chunk's products run.  Each chunk's operands are fetched as one group at
-  // one point (the compiler may not move memory accesses across the fences), so the
-  // in-order load counter never makes a wait for this chunk's operands wait for the
-  // next chunk's.
+  // Chunks in pairs with two operand sets: while chunk c runs on one set, chunk c + 1's
+  // operands are loaded into the other, spread over the chunk's matrix work.  Every
+  // load of chunk c precedes every load of chunk c + 1, so waiting for chunk c's
+  // operands (loads complete in issue order) never waits for the next chunk's.
   ChainOps<D> fa, fb;
-  frag_load(fa, 0);
+  fa.load(ws_of(0), min(C, L), w, lane, tile);
   for (int c = 0; c < nch; c += 2) {
-    __asm__ volatile("" ::: "memory");
-    frag_load(fb, c + 1);
-    __asm__ volatile("" ::: "memory");
-    body(c, fa);
+    body(c, fa, fb);
     if (c + 1 >= nch) break;
-    __asm__ volatile("" ::: "memory");
-    frag_load(fa, c + 2);
-    __asm__ volatile("" ::: "memory");
-    body(c + 1, fb);
+    body(c + 1, fb, fa);
   }
   if (dst >= 0) {
 #pragma unroll
