@@ -232,9 +232,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   __shared__ __attribute__((aligned(16))) float sBeta[C];  // beta_m
   __shared__ __attribute__((aligned(16))) float sSK[C];    // beta_m e^{G_m}
   __shared__ __attribute__((aligned(16))) float sA[C * LDC];  // strictly lower A, then T = (I + A)^{-1}
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * LDB];  // K^T (bf16): row d, column token m
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDB];  // V^T (bf16)
-  __shared__ float sRk[C], sRq[C];  // per-token k and q scale factors (1: inputs taken as given)
+  constexpr int LDK = D + 8;  // row length (bf16) of sK: 16-B aligned rows
+  __shared__ __attribute__((aligned(16))) uint16_t sK[C * LDK];   // K (bf16): row token m, column d
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDB];  // V^T (bf16): row d, column token m
+  __shared__ float sRk[C];  // per-token k scale factors (1: inputs taken as given)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -280,46 +281,45 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     ws.G[lane] = G;
     ws.eG[lane] = float(exp(G));
   }
-  // Transposing stage: lane (m_lo, dg) of wave mh loads 4 dims of token
-  // m = 16 mh + m_lo, so the 16 lanes of a group write 16 consecutive columns of a
-  // K^T row and the 4 groups land on disjoint banks (row pitch 136 B).
+  // K rows to sK and V rows, transposed, to sVt, with the k norms when normalising.
+  // Thread tid takes 8 dims (16 bytes) of one token, so each load instruction reads whole
+  // 256-byte rows of 4 tokens (a wave reading 16 rows of 32 bytes instead measured ~3x
+  // slower per byte).  Rows past the chunk's end are zero.
   {
-    const int m = 16 * w + (lane & 15), dg = lane >> 4;
+    constexpr int TPT = D / 8;       // threads per token
+    constexpr int TPR = 256 / TPT;   // tokens per round
     const bool norm = args.qk_norm != 0;
-    float ssk = 0.0f, ssq = 0.0f;  // this lane's D/4 dims of token m
-    for (int it = 0; it < D / 16; ++it) {
-      const int d4 = (4 * it + dg) * 4;
-      uint2 kw = make_uint2(0u, 0u), vw = kw, qw = kw;
+    const int d8 = 8 * (tid % TPT);
+#pragma unroll
+    for (int it = 0; it < (C + TPR - 1) / TPR; ++it) {
+      const int m = tid / TPT + TPR * it;
+      if (m >= C) break;
+      uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw;
       if (m < n) {
-        kw = *reinterpret_cast<const uint2 *>(Kc + int64_t(m) * ldqk + d4);
-        vw = *reinterpret_cast<const uint2 *>(Vc + int64_t(m) * ldv + d4);
-        if (norm) qw = *reinterpret_cast<const uint2 *>(Qc + int64_t(m) * ldqk + d4);
+        kw = *reinterpret_cast<const uint4 *>(Kc + int64_t(m) * ldqk + d8);
+        vw = *reinterpret_cast<const uint4 *>(Vc + int64_t(m) * ldv + d8);
       }
-      if (norm) {
-        const float4 kf = unpack_bf16x4(kw), qf = unpack_bf16x4(qw);
-        ssk = fmaf(kf.x, kf.x, ssk); ssk = fmaf(kf.y, kf.y, ssk);
-        ssk = fmaf(kf.z, kf.z, ssk); ssk = fmaf(kf.w, kf.w, ssk);
-        ssq = fmaf(qf.x, qf.x, ssq); ssq = fmaf(qf.y, qf.y, ssq);
-        ssq = fmaf(qf.z, qf.z, ssq); ssq = fmaf(qf.w, qf.w, ssq);
+      *reinterpret_cast<uint4 *>(sK + m * LDK + d8) = kw;
+      const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sVt[(d8 + 2 * e) * LDB + m] = uint16_t(vv[e]);
+        sVt[(d8 + 2 * e + 1) * LDB + m] = uint16_t(vv[e] >> 16);
       }
-      sKt[(d4 + 0) * LDB + m] = uint16_t(kw.x);
-      sKt[(d4 + 1) * LDB + m] = uint16_t(kw.x >> 16);
-      sKt[(d4 + 2) * LDB + m] = uint16_t(kw.y);
-      sKt[(d4 + 3) * LDB + m] = uint16_t(kw.y >> 16);
-      sVt[(d4 + 0) * LDB + m] = uint16_t(vw.x);
-      sVt[(d4 + 1) * LDB + m] = uint16_t(vw.x >> 16);
-      sVt[(d4 + 2) * LDB + m] = uint16_t(vw.y);
-      sVt[(d4 + 3) * LDB + m] = uint16_t(vw.y >> 16);
-    }
-    if (norm) {  // the 4 lanes of token m (lane bits 4 and 5) hold its partial sums
-      ssk += __shfl_xor(ssk, 16, 64);
-      ssk += __shfl_xor(ssk, 32, 64);
-      ssq += __shfl_xor(ssq, 16, 64);
-      ssq += __shfl_xor(ssq, 32, 64);
-    }
-    if (dg == 0) {
-      sRk[m] = !norm ? 1.0f : m < n ? 1.0f / sqrtf(ssk + kNormEps) : 0.0f;
-      sRq[m] = !norm ? 1.0f : m < n ? 1.0f / sqrtf(ssq + kNormEps) * inv_sqrt_d<D>() : 0.0f;
+      if (norm) {  // the TPT consecutive lanes of token m hold its partial sums
+        const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ss = fmaf(bf16_lo(kk[e]), bf16_lo(kk[e]), ss);
+          ss = fmaf(bf16_hi(kk[e]), bf16_hi(kk[e]), ss);
+        }
+#pragma unroll
+        for (int off = 1; off < TPT; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        if (d8 == 0) sRk[m] = m < n ? 1.0f / sqrtf(ss + kNormEps) : 0.0f;
+      } else if (d8 == 0) {
+        sRk[m] = 1.0f;
+      }
     }
   }
   lds_barrier();
@@ -330,15 +330,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     ws.eL[lane] = lane < n ? float(exp(Gl - G)) * rk : 0.0f;
     sSK[lane] *= rk;
     ws.rk[lane] = rk;
-    ws.eGq[lane] = float(exp(G)) * sRq[lane];
   }
   // K^T in fragment order for the chain kernel's carry: piece (nt, kb, l = r + 16 g) is
-  // K^T[16 nt + r][32 kb + 8 g .. +7]
+  // K^T[16 nt + r][32 kb + 8 g .. +7], a column of sK
   for (int idx = tid; idx < (D / 16) * 2 * 64; idx += 256) {
     const int nt = idx >> 7, kb = (idx >> 6) & 1, l = idx & 63;
-    const uint16_t *src = sKt + (16 * nt + (l & 15)) * LDB + 32 * kb + 8 * (l >> 4);  // 8-B aligned rows
-    const uint2 lo = *reinterpret_cast<const uint2 *>(src), hi = *reinterpret_cast<const uint2 *>(src + 4);
-    *reinterpret_cast<uint4 *>(ws.KF + idx * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    const uint16_t *src = sK + (32 * kb + 8 * (l >> 4)) * LDK + 16 * nt + (l & 15);
+    uint32_t wv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wv[e] = uint32_t(src[(2 * e) * LDK]) | (uint32_t(src[(2 * e + 1) * LDK]) << 16);
+    *reinterpret_cast<uint4 *>(ws.KF + idx * 8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
 
   // 2. K K^T -> A (strictly lower, scaled) and Q K^T -> P (lower with diagonal) on
@@ -352,14 +353,29 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   {
     constexpr int NK32 = (D + 31) / 32;  // 32-wide k blocks over d (D = 16: half of one)
     bf16x8 fk[4][NK32], fa[NK32], fq[NK32];  // fa: this wave's K rows (register arrays
-#pragma unroll                                 // are indexed by constants only)
-    for (int kb = 0; kb < NK32; ++kb) {
-      fq[kb] = frag32(Qc, ldqk, 16 * w + r16, kb);
-      fa[kb] = frag32(Kc, ldqk, 16 * w + r16, kb);
+    const bf16x8 z8 = __builtin_bit_cast(bf16x8, u32x4v{0u, 0u, 0u, 0u});  // are indexed by constants only)
+    float ssq = 0.0f;
 #pragma unroll
-      for (int tj = 0; tj < 4; ++tj) fk[tj][kb] = frag32(Kc, ldqk, 16 * tj + r16, kb);
+    for (int kb = 0; kb < NK32; ++kb) {
+      const int col = 32 * kb + 8 * g4;
+      fq[kb] = frag32(Qc, ldqk, 16 * w + r16, kb);
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj)
+        fk[tj][kb] = col < D ? *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + r16) * LDK + col) : z8;
+      fa[kb] = col < D ? *reinterpret_cast<const bf16x8 *>(sK + (16 * w + r16) * LDK + col) : z8;
       *reinterpret_cast<bf16x8 *>(ws.QF + Ws<D>::piece(w * NK32 + kb, lane)) = fq[kb];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ssq = fmaf(float(fq[kb][e]), float(fq[kb][e]), ssq);
     }
+    // q's factor for the lane's row t = 16 w + r16: its 4 lanes (g4) hold the partial sums
+    const int t_q = 16 * w + r16;
+    float rq = 1.0f;
+    if (args.qk_norm) {
+      ssq += __shfl_xor(ssq, 16, 64);
+      ssq += __shfl_xor(ssq, 32, 64);
+      rq = t_q < n ? 1.0f / sqrtf(ssq + kNormEps) * inv_sqrt_d<D>() : 0.0f;
+    }
+    if (g4 == 0) ws.eGq[t_q] = float(exp(sG[t_q])) * rq;
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
       floatx4 kk = zero4(), qk = zero4();
@@ -381,7 +397,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int t = 16 * w + r16, s = 16 * tj + 4 * g4 + v;
-        pv[v] = s <= t ? expf(float(sG[t] - sG[s])) * (qk[v] * sRq[t] * sRk[s]) : 0.0f;
+        pv[v] = s <= t ? expf(float(sG[t] - sG[s])) * (qk[v] * rq * sRk[s]) : 0.0f;
       }
       // lane (r16, g4) holds P[16 w + r16][16 tj + 4 g4 + 0..3]: half of the 16-byte piece
       // of lane r16 + 16 (2 (tj & 1) + g4 / 2) in block (w, tj / 2, part)
@@ -468,7 +484,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
         const float4 sk = *reinterpret_cast<const float4 *>(sSK + k0);
         const float4 sb = *reinterpret_cast<const float4 *>(sBeta + k0);
         const int d = 16 * nt + r16;
-        const float4 kt = unpack_bf16x4(*reinterpret_cast<const uint2 *>(sKt + d * LDB + k0));
+        const float4 kt = make_float4(bf16_lo(sK[(k0 + 0) * LDK + d]), bf16_lo(sK[(k0 + 1) * LDK + d]),
+                                      bf16_lo(sK[(k0 + 2) * LDK + d]), bf16_lo(sK[(k0 + 3) * LDK + d]));
         const float4 vt = unpack_bf16x4(*reinterpret_cast<const uint2 *>(sVt + d * LDB + k0));
         wa = mma4(wa, kt, mul4(tr, sk));  // W^T: lane holds W[16 ti + r16][16 nt + 4 g4 + v]
         ua = mma4(ua, mul4(tr, sb), vt);
