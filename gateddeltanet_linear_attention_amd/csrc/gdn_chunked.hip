@@ -470,36 +470,76 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     }
   }
 
-  // 4. W = T diag(beta e^G) K (stored as three bf16 parts) and U' = T diag(beta) V.
-  //    Wave w owns column tiles {2w, 2w+1} of every row tile (T is lower triangular:
-  //    k < 16(ti+1)).
-  for (int nt = 2 * w; nt < 2 * w + 2 && nt < D / 16; ++nt) {
-    for (int ti = 0; ti < 4; ++ti) {
-      floatx4 wa = zero4(), ua = zero4();
-      for (int kb = 0; kb <= ti; ++kb) {
-        const int k0 = 16 * kb + 4 * g4;
-        // block (ti, kb) of T: the diagonal block in place, the others right of it
-        const float *tb = kb == ti ? sA + (16 * ti) * LDC + 16 * ti : sA + (16 * kb) * LDC + 16 * ti;
-        const float4 tr = *reinterpret_cast<const float4 *>(tb + r16 * LDC + 4 * g4);
-        const float4 sk = *reinterpret_cast<const float4 *>(sSK + k0);
-        const float4 sb = *reinterpret_cast<const float4 *>(sBeta + k0);
-        const int d = 16 * nt + r16;
-        const float4 kt = make_float4(bf16_lo(sK[(k0 + 0) * LDK + d]), bf16_lo(sK[(k0 + 1) * LDK + d]),
-                                      bf16_lo(sK[(k0 + 2) * LDK + d]), bf16_lo(sK[(k0 + 3) * LDK + d]));
-        const float4 vt = unpack_bf16x4(*reinterpret_cast<const uint2 *>(sVt + d * LDB + k0));
-        wa = mma4(wa, kt, mul4(tr, sk));  // W^T: lane holds W[16 ti + r16][16 nt + 4 g4 + v]
-        ua = mma4(ua, mul4(tr, sb), vt);
+  // 4. W = T diag(beta e^G rk) K (stored as three bf16 parts) and U' = T diag(beta) V on
+  //    the bf16 matrix cores: K and V are exact bf16 operands, and each scaled row of T
+  //    enters in three parts.  Wave w owns state column tiles nt = 2w, 2w+1; T is lower
+  //    triangular, so row tile ti needs only the 32-token blocks kb <= ti / 2.  W comes out
+  //    transposed (lane: token 16 ti + r16, columns 16 nt + 4 g4 + 0..3), U' as
+  //    U'[16 ti + 4 g4 + v][16 nt + r16]: both in the chain kernel's fragment order.
+  {
+    bf16x8 kt8[2][2], vt8[2][2];  // K and V columns d = 16 nt + r16, tokens 32 kb + 8 g4 + 0..7
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int d = 16 * min(2 * w + j, D / 16 - 1) + r16;  // waves without a tile read tile 0, unused
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int s0 = 32 * kb + 8 * g4;
+        uint32_t kw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          kw[e] = uint32_t(sK[(s0 + 2 * e) * LDK + d]) | (uint32_t(sK[(s0 + 2 * e + 1) * LDK + d]) << 16);
+        kt8[j][kb] = __builtin_bit_cast(bf16x8, u32x4v{kw[0], kw[1], kw[2], kw[3]});
+        const uint2 v0 = *reinterpret_cast<const uint2 *>(sVt + d * LDB + s0);  // 8-B aligned rows
+        const uint2 v1 = *reinterpret_cast<const uint2 *>(sVt + d * LDB + s0 + 4);
+        vt8[j][kb] = __builtin_bit_cast(bf16x8, u32x4v{v0.x, v0.y, v1.x, v1.y});
       }
-      // W in parts, in fragment order: lane (r16, g4) holds W[16 ti + r16][16 nt + 4 g4 + 0..3],
-      // half of the piece of lane r16 + 16 (2 (nt & 1) + g4 / 2) in block (ti, nt / 2, part)
-      const Parts4 wp = split4(make_float4(wa[0], wa[1], wa[2], wa[3]));
-      const int l2 = r16 + 16 * (2 * (nt & 1) + (g4 >> 1)), half = 4 * (g4 & 1);
-      const int wb = (ti * Ws<D>::NK + (nt >> 1)) * 3;
-      *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 0, l2) + half) = wp.h;
-      *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 1, l2) + half) = wp.m;
-      *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 2, l2) + half) = wp.l;
-      // U': lane (r16, g4) holds U'[16 ti + 4 g4 + v][16 nt + r16], the piece of block (nt, ti)
-      *reinterpret_cast<float4 *>(ws.UF + ((nt * 4 + ti) * 64 + lane) * 4) = make_float4(ua[0], ua[1], ua[2], ua[3]);
+    }
+    const bool has0 = 2 * w < D / 16, has1 = 2 * w + 1 < D / 16;
+    for (int ti = 0; ti < 4; ++ti) {
+      floatx4 wa[2] = {zero4(), zero4()}, ua[2] = {zero4(), zero4()};
+      for (int kb = 0; kb <= ti / 2; ++kb) {
+        // T[16 ti + r16][32 kb + 8 g4 + 0..7]: token block j = 2 kb + g4 / 2 of row tile ti,
+        // stored right of the diagonal at rows 16 j when j < ti, in place when j == ti, zero above
+        const int j = 2 * kb + (g4 >> 1), c = 8 * (g4 & 1);
+        float4 x0 = zf4(), x1 = zf4();
+        if (j <= ti) {
+          const float *src = j < ti ? sA + (16 * j + r16) * LDC + 16 * ti + c : sA + (16 * ti + r16) * LDC + 16 * ti + c;
+          x0 = *reinterpret_cast<const float4 *>(src);
+          x1 = *reinterpret_cast<const float4 *>(src + 4);
+        }
+        const int s0 = 32 * kb + 8 * g4;
+        const float4 sk0 = *reinterpret_cast<const float4 *>(sSK + s0), sk1 = *reinterpret_cast<const float4 *>(sSK + s0 + 4);
+        const float4 sb0 = *reinterpret_cast<const float4 *>(sBeta + s0), sb1 = *reinterpret_cast<const float4 *>(sBeta + s0 + 4);
+        const Parts4 k0 = split4(mul4(x0, sk0)), k1 = split4(mul4(x1, sk1));
+        const Parts4 b0 = split4(mul4(x0, sb0)), b1 = split4(mul4(x1, sb1));
+        const Parts8 tk{__builtin_bit_cast(bf16x8, u32x4v{k0.h.x, k0.h.y, k1.h.x, k1.h.y}),
+                        __builtin_bit_cast(bf16x8, u32x4v{k0.m.x, k0.m.y, k1.m.x, k1.m.y}),
+                        __builtin_bit_cast(bf16x8, u32x4v{k0.l.x, k0.l.y, k1.l.x, k1.l.y})};
+        const Parts8 tv{__builtin_bit_cast(bf16x8, u32x4v{b0.h.x, b0.h.y, b1.h.x, b1.h.y}),
+                        __builtin_bit_cast(bf16x8, u32x4v{b0.m.x, b0.m.y, b1.m.x, b1.m.y}),
+                        __builtin_bit_cast(bf16x8, u32x4v{b0.l.x, b0.l.y, b1.l.x, b1.l.y})};
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          wa[jj] = mma3b(wa[jj], kb == 0 ? kt8[jj][0] : kt8[jj][1], tk);
+          ua[jj] = mma3a(ua[jj], tv, kb == 0 ? vt8[jj][0] : vt8[jj][1]);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        if (!(jj == 0 ? has0 : has1)) continue;
+        const int nt = 2 * w + jj;
+        // W in parts, in fragment order: lane (r16, g4) holds W[16 ti + r16][16 nt + 4 g4 + 0..3],
+        // half of the piece of lane r16 + 16 (2 (nt & 1) + g4 / 2) in block (ti, nt / 2, part)
+        const Parts4 wp = split4(make_float4(wa[jj][0], wa[jj][1], wa[jj][2], wa[jj][3]));
+        const int l2 = r16 + 16 * (2 * (nt & 1) + (g4 >> 1)), half = 4 * (g4 & 1);
+        const int wb = (ti * Ws<D>::NK + (nt >> 1)) * 3;
+        *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 0, l2) + half) = wp.h;
+        *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 1, l2) + half) = wp.m;
+        *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 2, l2) + half) = wp.l;
+        // U': lane (r16, g4) holds U'[16 ti + 4 g4 + v][16 nt + r16], the piece of block (nt, ti)
+        *reinterpret_cast<float4 *>(ws.UF + ((nt * 4 + ti) * 64 + lane) * 4) =
+            make_float4(ua[jj][0], ua[jj][1], ua[jj][2], ua[jj][3]);
+      }
     }
   }
 }
