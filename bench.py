@@ -2,11 +2,13 @@
 """Throughput of the K=3 draft-verification step of the gated delta rule on one MI355X.
 
 A step is one speculative-decoding verification round of a batch through L
-GatedDeltaNet layers, in the order a target model runs it: gdn_verify_window for
-every layer (each row runs its previous bonus token and 3 drafts from the
-committed state, publishing the state after every token), then, once acceptance
-is known, gdn_commit_accepted for every layer (rollback of each row to its
-accepted length; accepted counts ~ Binomial(3, 0.85) resident on the device).
+GatedDeltaNet layers, in the order a target model runs it: gdn_verify_window_select
+for every layer (each row runs its previous bonus token and 3 drafts from its
+committed state, publishing the state after every token into the row's free bank of
+pool slots), then, once acceptance is known, gdn_commit_select for every layer
+(rollback of each row to its accepted length by pointing the row's entry of the
+device slot table at that checkpoint; accepted counts ~ Binomial(3, 0.85) resident on
+the device; nothing is copied).
 Inputs are synthetic (seeded), at the head shape of a hybrid GatedDeltaNet layer:
 16 q/k heads, 32 value heads, d_k = d_v = 128, fp32 128x128 state per value head,
 bf16 q/k/v/o.
@@ -20,9 +22,11 @@ the verify launch's algorithmic bytes over its mean duration (HIP events on the
 launch stream), with the calibrated HBM traffic from the committed rocprofv3
 counter summary when it was taken on the current kernel sources.
 
-Reported beside the headline, on the same synthetic data: batch 1 (eager and
-HIP-graph steps), mixed draft lengths, the other rollback forms (replay, delta
-checkpoints with a fold commit or folded into the next verify, checkpoint select),
+Reported beside the headline, on the same synthetic data: the same step with dense
+checkpoints in a separate buffer and a copy commit (gdn_verify_window +
+gdn_commit_accepted), batch 1 (eager and HIP-graph steps), mixed draft lengths, the
+other rollback forms (replay, delta checkpoints with a fold commit or folded into the
+next verify),
 token trees, raw q/k normalised in the kernels, the in-place decode step, the
 2048-token chunked prefill, the mixed ragged transaction (4 prefill rows and 12
 verify rows planned per row in one call), the streaming-bandwidth ceilings of a plain
@@ -47,7 +51,7 @@ METRIC = "GDN verify head-token updates/s + HBM GB/s vs peak, K=3, batch 1 and 1
 HBM_PEAK_GBPS = 8000.0
 STATE_BYTES = 128 * 128 * 4          # one value head's fp32 state
 TOKEN_BYTES = 776                    # per head-token: q,k (shared by 2 v-heads) 256 + v 256 + a,b 8 + o 256
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_conc16_k3_counters.json")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_select_conc16_k3_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gateddeltanet_linear_attention_amd", "csrc", f)
                   for f in ("gdn_recurrent.hip", "gdn_internal.h", "gdn_device.h")]
 V_HEADS = 32
@@ -235,8 +239,13 @@ class VerifySet:
             self.commit = gb.prepare_commit_accepted(dims, Ts, self.ckpt, self.acc, self.pool, dst_slot=rows,
                                                      status=self.status, stream=stream)
         self.acc_host = acc
+        self.select = select
         # the window's tokens, for the CPU baseline
         self.tok, self.A_log, self.dt_bias, self.T, self.B = tok, A_log, dt_bias, Ts, B
+
+    def committed_states(self):
+        """The rows' committed states (checkpoint select: the pool slots the table names)."""
+        return self.pool[self.table.long()] if self.select else self.pool
 
 
 def run_steps(layers, steps, warmup, stream, torch):
@@ -269,16 +278,18 @@ def run_steps(layers, steps, warmup, stream, torch):
     return wall, verify_ms, commit_ms
 
 
-def measure_graph(gb, synth, torch, Ts, steps, warmup, n_layers, seed0, replay=False, folded=False):
+def measure_graph(gb, synth, torch, Ts, steps, warmup, n_layers, seed0, replay=False, folded=False,
+                  select=False):
     """The same step captured once as a HIP graph on a side stream and replayed:
     wall time per step (launch costs of the 2 L calls removed from the host side).
     folded: one launch per layer and step (the previous window's commit inside the
-    next verify); the graph holds two steps, so the two factor buffers alternate as
-    they do in a real decode loop."""
+    next verify); folded and select graphs hold two steps, so the two factor buffers
+    (pool banks) alternate as they do in a real decode loop."""
     dims = gb.Dims(16, 32, 128, 128, 3)
     cap = torch.cuda.Stream()
-    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, cap, replay, folded=folded) for i in range(n_layers)]
-    per_replay = 2 if folded else 1
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, cap, replay, folded=folded, select=select)
+            for i in range(n_layers)]
+    per_replay = 2 if (folded or select) else 1
 
     def step():
         for s in sets:
@@ -465,7 +476,7 @@ def cpu_baseline(s: "VerifySet", seconds: float, seconds_1thread: float):
     import numpy as np
     import oracle
     tok = s.tok
-    S0 = s.pool.double().cpu().numpy()
+    S0 = s.committed_states().double().cpu().numpy()
     out = dict(S_final=np.zeros(S0.shape), ckpt=np.zeros((s.B, 4) + S0.shape[1:]),
                o=np.zeros((int(s.T.sum()),) + S0.shape[1:3]))
 
@@ -652,7 +663,9 @@ def main():
         return
 
     import numpy as np
-    sets16, r16 = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500)
+    sets_sel, rs = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
+                           select=True)
+    _, r16 = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500)
 
     def side(r, Ts):
         return {"row_tokens": [int(t) for t in Ts],
@@ -661,12 +674,21 @@ def main():
                 "verify_us_mean": 1e3 * r["verify_ms_mean"], "verify_us_p50": 1e3 * r["verify_ms_p50"],
                 "verify_gbps": r["verify_gbps"], "verify_frac_of_hbm_peak": r["verify_gbps"] / HBM_PEAK_GBPS,
                 "commit_us_mean": 1e3 * r["commit_ms_mean"], "commit_gbps": r["commit_gbps"]}
+    out_copy = side(r16, [4] * 16)
+    out_copy["mode"] = ("dense checkpoints in a separate buffer (gdn_verify_window), commit copies the accepted "
+                        "one into the row's pool slot (gdn_commit_accepted)")
     out_b1 = out_mixed = None
     if not args.no_batch1:
+        _, r1s = measure(gb, synth, torch, [4], args.steps, args.warmup, args.layers, stream, 600, select=True)
         _, r1 = measure(gb, synth, torch, [4], args.steps, args.warmup, args.layers, stream, 600)
-        out_b1 = side(r1, [4])
+        out_b1 = side(r1s, [4])
+        out_b1["mode"] = "checkpoint select, as the headline"
+        out_b1["copy_commit"] = side(r1, [4])
         if not args.no_graph:
-            out_b1["graph"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup, args.layers, 600)
+            out_b1["graph"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup, args.layers, 600,
+                                            select=True)
+            out_b1["graph_copy_commit"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup,
+                                                        args.layers, 600)
             out_b1["graph_replay_mode"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup,
                                                         args.layers, 600, replay=True)
             if not args.no_replay:
@@ -733,13 +755,6 @@ def main():
               "conc16_two_slot_sets": measure_decode(gb, synth, torch, 16, args.steps, args.warmup, args.layers,
                                                      stream, 900, two_sets=True),
               "batch1": measure_decode(gb, synth, torch, 1, args.steps, args.warmup, args.layers, stream, 950)}
-    out_select = None
-    if not args.no_replay:
-        _, rs = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
-                        select=True)
-        out_select = side(rs, [4] * 16)
-        out_select["mode"] = ("dense checkpoints written into two pool banks per row, used alternately; commit "
-                              "selects the accepted one in a device slot table (nothing copied)")
     out_tree = None
     if not args.no_tree:
         tree = np.array(TREE4, np.int32)
@@ -752,45 +767,46 @@ def main():
     if not args.no_ceilings:
         ceilings = measure_ceilings(torch, stream)
         # ceiling time / kernel time: 1 means the kernel runs as fast as the best plain stream
-        ceilings["verify_frac_of_1r4w_ceiling"] = ceilings["stream_1r4w_32MiB"]["us"] / (1e3 * r16["verify_ms_mean"])
+        ceilings["verify_frac_of_1r4w_ceiling"] = ceilings["stream_1r4w_32MiB"]["us"] / (1e3 * rs["verify_ms_mean"])
         ceilings["commit_frac_of_copy_ceiling"] = ceilings["copy_1r1w_32MiB"]["us"] / (1e3 * r16["commit_ms_mean"])
     transaction = None
     if not (args.no_prefill or args.no_transaction):
         transaction = measure_transaction(gb, synth, torch, stream, args.prefill_reps)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(sets16[0], args.cpu_seconds, args.cpu_seconds_1thread)
+        cpu = cpu_baseline(sets_sel[0], args.cpu_seconds, args.cpu_seconds_1thread)
 
-    traffic = traffic_from_profile(r16["verify_bytes"])
+    traffic = traffic_from_profile(rs["verify_bytes"])
     line = {
         "metric": METRIC,
-        "value": r16["updates_per_s"],
+        "value": rs["updates_per_s"],
         "unit": "head-token updates/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": r16["ms_per_step"],
+        "ms_per_step": rs["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "config": {"workload": "conc16_k3_verify_commit", "rows": 16, "drafts_per_row": 3,
+        "config": {"workload": "conc16_k3_verify_select_commit", "rows": 16, "drafts_per_row": 3,
                    "tokens_per_window": 4, "qk_heads": 16, "v_heads": 32, "d_k": 128, "d_v": 128,
                    "state": "fp32", "io": "bf16", "layers_per_step": args.layers},
-        "roofline": {"bound": "hbm", "achieved": r16["verify_gbps"], "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": r16["verify_gbps"] / HBM_PEAK_GBPS,
-                     "traffic": traffic, "kernel": "recurrent_kernel<128,16,1,4,chain,stream> (gdn_verify_window)",
-                     "algorithmic_bytes_per_launch": r16["verify_bytes"],
-                     "launch_us_mean": 1e3 * r16["verify_ms_mean"],
-                     "launch_us_p10": 1e3 * r16["verify_ms_p10"],
-                     "launch_us_p50": 1e3 * r16["verify_ms_p50"],
-                     "launch_us_p90": 1e3 * r16["verify_ms_p90"]},
-        "ms_per_layer": r16["ms_per_step"] / args.layers,
-        "verify_head_token_updates_per_s": r16["verify_updates_per_s"],
-        "commit_us_mean": 1e3 * r16["commit_ms_mean"],
-        "commit_gbps": r16["commit_gbps"],
-        "step_gbps": r16["step_gbps"],
+        "roofline": {"bound": "hbm", "achieved": rs["verify_gbps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": rs["verify_gbps"] / HBM_PEAK_GBPS,
+                     "traffic": traffic,
+                     "kernel": "recurrent_kernel<128,16,1,4,select,stream,ntload> (gdn_verify_window_select)",
+                     "algorithmic_bytes_per_launch": rs["verify_bytes"],
+                     "launch_us_mean": 1e3 * rs["verify_ms_mean"],
+                     "launch_us_p10": 1e3 * rs["verify_ms_p10"],
+                     "launch_us_p50": 1e3 * rs["verify_ms_p50"],
+                     "launch_us_p90": 1e3 * rs["verify_ms_p90"]},
+        "ms_per_layer": rs["ms_per_step"] / args.layers,
+        "verify_head_token_updates_per_s": rs["verify_updates_per_s"],
+        "commit_us_mean": 1e3 * rs["commit_ms_mean"],
+        "step_gbps": rs["step_gbps"],
+        "conc16_k3_copy_commit": out_copy,
         "batch1": out_b1,
         "conc16_mixed_k": out_mixed,
         "conc16_k3_replay": out_replay,
@@ -798,7 +814,6 @@ def main():
         "conc16_k3_delta": out_delta,
         "conc16_k3_delta_folded": out_folded,
         "conc16_k3_fused_qk_norm": out_fused,
-        "conc16_k3_select": out_select,
         "decode": decode,
         "prefill": prefill,
         "mixed_transaction": transaction,

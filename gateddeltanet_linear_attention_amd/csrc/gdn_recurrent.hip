@@ -137,7 +137,11 @@ enum Mode { kChain = 0, kReplay = 1, kTree = 2, kDelta = 3, kSelect = 4 };
 // each output goes straight to memory from the lane that reduced it, so a block retires
 // as soon as its last store is issued.  (Launches that write no dense state measured
 // slower in this form.)
-template <int D, int LPR, int RPL, int WAVES, int MODE, bool STREAM>
+// NTLOAD: the state is read with non-temporal loads (each byte is read once per launch).
+// Measured on the 16-row launches: in-place decode 15.3 -> 12.4 us, select verify 30.1 ->
+// 29.9 us, and the commit that follows a verify runs ~0.4 us faster; the verify with dense
+// checkpoints alone measured 29.25 -> 29.45 us, so it keeps plain loads.
+template <int D, int LPR, int RPL, int WAVES, int MODE, bool STREAM, bool NTLOAD>
 __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs args) {
   if constexpr (STREAM) __builtin_amdgcn_s_setprio(3);
   constexpr bool REPLAY = MODE == kReplay, TREE = MODE == kTree;
@@ -215,9 +219,9 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   const float ga = args.a[tg * n_v + h], gb = args.b[tg * n_v + h];
   const float A_log_h = args.A_log[h], dt_bias_h = args.dt_bias[h];
   __builtin_amdgcn_sched_barrier(0);  // keep every token load ahead of the state loads
-  // the state is loaded from the selected slot clamped into the pool, and the check
-  // that it lies outside every bank this launch writes runs while those loads are in
-  // flight -- a refused row leaves before any store or barrier
+  // the state is loaded from the selected slot clamped into the pool; the check that it
+  // lies outside every bank this launch writes runs after staging, while those loads are
+  // in flight -- a refused row leaves before any store
   constexpr bool select = MODE == kSelect;
   const int sel_src = select ? __builtin_amdgcn_readfirstlane(sel_raw) : 0;
   if (select) src = min(max(sel_src, -1), args.n_slots - 1);
@@ -231,8 +235,13 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
         args.state_in + (size_t(max(src, 0)) * n_v + h) * UNIT + size_t(i0 + q) * D);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const float4 x = p[sub + LPR * j];
-      s[q][j][0] = x.x; s[q][j][1] = x.y; s[q][j][2] = x.z; s[q][j][3] = x.w;
+      if constexpr (NTLOAD) {
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + sub + LPR * j));
+        s[q][j][0] = x[0]; s[q][j][1] = x[1]; s[q][j][2] = x[2]; s[q][j][3] = x[3];
+      } else {
+        const float4 x = p[sub + LPR * j];
+        s[q][j][0] = x.x; s[q][j][1] = x.y; s[q][j][2] = x.z; s[q][j][3] = x.w;
+      }
     }
   }
   if constexpr (STREAM) __builtin_amdgcn_s_setprio(0);  // every load of the block is issued
@@ -250,19 +259,6 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     }
     ntok = acc + 1;
   }
-  if (select) {
-    bool bad = sel_src < -1 || sel_src >= args.n_slots;
-#pragma unroll
-    for (int j = 0; j < kRowsPerLaunch; ++j) {
-      const int lo = args.ck_row[j] * args.ck_slots;
-      bad |= j < args.n_rows && sel_src >= lo && sel_src < lo + args.ck_slots;
-    }
-    if (bad) {
-      if (tile == 0 && h == 0 && tid == 0) atomicOr(args.status + (r >> 5), 1u << (r & 31));
-      return;  // the whole block leaves before any store or barrier
-    }
-  }
-
   if constexpr (MODE == kDelta) {
     if (args.fold_k) {
       // commit the previous window first: fold its accepted prefix into the state
@@ -336,6 +332,21 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   if (vt < ntok) sV[vt][vr] = __uint_as_float(vw << 16);
   if (tid < ntok) eval_gates(ga, gb, A_log_h, dt_bias_h, sAlpha[tid], sBeta[tid]);
   lds_barrier();
+  if (select) {
+    // The selected slot must lie in the pool and outside every bank this launch writes.
+    // Checked here, after staging and before any store: its one load (lane j reads row
+    // j's bank from the argument block) completes with the state loads issued before it,
+    // which the first step waits for anyway (checked before staging, as 64 scalar
+    // compares, it delayed every block: 31.3 against 30.1 us on the 16-row K=3 verify).
+    const int ln = tid & 63;
+    const int bank_j = ln < args.n_rows ? args.ck_row[ln] : -1;
+    const int sel_bank = sel_src >= 0 ? sel_src / args.ck_slots : -2;
+    const bool bad = sel_src < -1 || sel_src >= args.n_slots || __ballot(bank_j == sel_bank) != 0ull;
+    if (bad) {
+      if (tile == 0 && h == 0 && tid == 0) atomicOr(args.status + (r >> 5), 1u << (r & 31));
+      return;  // the whole block leaves before any store (its one barrier is behind it)
+    }
+  }
   if (src < 0) {  // after staging: replacing a register whose load is in flight would wait for it
 #pragma unroll
     for (int q = 0; q < RPL; ++q)
@@ -461,11 +472,12 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 
 }  // namespace
 
-template <int D, int LPR, int RPL, int WAVES, int MODE, bool STREAM>
+template <int D, int LPR, int RPL, int WAVES, int MODE, bool STREAM, bool NTLOAD = false>
 static void launch_one(const RecurrentArgs &args, hipStream_t stream) {
   constexpr int TILES = D / (WAVES * 64 / LPR * RPL);
   const dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * TILES);
-  hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, MODE, STREAM>), grid, dim3(64 * WAVES), 0, stream, args);
+  hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, MODE, STREAM, NTLOAD>), grid, dim3(64 * WAVES), 0, stream,
+                     args);
 }
 
 template <int D, int LPR, int RPL, int WAVES>
@@ -474,22 +486,26 @@ static void launch_d(const RecurrentArgs &args, hipStream_t stream) {
   bool writes_state = args.ckpt != nullptr;
   for (int r = 0; r < args.n_rows; ++r) writes_state |= args.dst[r] >= 0;
   if (args.accepted)
-    launch_one<D, LPR, RPL, WAVES, kReplay, true>(args, stream);
+    launch_one<D, LPR, RPL, WAVES, kReplay, true, true>(args, stream);
   else if (args.delta)
     launch_one<D, LPR, RPL, WAVES, kDelta, false>(args, stream);
   else if constexpr (RPL == 1) {  // trees always store checkpoints: one lane layout
     if (args.tree_mode)
       launch_one<D, LPR, RPL, WAVES, kTree, true>(args, stream);
     else if (args.src_table)
-      launch_one<D, LPR, RPL, WAVES, kSelect, true>(args, stream);
-    else if (writes_state)
+      launch_one<D, LPR, RPL, WAVES, kSelect, true, true>(args, stream);
+    else if (args.ckpt)
       launch_one<D, LPR, RPL, WAVES, kChain, true>(args, stream);
+    else if (writes_state)  // decode: the new state goes to a slot
+      launch_one<D, LPR, RPL, WAVES, kChain, true, true>(args, stream);
     else
       launch_one<D, LPR, RPL, WAVES, kChain, false>(args, stream);
   } else if (args.src_table)
-    launch_one<D, LPR, RPL, WAVES, kSelect, true>(args, stream);
-  else if (writes_state)
+    launch_one<D, LPR, RPL, WAVES, kSelect, true, true>(args, stream);
+  else if (args.ckpt)
     launch_one<D, LPR, RPL, WAVES, kChain, true>(args, stream);
+  else if (writes_state)
+    launch_one<D, LPR, RPL, WAVES, kChain, true, true>(args, stream);
   else
     launch_one<D, LPR, RPL, WAVES, kChain, false>(args, stream);
 }
@@ -519,14 +535,15 @@ hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream
         if (int((args.tree[r] >> (8 * t)) & 0xFFu) > t) return hipErrorInvalidValue;
   if (d == 128) {
     // A launch that stores no dense checkpoints moves little data per block and waits
-    // mostly on its state loads, and a checkpoint-select launch first waits for each
-    // row's slot from the device table; with two rounds of blocks or more, two state
-    // rows per lane halve the block count (those waits are paid once) and double the
-    // loads each lane has in flight.  Each state row keeps its 16 lanes, columns and
-    // butterfly, so every result is bit-identical in both layouts.
-    // Otherwise one row per lane in 4-wave blocks: with checkpoints, smaller blocks
-    // turn over more often, which keeps each CU's loads and stores interleaved.
-    if ((!args.ckpt || args.src_table) && !args.tree_mode && int64_t(args.n_rows) * args.n_v >= 512)
+    // mostly on its state loads; with two rounds of blocks or more, two state rows per
+    // lane halve the block count (that wait is paid once) and double the loads each lane
+    // has in flight.  Each state row keeps its 16 lanes, columns and butterfly, so every
+    // result is bit-identical in both layouts.
+    // Otherwise (checkpoints, dense or into pool banks) one row per lane in 4-wave
+    // blocks: smaller blocks turn over more often, which keeps each CU's loads and
+    // stores interleaved (the 16-row K=3 select verify: 31.8 us with two rows per lane
+    // in 8-wave blocks, 31.3 with one).
+    if (!args.ckpt && !args.tree_mode && int64_t(args.n_rows) * args.n_v >= 512)
       launch_d<128, 16, 2, 8>(args, stream);
     else
       launch_d<128, 16, 1, 4>(args, stream);
