@@ -2,13 +2,14 @@
 """Throughput of the K=3 draft-verification step of the gated delta rule on one MI355X.
 
 A step is one speculative-decoding verification round of a batch through L
-GatedDeltaNet layers, in the order a target model runs it: gdn_verify_window_select
-for every layer (each row runs its previous bonus token and 3 drafts from its
-committed state, publishing the state after every token into the row's free bank of
-pool slots), then, once acceptance is known, gdn_commit_select for every layer
-(rollback of each row to its accepted length by pointing the row's entry of the
-device slot table at that checkpoint; accepted counts ~ Binomial(3, 0.85) resident on
-the device; nothing is copied).
+GatedDeltaNet layers, in the order a target model runs it: one
+gdn_verify_window_select_commit launch per layer.  Each row first commits its
+previous window (rollback to the accepted length: the row's entry of the device
+slot table is pointed at that window's accepted checkpoint, accepted counts ~
+Binomial(3, 0.85) resident on the device; nothing is copied), then runs its previous
+bonus token and 3 drafts from that state, publishing the state after every token
+into the row's other bank of pool slots.  The same step as two launches per layer
+(gdn_verify_window_select for every layer, then gdn_commit_select) is a side line.
 Inputs are synthetic (seeded), at the head shape of a hybrid GatedDeltaNet layer:
 16 q/k heads, 32 value heads, d_k = d_v = 128, fp32 128x128 state per value head,
 bf16 q/k/v/o.
@@ -129,7 +130,8 @@ class VerifySet:
     and the two prepared C-ABI calls of a step."""
 
     def __init__(self, gb, synth, dims, Ts, seed, stream, replay=False, parents=None, delta=False,
-                 folded=False, select=False, two_sets=False):
+                 folded=False, select=False, two_sets=False, select_commit=False):
+        select = select or select_commit
         raw_qk = bool(dims.flags & gb.QK_L2NORM)
         import numpy as np
         import torch
@@ -174,6 +176,20 @@ class VerifySet:
                 sc[phase[0]]()
                 phase[0] ^= 1
             self.verify, self.commit = verify, commit
+            if select_commit:  # the previous window's select inside the next verify: no commit launch
+                svc = [gb.prepare_verify_window_select_commit(
+                    dims, Ts, Ts, banks[j], self.acc, **self.t, state_pool=self.pool, slot_table=self.table,
+                    bank=banks[1 - j], o=self.o, status=self.status, stream=stream) for j in (0, 1)]
+                cphase = [None]
+
+                def verify_commit():
+                    if cphase[0] is None:
+                        sv[0]()
+                        cphase[0] = 0
+                    else:
+                        svc[cphase[0]]()
+                        cphase[0] ^= 1
+                self.verify, self.commit = verify_commit, (lambda: None)
         elif folded:  # each verify first folds the previous window's accepted prefix: no commit launch
             self.deltas = [torch.empty(gb.delta_shape(dims, B), device=dev) for _ in range(2)]
             first = gb.prepare_verify_window_delta(dims, Ts, **self.t, state_pool=self.pool, src_slot=rows,
@@ -279,7 +295,7 @@ def run_steps(layers, steps, warmup, stream, torch):
 
 
 def measure_graph(gb, synth, torch, Ts, steps, warmup, n_layers, seed0, replay=False, folded=False,
-                  select=False):
+                  select=False, select_commit=False):
     """The same step captured once as a HIP graph on a side stream and replayed:
     wall time per step (launch costs of the 2 L calls removed from the host side).
     folded: one launch per layer and step (the previous window's commit inside the
@@ -287,9 +303,9 @@ def measure_graph(gb, synth, torch, Ts, steps, warmup, n_layers, seed0, replay=F
     (pool banks) alternate as they do in a real decode loop."""
     dims = gb.Dims(16, 32, 128, 128, 3)
     cap = torch.cuda.Stream()
-    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, cap, replay, folded=folded, select=select)
-            for i in range(n_layers)]
-    per_replay = 2 if (folded or select) else 1
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, cap, replay, folded=folded, select=select,
+                      select_commit=select_commit) for i in range(n_layers)]
+    per_replay = 2 if (folded or select or select_commit) else 1
 
     def step():
         for s in sets:
@@ -562,14 +578,14 @@ def measure_prefill(gb, synth, torch, stream, reps, raw_qk=False):
 
 
 def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay=False, parents=None,
-            delta=False, folded=False, raw_qk=False, select=False, two_sets=False):
+            delta=False, folded=False, raw_qk=False, select=False, two_sets=False, select_commit=False):
     """Steps over n_layers layers of windows with per-row token counts Ts (replay:
     verify without checkpoints, commit by replay; parents: one draft tree per row;
     delta: delta checkpoints folded by a commit launch; folded: folded by the next
     verify, one launch per layer per step; raw_qk: q and k normalised inside the kernels)."""
     dims = gb.Dims(16, 32, 128, 128, 3, gb.QK_L2NORM if raw_qk else 0)
-    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents, delta, folded, select, two_sets)
-            for i in range(n_layers)]
+    sets = [VerifySet(gb, synth, dims, Ts, seed0 + i, stream, replay, parents, delta, folded, select, two_sets,
+                      select_commit) for i in range(n_layers)]
     wall, verify_ms, commit_ms = run_steps(sets, steps, warmup, stream, torch)
     for s in sets:
         assert int(s.status.abs().sum()) == 0
@@ -578,7 +594,7 @@ def measure(gb, synth, torch, Ts, steps, warmup, n_layers, stream, seed0, replay
     if folded:
         vb = sum(folded_verify_bytes(Ts, s.acc_host) for s in sets) / len(sets)
         cb = 0
-    elif select:  # same verify traffic; the commit moves no state
+    elif select or select_commit:  # same verify traffic; the commit moves no state
         vb = verify_bytes(Ts)
         cb = 0
     elif delta:
@@ -664,7 +680,9 @@ def main():
 
     import numpy as np
     sets_sel, rs = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
-                           select=True)
+                           select_commit=True)
+    _, rsel = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
+                      select=True)
     _, r16 = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500)
 
     def side(r, Ts):
@@ -677,16 +695,24 @@ def main():
     out_copy = side(r16, [4] * 16)
     out_copy["mode"] = ("dense checkpoints in a separate buffer (gdn_verify_window), commit copies the accepted "
                         "one into the row's pool slot (gdn_commit_accepted)")
+    out_sel = side(rsel, [4] * 16)
+    out_sel["mode"] = ("checkpoint select, the commit its own launch (gdn_verify_window_select, then "
+                       "gdn_commit_select): two launches per layer-step")
     out_b1 = out_mixed = None
     if not args.no_batch1:
-        _, r1s = measure(gb, synth, torch, [4], args.steps, args.warmup, args.layers, stream, 600, select=True)
+        _, r1s = measure(gb, synth, torch, [4], args.steps, args.warmup, args.layers, stream, 600,
+                         select_commit=True)
+        _, r1t = measure(gb, synth, torch, [4], args.steps, args.warmup, args.layers, stream, 600, select=True)
         _, r1 = measure(gb, synth, torch, [4], args.steps, args.warmup, args.layers, stream, 600)
         out_b1 = side(r1s, [4])
-        out_b1["mode"] = "checkpoint select, as the headline"
+        out_b1["mode"] = "as the headline: checkpoint select, the commit inside the next verify"
+        out_b1["select_two_launches"] = side(r1t, [4])
         out_b1["copy_commit"] = side(r1, [4])
         if not args.no_graph:
             out_b1["graph"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup, args.layers, 600,
-                                            select=True)
+                                            select_commit=True)
+            out_b1["graph_select_two_launches"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup,
+                                                                args.layers, 600, select=True)
             out_b1["graph_copy_commit"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup,
                                                         args.layers, 600)
             out_b1["graph_replay_mode"] = measure_graph(gb, synth, torch, [4], args.steps, args.warmup,
@@ -796,7 +822,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": rs["verify_gbps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": rs["verify_gbps"] / HBM_PEAK_GBPS,
                      "traffic": traffic,
-                     "kernel": "recurrent_kernel<128,16,1,4,select,stream,ntload> (gdn_verify_window_select)",
+                     "kernel": "recurrent_kernel<128,16,1,4,select,stream,ntload> (gdn_verify_window_select_commit)",
                      "algorithmic_bytes_per_launch": rs["verify_bytes"],
                      "launch_us_mean": 1e3 * rs["verify_ms_mean"],
                      "launch_us_p10": 1e3 * rs["verify_ms_p10"],
@@ -807,6 +833,7 @@ def main():
         "commit_us_mean": 1e3 * rs["commit_ms_mean"],
         "step_gbps": rs["step_gbps"],
         "conc16_k3_copy_commit": out_copy,
+        "conc16_k3_select_two_launches": out_sel,
         "batch1": out_b1,
         "conc16_mixed_k": out_mixed,
         "conc16_k3_replay": out_replay,

@@ -72,6 +72,8 @@ _SIGS = {
                          ctypes.c_int32, _I32P, _I32P, _VP, _VP],
     "gdn_verify_window_select": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
                                 [ctypes.c_int32, _VP, _I32P, _VP, _VP, _VP],
+    "gdn_verify_window_select_commit": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _I32P, _I32P, _VP] +
+                                       [_VP] * 8 + [ctypes.c_int32, _VP, _I32P, _VP, _VP, _VP],
     "gdn_commit_select": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P, _VP, _I32P, ctypes.c_int32, _VP, _VP,
                           _VP],
     "gdn_commit_replay": [ctypes.POINTER(_Dims), ctypes.c_int32, _I32P] + [_VP] * 8 +
@@ -393,6 +395,24 @@ def _verify_select_args(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, s
     return args, (cd, T, bk, q, k, v, a, b, A_log, dt_bias, state_pool, slot_table, o, status)
 
 
+def _verify_select_commit_args(dims: Dims, row_tokens, prev_row_tokens, prev_bank, accepted, q, k, v, a, b, A_log,
+                               dt_bias, state_pool, slot_table, bank, o, status, stream):
+    import torch
+    T, PT, PB, bk = _i32(row_tokens), _i32(prev_row_tokens), _i32(prev_bank), _i32(bank)
+    n_rows = T.size
+    if not (PT.size == PB.size == bk.size == n_rows):
+        raise ValueError("per-row arrays differ in length")
+    toks, op = _token_ptrs(dims, int(T.sum()), q, k, v, a, b, A_log, dt_bias, o)
+    pp, n_slots = _pool(dims, state_pool)
+    ap = _dev(accepted, "accepted", torch.int32, (n_rows,))
+    tp = _dev(slot_table, "slot_table", torch.int32, (n_rows,))
+    sp = _dev(status, "status", torch.int32, ((n_rows + 31) // 32,))
+    cd = dims.c()
+    args = (ctypes.byref(cd), n_rows, _ip(T), _ip(PT), _ip(PB), ap, *toks, pp, n_slots, tp, _ip(bk), op, sp,
+            _stream(stream))
+    return args, (cd, T, PT, PB, bk, accepted, q, k, v, a, b, A_log, dt_bias, state_pool, slot_table, o, status)
+
+
 def _commit_select_args(dims: Dims, row_tokens, accepted, bank, state_pool, slot_table, status, stream):
     import torch
     T, bk = _i32(row_tokens), _i32(bank)
@@ -422,6 +442,23 @@ def gdn_commit_select(dims: Dims, row_tokens, accepted, bank, state_pool, slot_t
     state_pool is passed for its slot count only; nothing in it is read or written."""
     args, _keep = _commit_select_args(dims, row_tokens, accepted, bank, state_pool, slot_table, status, stream)
     _check("gdn_commit_select", lib().gdn_commit_select(*args))
+
+
+def gdn_verify_window_select_commit(dims: Dims, row_tokens, prev_row_tokens, prev_bank, accepted, q, k, v, a, b,
+                                    A_log, dt_bias, state_pool, slot_table, bank, o, status, stream=None) -> None:
+    """gdn_commit_select of the previous window (prev_row_tokens, prev_bank, accepted on the
+    device), then gdn_verify_window_select of this one, in one launch."""
+    args, _keep = _verify_select_commit_args(dims, row_tokens, prev_row_tokens, prev_bank, accepted, q, k, v, a, b,
+                                             A_log, dt_bias, state_pool, slot_table, bank, o, status, stream)
+    _check("gdn_verify_window_select_commit", lib().gdn_verify_window_select_commit(*args))
+
+
+def prepare_verify_window_select_commit(dims: Dims, row_tokens, prev_row_tokens, prev_bank, accepted, q, k, v, a,
+                                        b, A_log, dt_bias, state_pool, slot_table, bank, o, status,
+                                        stream=None) -> PreparedCall:
+    args, keep = _verify_select_commit_args(dims, row_tokens, prev_row_tokens, prev_bank, accepted, q, k, v, a, b,
+                                            A_log, dt_bias, state_pool, slot_table, bank, o, status, stream)
+    return PreparedCall("gdn_verify_window_select_commit", args, keep)
 
 
 def prepare_verify_window_select(dims: Dims, row_tokens, q, k, v, a, b, A_log, dt_bias, state_pool, slot_table,

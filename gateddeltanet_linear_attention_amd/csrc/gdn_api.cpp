@@ -560,7 +560,7 @@ int gdn_commit_replay(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
 }
 
 // Banks of a checkpoint-select call: inside the pool, distinct, one launch of rows.
-int check_banks(const gdn_dims *dims, int32_t n_rows, int32_t n_slots, const int32_t *bank) {
+static int check_banks(const gdn_dims *dims, int32_t n_rows, int32_t n_slots, const int32_t *bank) {
   if (n_rows > kRowsPerLaunch) return GDN_E_RANGE;
   const int64_t per_bank = dims->k_max + 1;
   for (int32_t r = 0; r < n_rows; ++r)
@@ -571,11 +571,13 @@ int check_banks(const gdn_dims *dims, int32_t n_rows, int32_t n_slots, const int
   return GDN_OK;
 }
 
-int gdn_verify_window_select(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
-                             const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
-                             const float *b, const float *A_log, const float *dt_bias, float *state_pool,
-                             int32_t n_slots, const int32_t *slot_table, const int32_t *bank, uint16_t *o,
-                             uint32_t *status, void *stream) {
+// Checkpoint-select verification, optionally committing the previous window first
+// (prev_* non-null): both forms are checked in full before the one launch.
+static int verify_select(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                  const int32_t *prev_row_tokens, const int32_t *prev_bank, const int32_t *accepted,
+                  const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a, const float *b,
+                  const float *A_log, const float *dt_bias, float *state_pool, int32_t n_slots,
+                  int32_t *slot_table, const int32_t *bank, uint16_t *o, uint32_t *status, hipStream_t stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (n_rows < 0 || n_slots < 0) return GDN_E_RANGE;
@@ -584,16 +586,27 @@ int gdn_verify_window_select(const gdn_dims *dims, int32_t n_rows, const int32_t
   if ((rc = check_tokens(q, k, v, a, b, A_log, dt_bias, o))) return rc;
   if (!state_pool) return GDN_E_NULL;
   if (!aligned(state_pool, 16) || !aligned(slot_table, 4) || !aligned(status, 4)) return GDN_E_ALIGN;
+  if (accepted && !aligned(accepted, 4)) return GDN_E_ALIGN;
   for (int32_t r = 0; r < n_rows; ++r)
     if (row_tokens[r] < 1 || row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
   if ((rc = check_banks(dims, n_rows, n_slots, bank))) return rc;
+  if (prev_bank) {
+    for (int32_t r = 0; r < n_rows; ++r)
+      if (prev_row_tokens[r] < 1 || prev_row_tokens[r] > dims->k_max + 1) return GDN_E_RANGE;
+    if ((rc = check_banks(dims, n_rows, n_slots, prev_bank))) return rc;
+    // the committed checkpoint must not be a slot this window writes
+    for (int32_t r = 0; r < n_rows; ++r)
+      for (int32_t j = 0; j < n_rows; ++j)
+        if (prev_bank[r] == bank[j]) return GDN_E_ALIAS;
+  }
   const std::vector<int64_t> cu = prefix(n_rows, row_tokens);
   if (cu.back() > INT32_MAX) return GDN_E_RANGE;  // token offsets are int32
   const Sizes s = sizes_of(dims);
   const size_t pool_b = size_t(n_slots) * s.row_floats * 4;
   const size_t o_b = size_t(cu[n_rows]) * size_t(dims->n_v_heads) * size_t(dims->d_v) * 2;
   if (overlap(o, o_b, state_pool, pool_b) || overlap(slot_table, size_t(n_rows) * 4, state_pool, pool_b) ||
-      overlap(status, size_t((n_rows + 31) / 32) * 4, state_pool, pool_b))
+      overlap(status, size_t((n_rows + 31) / 32) * 4, state_pool, pool_b) ||
+      (accepted && overlap(accepted, size_t(n_rows) * 4, state_pool, pool_b)))
     return GDN_E_ALIAS;
 
   std::vector<int32_t> rows(static_cast<size_t>(n_rows));
@@ -603,8 +616,40 @@ int gdn_verify_window_select(const gdn_dims *dims, int32_t n_rows, const int32_t
   proto.src_table = slot_table;
   proto.status = status;
   proto.n_slots = n_slots;
-  return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, nullptr, nullptr, row_tokens,
-                               static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, bank);
+  if (prev_bank) {  // one launch holds every row of a select call (n_rows <= 64, checked above)
+    proto.prev_accepted = accepted;
+    for (int32_t r = 0; r < n_rows; ++r) {
+      proto.prev_bank[r] = prev_bank[r];
+      proto.prev_ntok[r] = prev_row_tokens[r];
+    }
+  }
+  return launch_recurrent_rows(dims, proto, rows, cu, row_tokens, nullptr, nullptr, row_tokens, stream, nullptr,
+                               nullptr, nullptr, bank);
+}
+
+
+int gdn_verify_window_select(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                             const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *a,
+                             const float *b, const float *A_log, const float *dt_bias, float *state_pool,
+                             int32_t n_slots, const int32_t *slot_table, const int32_t *bank, uint16_t *o,
+                             uint32_t *status, void *stream) {
+  // without a pending commit the kernel only reads the table
+  return verify_select(dims, n_rows, row_tokens, nullptr, nullptr, nullptr, q, k, v, a, b, A_log, dt_bias,
+                       state_pool, n_slots, const_cast<int32_t *>(slot_table), bank, o, status,
+                       static_cast<hipStream_t>(stream));
+}
+
+int gdn_verify_window_select_commit(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                                    const int32_t *prev_row_tokens, const int32_t *prev_bank,
+                                    const int32_t *accepted, const uint16_t *q, const uint16_t *k,
+                                    const uint16_t *v, const float *a, const float *b, const float *A_log,
+                                    const float *dt_bias, float *state_pool, int32_t n_slots,
+                                    int32_t *slot_table, const int32_t *bank, uint16_t *o, uint32_t *status,
+                                    void *stream) {
+  if (n_rows > 0 && (!prev_row_tokens || !prev_bank || !accepted)) return GDN_E_NULL;
+  return verify_select(dims, n_rows, row_tokens, prev_row_tokens, prev_bank, accepted, q, k, v, a, b, A_log,
+                       dt_bias, state_pool, n_slots, slot_table, bank, o, status,
+                       static_cast<hipStream_t>(stream));
 }
 
 int gdn_commit_select(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,

@@ -67,8 +67,16 @@ struct RecurrentArgs {
   // + j (ckpt == state_out == the pool, ck_row = the bank), and row r's source slot is
   // src_table[r] on the device.  A source outside [-1, n_slots) or inside any row's bank
   // leaves the row untouched and sets bit r of status.
-  const int32_t *src_table;
+  int32_t *src_table;
   int32_t n_slots;
+  // Pending select commit (checkpoint select only, may be null): row r first commits the
+  // previous window -- slot prev_bank[r] * ck_slots + prev_accepted[r] (device) when that
+  // count lies in [0, prev_ntok[r]), written to src_table[r] and used as the source; a
+  // count outside that range leaves src_table[r] as it was (the window then runs from it)
+  // and sets bit r of status.
+  const int32_t *prev_accepted;
+  int32_t prev_bank[kRowsPerLaunch];
+  int32_t prev_ntok[kRowsPerLaunch];
 };
 
 // Commit: row r copies checkpoint slot accepted[r] of its ckpt row to pool slot

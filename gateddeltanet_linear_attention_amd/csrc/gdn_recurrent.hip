@@ -176,6 +176,8 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   const int dst = args.dst[r], ck_first = args.ck_first[r];
   const int ck_row = args.ck_row[r];
   const int n_v = args.n_v, n_qk = args.n_qk;
+  const int prev_ntok = MODE == kSelect ? args.prev_ntok[r] : 0;
+  const int prev_bank = MODE == kSelect ? args.prev_bank[r] : 0;
   constexpr bool write_o = !REPLAY;
   // replay: a_r is read first, as a vector load like the select table below, and
   // checked once the state loads are in flight
@@ -189,11 +191,14 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   // checkpoint select: the row's source slot is read first, as a vector load (the
   // index is hidden from the compiler's uniformity analysis), so waiting for it later
   // leaves the token loads issued after it in flight
-  int sel_raw = 0;
+  int sel_raw = 0, pacc_raw = 0;
   if constexpr (MODE == kSelect) {
     int idx = r;
     asm volatile("" : "+v"(idx));
     sel_raw = args.src_table[idx];
+    // a pending commit's count; issued unconditionally (from the table itself when there
+    // is none) so the number of loads in flight stays fixed for the waits below
+    pacc_raw = (args.prev_accepted ? args.prev_accepted : args.src_table)[idx];
   }
 
   // The row's token inputs are loaded before the state: one counter tracks loads in
@@ -218,13 +223,33 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   const size_t tg = size_t(tok0) + min(tid, ntok - 1);
   const float ga = args.a[tg * n_v + h], gb = args.b[tg * n_v + h];
   const float A_log_h = args.A_log[h], dt_bias_h = args.dt_bias[h];
+  // every scalar the state address needs is in registers before the wait for the slot:
+  // the compiler would otherwise load some of them only once the slot has arrived
+  const float *const state_in = args.state_in;
+  const int ck_slots = args.ck_slots, n_slots = args.n_slots;
+  if constexpr (MODE == kSelect) asm volatile("" ::"s"(state_in), "s"(ck_slots), "s"(n_slots), "s"(prev_ntok),
+                                              "s"(prev_bank));
   __builtin_amdgcn_sched_barrier(0);  // keep every token load ahead of the state loads
   // the state is loaded from the selected slot clamped into the pool; the check that it
   // lies outside every bank this launch writes runs after staging, while those loads are
   // in flight -- a refused row leaves before any store
   constexpr bool select = MODE == kSelect;
-  const int sel_src = select ? __builtin_amdgcn_readfirstlane(sel_raw) : 0;
-  if (select) src = min(max(sel_src, -1), args.n_slots - 1);
+  int sel_src = select ? __builtin_amdgcn_readfirstlane(sel_raw) : 0;
+  // the previous window's commit first: its accepted checkpoint becomes the committed
+  // state (and the table entry), exactly as a gdn_commit_select launch before this one;
+  // the table store (or the status bit of a count out of range, the entry then kept)
+  // waits until the state loads are issued, so no store sits ahead of them
+  int pending = 0;  // 1: store the new table entry, 2: flag the row
+  if (select) {
+    // branch-free, so the row's previous bank and token count (read with the other
+    // per-row arguments, above) are not loaded only once the count has arrived
+    const int pacc = __builtin_amdgcn_readfirstlane(pacc_raw);
+    const bool ok = pacc >= 0 && pacc < prev_ntok;
+    const bool fold = args.prev_accepted != nullptr;
+    sel_src = fold && ok ? prev_bank * ck_slots + pacc : sel_src;
+    pending = fold ? (ok ? 1 : 2) : 0;
+  }
+  if (select) src = min(max(sel_src, -1), n_slots - 1);
 
   // the committed state (slot -1: zero; slot 0, which every pool has, is read and
   // discarded, keeping the load unconditional)
@@ -232,7 +257,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 #pragma unroll
   for (int q = 0; q < RPL; ++q) {
     const float4 *p = reinterpret_cast<const float4 *>(
-        args.state_in + (size_t(max(src, 0)) * n_v + h) * UNIT + size_t(i0 + q) * D);
+        state_in + (size_t(max(src, 0)) * n_v + h) * UNIT + size_t(i0 + q) * D);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       if constexpr (NTLOAD) {
@@ -245,6 +270,10 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     }
   }
   if constexpr (STREAM) __builtin_amdgcn_s_setprio(0);  // every load of the block is issued
+  if (select && pending != 0 && tile == 0 && h == 0 && tid == 0) {
+    if (pending == 1) args.src_table[r] = sel_src;
+    else atomicOr(args.status + (r >> 5), 1u << (r & 31));
+  }
   if constexpr (REPLAY) {
     // Replay of the accepted prefix: the bonus token and a_r drafts, the same
     // sequence of operations as the first a_r + 1 tokens of the window, so the

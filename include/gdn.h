@@ -267,6 +267,28 @@ int gdn_commit_select(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
                       int32_t *slot_table, uint32_t *status, void *stream);
 
 /*
+ * gdn_verify_window_select_commit -- gdn_commit_select of the previous window followed
+ * by gdn_verify_window_select of this one, in one launch: row r first makes slot
+ * prev_bank[r] * (k_max + 1) + accepted[r] its committed state (and slot_table[r]) when
+ * 0 <= accepted[r] < prev_row_tokens[r], then verifies this window from it into bank[r].
+ * The results are those of the two calls bit for bit, including an accepted count out of
+ * range: slot_table[r] is left as it was, bit (r % 32) of status[r / 32] is set, and the
+ * window runs from the entry it was left at.  Saves a launch per layer per step, which a
+ * latency-bound batch of one request feels most.  prev_row_tokens, prev_bank: host int32
+ * [n_rows], the previous call's row_tokens and bank; accepted: device int32 [n_rows].
+ * Errors as gdn_verify_window_select, plus GDN_E_RANGE for prev_row_tokens outside
+ * [1, k_max + 1] or a previous bank outside the pool, GDN_E_ALIAS when a previous bank is
+ * one this window writes.
+ */
+int gdn_verify_window_select_commit(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
+                                    const int32_t *prev_row_tokens, const int32_t *prev_bank,
+                                    const int32_t *accepted, const uint16_t *q, const uint16_t *k,
+                                    const uint16_t *v, const float *a, const float *b,
+                                    const float *A_log, const float *dt_bias, float *state_pool,
+                                    int32_t n_slots, int32_t *slot_table, const int32_t *bank,
+                                    uint16_t *o, uint32_t *status, void *stream);
+
+/*
  * gdn_chunked_workspace_bytes -- device workspace that gdn_chunked_prefill_with_
  * checkpoints and gdn_run_transaction need for these rows (0 on a bad argument).
  */

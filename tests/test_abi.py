@@ -41,7 +41,8 @@ def test_library_exports_every_declared_function():
             "gdn_plan_transaction", "gdn_run_transaction", "gdn_status_str", "gdn_version",
             "gdn_commit_replay", "gdn_verify_tree", "gdn_verify_window_delta",
             "gdn_commit_delta", "gdn_verify_window_delta_fold", "gdn_verify_window_select",
-            "gdn_commit_select", "gdn_chunked_prefill_with_checkpoints_static"} <= set(names)
+            "gdn_commit_select", "gdn_chunked_prefill_with_checkpoints_static",
+            "gdn_verify_window_select_commit"} <= set(names)
     lib = gb.lib()
     for n in names:
         assert hasattr(lib, n), "libgdn.so does not export %s" % n
@@ -316,6 +317,30 @@ def test_select_validation_codes():
     assert commit([4, 2], [2, 2]) == -4
     assert commit([4, 0], [0, 1]) == -3
     assert verify([], []) == 0 and commit([], []) == 0
+
+
+@no_gpu
+def test_select_commit_validation_codes():
+    lib = gb.lib()
+    b = Bufs()
+    d = _dims()
+
+    def call(T, PT, PB, bank, n_slots=72, acc=None):
+        Ta, Tp = _i32(T)
+        pa, pp = _i32(PT)
+        ba, bp = _i32(PB)
+        ka, kp = _i32(bank)
+        return lib.gdn_verify_window_select_commit(
+            ctypes.byref(d), len(Ta), Tp, pp, bp, acc if acc is not None else b.ptr(), *[b.ptr() for _ in range(7)],
+            b.ptr(), n_slots, b.ptr(), kp, b.ptr(), b.ptr(), ctypes.c_void_p(0))
+
+    assert call([4, 4], [4, 4], [0, 1], [2, 3], acc=ctypes.c_void_p(0)) == -1   # no accepted counts
+    assert call([4, 4], [5, 4], [0, 1], [2, 3]) == -3                           # previous window too long
+    assert call([4, 4], [4, 0], [0, 1], [2, 3]) == -3                           # previous window empty
+    assert call([4, 4], [4, 4], [0, 18], [2, 3]) == -3                          # previous bank past the pool
+    assert call([4, 4], [4, 4], [0, 0], [2, 3]) == -4                           # two rows share a previous bank
+    assert call([4, 4], [4, 4], [0, 3], [2, 3]) == -4                           # a previous bank is written now
+    assert call([4, 4], [4, 4], [0, 1], [2, 3], acc=b.ptr(misalign=2)) == -5    # misaligned counts
 
 
 @no_gpu

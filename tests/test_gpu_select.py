@@ -123,3 +123,58 @@ def test_conc16_workload_in_select_mode():
     w = synth.verify_workload("conc16", n_windows=128)
     worst = run_verify_workload(w, n_windows=w.n_windows, check_every=32, mode="select")
     say("conc16 select worst:", worst)
+
+
+@pytest.mark.parametrize("B", [1, 16], ids=["batch1", "rows16"])
+def test_commit_inside_verify_equals_commit_then_verify(B):
+    """gdn_verify_window_select_commit is gdn_commit_select followed by
+    gdn_verify_window_select, bit for bit: outputs every window, table and selected states
+    at the end, including a row whose accepted count is out of range (its table entry is
+    kept, its status bit set, and its window runs from the kept entry)."""
+    shape = synth.FULL
+    dims = dims_of(shape)
+    Hv, d = shape.n_v_heads, shape.d
+    n_windows = 6
+    g = synth.streams(131, 2 + 2 * n_windows)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    P = dev_params(A_log, dt_bias)
+    rows = np.arange(B, dtype=np.int32)
+    gen = torch.Generator(device="cpu").manual_seed(131)
+    start = (0.2 * torch.randn(B, Hv, d, d, generator=gen)).cuda()
+    pools = [torch.zeros(9 * B, Hv, d, d, device="cuda") for _ in range(2)]
+    tables = [torch.arange(8 * B, 9 * B, dtype=torch.int32, device="cuda") for _ in range(2)]
+    sts = [torch.zeros((B + 31) // 32, dtype=torch.int32, device="cuda") for _ in range(2)]
+    for p in pools:
+        p[8 * B:] = start
+    prev = None  # (T, bank, accepted) of the previous window, for the folded calls
+    for i in range(n_windows):
+        T = g[1].integers(1, 5, size=B).astype(np.int32)
+        tok = dev_tokens(synth.tokens(g[2 + i], shape, int(T.sum())))
+        acc_h = np.array([g[2 + n_windows + i].integers(0, t) for t in T], np.int32)
+        if i == 3:
+            acc_h[B // 2] = T[B // 2]  # out of range: the commit is refused for that row
+        acc = torch.from_numpy(acc_h).cuda()
+        bank = 2 * rows + (i % 2)
+        outs = []
+        for path in (0, 1):
+            o = torch.zeros(int(T.sum()), Hv, d, dtype=torch.bfloat16, device="cuda")
+            if path == 0 or prev is None:
+                gb.gdn_verify_window_select(dims, T, **tok, **P, state_pool=pools[path], slot_table=tables[path],
+                                            bank=bank, o=o, status=sts[path])
+            else:
+                gb.gdn_verify_window_select_commit(dims, T, prev[0], prev[1], prev[2], **tok, **P,
+                                                   state_pool=pools[path], slot_table=tables[path], bank=bank,
+                                                   o=o, status=sts[path])
+            if path == 0:
+                gb.gdn_commit_select(dims, T, acc, bank, pools[0], tables[0], sts[0])
+            outs.append(o)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "window %d: outputs differ" % i
+        prev = (T, bank, acc)
+    gb.gdn_commit_select(dims, prev[0], prev[2], prev[1], pools[1], tables[1], sts[1])  # the last window's commit
+    torch.cuda.synchronize()
+    assert torch.equal(tables[0], tables[1]), "slot tables differ"
+    assert torch.equal(sts[0], sts[1]), "status words differ"
+    assert int(sts[0][0]) & (1 << (B // 2)), "refused commit not flagged"
+    assert torch.equal(bits(pools[1][tables[1].long()]), bits(pools[0][tables[0].long()])), "committed states differ"
+    say("commit inside verify == commit then verify, %d rows, %d windows" % (B, n_windows))
