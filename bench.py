@@ -654,7 +654,15 @@ def main():
                     help="skip the streaming-bandwidth ceilings (plain 1:4 and 1:1 streams) reported for context")
     ap.add_argument("--no-transaction", action="store_true",
                     help="skip the mixed ragged transaction (4 prefills + 12 verify rows); --no-prefill skips it too")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode side lines")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline step and the copy-commit step (whose commit kernel, a plain copy "
+                         "of known size, calibrates the HBM counters); every other line is skipped")
     args = ap.parse_args()
+    if args.headline_only:
+        for flag in ("no_cpu_baseline", "no_batch1", "no_mixed", "no_prefill", "no_replay", "no_tree", "no_fused",
+                     "no_graph", "no_ceilings", "no_transaction", "no_decode"):
+            setattr(args, flag, True)
     if args.gpus != 1:
         print("bench.py: this path runs on one GPU; --gpus %d is not supported "
               "(rows and heads are independent, see the design notes on sharding)" % args.gpus,
@@ -681,8 +689,10 @@ def main():
     import numpy as np
     sets_sel, rs = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
                            select_commit=True)
-    _, rsel = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
-                      select=True)
+    rsel = None
+    if not args.headline_only:
+        _, rsel = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500,
+                          select=True)
     _, r16 = measure(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, stream, 500)
 
     def side(r, Ts):
@@ -695,9 +705,11 @@ def main():
     out_copy = side(r16, [4] * 16)
     out_copy["mode"] = ("dense checkpoints in a separate buffer (gdn_verify_window), commit copies the accepted "
                         "one into the row's pool slot (gdn_commit_accepted)")
-    out_sel = side(rsel, [4] * 16)
-    out_sel["mode"] = ("checkpoint select, the commit its own launch (gdn_verify_window_select, then "
-                       "gdn_commit_select): two launches per layer-step")
+    out_sel = None
+    if rsel is not None:
+        out_sel = side(rsel, [4] * 16)
+        out_sel["mode"] = ("checkpoint select, the commit its own launch (gdn_verify_window_select, then "
+                           "gdn_commit_select): two launches per layer-step")
     out_b1 = out_mixed = None
     if not args.no_batch1:
         _, r1s = measure(gb, synth, torch, [4], args.steps, args.warmup, args.layers, stream, 600,
@@ -777,7 +789,7 @@ def main():
         if not args.no_prefill:
             out_fused["prefill_us_per_call"] = measure_prefill(gb, synth, torch, stream, args.prefill_reps,
                                                                raw_qk=True)["us_per_call"]
-    decode = {"conc16": measure_decode(gb, synth, torch, 16, args.steps, args.warmup, args.layers, stream, 900),
+    decode = None if args.no_decode else {"conc16": measure_decode(gb, synth, torch, 16, args.steps, args.warmup, args.layers, stream, 900),
               "conc16_two_slot_sets": measure_decode(gb, synth, torch, 16, args.steps, args.warmup, args.layers,
                                                      stream, 900, two_sets=True),
               "batch1": measure_decode(gb, synth, torch, 1, args.steps, args.warmup, args.layers, stream, 950)}
