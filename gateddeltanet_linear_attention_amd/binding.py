@@ -16,7 +16,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgdn.so")
+# GDN_LIBRARY: another build of the library to load instead (the host-only sanitizer
+# build, whose launches are stubbed out, runs the validation tests under ASan/UBSan)
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_PKG, "libgdn.so")
 _lib = None
 
 GDN_OK = 0

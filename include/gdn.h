@@ -47,6 +47,25 @@
  *    the static workspace of gdn_chunked_prefill_with_checkpoints_static, filled once
  *    per GPU under a lock.  Calls are thread-safe, except that calls of that entry point
  *    overlapping on one GPU share its workspace (see there).
+ *
+ * Interface notes (choices in the signatures below, with their reasons).
+ *  - Token offsets are not passed: rows are packed in order, so row r's first token is
+ *    the sum of the host token counts before it, which the library computes while it
+ *    validates them (a separate device offset array could disagree with the counts).
+ *  - gdn_commit_accepted takes the window lengths as a host array, like every other
+ *    per-row count: they were fixed when the window was launched, so only the accepted
+ *    counts need to stay on the device.
+ *  - gdn_chunked_workspace_bytes takes the per-row token counts, not a token total: the
+ *    workspace holds one unit per (chunk, value head), and chunks never span rows.
+ *  - gdn_plan_transaction returns one route per row: the plan depends on row lengths
+ *    only (every row gets its checkpoints on either route), so no checkpoint counts and
+ *    no plan structure are needed.
+ *  - Streams are passed as void * (a hipStream_t), so the header needs no HIP header.
+ *  - gdn_dims carries a flags word (GDN_QK_L2NORM).
+ *  - Beyond decode, verification, the copy commit, the chunked prefill and the
+ *    transaction planner, the library offers other rollback forms (replay, rank-1
+ *    factors, checkpoint select), token-tree verification and a chunked prefill that
+ *    allocates nothing; each is described at its declaration.
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -104,10 +123,12 @@ enum { GDN_ROUTE_RECURRENT = 0, GDN_ROUTE_CHUNKED = 1 };
  * Reads the state of slot src_slot[r] (-1: zero state), applies the rule once,
  * writes o[r] and the new state to slot dst_slot[r] (== src_slot[r] updates in
  * place).  Decode is the single-token case of the verify window below: both run
- * one device routine, so verify checkpoint j is bit-identical to j+1 decode calls.
- * Both forms give the same bits; a new state bound for another slot is streamed
- * past the caches, which measured faster than updating in place (a caller with two
- * slot sets per request can alternate between them).
+ * one device routine, so verify checkpoint j is bit-identical to j+1 decode calls
+ * (decode fixes the rounding that verification must reproduce: "Native three-step
+ * MTP", section "What changed").  In place or into another slot, the bits are the
+ * same; a new state bound for another slot is streamed past the caches, which
+ * measured slightly faster than updating in place (a caller with two slot sets per
+ * request can alternate between them).
  * Errors: GDN_E_RANGE for a slot outside [0, n_slots) (src may be -1);
  * GDN_E_ALIAS if two rows share a dst slot or a dst slot is another row's src.
  */
@@ -142,7 +163,10 @@ int gdn_verify_window(const gdn_dims *dims, int32_t n_rows, const int32_t *row_t
  * window length T_r.  A row whose a_r is outside [0, T_r - 1] is left untouched
  * and bit (r % 32) of status[r / 32] is set (status: device uint32
  * [(n_rows + 31) / 32]; bits are OR-ed in, the caller clears them).  Accepted
- * lengths stay on the device: no host readback.
+ * lengths stay on the device: no host readback.  Restoring the checkpoint at the
+ * accepted length is how a rejected draft is undone (pull request "Run chained MTP
+ * drafting in the batch Engine", sections "Correctness fix" and "Rollback fix and
+ * corrected quality disposition"); device-resident draft data follows its "Summary".
  */
 int gdn_commit_accepted(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
                         const float *ckpt, const int32_t *accepted, float *state_pool,
@@ -303,8 +327,11 @@ size_t gdn_chunked_workspace_bytes(const gdn_dims *dims, int32_t n_rows,
  * o for all its tokens, the final state to slot dst_slot[r] (-1: not written),
  * and checkpoint slot j = the state after L_r - n_tail[r] + j + 1 tokens for
  * j < n_tail[r] <= min(L_r, k_max + 1), the same slot meaning as a verify window,
- * so gdn_commit_accepted works on either path.  Matches the sequential rule to
- * fp32 rounding, not bit for bit.
+ * so gdn_commit_accepted works on either path: a long prefill that takes the
+ * chunked form still publishes the checkpoints that draft rejection needs (the pull
+ * request's "Correctness fix").  The chunkwise form is the gated delta rule's
+ * blocked (UT transform / WY representation) evaluation (Yang, Kautz & Hatamizadeh,
+ * ICLR 2025).  Matches the sequential rule to fp32 rounding, not bit for bit.
  * Errors: GDN_E_WORKSPACE if ws_bytes < gdn_chunked_workspace_bytes(...);
  * GDN_E_UNSUPPORTED for chunk != 64; slot checks as gdn_decode_step.
  */

@@ -36,27 +36,36 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
-_LIB = os.path.join(_HERE, "libgdn_oracle.so")
+# GDN_ORACLE_LIBRARY: a prebuilt copy to load instead (the sanitizer build below);
+# it is then never rebuilt here
+_LIB = os.environ.get("GDN_ORACLE_LIBRARY") or os.path.join(_HERE, "libgdn_oracle.so")
+_PREBUILT = bool(os.environ.get("GDN_ORACLE_LIBRARY"))
 _lib = None
 
 _D = ctypes.POINTER(ctypes.c_double)
 _I = ctypes.POINTER(ctypes.c_int)
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (fp64, no contraction, OpenMP over units)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+def build(force: bool = True, out: str | None = None, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, no contraction, OpenMP over units).  out: another
+    path to write; sanitize: with AddressSanitizer and UndefinedBehaviorSanitizer (any
+    finding aborts), for a run with the ASan runtime preloaded."""
+    lib = out or _LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp%d" % os.getpid()
+        opt = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                "-fno-sanitize-recover=all"] if sanitize else ["-O2"])
+        subprocess.run(["gcc", *opt, "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
                         "-o", tmp, _SRC, "-lm"], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
+        if not _PREBUILT:
+            build(force=False)
         lib = ctypes.CDLL(_LIB)
         lib.gdn_oracle_gates.argtypes = [ctypes.c_int, _D, _D, ctypes.c_double, ctypes.c_double, _D, _D]
         lib.gdn_oracle_gates.restype = None

@@ -44,14 +44,16 @@ def test_library_exports_every_declared_function():
             "gdn_commit_select", "gdn_chunked_prefill_with_checkpoints_static",
             "gdn_verify_window_select_commit"} <= set(names)
     lib = gb.lib()
+    import gateddeltanet_linear_attention_amd as pkg
     for n in names:
         assert hasattr(lib, n), "libgdn.so does not export %s" % n
+        assert callable(getattr(pkg, n, None)), "the package does not export %s" % n
 
 
 def test_bandwidth_probe_library_loads_and_refuses_bad_arguments():
     """The benchmark's streaming-ceiling probe is a library of its own beside libgdn.so;
     its argument checks run on the host, so bad calls return -1 without a GPU."""
-    path = os.path.join(os.path.dirname(gb.LIB_PATH), "libgdn_probe.so")
+    path = os.path.join(os.path.dirname(os.path.abspath(gb.__file__)), "libgdn_probe.so")
     lib = ctypes.CDLL(path)
     f = lib.gdn_probe_stream
     f.restype = ctypes.c_int
