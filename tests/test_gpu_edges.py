@@ -115,10 +115,11 @@ def test_readme_example_runs_and_matches_the_oracle():
     import re
     import os
     src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "README.md")).read()
-    code = re.search(r"```python\n(.*?)```", src, re.S).group(1)
+    blocks = re.findall(r"```python\n(.*?)```", src, re.S)
+    assert len(blocks) == 2
     env = {}
     torch.manual_seed(0)
-    exec(compile(code, "README.md", "exec"), env)
+    exec(compile(blocks[0], "README.md", "exec"), env)
     torch.cuda.synchronize()
     host_ = lambda t: t.float().cpu().numpy().astype(np.float64)
     qh, kh = host_(env["q"]), host_(env["k"])
@@ -126,4 +127,15 @@ def test_readme_example_runs_and_matches_the_oracle():
                                      host_(env["A_log"]), host_(env["dt_bias"]), np.zeros((16, 32, 128, 128)))
     assert_o(host(env["o"]), o_o, "README example outputs")
     assert_state(host(env["pool"]), oracle.commit(ck_o, env["T"], np.full(16, 3)), "README example commit")
+    assert int(env["status"][0]) == 0
+    # the second example: four windows of the same tokens, each committing 3 drafts
+    exec(compile(blocks[1], "README.md", "exec"), env)
+    torch.cuda.synchronize()
+    S = np.zeros((16, 32, 128, 128))
+    for _ in range(4):
+        ck_s, o_s = oracle.verify_window(env["T"], qh, kh, host_(env["v"]), host_(env["a"]), host_(env["b"]),
+                                         host_(env["A_log"]), host_(env["dt_bias"]), S)
+        S = oracle.commit(ck_s, env["T"], np.full(16, 3))
+    assert_o(host(env["o"]), o_s, "README select example outputs (last window)")
+    assert_state(host(env["committed"]), S, "README select example committed states")
     assert int(env["status"][0]) == 0
