@@ -641,7 +641,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
   __shared__ __attribute__((aligned(16))) uint16_t sUr[3 * UPL];    // U^T
   __shared__ __attribute__((aligned(16))) uint16_t sUt[3 * UPL];    // U^T diag(e^{G_j - G}) of a checkpoint
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int r16 = lane & 15, g4 = lane >> 4;
   const int b = blockIdx.x;
   const int k8 = b >> 3;
@@ -659,7 +660,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
   auto ws_of = [&](int c) {
     return Ws<D>(args.ws + (int64_t(args.chunk0[row] + c) * n_v + h) * ChunkArgs::ws_unit_floats(D));
   };
-  auto has_tile = [&](int q) { return w + 4 * q < D / 16; };
+  // every wave has all NT column tiles when D / 16 is a multiple of 4 (d = 128)
+  auto has_tile = [&](int q) { return (D / 16) % 4 == 0 || w + 4 * q < D / 16; };
   // parts of S_c for 32-wide d block kb (lane (r16, g4): S_c[i0 + r16][32 kb + 8 g4 + e])
   auto s_parts = [&](const uint16_t *buf, int kb) {
     const int col = 32 * kb + 8 * g4;
@@ -718,12 +720,13 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
 
     // B. the carry on the wave's column tiles
     float4 Sn[NT];
+    const Parts8 uc0 = lds_get8<LDP>(sUc, UPL, r16, 8 * g4), uc1 = lds_get8<LDP>(sUc, UPL, r16, 32 + 8 * g4);
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
       floatx4 a = {f.e_last * S[q].x, f.e_last * S[q].y, f.e_last * S[q].z, f.e_last * S[q].w};
       if (has_tile(q)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) a = mma3b(a, f.kt[q][kb], lds_get8<LDP>(sUc, UPL, r16, 32 * kb + 8 * g4));
+        a = mma3b(a, f.kt[q][0], uc0);
+        a = mma3b(a, f.kt[q][1], uc1);
       }
       Sn[q] = make_float4(a[0], a[1], a[2], a[3]);
     }
