@@ -26,10 +26,10 @@
 //       gates, fp64 prefix sum of g, K K^T and Q K^T, forward substitution for T,
 //       W, U', P = Gamma o Q K^T, K^T and the decay factors -> workspace.
 //   chunk_chain_kernel  one block per (row, value head, 16 value channels), chunks in
-//       order: U = U' - W S_c^T, the outputs O of the block's channels, the state
-//       carry, the requested checkpoints and the final state.  The state tile never
-//       leaves the block: each lane keeps its part in registers, and LDS holds the
-//       bf16 parts that the products read.
+//       order: U = U' - W S_c^T, the state carry, the requested checkpoints and the
+//       final state in four waves, the outputs O of the block's channels in four more.
+//       The state tile never leaves the block: each carrying lane keeps its part in
+//       registers, and LDS holds the bf16 parts that the products read.
 // Every product runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, 2.5 PF dense
 // on MI355X) at fp32 accuracy: an fp32 operand enters as three bf16 parts that sum to it
 // to within 2^-24 of its magnitude (hi, the round of what hi leaves, the round of what
@@ -544,31 +544,26 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   }
 }
 
-// One chunk's operands of a chain wave (w, lane = r16 + 16 g4), fetched a chunk ahead:
-// every load reads one 1-KiB fragment block of the workspace.
+// One chunk's operands of a chain wave (w < 4, lane = r16 + 16 g4), fetched a chunk
+// ahead; every load reads one 1-KiB fragment block of the workspace.
 template <int D>
-struct ChainOps {
+struct CarryOps {
   static constexpr int NK = Ws<D>::NK;
   static constexpr int NT = (D / 16 + 3) / 4;  // 16-wide state column tiles per wave
   Parts8 w[NK];       // W[16 w + r16][32 kb + 8 g4 + 0..7] in parts (zero past d)
-  bf16x8 q[NK];       // Q[16 w + r16][32 kb + 8 g4 + 0..7] (zero past d)
   bf16x8 kt[NT][2];   // K^T[16 nt + r16][32 kb + 8 g4 + 0..7], nt = w + 4 q
-  Parts8 p[2];        // P[16 w + r16][32 kb + 8 g4 + 0..7] in parts
   float4 up;          // U'[16 w + 4 g4 + v][i0 + r16], v = 0..3
   float4 el;          // eL[16 w + 4 g4 + v]
-  float egq;          // eGq[16 w + r16]
   float e_last;       // e^{G_{n-1}}
-  // The operands arrive in three groups, each loaded where the chunk before has a
-  // stretch of matrix work to hide it behind: (a) W and Q of block kb, used by phase A;
-  // (b) K^T, U', eL, e_last, used by the U exchange and the carry; (c) P and eGq, used by
-  // the outputs.
+  // Two groups, each loaded where the chunk before has matrix work to hide it behind:
+  // (a) W of block kb, used by the U stage; (b) K^T, U', eL, e_last, used by the U
+  // exchange and the carry.
   __device__ void load_a(const Ws<D> &ws, int kb, int wv, int lane) {
     const int g4 = lane >> 4;
     const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4v{0u, 0u, 0u, 0u});
     const int b3 = (wv * NK + kb) * 3;
     w[kb] = 32 * kb + 8 * g4 < D ? Parts8{frag(ws.WF, b3, lane), frag(ws.WF, b3 + 1, lane), frag(ws.WF, b3 + 2, lane)}
                                  : Parts8{z, z, z};
-    q[kb] = frag(ws.QF, wv * NK + kb, lane);
   }
   __device__ void load_b(const Ws<D> &ws, int n, int wv, int lane, int tile) {
     const int g4 = lane >> 4;
@@ -584,22 +579,37 @@ struct ChainOps {
     el = *reinterpret_cast<const float4 *>(ws.eL + 16 * wv + 4 * g4);
     e_last = ws.eG[n - 1];
   }
-  __device__ void load_c(const Ws<D> &ws, int wv, int lane) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int b3 = (wv * 2 + kb) * 3;
-      p[kb] = Parts8{frag(ws.PF, b3, lane), frag(ws.PF, b3 + 1, lane), frag(ws.PF, b3 + 2, lane)};
-    }
-    egq = ws.eGq[16 * wv + (lane & 15)];
-  }
   __device__ void load(const Ws<D> &ws, int n, int wv, int lane, int tile) {
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) load_a(ws, kb, wv, lane);
     load_b(ws, n, wv, lane, tile);
-    load_c(ws, wv, lane);
   }
   static __device__ __forceinline__ bf16x8 frag(const uint16_t *a, int blk, int lane) {
     return *reinterpret_cast<const bf16x8 *>(a + Ws<D>::piece(blk, lane));
+  }
+};
+
+// One chunk's operands of an output wave (token tile t = w - 4), fetched a chunk ahead.
+template <int D>
+struct OutOps {
+  static constexpr int NK = Ws<D>::NK;
+  bf16x8 q[NK];       // Q[16 t + r16][32 kb + 8 g4 + 0..7] (zero past d)
+  Parts8 p[2];        // P[16 t + r16][32 kb + 8 g4 + 0..7] in parts
+  float egq;          // eGq[16 t + r16]
+  __device__ void load_q(const Ws<D> &ws, int kb, int t, int lane) { q[kb] = CarryOps<D>::frag(ws.QF, t * NK + kb, lane); }
+  __device__ void load_p(const Ws<D> &ws, int t, int lane) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int b3 = (t * 2 + kb) * 3;
+      p[kb] = Parts8{CarryOps<D>::frag(ws.PF, b3, lane), CarryOps<D>::frag(ws.PF, b3 + 1, lane),
+                     CarryOps<D>::frag(ws.PF, b3 + 2, lane)};
+    }
+    egq = ws.eGq[16 * t + (lane & 15)];
+  }
+  __device__ void load(const Ws<D> &ws, int t, int lane) {
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) load_q(ws, kb, t, lane);
+    load_p(ws, t, lane);
   }
 };
 
@@ -612,26 +622,33 @@ __device__ __forceinline__ void store_nt(float *dst, floatx4 x) {
   __builtin_nontemporal_store(x, reinterpret_cast<floatx4 *>(dst));
 }
 
-// The chain of one (row, value head, 16 value channels i0..i0+15): chunks in order.
-// Wave w owns tokens 16w..16w+15 of each chunk (U, outputs) and state column tiles
-// w and w + 4 (the carry).  Per chunk:
-//   A  U = U' - W S_c^T for the wave's tokens (S_c's parts from LDS, W split in
-//      registers); U^T diag(e^{G_n - G}) and U^T in parts -> LDS; barrier.
-//   B  the carry S_{c+1} = e^{G_n} S_c + U^T diag(.) K on the wave's column tiles, the
-//      outputs O = diag(e^G rq) Q S_c^T + P U of its tokens, the checkpoints this
-//      chunk holds, and S_{c+1}'s parts -> LDS; barrier.
-// The state stays in registers in the carry's output layout (lane (r16, g4) of wave w
-// holds S[i0 + r16][16 nt + 4 g4 + v]), which is also where the next carry's
-// accumulator starts from; LDS holds the parts of S_c that the U and output products
-// read, in two buffers used alternately (chunk c reads one while S_{c+1} is written to
-// the other).  Blocks of one (row, head) unit are spaced 8 apart in launch order, which
-// places all its tiles on one of the 8 chiplets and lets them share that L2's copy of
-// the chunk operands (W, K^T, P).
+// The chain of one (row, value head, 16 value channels i0..i0+15): chunks in order, in
+// blocks of 8 waves, two per SIMD.  Waves 0..3 carry the state: wave w owns tokens
+// 16w..16w+15 of each chunk for U and state column tiles w and w + 4 for the carry.
+// Waves 4..7 compute the outputs: wave 4 + t those of tokens 16t..16t+15.  Per chunk:
+//   A  chain waves: U = U' - W S_c^T for their tokens (S_c's parts from LDS, W split in
+//      registers); U^T diag(e^{G_n - G}) and U^T in parts -> LDS.
+//      output waves: (Q S_c^T)^T for their tokens from the same S_c parts.   barrier
+//   B  chain waves: the carry S_{c+1} = e^{G_n} S_c + U^T diag(.) K on their column
+//      tiles, the checkpoints this chunk holds, S_{c+1}'s parts -> LDS.
+//      output waves: O = diag(e^G rq) Q S_c^T + P U for their tokens (U's parts from
+//      LDS), stored.                                                          barrier
+// The output products are off the carry's path: on a SIMD the output wave's matrix and
+// vector work fills the chain wave's waits (one 4-wave block doing both kinds of work:
+// 2048-token prefill 108 us; this layout 101; the carry alone, outputs skipped, 90).  Every wave passes the same
+// sequence of barriers (the checkpoint positions are uniform over the block).
+// The state stays in the chain waves' registers in the carry's output layout (lane
+// (r16, g4) of wave w holds S[i0 + r16][16 nt + 4 g4 + v]), which is also where the
+// next carry's accumulator starts from; LDS holds the parts of S_c that the U and output
+// products read, in two buffers used alternately (chunk c reads one while S_{c+1} is
+// written to the other).  Blocks of one (row, head) unit are spaced 8 apart in launch
+// order, which places all its tiles on one of the 8 chiplets and lets them share that
+// L2's copy of the chunk operands (W, K^T, P).
 template <int D>
-__global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_units) {
+__global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_units) {
   constexpr int TILES = D / VT;
-  constexpr int NK = ChainOps<D>::NK;
-  constexpr int NT = ChainOps<D>::NT;
+  constexpr int NK = CarryOps<D>::NK;
+  constexpr int NT = CarryOps<D>::NT;
   constexpr int LDS_ = D + 8;     // S part row (bf16): 16-B aligned rows
   constexpr int SPL = VT * LDS_;  // elements per plane of S parts
   constexpr int UPL = VT * LDP;   // elements per plane of U parts
@@ -648,7 +665,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
   const int k8 = b >> 3;
   const int tile = k8 % TILES;
   const int unit = (k8 / TILES) * 8 + (b & 7);
-  if (unit >= n_units) return;
+  if (unit >= n_units) return;  // the whole block
   const int h = unit % args.n_v;
   const int row = unit / args.n_v;
   const int i0 = tile * VT;
@@ -660,8 +677,6 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
   auto ws_of = [&](int c) {
     return Ws<D>(args.ws + (int64_t(args.chunk0[row] + c) * n_v + h) * ChunkArgs::ws_unit_floats(D));
   };
-  // every wave has all NT column tiles when D / 16 is a multiple of 4 (d = 128)
-  auto has_tile = [&](int q) { return (D / 16) % 4 == 0 || w + 4 * q < D / 16; };
   // parts of S_c for 32-wide d block kb (lane (r16, g4): S_c[i0 + r16][32 kb + 8 g4 + e])
   auto s_parts = [&](const uint16_t *buf, int kb) {
     const int col = 32 * kb + 8 * g4;
@@ -669,7 +684,65 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
     const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4v{0u, 0u, 0u, 0u});
     return Parts8{z, z, z};
   };
+  // the checkpoint positions of chunk c: p in [max(tail0, c0), c0 + n); each but the
+  // row's last takes two barriers (the output waves pass them too)
+  auto tail_barriers = [&](int c0, int n) {
+    for (int p = max(tail0, c0); p < c0 + n; ++p)
+      if (p != L - 1) {
+        lds_barrier();
+        lds_barrier();
+      }
+  };
 
+  if (w >= 4) {  // ------------------------------------------------ output waves
+    const int t = w - 4;
+    lds_barrier();  // the start state's parts
+    auto body = [&](int c, const OutOps<D> &f, OutOps<D> &nx) {
+      const int cn = min(c + 1, nch - 1);
+      const Ws<D> wsn = ws_of(cn);
+      const int c0 = c * C;
+      const int n = min(C, L - c0);
+      const int64_t tok_base = int64_t(args.tok0[row]) + c0;
+      const uint16_t *sSc = sS[c & 1];
+      floatx4 oq = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb) {
+        const Parts8 sp = s_parts(sSc, kb);
+        nx.load_q(wsn, kb, t, lane);
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch stays where it is issued
+        oq = mma3a(oq, sp, f.q[kb]);  // O^T: rows are channels, columns tokens
+      }
+      lds_barrier();  // U of all 64 tokens in LDS
+      // O^T = S_c Q^T diag(e^G rq) + U^T P^T, lane (r16, g4) holding
+      // O[16 t + r16][i0 + 4 g4 + 0..3] (one 8-byte store)
+      floatx4 op = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)  // P is zero right of the diagonal: tokens >= 32 only for t >= 2
+        if (kb == 0 || t >= 2) op = mma6(op, lds_get8<LDP>(sUr, UPL, r16, 32 * kb + 8 * g4), f.p[kb]);
+      const float egq = f.egq;
+      nx.load_p(wsn, t, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (16 * t + r16 < n) {
+        const uint2 ob = make_uint2(bf16x2_rn(egq * oq[0] + op[0], egq * oq[1] + op[1]),
+                                    bf16x2_rn(egq * oq[2] + op[2], egq * oq[3] + op[3]));
+        *reinterpret_cast<uint2 *>(args.o + ((tok_base + 16 * t + r16) * n_v + h) * D + i0 + 4 * g4) = ob;
+      }
+      tail_barriers(c0, n);
+      lds_barrier();  // S_{c+1}'s parts complete; every read of this chunk's U parts done
+    };
+    OutOps<D> fa, fb;
+    fa.load(ws_of(0), t, lane);
+    for (int c = 0; c < nch; c += 2) {
+      body(c, fa, fb);
+      if (c + 1 >= nch) break;
+      body(c + 1, fb, fa);
+    }
+    return;
+  }
+
+  // --------------------------------------------------------------- chain waves
+  // every wave has all NT column tiles when D / 16 is a multiple of 4 (d = 128)
+  auto has_tile = [&](int q) { return (D / 16) % 4 == 0 || w + 4 * q < D / 16; };
   // the start state: registers, and its parts in LDS
   float4 S[NT];
 #pragma unroll
@@ -687,7 +760,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
   put_state(sS[0]);
   lds_barrier();
 
-  auto body = [&](int c, const ChainOps<D> &f, ChainOps<D> &nx) {
+  auto body = [&](int c, const CarryOps<D> &f, CarryOps<D> &nx) {
     const Ws<D> ws = ws_of(c);
     // the next chunk's operands (past the end: the last chunk again, never read)
     const int cn = min(c + 1, nch - 1);
@@ -695,22 +768,20 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
     const int nn = min(C, L - cn * C);
     const int c0 = c * C;
     const int n = min(C, L - c0);
-    const int64_t tok_base = int64_t(args.tok0[row]) + c0;
     const uint16_t *sSc = sS[c & 1];
 
-    // A. U = U' - W S_c^T and (Q S_c^T)^T for tokens 16w..16w+15, channels i0..i0+15 (one
-    //    read of S_c's parts serves both; two accumulators for U interleave the chains)
-    floatx4 ua = zero4(), ub = zero4(), oq = zero4();
+    // A. U = U' - W S_c^T for tokens 16w..16w+15, channels i0..i0+15 (two accumulators
+    //    interleave the chains)
+    floatx4 ua = zero4(), ub = zero4();
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) {
       const Parts8 sp = s_parts(sSc, kb);
       nx.load_a(wsn, kb, w, lane);
-      __builtin_amdgcn_sched_barrier(0);  // the prefetch stays where it is issued (see below)
+      __builtin_amdgcn_sched_barrier(0);  // the prefetch stays where it is issued
       if (kb & 1)
         ub = mma6(ub, f.w[kb], sp);
       else
         ua = mma6(ua, f.w[kb], sp);
-      oq = mma3a(oq, sp, f.q[kb]);  // O^T: rows are channels, columns tokens
     }
     ua += ub;
     const float4 u = make_float4(f.up.x - ua[0], f.up.y - ua[1], f.up.z - ua[2], f.up.w - ua[3]);
@@ -731,19 +802,6 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
         a = mma3b(a, f.kt[q][1], uc1);
       }
       Sn[q] = make_float4(a[0], a[1], a[2], a[3]);
-    }
-    nx.load_c(wsn, w, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    // the outputs of the wave's tokens, transposed: O^T = S_c Q^T diag(e^G rq) + U^T P^T,
-    // lane (r16, g4) holding O[16 w + r16][i0 + 4 g4 + 0..3] (one 8-byte store)
-    floatx4 op = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)  // P is zero right of the diagonal: tokens >= 32 only for waves 2, 3
-      if (kb == 0 || w >= 2) op = mma6(op, lds_get8<LDP>(sUr, UPL, r16, 32 * kb + 8 * g4), f.p[kb]);
-    if (16 * w + r16 < n) {
-      const uint2 ob = make_uint2(bf16x2_rn(f.egq * oq[0] + op[0], f.egq * oq[1] + op[1]),
-                                  bf16x2_rn(f.egq * oq[2] + op[2], f.egq * oq[3] + op[3]));
-      *reinterpret_cast<uint2 *>(args.o + ((tok_base + 16 * w + r16) * n_v + h) * D + i0 + 4 * g4) = ob;
     }
     // checkpoints at the positions p of this chunk with p >= tail0: slot p - tail0
     const int p_hi = c0 + n;
@@ -788,8 +846,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(ChunkArgs args, int n_
   // operands (loads complete in issue order) never waits for the next chunk's.  The
   // scheduling barriers after each prefetch group keep the compiler from sinking those
   // loads toward their use a chunk later: a load issued last is one whose wait drains
-  // every load before it (2048-token prefill 110 -> 108 us, mixed transaction 707 -> 689).
-  ChainOps<D> fa, fb;
+  // every load before it.
+  CarryOps<D> fa, fb;
   fa.load(ws_of(0), min(C, L), w, lane, tile);
   for (int c = 0; c < nch; c += 2) {
     body(c, fa, fb);
@@ -811,7 +869,7 @@ hipError_t launch_d(const ChunkArgs &args, int n_chunks, hipStream_t stream) {
                      stream, args);
   const int n_units = args.n_rows * args.n_v;
   const int groups = (n_units + 7) / 8;  // units are dealt to the 8 chiplets in groups of 8
-  hipLaunchKernelGGL(chunk_chain_kernel<D>, dim3(unsigned(groups * 8 * (D / VT))), dim3(256), 0, stream,
+  hipLaunchKernelGGL(chunk_chain_kernel<D>, dim3(unsigned(groups * 8 * (D / VT))), dim3(512), 0, stream,
                      args, n_units);
   return hipGetLastError();
 }
