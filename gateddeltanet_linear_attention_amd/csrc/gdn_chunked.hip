@@ -194,6 +194,26 @@ __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
 // term); rk = rq = 1 unless q/k are normalised in the kernels.  For d = 16 the pieces of
 // lanes g >= 2 of WF lie past the head width and are not written (the chain kernel reads
 // zeros in their place); QF holds zeros there.
+// A workspace store: cached (NT = false), or streamed past the caches (NT = true).  The
+// chain kernel reads the workspace right after this one; when it fits well within the
+// 256 MB last-level cache it is read from there (the 2048-token prefill's 144 MB: 103 us
+// cached against 120 us streamed), and when it does not, streaming the writes spares the
+// caches (the 4-prefill transaction's 1.1 GB: 690 -> 662 us).
+template <bool NT, typename T>
+__device__ __forceinline__ void ws_st(T *p, T v) {
+  if constexpr (NT) {
+    if constexpr (sizeof(T) == 8) {
+      typedef unsigned int u32x2s __attribute__((ext_vector_type(2)));
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x2s, v), reinterpret_cast<u32x2s *>(p));
+    } else {
+      typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4s, v), reinterpret_cast<u32x4s *>(p));
+    }
+  } else {
+    *p = v;
+  }
+}
+
 template <int D>
 struct Ws {
   static constexpr int NK = D >= 32 ? D / 32 : 1;  // 32-wide blocks over d
@@ -226,7 +246,7 @@ constexpr float inv_sqrt_d() {
   return D == 16 ? 0.25f : 0.0883883476483184405501f;
 }
 
-template <int D>
+template <int D, bool NT>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   __shared__ double sG[C];
   __shared__ __attribute__((aligned(16))) float sBeta[C];  // beta_m
@@ -339,7 +359,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     uint32_t wv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) wv[e] = uint32_t(src[(2 * e) * LDK]) | (uint32_t(src[(2 * e + 1) * LDK]) << 16);
-    *reinterpret_cast<uint4 *>(ws.KF + idx * 8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    ws_st<NT>(reinterpret_cast<uint4 *>(ws.KF + idx * 8), make_uint4(wv[0], wv[1], wv[2], wv[3]));
   }
 
   // 2. K K^T -> A (strictly lower, scaled) and Q K^T -> P (lower with diagonal) on
@@ -404,9 +424,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
       const Parts4 pp = split4(make_float4(pv[0], pv[1], pv[2], pv[3]));
       const int l2 = r16 + 16 * (2 * (tj & 1) + (g4 >> 1)), half = 4 * (g4 & 1);
       const int pb = (w * 2 + (tj >> 1)) * 3;
-      *reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 0, l2) + half) = pp.h;
-      *reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 1, l2) + half) = pp.m;
-      *reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 2, l2) + half) = pp.l;
+      ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 0, l2) + half), pp.h);
+      ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 1, l2) + half), pp.m);
+      ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 2, l2) + half), pp.l);
     }
   }
   lds_barrier();
@@ -533,12 +553,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
         const Parts4 wp = split4(make_float4(wa[jj][0], wa[jj][1], wa[jj][2], wa[jj][3]));
         const int l2 = r16 + 16 * (2 * (nt & 1) + (g4 >> 1)), half = 4 * (g4 & 1);
         const int wb = (ti * Ws<D>::NK + (nt >> 1)) * 3;
-        *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 0, l2) + half) = wp.h;
-        *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 1, l2) + half) = wp.m;
-        *reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 2, l2) + half) = wp.l;
+        ws_st<NT>(reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 0, l2) + half), wp.h);
+        ws_st<NT>(reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 1, l2) + half), wp.m);
+        ws_st<NT>(reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 2, l2) + half), wp.l);
         // U': lane (r16, g4) holds U'[16 ti + 4 g4 + v][16 nt + r16], the piece of block (nt, ti)
-        *reinterpret_cast<float4 *>(ws.UF + ((nt * 4 + ti) * 64 + lane) * 4) =
-            make_float4(ua[jj][0], ua[jj][1], ua[jj][2], ua[jj][3]);
+        ws_st<NT>(reinterpret_cast<float4 *>(ws.UF + ((nt * 4 + ti) * 64 + lane) * 4),
+                  make_float4(ua[jj][0], ua[jj][1], ua[jj][2], ua[jj][3]));
       }
     }
   }
@@ -865,8 +885,15 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
 
 template <int D>
 hipError_t launch_d(const ChunkArgs &args, int n_chunks, hipStream_t stream) {
-  hipLaunchKernelGGL(chunk_prep_kernel<D>, dim3(unsigned(n_chunks), unsigned(args.n_v)), dim3(256), 0,
-                     stream, args);
+  // the workspace streamed past the caches once it is well beyond a share of the
+  // last-level cache (see ws_st)
+  const bool nt = int64_t(n_chunks) * args.n_v * ChunkArgs::ws_unit_floats(D) * 4 > (int64_t(160) << 20);
+  if (nt)
+    hipLaunchKernelGGL((chunk_prep_kernel<D, true>), dim3(unsigned(n_chunks), unsigned(args.n_v)), dim3(256), 0,
+                       stream, args);
+  else
+    hipLaunchKernelGGL((chunk_prep_kernel<D, false>), dim3(unsigned(n_chunks), unsigned(args.n_v)), dim3(256), 0,
+                       stream, args);
   const int n_units = args.n_rows * args.n_v;
   const int groups = (n_units + 7) / 8;  // units are dealt to the 8 chiplets in groups of 8
   hipLaunchKernelGGL(chunk_chain_kernel<D>, dim3(unsigned(groups * 8 * (D / VT))), dim3(512), 0, stream,
