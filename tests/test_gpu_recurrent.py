@@ -50,8 +50,11 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
     each followed by commit of the accepted length -- mode "checkpoint" (dense
     checkpoints, gdn_commit_accepted), "replay" (verify without checkpoints, then
     gdn_commit_replay in place), "delta" (delta checkpoints, gdn_commit_delta in
-    place) or "select" (checkpoints into two pool banks per row used alternately,
-    gdn_commit_select updating the device slot table); the oracle runs the same chain independently from its own states.  A workload
+    place), "select" (checkpoints into two pool banks per row used alternately,
+    gdn_commit_select updating the device slot table) or "select_commit" (the same, each
+    window's commit made inside the next window's launch by
+    gdn_verify_window_select_commit, the last one by gdn_commit_select); the oracle runs the
+    same chain independently from its own states.  A workload
     with raw q/k runs with GDN_QK_L2NORM, the oracle on its own normalisation.
     Returns the worst errors seen."""
     dims = dims_of(w.shape, raw_qk=w.raw_qk)
@@ -80,7 +83,7 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
     say("%s: warm-up ok (o %.2e, state %.2e)" % (w.name, worst["o_abs"], worst["state"]))
 
     T = w.window_lens
-    if mode == "select":  # banks 2r, 2r + 1 per row; the warmed states in the slots after them
+    if mode in ("select", "select_commit"):  # banks 2r, 2r + 1 per row; the warmed states after them
         sel_pool = torch.zeros(9 * B, Hv, d, d, device="cuda")
         sel_pool[8 * B:] = pool
         table = torch.arange(8 * B, 9 * B, dtype=torch.int32, device="cuda")
@@ -93,11 +96,23 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
     out = dict(S_final=np.zeros_like(S_ref), ckpt=np.zeros((B, 4, Hv, d, d)),
                o=np.zeros((int(T.sum()), Hv, d)))
     cur = 0
+    prev = None  # select_commit: (bank, device accepted counts) of the window whose commit is pending
     for i in range(n_windows):
         win = w.window_tokens(i)
         acc = w.accepted(i)
         wd = dev_tokens(win)
-        if mode == "select":
+        if mode == "select_commit":
+            bank = 2 * rows + (i % 2)
+            if prev is None:
+                gb.gdn_verify_window_select(dims, T, **wd, **P, state_pool=sel_pool, slot_table=table, bank=bank,
+                                            o=o_win, status=status)
+            else:
+                gb.gdn_verify_window_select_commit(dims, T, T, prev[0], prev[1], **wd, **P, state_pool=sel_pool,
+                                                   slot_table=table, bank=bank, o=o_win, status=status)
+            prev = (bank, torch.from_numpy(acc).cuda())
+            if i == n_windows - 1:  # the last window's commit has no next launch to ride in
+                gb.gdn_commit_select(dims, T, prev[1], bank, sel_pool, table, status)
+        elif mode == "select":
             bank = 2 * rows + (i % 2)
             gb.gdn_verify_window_select(dims, T, **wd, **P, state_pool=sel_pool, slot_table=table, bank=bank,
                                         o=o_win, status=status)
@@ -126,8 +141,10 @@ def run_verify_workload(w: synth.VerifyWorkload, n_windows: int, check_every: in
                 e = assert_state(host(ckpt[r, :T[r]]), ck_o[r, :T[r]], "%s window 0 row %d ckpt" % (w.name, r))
                 worst["state"] = max(worst["state"], e)
         if (i + 1) % check_every == 0 or i == n_windows - 1:
-            committed = pool if mode != "select" else sel_pool[table.long()]
-            e = assert_state(host(committed), S_bufs[cur], "%s committed state after window %d" % (w.name, i))
+            committed = pool if mode not in ("select", "select_commit") else sel_pool[table.long()]
+            # select_commit: window i's commit is still pending until the next launch
+            ref = S_bufs[1 - cur] if (mode == "select_commit" and i < n_windows - 1) else S_bufs[cur]
+            e = assert_state(host(committed), ref, "%s committed state after window %d" % (w.name, i))
             worst["state"] = max(worst["state"], e)
             say("%s: window %d ok (o %.2e, state %.2e)" % (w.name, i, worst["o_abs"], worst["state"]))
     torch.cuda.synchronize()

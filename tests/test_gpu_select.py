@@ -10,7 +10,9 @@ after the accepted prefix becomes the committed state where it is.  Checked:
   q/k given or normalised in the kernels;
 * a source slot inside a bank of the call, or outside the pool, leaves the row
   untouched and sets its status bit; a bad accepted count leaves the table entry;
-* the batch-1 and concurrency-16 workloads in select mode against the oracle.
+* the batch-1 and concurrency-16 workloads in select mode against the oracle, with the
+  commit its own launch and with it inside the next window's verify;
+* the commit inside the verify against the two separate calls, bit for bit.
 """
 import numpy as np
 import pytest
@@ -123,6 +125,20 @@ def test_conc16_workload_in_select_mode():
     w = synth.verify_workload("conc16", n_windows=128)
     worst = run_verify_workload(w, n_windows=w.n_windows, check_every=32, mode="select")
     say("conc16 select worst:", worst)
+
+
+def test_batch1_workload_with_the_commit_inside_the_next_verify():
+    w = synth.verify_workload("batch1", n_windows=64)
+    worst = run_verify_workload(w, n_windows=w.n_windows, check_every=16, mode="select_commit")
+    say("batch1 select-commit worst:", worst)
+
+
+def test_conc16_workload_with_the_commit_inside_the_next_verify():
+    """The headline form (one gdn_verify_window_select_commit launch per window) on the
+    concurrency-16 workload (warm rows, K_r in {1, 2, 3}) against the oracle."""
+    w = synth.verify_workload("conc16", n_windows=128)
+    worst = run_verify_workload(w, n_windows=w.n_windows, check_every=32, mode="select_commit")
+    say("conc16 select-commit worst:", worst)
 
 
 @pytest.mark.parametrize("B", [1, 16], ids=["batch1", "rows16"])
