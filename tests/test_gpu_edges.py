@@ -1,6 +1,8 @@
 """Edge cases through the C ABI on the GPU.
 
 * Zero rows: every entry point returns without launching or writing anything.
+* The largest head count (H_v = 1024) with pool offsets past 2^31 elements, against the
+  oracle, through verify, commit, decode and the chunked prefill.
 * Degenerate gates and vectors, against the oracle: write strength beta -> 1 (the
   delta-rule overwrite) and -> 0 (pure decay), decay alpha -> 0 (state reset) and
   -> 1 (no decay), zero keys, zero values and zero queries, with q/k given or
@@ -139,3 +141,70 @@ def test_readme_example_runs_and_matches_the_oracle():
     assert_o(host(env["o"]), o_s, "README select example outputs (last window)")
     assert_state(host(env["committed"]), S, "README select example committed states")
     assert int(env["status"][0]) == 0
+
+
+def test_largest_head_count_with_slot_offsets_past_2_31_elements():
+    """H_v = 1024 (the largest supported), H_qk = 512, d = 128, in a 132-slot pool: one
+    slot is 2^24 floats, so the source and destination slots used here (128..131) lie
+    past 2^31 elements.  A verify window with every checkpoint, the copy commit, an
+    in-place decode step, and a 130-token chunked prefill (two full chunks and a partial
+    one) with four tail checkpoints, each against the oracle."""
+    shape = synth.HeadShape(512, 1024, 128)
+    dims = dims_of(shape)
+    Hv, d = shape.n_v_heads, shape.d
+    g = synth.streams(177, 5)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    P = dev_params(A_log, dt_bias)
+    n_slots = 132
+    pool = torch.zeros(n_slots, Hv, d, d, device="cuda")  # 8.6 GB
+    gen = torch.Generator(device="cpu").manual_seed(177)
+    S0 = 0.2 * torch.randn(2, Hv, d, d, generator=gen)
+    src = np.array([131, 129], np.int32)
+    pool[torch.as_tensor(src.astype(np.int64), device="cuda")] = S0.cuda()
+    S0 = S0.numpy().astype(np.float64)
+
+    # verify window (T = 4, 3) with checkpoints, then the copy commit into slots 130, 128
+    T = np.array([4, 3], np.int32)
+    win = synth.tokens(g[1], shape, int(T.sum()))
+    ckpt = torch.full((2, 4, Hv, d, d), float("nan"), device="cuda")
+    o = torch.empty(int(T.sum()), Hv, d, dtype=torch.bfloat16, device="cuda")
+    gb.gdn_verify_window(dims, T, **dev_tokens(win), **P, state_pool=pool, src_slot=src, ckpt=ckpt, o=o)
+    ck_o, o_o = oracle.verify_window(T, win.q, win.k, win.v, win.a, win.b, A_log, dt_bias, S0)
+    torch.cuda.synchronize()
+    assert_o(host(o), o_o, "H_v 1024 verify outputs")
+    for r in range(2):
+        assert_state(host(ckpt[r, :T[r]]), ck_o[r, :T[r]], "H_v 1024 verify row %d checkpoints" % r)
+    acc = np.array([3, 1], np.int32)
+    dst = np.array([130, 128], np.int32)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gb.gdn_commit_accepted(dims, T, ckpt, torch.from_numpy(acc).cuda(), pool, dst_slot=dst, status=status)
+    S1 = oracle.commit(ck_o, T, acc)
+    torch.cuda.synchronize()
+    assert int(status[0]) == 0
+    assert_state(host(pool[torch.as_tensor(dst.astype(np.int64), device="cuda")]), S1, "H_v 1024 committed states")
+
+    # one decode step in place on the committed slots
+    dec = synth.tokens(g[2], shape, 2)
+    od = torch.empty(2, Hv, d, dtype=torch.bfloat16, device="cuda")
+    gb.gdn_decode_step(dims, **dev_tokens(dec), **P, state_pool=pool, src_slot=dst, dst_slot=dst, o=od)
+    S2, od_ref = oracle.decode_step(dec.q, dec.k, dec.v, dec.a, dec.b, A_log, dt_bias, S1)
+    torch.cuda.synchronize()
+    assert_o(host(od), od_ref, "H_v 1024 decode outputs")
+    assert_state(host(pool[torch.as_tensor(dst.astype(np.int64), device="cuda")]), S2, "H_v 1024 decode states")
+
+    # chunked prefill of 130 tokens from slot 131 into slot 129, last four checkpoints
+    L = np.array([130], np.int32)
+    n_tail = np.array([4], np.int32)
+    pre = synth.tokens(g[3], shape, 130)
+    ck_c = torch.full((1, 4, Hv, d, d), float("nan"), device="cuda")
+    o_c = torch.empty(130, Hv, d, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gb.gdn_chunked_workspace_bytes(dims, L), dtype=torch.uint8, device="cuda")
+    gb.gdn_chunked_prefill_with_checkpoints(dims, L, n_tail, **dev_tokens(pre), **P, state_pool=pool,
+                                            src_slot=[131], dst_slot=[129], ckpt=ck_c, o=o_c, workspace=ws)
+    S_f, ck_f, o_f = oracle.run_sequential(L, pre.q, pre.k, pre.v, pre.a, pre.b, A_log, dt_bias, S0[:1],
+                                           n_tail=n_tail, n_slot=4)
+    torch.cuda.synchronize()
+    assert_o(host(o_c), o_f, "H_v 1024 chunked outputs")
+    assert_state(host(pool[129:130]), S_f, "H_v 1024 chunked final state")
+    assert_state(host(ck_c[0]), ck_f[0], "H_v 1024 chunked tail checkpoints")
+    assert torch.equal(bits(ck_c[0, 3]), bits(pool[129])), "last checkpoint != published state"
