@@ -655,8 +655,9 @@ __device__ __forceinline__ void store_nt(float *dst, floatx4 x) {
 //      LDS), stored.                                                          barrier
 // The output products are off the carry's path: on a SIMD the output wave's matrix and
 // vector work fills the chain wave's waits (one 4-wave block doing both kinds of work:
-// 2048-token prefill 108 us; this layout 101; the carry alone, outputs skipped, 90).  Every wave passes the same
-// sequence of barriers (the checkpoint positions are uniform over the block).
+// 2048-token prefill 108 us; this layout 101; the carry alone, outputs skipped, 90).
+// Every wave passes the same sequence of barriers (the checkpoint positions are uniform
+// over the block).
 // The state stays in the chain waves' registers in the carry's output layout (lane
 // (r16, g4) of wave w holds S[i0 + r16][16 nt + 4 g4 + v]), which is also where the
 // next carry's accumulator starts from; LDS holds the parts of S_c that the U and output

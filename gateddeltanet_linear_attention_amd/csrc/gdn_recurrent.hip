@@ -481,8 +481,8 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   if (dst >= 0) {
     // A new state bound for another slot is streamed past the caches like a checkpoint;
     // one written over the state just read is stored plainly (measured on the 16-row
-    // decode: out of place 12.95 -> 11.95 us with non-temporal stores, in place 15.25
-    // plain against 15.9 non-temporal).
+    // decode with cached state loads: out of place 12.95 -> 11.95 us with non-temporal
+    // stores, in place 15.25 plain against 15.9 non-temporal).
     const bool stream_out = dst != src;
 #pragma unroll
     for (int q = 0; q < RPL; ++q) {
@@ -570,8 +570,8 @@ hipError_t launch_recurrent(const RecurrentArgs &args, int d, hipStream_t stream
     // result is bit-identical in both layouts.
     // Otherwise (checkpoints, dense or into pool banks) one row per lane in 4-wave
     // blocks: smaller blocks turn over more often, which keeps each CU's loads and
-    // stores interleaved (the 16-row K=3 select verify: 31.8 us with two rows per lane
-    // in 8-wave blocks, 31.3 with one).
+    // stores interleaved (the 16-row K=3 select verify: 31.2 us with two rows per lane
+    // in 8-wave blocks, 29.8 with one).
     if (!args.ckpt && !args.tree_mode && int64_t(args.n_rows) * args.n_v >= 512)
       launch_d<128, 16, 2, 8>(args, stream);
     else
