@@ -9,7 +9,8 @@ slot table is pointed at that window's accepted checkpoint, accepted counts ~
 Binomial(3, 0.85) resident on the device; nothing is copied), then runs its previous
 bonus token and 3 drafts from that state, publishing the state after every token
 into the row's other bank of pool slots.  The same step as two launches per layer
-(gdn_verify_window_select for every layer, then gdn_commit_select) is a side line.
+(gdn_verify_window_select for every layer, then gdn_commit_select) is a side line, and so
+is the headline step replayed from a HIP graph (the launch gaps removed).
 Inputs are synthetic (seeded), at the head shape of a hybrid GatedDeltaNet layer:
 16 q/k heads, 32 value heads, d_k = d_v = 128, fp32 128x128 state per value head,
 bf16 q/k/v/o.
@@ -710,6 +711,13 @@ def main():
         out_sel = side(rsel, [4] * 16)
         out_sel["mode"] = ("checkpoint select, the commit its own launch (gdn_verify_window_select, then "
                            "gdn_commit_select): two launches per layer-step")
+    out_graph16 = None
+    if not (args.no_graph or args.headline_only):
+        g16 = measure_graph(gb, synth, torch, [4] * 16, args.steps, args.warmup, args.layers, 500,
+                            select_commit=True)
+        out_graph16 = {"mode": "the headline step replayed from a HIP graph (two steps per replay, banks "
+                               "alternating)", "ms_per_layer": g16["ms_per_layer"],
+                       "head_token_updates_per_s": g16["head_token_updates_per_s"]}
     out_b1 = out_mixed = None
     if not args.no_batch1:
         _, r1s = measure(gb, synth, torch, [4], args.steps, args.warmup, args.layers, stream, 600,
@@ -846,6 +854,7 @@ def main():
         "step_gbps": rs["step_gbps"],
         "conc16_k3_copy_commit": out_copy,
         "conc16_k3_select_two_launches": out_sel,
+        "conc16_k3_graph": out_graph16,
         "batch1": out_b1,
         "conc16_mixed_k": out_mixed,
         "conc16_k3_replay": out_replay,
