@@ -6,7 +6,11 @@ and replayed, which removes the per-call host launch cost that dominates at batc
 Each replay is checked bit for bit against the same step run eagerly on a copy of the
 buffers, with eager work and device synchronisation between replays; the checkpoint
 and replay commits are covered, and the folded delta mode (one launch per layer and
-step, a graph of two steps alternating the two factor buffers).
+step, a graph of two steps alternating the two factor buffers).  The checkpoint-select
+loop (batch 1 and 16 rows, the commit inside the next verify or its own launch) is
+checked against the oracle instead: new windows and accepted counts are copied into the
+graph's input buffers between replays, and every replay's outputs and committed states
+are compared with the oracle's sequential run.
 """
 import numpy as np
 import pytest
@@ -146,14 +150,15 @@ def test_captured_folded_steps_match_eager_steps():
     say("graph replays of folded steps match eager steps")
 
 
+@pytest.mark.parametrize("B", [1, 16], ids=["batch1", "rows16"])
 @pytest.mark.parametrize("form", ["commit_inside_verify", "commit_then_verify"])
-def test_batch1_decode_loop_from_a_graph_against_the_oracle(form):
-    """A batch-1 speculative decoding loop of K=3 windows through 3 layers, captured once
-    as a HIP graph of two windows per layer (checkpoint select: the pool banks alternate)
-    and replayed 4 times.  Between replays the next windows' tokens and accepted counts
-    (Binomial(3, 0.85)) are copied into the device buffers the graph reads; after every
-    replay each layer's outputs of both windows and its committed state are checked
-    against the oracle's sequential run of the same windows and accepted prefixes.
+def test_decode_loop_from_a_graph_against_the_oracle(form, B):
+    """A speculative decoding loop of K=3 windows (B rows) through 3 layers, captured once
+    as a HIP graph of two windows per layer (checkpoint select: each row's two pool banks
+    alternate) and replayed 4 times.  Between replays the next windows' tokens and accepted
+    counts (Binomial(3, 0.85) per row) are copied into the device buffers the graph reads;
+    after every replay each layer's outputs of both windows and its committed states are
+    checked against the oracle's sequential run of the same windows and accepted prefixes.
     Forms: the previous window's commit inside the verify (one launch per layer and
     window), and gdn_commit_select then gdn_verify_window_select."""
     import oracle
@@ -163,25 +168,27 @@ def test_batch1_decode_loop_from_a_graph_against_the_oracle(form):
     Hv, d = shape.n_v_heads, shape.d
     n_layers, n_replays = 3, 4
     n_win = 1 + 2 * n_replays
-    T = np.array([4], np.int32)
+    rows = np.arange(B, dtype=np.int32)
+    T = np.full(B, 4, np.int32)
+    banks = [2 * rows + j for j in (0, 1)]
     cap = torch.cuda.Stream()
     layers = []
     for li in range(n_layers):
         g = synth.streams(140 + li, 3)
         A_log, dt_bias = synth.head_params(g[0], shape)
-        wins = [synth.tokens(g[1], shape, 4) for _ in range(n_win)]
-        accs = synth.accepted_counts(g[2], np.full(n_win, 3)).astype(np.int32)
+        wins = [synth.tokens(g[1], shape, 4 * B) for _ in range(n_win)]
+        accs = np.stack([synth.accepted_counts(g[2], np.full(B, 3)) for _ in range(n_win)]).astype(np.int32)
         gen = torch.Generator(device="cpu").manual_seed(140 + li)
-        start = (0.2 * torch.randn(1, Hv, d, d, generator=gen)).cuda()
-        pool = torch.zeros(9, Hv, d, d, device="cuda")
-        pool[8:] = start
+        start = (0.2 * torch.randn(B, Hv, d, d, generator=gen)).cuda()
+        pool = torch.zeros(9 * B, Hv, d, d, device="cuda")
+        pool[8 * B:] = start
         L = dict(P=dev_params(A_log, dt_bias), wins=wins, accs=accs, pool=pool, A_log=A_log, dt_bias=dt_bias,
-                 table=torch.tensor([8], dtype=torch.int32, device="cuda"),
-                 status=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                 table=torch.arange(8 * B, 9 * B, dtype=torch.int32, device="cuda"),
+                 status=torch.zeros((B + 31) // 32, dtype=torch.int32, device="cuda"),
                  tok=[dev_tokens(wins[1]), dev_tokens(wins[2])],
-                 acc=[torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(2)],
-                 o=[torch.zeros(4, Hv, d, dtype=torch.bfloat16, device="cuda") for _ in range(2)])
-        # the oracle's run: committed state before each window, outputs of each window
+                 acc=[torch.zeros(B, dtype=torch.int32, device="cuda") for _ in range(2)],
+                 o=[torch.zeros(4 * B, Hv, d, dtype=torch.bfloat16, device="cuda") for _ in range(2)])
+        # the oracle's run: committed states before each window, outputs of each window
         S = host(start)
         L["S_before"], L["o_ref"] = [], []
         for w in range(n_win):
@@ -189,28 +196,28 @@ def test_batch1_decode_loop_from_a_graph_against_the_oracle(form):
             ck, o_ref = oracle.verify_window(T, wins[w].q, wins[w].k, wins[w].v, wins[w].a, wins[w].b, A_log,
                                              dt_bias, S)
             L["o_ref"].append(o_ref)
-            S = oracle.commit(ck, T, accs[w:w + 1])
+            S = oracle.commit(ck, T, accs[w])
         L["S_after"] = S
-        # window 0, eagerly, into bank 0
-        o0 = torch.zeros(4, Hv, d, dtype=torch.bfloat16, device="cuda")
+        # window 0, eagerly, into bank 0 of every row
+        o0 = torch.zeros(4 * B, Hv, d, dtype=torch.bfloat16, device="cuda")
         gb.gdn_verify_window_select(dims, T, **dev_tokens(wins[0]), **L["P"], state_pool=pool,
-                                    slot_table=L["table"], bank=[0], o=o0, status=L["status"])
+                                    slot_table=L["table"], bank=banks[0], o=o0, status=L["status"])
         torch.cuda.synchronize()
         assert_o(host(o0), L["o_ref"][0], "layer %d window 0 outputs" % li)
         # the graph's calls: window j of a replay verifies into bank 1 - j, committing the
-        # previous window (bank j, count acc[j]) first
+        # previous window (bank j, counts acc[j]) first
         calls = [[], []]
         for j in (0, 1):
             if form == "commit_inside_verify":
                 calls[j].append(gb.prepare_verify_window_select_commit(
-                    dims, T, T, [j], L["acc"][j], **L["tok"][j], **L["P"], state_pool=pool,
-                    slot_table=L["table"], bank=[1 - j], o=L["o"][j], status=L["status"], stream=cap))
+                    dims, T, T, banks[j], L["acc"][j], **L["tok"][j], **L["P"], state_pool=pool,
+                    slot_table=L["table"], bank=banks[1 - j], o=L["o"][j], status=L["status"], stream=cap))
             else:
-                calls[j].append(gb.prepare_commit_select(dims, T, L["acc"][j], [j], pool, L["table"], L["status"],
-                                                         stream=cap))
+                calls[j].append(gb.prepare_commit_select(dims, T, L["acc"][j], banks[j], pool, L["table"],
+                                                         L["status"], stream=cap))
                 calls[j].append(gb.prepare_verify_window_select(dims, T, **L["tok"][j], **L["P"], state_pool=pool,
-                                                                slot_table=L["table"], bank=[1 - j], o=L["o"][j],
-                                                                status=L["status"], stream=cap))
+                                                                slot_table=L["table"], bank=banks[1 - j],
+                                                                o=L["o"][j], status=L["status"], stream=cap))
         L["calls"] = calls
         layers.append(L)
 
@@ -227,24 +234,23 @@ def test_batch1_decode_loop_from_a_graph_against_the_oracle(form):
                 src = dev_tokens(L["wins"][w])
                 for key in src:
                     L["tok"][j][key].copy_(src[key])
-            L["acc"][0].fill_(int(L["accs"][w1 - 1]))
-            L["acc"][1].fill_(int(L["accs"][w2 - 1]))
+            L["acc"][0].copy_(torch.from_numpy(L["accs"][w1 - 1]))
+            L["acc"][1].copy_(torch.from_numpy(L["accs"][w2 - 1]))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         for li, L in enumerate(layers):
-            assert int(L["status"][0]) == 0, "layer %d replay %d: status %d" % (li, i, int(L["status"][0]))
+            assert int(L["status"].abs().sum()) == 0, "layer %d replay %d: status set" % (li, i)
             assert_o(host(L["o"][0]), L["o_ref"][w1], "layer %d window %d outputs" % (li, w1))
             assert_o(host(L["o"][1]), L["o_ref"][w2], "layer %d window %d outputs" % (li, w2))
-            # committed state: window w1's accepted checkpoint (the graph committed it)
-            slot = int(L["table"][0])
-            assert slot == 4 + int(L["accs"][w1]), "layer %d: table entry %d" % (li, slot)
-            assert_state(host(L["pool"][slot:slot + 1]), L["S_before"][w2], "layer %d committed state" % li)
-    for li, L in enumerate(layers):  # the last window's commit, eagerly: the oracle's final state
-        gb.gdn_commit_select(dims, T, torch.tensor([int(L["accs"][-1])], dtype=torch.int32, device="cuda"), [0],
-                             L["pool"], L["table"], L["status"])
+            # committed states: window w1's accepted checkpoints (the graph committed them)
+            expect = 4 * banks[1] + L["accs"][w1]
+            assert np.array_equal(L["table"].cpu().numpy(), expect), "layer %d: table entries" % li
+            assert_state(host(L["pool"][L["table"].long()]), L["S_before"][w2], "layer %d committed states" % li)
+    for li, L in enumerate(layers):  # the last window's commit, eagerly: the oracle's final states
+        gb.gdn_commit_select(dims, T, torch.from_numpy(L["accs"][-1]).cuda(), banks[0], L["pool"], L["table"],
+                             L["status"])
         torch.cuda.synchronize()
-        slot = int(L["table"][0])
-        assert_state(host(L["pool"][slot:slot + 1]), L["S_after"], "layer %d final committed state" % li)
-    say("batch-1 loop from a graph (%s): %d replays x 2 windows x %d layers vs the oracle" % (form, n_replays,
-                                                                                              n_layers))
+        assert_state(host(L["pool"][L["table"].long()]), L["S_after"], "layer %d final committed states" % li)
+    say("decode loop from a graph (%s, %d rows): %d replays x 2 windows x %d layers vs the oracle"
+        % (form, B, n_replays, n_layers))
