@@ -651,6 +651,8 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--transaction-only", action="store_true",
                     help="time only the mixed ragged transaction and print its figures")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode lines (16 rows in place, into a second slot set, batch 1)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the streaming-bandwidth ceilings (plain 1:4 and 1:1 streams) reported for context")
     ap.add_argument("--no-transaction", action="store_true",
@@ -685,6 +687,14 @@ def main():
         return
     if args.transaction_only:
         print(json.dumps(measure_transaction(gb, synth, torch, stream, args.prefill_reps)), flush=True)
+        return
+    if args.decode_only:
+        print(json.dumps({
+            "conc16": measure_decode(gb, synth, torch, 16, args.steps, args.warmup, args.layers, stream, 900),
+            "conc16_two_slot_sets": measure_decode(gb, synth, torch, 16, args.steps, args.warmup, args.layers,
+                                                   stream, 900, two_sets=True),
+            "batch1": measure_decode(gb, synth, torch, 1, args.steps, args.warmup, args.layers, stream, 950)}),
+            flush=True)
         return
 
     import numpy as np
