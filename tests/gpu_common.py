@@ -106,3 +106,27 @@ def bits(t):
     """int32 view of an fp32 device tensor (bitwise comparisons, NaN-safe)."""
     import torch
     return t.contiguous().view(torch.int32)
+
+
+def _raw(t):
+    import torch
+    return t.contiguous().view({4: torch.int32, 2: torch.int16}[t.element_size()])
+
+
+def assert_same_bits(a, b, what: str = "tensors"):
+    """Bitwise equality of two device tensors of one shape and element size (fp32 states,
+    bf16 outputs; NaN-safe).  On a mismatch the message gives how many elements differ,
+    the index of the first one and both values with their bit patterns."""
+    assert tuple(a.shape) == tuple(b.shape), "%s: shapes %s and %s" % (what, tuple(a.shape), tuple(b.shape))
+    ra, rb = _raw(a), _raw(b)
+    if bool((ra == rb).all()):
+        return
+    diff = (ra != rb).flatten()
+    n = int(diff.sum())
+    first = int(diff.nonzero()[0])
+    idx = tuple(int(i) for i in np.unravel_index(first, tuple(a.shape)))
+    fa, fb = a.contiguous().flatten()[first], b.contiguous().flatten()[first]
+    mask = (1 << (8 * a.element_size())) - 1
+    raise AssertionError("%s: %d of %d elements differ; first at %s: %r (0x%0*x) vs %r (0x%0*x)" % (
+        what, n, a.numel(), idx, float(fa), 2 * a.element_size(), int(ra.flatten()[first]) & mask,
+        float(fb), 2 * b.element_size(), int(rb.flatten()[first]) & mask))

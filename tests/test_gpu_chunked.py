@@ -20,8 +20,8 @@ import pytest
 import oracle
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
-from tests.gpu_common import (assert_o, assert_state, bits, dev_params, dev_tokens, dims_of, host,
-                              index_tokens, ref_qk, say)
+from tests.gpu_common import (assert_o, assert_same_bits, assert_state, bits, dev_params, dev_tokens, dims_of,
+                              host, index_tokens, ref_qk, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +74,7 @@ def run_chunked_case(shape, lens, n_tail, src_kind, seed, gate_shift=0.0, what="
             ms = max(ms, assert_state(host(ckpt[r, :n_tail[r]]), ck_ref[r, :n_tail[r]],
                                       what + " row %d checkpoints" % r))
         assert bool((bits(ckpt[r, n_tail[r]:]) == POISON).all()), what + " row %d: extra slot written" % r
-    assert torch.equal(bits(pool[:B]), bits(before[:B])), what + ": a source slot was written"
+    assert_same_bits(pool[:B], before[:B], what + ": a source slot was written")
     say("%s: max |do| %.2e, state rel %.2e" % (what, mo, ms))
 
 
@@ -99,7 +99,7 @@ def test_prefill_2048_tokens_with_last_four_checkpoints(raw_qk):
     ms = assert_state(host(pool), S_ref, "prefill final state")
     ms = max(ms, assert_state(host(ckpt[0]), ck_ref[0], "prefill checkpoints (last 4 positions)"))
     # checkpoint 3 is the final state (bit for bit); checkpoint j is the state after L-3+j tokens
-    assert torch.equal(bits(ckpt[0, 3]), bits(pool[0])), "last checkpoint differs from the final state"
+    assert_same_bits(ckpt[0, 3], pool[0], "last checkpoint differs from the final state")
     say("prefill 2048: max |do| %.2e, state rel %.2e" % (mo, ms))
 
 
@@ -178,9 +178,8 @@ def test_transaction_of_140_rows_mixing_routes():
         if n_ck[r]:
             ms = max(ms, assert_state(ck_h[r, :n_ck[r]], ck_ref[r, :n_ck[r]], "row %d checkpoints" % r))
         assert bool((bits(ckpt[r, n_ck[r]:]) == POISON).all()), "row %d: extra checkpoint slot written" % r
-    assert torch.equal(bits(pool[:B]), bits(before[:B])), "a source slot was written"
-    assert torch.equal(bits(pool[B:].index_select(0, vf_i)), bits(before[B:].index_select(0, vf_i))), \
-        "a verify row published a state"
+    assert_same_bits(pool[:B], before[:B], "a source slot was written")
+    assert_same_bits(pool[B:].index_select(0, vf_i), before[B:].index_select(0, vf_i), "a verify row published a state")
     say("140-row transaction: max |do| %.2e, state rel %.2e" % (mo, ms))
 
 
@@ -209,8 +208,8 @@ def test_chunked_matches_verify_within_tolerance_and_commit_works_on_it():
     torch.cuda.synchronize()
     assert_state(host(ck_c[0]), host(ck_v[0]), "chunked vs verify checkpoints")
     assert_o(host(o_c), host(o_v), "chunked vs verify outputs")
-    assert torch.equal(bits(pool[2]), bits(ck_c[0, 2]))
-    assert torch.equal(bits(pool[1]), bits(ck_c[0, 3]))
+    assert_same_bits(pool[2], ck_c[0, 2], "pool[2] vs ck_c[0, 2]")
+    assert_same_bits(pool[1], ck_c[0, 3], "pool[1] vs ck_c[0, 3]")
 
 
 # ---------------------------------------------------------------- mixed transaction
@@ -337,8 +336,9 @@ def test_transaction_verify_rows_bit_identical_to_verify_window(raw_qk):
                          src_slot=short.astype(np.int32), ckpt=ck2, o=o2)
     torch.cuda.synchronize()
     for j, r in enumerate(short):
-        assert torch.equal(bits(ckpt[r, :n_ck[r]]), bits(ck2[j, lens[r] - n_ck[r]:lens[r]]))
-    assert torch.equal(o[torch.as_tensor(idx, device="cuda")].view(torch.int16), o2.view(torch.int16))
+        assert_same_bits(ckpt[r, :n_ck[r]], ck2[j, lens[r] - n_ck[r]:lens[r]],
+                         "row %d: transaction checkpoints vs the verify window's" % r)
+    assert_same_bits(o[torch.as_tensor(idx, device="cuda")], o2, "o[torch.as_tensor(idx, device='cuda')] vs o2")
     # the long rows' checkpoints are the oracle's
     S_ref, ck_ref, o_ref = oracle.run_sequential(lens, *ref_qk(tok, raw_qk), tok.v, tok.a, tok.b, A_log, dt_bias,
                                                  host(pool), n_tail=n_ck, n_slot=4)
@@ -377,8 +377,8 @@ def test_prefill_published_on_one_stream_is_seen_by_verify_on_another():
 
     a = run(False)
     b = run(True)
-    assert torch.equal(bits(a[0]), bits(b[0]))
-    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+    assert_same_bits(a[0], b[0], "a[0] vs b[0]")
+    assert_same_bits(a[1], b[1], "a[1] vs b[1]")
 
 
 def test_chunked_errors_write_nothing():

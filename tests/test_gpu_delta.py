@@ -19,7 +19,7 @@ import pytest
 
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
-from tests.gpu_common import bits, dev_params, dev_tokens, dims_of, say
+from tests.gpu_common import assert_same_bits, bits, dev_params, dev_tokens, dims_of, say
 from tests.test_gpu_recurrent import run_verify_workload
 
 pytestmark = pytest.mark.gpu
@@ -63,11 +63,11 @@ def test_delta_commit_equals_checkpoint_commit_bitwise(shape, raw_qk):
     gb.gdn_commit_delta(dims, T, td["k"], delta, acc, pool, src_slot=rows, dst_slot=rows + 2 * B, status=status)
     torch.cuda.synchronize()
     assert int(status.abs().sum()) == 0
-    assert torch.equal(o_ck.view(torch.int16), o_dl.view(torch.int16))
-    assert torch.equal(bits(pool[:B]), bits(before[:B])), "verify wrote the committed pool"
+    assert_same_bits(o_ck, o_dl, "o_ck vs o_dl")
+    assert_same_bits(pool[:B], before[:B], "verify wrote the committed pool")
     for r in range(B):
-        assert torch.equal(bits(pool[2 * B + r]), bits(pool[B + r])), \
-            "row %d (T=%d, a=%d): delta fold differs from checkpoint commit" % (r, T[r], pairs[r][1])
+        assert_same_bits(pool[2 * B + r], pool[B + r],
+                         "row %d (T=%d, a=%d): delta fold differs from checkpoint commit" % (r, T[r], pairs[r][1]))
 
 
 def test_delta_in_place_flags_bad_counts_zero_source_and_spans_launches():
@@ -104,7 +104,7 @@ def test_delta_in_place_flags_bad_counts_zero_source_and_spans_launches():
         expect[r // 32] |= 1 << (r % 32)
     assert [int(x) & 0xFFFFFFFF for x in st.cpu()] == expect
     assert torch.equal(st, st_ref)
-    assert torch.equal(bits(pool), bits(ref)), "delta fold differs from checkpoint commit"
+    assert_same_bits(pool, ref, "delta fold differs from checkpoint commit")
 
 
 def test_batch1_workload_in_delta_mode():
@@ -162,12 +162,12 @@ def test_folded_verify_equals_commit_then_verify_bitwise(raw_qk):
     cu2 = np.concatenate([[0], np.cumsum(T2)])
     for r in range(B):
         if r == 4:
-            assert torch.equal(bits(pool[r]), bits(base[r])), "flagged row was folded"
+            assert_same_bits(pool[r], base[r], "flagged row was folded")
             assert not bool(o2[cu2[r]:cu2[r + 1]].view(torch.int16).any()), "flagged row wrote outputs"
             continue
-        assert torch.equal(bits(pool[r]), bits(ref[r])), "row %d: folded state differs" % r
-        assert torch.equal(o2[cu2[r]:cu2[r + 1]].view(torch.int16), o2_ref[cu2[r]:cu2[r + 1]].view(torch.int16))
-        assert torch.equal(bits(d2[r, :T2[r]]), bits(d2_ref[r, :T2[r]])), "row %d: factors differ" % r
+        assert_same_bits(pool[r], ref[r], "row %d: folded state differs" % r)
+        assert_same_bits(o2[cu2[r]:cu2[r + 1]], o2_ref[cu2[r]:cu2[r + 1]], "row %d: folded verify outputs" % r)
+        assert_same_bits(d2[r, :T2[r]], d2_ref[r, :T2[r]], "row %d: factors differ" % r)
 
 
 def test_conc16_workload_with_folded_verify():

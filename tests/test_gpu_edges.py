@@ -15,7 +15,8 @@ import pytest
 import oracle
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
-from tests.gpu_common import assert_o, assert_state, bits, dev_params, dev_tokens, dims_of, host, ref_qk
+from tests.gpu_common import (assert_o, assert_same_bits, assert_state, bits, dev_params, dev_tokens, dims_of,
+                              host, ref_qk)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +61,7 @@ def test_zero_row_calls_write_nothing():
     gb.gdn_run_transaction(dims, none, none, **tok, **P, state_pool=pool, src_slot=none, dst_slot=none,
                            ckpt=ckpt, o=o, workspace=ws)
     torch.cuda.synchronize()
-    assert torch.equal(bits(pool), bits(before))
+    assert_same_bits(pool, before, "pool vs before")
 
 
 def _degenerate_tokens(shape, raw_qk, seed):
@@ -207,4 +208,4 @@ def test_largest_head_count_with_slot_offsets_past_2_31_elements():
     assert_o(host(o_c), o_f, "H_v 1024 chunked outputs")
     assert_state(host(pool[129:130]), S_f, "H_v 1024 chunked final state")
     assert_state(host(ck_c[0]), ck_f[0], "H_v 1024 chunked tail checkpoints")
-    assert torch.equal(bits(ck_c[0, 3]), bits(pool[129])), "last checkpoint != published state"
+    assert_same_bits(ck_c[0, 3], pool[129], "last checkpoint != published state")

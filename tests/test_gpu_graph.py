@@ -17,7 +17,7 @@ import pytest
 
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
-from tests.gpu_common import bits, dev_params, dev_tokens, dims_of, say
+from tests.gpu_common import assert_same_bits, bits, dev_params, dev_tokens, dims_of, say
 
 pytestmark = pytest.mark.gpu
 
@@ -92,16 +92,16 @@ def test_captured_step_replays_match_eager_steps(replay):
     torch.cuda.synchronize()
     # capture records the launches without running them: both sides start equal
     for gl, el in zip(graph_layers, eager_layers):
-        assert torch.equal(bits(gl.pool), bits(el.pool))
+        assert_same_bits(gl.pool, el.pool, "gl.pool vs el.pool")
     for k in range(n_replays):
         graph.replay()
         _step(eager_layers)
         torch.cuda.synchronize()
         for li, (gl, el) in enumerate(zip(graph_layers, eager_layers)):
-            assert torch.equal(bits(gl.pool), bits(el.pool)), "replay %d layer %d: state differs" % (k, li)
-            assert torch.equal(gl.o.view(torch.int16), el.o.view(torch.int16)), "replay %d layer %d: o" % (k, li)
+            assert_same_bits(gl.pool, el.pool, "replay %d layer %d: state differs" % (k, li))
+            assert_same_bits(gl.o, el.o, "replay %d layer %d: o" % (k, li))
             if gl.ckpt is not None:
-                assert torch.equal(bits(gl.ckpt), bits(el.ckpt)), "replay %d layer %d: checkpoints" % (k, li)
+                assert_same_bits(gl.ckpt, el.ckpt, "replay %d layer %d: checkpoints" % (k, li))
             assert int(gl.status.abs().sum()) == 0
     say("graph replays match eager steps (%s)" % ("replay" if replay else "checkpoint"))
 
@@ -142,10 +142,10 @@ def test_captured_folded_steps_match_eager_steps():
         two_steps(eager_layers)
         torch.cuda.synchronize()
         for li, (gl, el) in enumerate(zip(graph_layers, eager_layers)):
-            assert torch.equal(bits(gl.pool), bits(el.pool)), "replay %d layer %d: state differs" % (k, li)
-            assert torch.equal(gl.o.view(torch.int16), el.o.view(torch.int16)), "replay %d layer %d: o" % (k, li)
+            assert_same_bits(gl.pool, el.pool, "replay %d layer %d: state differs" % (k, li))
+            assert_same_bits(gl.o, el.o, "replay %d layer %d: o" % (k, li))
             for j in (0, 1):
-                assert torch.equal(bits(gl.deltas[j]), bits(el.deltas[j])), "replay %d layer %d: factors" % (k, li)
+                assert_same_bits(gl.deltas[j], el.deltas[j], "replay %d layer %d: factors" % (k, li))
             assert int(gl.status.abs().sum()) == 0 and int(el.status.abs().sum()) == 0
     say("graph replays of folded steps match eager steps")
 

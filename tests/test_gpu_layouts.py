@@ -10,7 +10,7 @@ import pytest
 
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
-from tests.gpu_common import bits, dev_params, dev_tokens, dims_of, index_tokens
+from tests.gpu_common import assert_same_bits, bits, dev_params, dev_tokens, dims_of, index_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -84,9 +84,9 @@ def test_two_row_layout_matches_one_row_layout_bitwise(raw_qk):
     i16 = lambda t: t.view(torch.int16)
     assert torch.equal(i16(o_nock), i16(o_ck)), "verify without checkpoints: outputs differ"
     assert torch.equal(i16(o_dl), i16(o_ck)), "delta verify: outputs differ"
-    assert torch.equal(bits(pool_r), bits(committed)), "replay commit differs from the checkpoint commit"
-    assert torch.equal(bits(pool_d), bits(committed)), "fold commit differs from the checkpoint commit"
+    assert_same_bits(pool_r, committed, "replay commit differs from the checkpoint commit")
+    assert_same_bits(pool_d, committed, "fold commit differs from the checkpoint commit")
     assert torch.equal(i16(o2_f), i16(o2_ck)), "folded verify: outputs differ"
-    assert torch.equal(bits(pool_f), bits(committed)), "folded verify: committed state differs"
-    assert torch.equal(bits(pool_dec), bits(ck2[:, 0])), "decode differs from checkpoint slot 0"
+    assert_same_bits(pool_f, committed, "folded verify: committed state differs")
+    assert_same_bits(pool_dec, ck2[:, 0], "decode differs from checkpoint slot 0")
     assert torch.equal(i16(o_dec), i16(o2_ck[torch.as_tensor(cu2[:-1], device="cuda")]))

@@ -20,8 +20,8 @@ import pytest
 import oracle
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
-from tests.gpu_common import (assert_o, assert_state, bits, dev_params, dev_tokens, dims_of, host,
-                              index_tokens, o_err, ref_qk, say, state_err)
+from tests.gpu_common import (assert_o, assert_same_bits, assert_state, bits, dev_params, dev_tokens, dims_of,
+                              host, index_tokens, o_err, ref_qk, say, state_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -192,7 +192,7 @@ def test_tiny_prompt_decode_then_window_every_accepted_count():
         gb.gdn_decode_step(dims, **index_tokens(wd, [j]), **P, state_pool=pool, src_slot=[1],
                            dst_slot=[1], o=o_dec[j:j + 1])
         torch.cuda.synchronize()
-        assert torch.equal(bits(pool[1]), bits(ckpt[0, j])), "checkpoint %d != %d decode calls" % (j, j + 1)
+        assert_same_bits(pool[1], ckpt[0, j], "checkpoint %d != %d decode calls" % (j, j + 1))
     assert torch.equal(_bf16_bits(o_dec), _bf16_bits(o_win))
 
     drawn = int(w.accepted(0)[0])
@@ -203,7 +203,7 @@ def test_tiny_prompt_decode_then_window_every_accepted_count():
                                pool, dst_slot=[2], status=status)
         torch.cuda.synchronize()
         assert int(status[0]) == 0
-        assert torch.equal(bits(pool[2]), bits(ckpt[0, a]))
+        assert_same_bits(pool[2], ckpt[0, a], "committed slot vs checkpoint %d" % a)
         assert_state(host(pool[2]), oracle.commit(ck_o, [4], [a])[0], "committed state a=%d" % a)
 
 
@@ -271,10 +271,10 @@ def test_verify_checkpoint_j_bit_identical_to_decode_chain(shape, raw_qk):
         o_dec[torch.as_tensor(idx, device="cuda")] = o_step
         torch.cuda.synchronize()
         for r in act:
-            assert torch.equal(bits(dec[r]), bits(ckpt[r, j])), "row %d: slot %d differs from %d decode calls" % (r, j, j + 1)
+            assert_same_bits(dec[r], ckpt[r, j], "row %d: slot %d differs from %d decode calls" % (r, j, j + 1))
     assert torch.equal(_bf16_bits(o_dec), _bf16_bits(o_win))
     # verify never writes the pool; unrequested slots keep the poison
-    assert torch.equal(bits(pool), bits(ref_pool))
+    assert_same_bits(pool, ref_pool, "pool vs ref_pool")
     for r in range(B):
         assert bool((bits(ckpt[r, T[r]:]) == POISON).all()), "row %d: slot >= T_r written" % r
     # and the values are right
@@ -307,9 +307,9 @@ def test_decode_to_another_slot_equals_decode_in_place(B):
     gb.gdn_decode_step(dims, **td, **P, state_pool=out, src_slot=rows + B, dst_slot=rows + B, o=o_in)
     gb.gdn_decode_step(dims, **td, **P, state_pool=out, src_slot=rows, dst_slot=rows + 2 * B, o=o_out)
     torch.cuda.synchronize()
-    assert torch.equal(bits(out[2 * B:]), bits(out[B:2 * B]))
-    assert torch.equal(o_in.view(torch.int16), o_out.view(torch.int16))
-    assert torch.equal(bits(out[:B]), bits(before)), "the source slots were written"
+    assert_same_bits(out[2 * B:], out[B:2 * B], "out[2 * B:] vs out[B:2 * B]")
+    assert_same_bits(o_in, o_out, "o_in vs o_out")
+    assert_same_bits(out[:B], before, "the source slots were written")
 
 
 @pytest.mark.parametrize("accepted", [0, 1, 2, 3])
@@ -348,7 +348,7 @@ def test_rollback_leaves_no_trace(accepted):
         outs_b.append(o1.clone())
     torch.cuda.synchronize()
     assert int(status[0]) == 0
-    assert torch.equal(bits(pool[0]), bits(pool[1]))
+    assert_same_bits(pool[0], pool[1], "pool[0] vs pool[1]")
     for x, y in zip(outs_a, outs_b):
         assert torch.equal(_bf16_bits(x), _bf16_bits(y))
 
@@ -370,11 +370,11 @@ def test_commit_is_a_bit_copy_and_flags_bad_accepted_counts():
     assert int(status[0]) == (1 << 1) | (1 << 3)
     for r, a in enumerate([3, None, 1, None, 0]):
         if a is None:
-            assert torch.equal(bits(pool[dst[r]]), bits(before[dst[r]]))
+            assert_same_bits(pool[dst[r]], before[dst[r]], "row %d: refused commit wrote its slot" % r)
         else:
-            assert torch.equal(bits(pool[dst[r]]), bits(ckpt[r, a]))
+            assert_same_bits(pool[dst[r]], ckpt[r, a], "row %d: committed slot vs checkpoint %d" % (r, a))
     for s in set(range(8)) - set(dst.tolist()):
-        assert torch.equal(bits(pool[s]), bits(before[s]))
+        assert_same_bits(pool[s], before[s], "slot %d, no row's destination, was written" % s)
 
 
 def test_two_runs_are_bit_identical():
@@ -394,7 +394,7 @@ def test_two_runs_are_bit_identical():
         gb.gdn_verify_window(dims, T, **td, **P, state_pool=pool, src_slot=np.arange(B), ckpt=ckpt, o=o)
         outs.append((ckpt, o))
     torch.cuda.synchronize()
-    assert torch.equal(bits(outs[0][0]), bits(outs[1][0]))
+    assert_same_bits(outs[0][0], outs[1][0], "outs[0][0] vs outs[1][0]")
     assert torch.equal(_bf16_bits(outs[0][1]), _bf16_bits(outs[1][1]))
 
 
@@ -443,7 +443,7 @@ def test_errors_write_nothing():
 
     def untouched():
         torch.cuda.synchronize()
-        assert torch.equal(bits(pool), bits(before))
+        assert_same_bits(pool, before, "pool vs before")
         assert bool((bits(ckpt) == POISON).all())
         assert torch.equal(_bf16_bits(o), _bf16_bits(o_before))
 

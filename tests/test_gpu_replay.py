@@ -21,7 +21,7 @@ import pytest
 
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
-from tests.gpu_common import bits, dev_params, dev_tokens, dims_of, say
+from tests.gpu_common import assert_same_bits, bits, dev_params, dev_tokens, dims_of, say
 from tests.test_gpu_recurrent import run_verify_workload
 
 pytestmark = pytest.mark.gpu
@@ -71,11 +71,11 @@ def test_replay_equals_checkpoint_commit_bitwise(shape, raw_qk):
                          dst_slot=rows + 2 * B, status=status)
     torch.cuda.synchronize()
     assert int(status.abs().sum()) == 0
-    assert torch.equal(o_ck.view(torch.int16), o_nock.view(torch.int16))
-    assert torch.equal(bits(pool[:B]), bits(before[:B])), "verify wrote the committed pool"
+    assert_same_bits(o_ck, o_nock, "o_ck vs o_nock")
+    assert_same_bits(pool[:B], before[:B], "verify wrote the committed pool")
     for r in range(B):
-        assert torch.equal(bits(pool[2 * B + r]), bits(pool[B + r])), \
-            "row %d (T=%d, a=%d): replay differs from checkpoint commit" % (r, T[r], pairs[r][1])
+        assert_same_bits(pool[2 * B + r], pool[B + r],
+                         "row %d (T=%d, a=%d): replay differs from checkpoint commit" % (r, T[r], pairs[r][1]))
 
 
 def test_replay_in_place_flags_bad_counts_and_spans_launches():
@@ -106,7 +106,7 @@ def test_replay_in_place_flags_bad_counts_and_spans_launches():
         expect[r // 32] |= 1 << (r % 32)
     assert [int(x) & 0xFFFFFFFF for x in status.cpu()] == expect
     assert torch.equal(status, status_ref)
-    assert torch.equal(bits(pool), bits(ref)), "in-place replay differs from checkpoint commit"
+    assert_same_bits(pool, ref, "in-place replay differs from checkpoint commit")
 
 
 def test_replay_zero_source_state():
@@ -127,7 +127,7 @@ def test_replay_zero_source_state():
                          dst_slot=[3, 4, 5], status=status)
     torch.cuda.synchronize()
     assert int(status[0]) == 0
-    assert torch.equal(bits(pool[3:]), bits(pool[:3]))
+    assert_same_bits(pool[3:], pool[:3], "pool[3:] vs pool[:3]")
 
 
 def test_batch1_workload_in_replay_mode():

@@ -19,7 +19,7 @@ import pytest
 
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
-from tests.gpu_common import bits, dev_params, dev_tokens, dims_of, say
+from tests.gpu_common import assert_same_bits, bits, dev_params, dev_tokens, dims_of, say
 from tests.test_gpu_recurrent import run_verify_workload
 
 pytestmark = pytest.mark.gpu
@@ -62,10 +62,10 @@ def test_select_equals_checkpoint_commit_window_after_window(raw_qk, B):
         gb.gdn_commit_select(dims, T, acc, bank, sel, table, st)
         torch.cuda.synchronize()
         assert int(st[0]) == 0
-        assert torch.equal(o_s.view(torch.int16), o_d.view(torch.int16)), "window %d: outputs differ" % i
+        assert_same_bits(o_s, o_d, "window %d: outputs differ" % i)
         expect = (bank * 4 + acc.cpu().numpy()).astype(np.int32)
         assert np.array_equal(table.cpu().numpy(), expect), "window %d: slot table" % i
-        assert torch.equal(bits(sel[table.long()]), bits(dense)), "window %d: selected states differ" % i
+        assert_same_bits(sel[table.long()], dense, "window %d: selected states differ" % i)
     say("select == checkpoint commit over %d windows" % n_windows)
 
 
@@ -97,11 +97,11 @@ def test_select_refuses_sources_inside_banks_and_bad_accepted_counts():
     for r in (1, 3):
         assert bool((o[cu[r]:cu[r + 1]].view(torch.int16) == 0x7FC1).all()), "refused row %d wrote outputs" % r
         lo = 4 * bank[r]
-        assert torch.equal(bits(pool[lo:lo + 4]), bits(before[lo:lo + 4])), "refused row %d wrote its bank" % r
+        assert_same_bits(pool[lo:lo + 4], before[lo:lo + 4], "refused row %d wrote its bank" % r)
     for r in (0, 2):
         lo = 4 * bank[r]
         assert not bool((bits(pool[lo:lo + T[r]]) == POISON).any()), "row %d: checkpoints missing" % r
-        assert torch.equal(bits(pool[lo + T[r]:lo + 4]), bits(before[lo + T[r]:lo + 4])), "row %d: extra slot" % r
+        assert_same_bits(pool[lo + T[r]:lo + 4], before[lo + T[r]:lo + 4], "row %d: extra slot" % r)
     # commit: row 2's accepted count is past its window; its entry stays
     acc = torch.tensor([1, 0, 2, 3], dtype=torch.int32, device="cuda")
     st2 = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -185,12 +185,12 @@ def test_commit_inside_verify_equals_commit_then_verify(B):
                 gb.gdn_commit_select(dims, T, acc, bank, pools[0], tables[0], sts[0])
             outs.append(o)
         torch.cuda.synchronize()
-        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "window %d: outputs differ" % i
+        assert_same_bits(outs[0], outs[1], "window %d: outputs differ" % i)
         prev = (T, bank, acc)
     gb.gdn_commit_select(dims, prev[0], prev[2], prev[1], pools[1], tables[1], sts[1])  # the last window's commit
     torch.cuda.synchronize()
     assert torch.equal(tables[0], tables[1]), "slot tables differ"
     assert torch.equal(sts[0], sts[1]), "status words differ"
     assert int(sts[0][0]) & (1 << (B // 2)), "refused commit not flagged"
-    assert torch.equal(bits(pools[1][tables[1].long()]), bits(pools[0][tables[0].long()])), "committed states differ"
+    assert_same_bits(pools[1][tables[1].long()], pools[0][tables[0].long()], "committed states differ")
     say("commit inside verify == commit then verify, %d rows, %d windows" % (B, n_windows))

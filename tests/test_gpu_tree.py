@@ -21,7 +21,8 @@ import pytest
 import oracle
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
-from tests.gpu_common import assert_o, assert_state, bits, dev_params, dev_tokens, dims_of, host, index_tokens
+from tests.gpu_common import (assert_o, assert_same_bits, assert_state, bits, dev_params, dev_tokens, dims_of,
+                              host, index_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +72,7 @@ def test_every_four_node_tree_against_the_oracle_d16():
     ck_o, o_o = oracle.verify_tree(T, parents, tok.q, tok.k, tok.v, tok.a, tok.b, A_log, dt_bias, host(before))
     assert_o(host(o), o_o, "tree outputs (d=16)")
     assert_state(host(ckpt), ck_o, "tree node states (d=16)")
-    assert torch.equal(bits(pool), bits(before))
+    assert_same_bits(pool, before, "pool vs before")
 
 
 def test_random_trees_full_shape_against_the_oracle():
@@ -105,8 +106,8 @@ def test_chain_shaped_tree_is_bit_identical_to_the_window(shape, raw_qk):
     gb.gdn_verify_window(dims, T, **dev_tokens(tok), **dev_params(A_log, dt_bias), state_pool=pool,
                          src_slot=np.arange(len(T)), ckpt=ck_w, o=o_w)
     torch.cuda.synchronize()
-    assert torch.equal(bits(ck_t), bits(ck_w))
-    assert torch.equal(o_t.view(torch.int16), o_w.view(torch.int16))
+    assert_same_bits(ck_t, ck_w, "ck_t vs ck_w")
+    assert_same_bits(o_t, o_w, "o_t vs o_w")
 
 
 def test_nodes_equal_decode_along_their_paths_and_commit_leaves_no_trace():
@@ -134,8 +135,8 @@ def test_nodes_equal_decode_along_their_paths_and_commit_leaves_no_trace():
                 gb.gdn_decode_step(dims, **index_tokens(td, [cu[r] + x]), **P, state_pool=work, src_slot=[0],
                                    dst_slot=[0], o=o1)
             torch.cuda.synchronize()
-            assert torch.equal(bits(work[0]), bits(ckpt[r, t])), "row %d node %d differs from its path" % (r, t)
-            assert torch.equal(o1.view(torch.int16)[0], o[cu[r] + t].view(torch.int16)), "row %d node %d output" % (r, t)
+            assert_same_bits(work[0], ckpt[r, t], "row %d node %d differs from its path" % (r, t))
+            assert_same_bits(o1[0], o[cu[r] + t], "row %d node %d output" % (r, t))
     # commit node 3 of row 0 (path 0 -> 1 -> 3) and node 2 of row 1 (path 1 -> 2)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     acc = torch.tensor([3, 2, 0], dtype=torch.int32, device="cuda")
@@ -143,4 +144,4 @@ def test_nodes_equal_decode_along_their_paths_and_commit_leaves_no_trace():
     torch.cuda.synchronize()
     assert int(status[0]) == 0
     for r, a in enumerate([3, 2, 0]):
-        assert torch.equal(bits(pool[r]), bits(ckpt[r, a]))
+        assert_same_bits(pool[r], ckpt[r, a], "row %d: committed node %d" % (r, a))

@@ -11,8 +11,8 @@ import pytest
 import oracle
 from gateddeltanet_linear_attention_amd import binding as gb
 from gateddeltanet_linear_attention_amd import synth
-from tests.gpu_common import (assert_o, assert_state, bits, dev_params, dev_tokens, dims_of, host,
-                              ref_qk, say)
+from tests.gpu_common import (assert_o, assert_same_bits, assert_state, bits, dev_params, dev_tokens, dims_of,
+                              host, ref_qk, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,9 +53,9 @@ def _case(lens, n_tail, src_rows, seed):
         torch.cuda.synchronize()
         out[kind] = (pool, ckpt, o)
     (pw, cw, ow), (ps, cs, os_) = out["workspace"], out["static"]
-    assert torch.equal(bits(ps), bits(pw)), "states differ from the workspace entry point"
-    assert torch.equal(bits(cs), bits(cw)), "checkpoints differ from the workspace entry point"
-    assert torch.equal(os_.view(torch.int16), ow.view(torch.int16)), "outputs differ from the workspace entry point"
+    assert_same_bits(ps, pw, "states differ from the workspace entry point")
+    assert_same_bits(cs, cw, "checkpoints differ from the workspace entry point")
+    assert_same_bits(os_, ow, "outputs differ from the workspace entry point")
     S0 = host(pool0[:B])
     S0[src < 0] = 0.0
     S_ref, ck_ref, o_ref = oracle.run_sequential(lens, *ref_qk(tok, False), tok.v, tok.a, tok.b, A_log, dt_bias,
