@@ -186,17 +186,18 @@ __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
 //   WF [tt][kb][p][l]  W[16 tt + r][32 kb + 8 g + e]      (e = 0..7, bf16 parts)
 //   QF [tt][kb][l]     Q[16 tt + r][32 kb + 8 g + e]      (bf16, the input q)
 //   KF [nt][kb][l]     K[32 kb + 8 g + e][16 nt + r]      (bf16, kb < 2: tokens)
-//   PF [tt][kb][p][l]  P[16 tt + r][32 kb + 8 g + e]      (bf16 parts, kb < 2)
+//   PF [b][p][l]       P[16 tt + r][32 kb + 8 g + e]      (bf16 parts, block b = pblk(tt, kb))
 //   UF [nt][tt][l]     U'[16 tt + 4 g + v][16 nt + r]     (fp32, v = 0..3)
 // with P[t][s] = e^{G_t - G_s} rq_t rk_s q_t.k_s for s <= t, else 0; then G [C] fp64,
 // eG[t] = e^{G_t}, eL[s] = e^{G_{n-1} - G_s} rk_s (s < n, else 0), rk[s] (the factor
 // token s's key is scaled by) and eGq[t] = e^{G_t} rq_t (the factor of the output's state
-// term); rk = rq = 1 unless q/k are normalised in the kernels.  For d = 16 the pieces of
+// term); rk = rq = 1 unless q/k are normalised in the kernels.  P is zero right of the
+// diagonal, so the blocks (tt < 2, kb = 1) are not stored.  For d = 16 the pieces of
 // lanes g >= 2 of WF lie past the head width and are not written (the chain kernel reads
 // zeros in their place); QF holds zeros there.
 // A workspace store: cached (NT = false), or streamed past the caches (NT = true).  The
 // chain kernel reads the workspace right after this one; when it fits well within the
-// 256 MB last-level cache it is read from there (the 2048-token prefill's 144 MB: 103 us
+// 256 MB last-level cache it is read from there (the 2048-token prefill's 138 MB: 103 us
 // cached against 120 us streamed), and when it does not, streaming the writes spares the
 // caches (the 4-prefill transaction's 1.1 GB: 690 -> 662 us).
 template <bool NT, typename T>
@@ -226,7 +227,7 @@ struct Ws {
     QF = WF + 4 * NK * 3 * 512;
     KF = QF + 4 * NK * 512;
     PF = KF + NT * 2 * 512;
-    UF = reinterpret_cast<float *>(PF + 4 * 2 * 3 * 512);
+    UF = reinterpret_cast<float *>(PF + 6 * 3 * 512);
     G = reinterpret_cast<double *>(UF + NT * 4 * 256);
     eG = reinterpret_cast<float *>(G + C);
     eL = eG + C;
@@ -235,6 +236,8 @@ struct Ws {
   }
   // element offset of lane l's 16-byte piece in 1-KiB fragment block `blk` of a bf16 array
   static __device__ __forceinline__ int piece(int blk, int l) { return (blk * 64 + l) * 8; }
+  // P block of token tile tt and 32-wide key block kb (kb = 1 only for tt >= 2)
+  static __device__ __forceinline__ int pblk(int tt, int kb) { return tt < 2 ? tt : 2 * tt - 2 + kb; }
 };
 
 // q/k normalisation of the fused input mode: x / sqrt(sum x^2 + eps), q also by
@@ -368,7 +371,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   //    fragments once (its Q rows, the K rows of all four blocks), computes tiles
   //    (w, tj <= w) and writes zeros to the tiles right of the diagonal.  Q K^T is
   //    formed transposed (lane: token 16 w + r16, keys 16 tj + 4 g4 + v), so each lane
-  //    holds 4 consecutive columns of a P row and P goes out in parts, in fragment order.
+  //    holds 4 consecutive columns of a P row and P goes out in parts, in fragment order
+  //    (the two blocks that are zero everywhere, rows < 32 and keys >= 32, are not stored).
   //    The wave's Q fragments are the chain kernel's: stored as they are.
   {
     constexpr int NK32 = (D + 31) / 32;  // 32-wide k blocks over d (D = 16: half of one)
@@ -420,13 +424,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
         pv[v] = s <= t ? expf(float(sG[t] - sG[s])) * (qk[v] * rq * sRk[s]) : 0.0f;
       }
       // lane (r16, g4) holds P[16 w + r16][16 tj + 4 g4 + 0..3]: half of the 16-byte piece
-      // of lane r16 + 16 (2 (tj & 1) + g4 / 2) in block (w, tj / 2, part)
-      const Parts4 pp = split4(make_float4(pv[0], pv[1], pv[2], pv[3]));
-      const int l2 = r16 + 16 * (2 * (tj & 1) + (g4 >> 1)), half = 4 * (g4 & 1);
-      const int pb = (w * 2 + (tj >> 1)) * 3;
-      ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 0, l2) + half), pp.h);
-      ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 1, l2) + half), pp.m);
-      ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 2, l2) + half), pp.l);
+      // of lane r16 + 16 (2 (tj & 1) + g4 / 2) in block (pblk(w, tj / 2), part)
+      if (w >= 2 || tj < 2) {  // wave-uniform
+        const Parts4 pp = split4(make_float4(pv[0], pv[1], pv[2], pv[3]));
+        const int l2 = r16 + 16 * (2 * (tj & 1) + (g4 >> 1)), half = 4 * (g4 & 1);
+        const int pb = Ws<D>::pblk(w, tj >> 1) * 3;
+        ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 0, l2) + half), pp.h);
+        ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 1, l2) + half), pp.m);
+        ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 2, l2) + half), pp.l);
+      }
     }
   }
   lds_barrier();
@@ -614,13 +620,14 @@ template <int D>
 struct OutOps {
   static constexpr int NK = Ws<D>::NK;
   bf16x8 q[NK];       // Q[16 t + r16][32 kb + 8 g4 + 0..7] (zero past d)
-  Parts8 p[2];        // P[16 t + r16][32 kb + 8 g4 + 0..7] in parts
+  Parts8 p[2];        // P[16 t + r16][32 kb + 8 g4 + 0..7] in parts (kb = 1: t >= 2 only)
   float egq;          // eGq[16 t + r16]
   __device__ void load_q(const Ws<D> &ws, int kb, int t, int lane) { q[kb] = CarryOps<D>::frag(ws.QF, t * NK + kb, lane); }
   __device__ void load_p(const Ws<D> &ws, int t, int lane) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int b3 = (t * 2 + kb) * 3;
+      if (kb == 1 && t < 2) break;  // that block of P is zero (wave-uniform)
+      const int b3 = Ws<D>::pblk(t, kb) * 3;
       p[kb] = Parts8{CarryOps<D>::frag(ws.PF, b3, lane), CarryOps<D>::frag(ws.PF, b3 + 1, lane),
                      CarryOps<D>::frag(ws.PF, b3 + 2, lane)};
     }

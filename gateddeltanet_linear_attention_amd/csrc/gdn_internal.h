@@ -130,11 +130,11 @@ constexpr int kChunk = 64;
 
 // Workspace floats per (chunk, value head), the chain kernel's operands in 1-KiB
 // fragment blocks: W in three bf16 parts [4][d/32][3] blocks, Q [4][d/32], K^T [d/16][2],
-// P in three bf16 parts [4][2][3], U' [d/16][4] blocks of 256 fp32 each, then
-// the 64 fp64 prefix sums of the log-decay and four 64-float factor vectors.
+// the six nonzero blocks of P in three bf16 parts [6][3], U' [d/16][4] blocks of 256 fp32
+// each, then the 64 fp64 prefix sums of the log-decay and four 64-float factor vectors.
 constexpr int64_t chunk_ws_unit_floats(int d) {
   const int64_t nk = d >= 32 ? d / 32 : 1, nt = d / 16;
-  return 3072 * nk + 1024 * nk + 512 * nt + 6144 + 1024 * nt + 2 * kChunk + 4 * kChunk;
+  return 3072 * nk + 1024 * nk + 512 * nt + 4608 + 1024 * nt + 2 * kChunk + 4 * kChunk;
 }
 
 struct ChunkArgs {

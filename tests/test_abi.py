@@ -399,8 +399,9 @@ def test_chunked_and_transaction_validation_codes():
     b = Bufs()
     d = _dims()
     need = gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100, 64, 1])
-    # per (chunk, value head): W parts 48 KiB, Q 16, K^T 16, P parts 24, U' 32 KiB, 1.5 KiB of factors
-    assert need == (2 + 1 + 1) * 32 * ((48 + 16 + 16 + 24 + 32) * 1024 + 1536)
+    # per (chunk, value head): W parts 48 KiB, Q 16, K^T 16, the six nonzero P blocks in
+    # parts 18, U' 32 KiB, 1.5 KiB of factors
+    assert need == (2 + 1 + 1) * 32 * ((48 + 16 + 16 + 18 + 32) * 1024 + 1536)
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100], chunk=32) == 0
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [0]) == 0
 
