@@ -387,7 +387,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
       for (int tj = 0; tj < 4; ++tj)
         fk[tj][kb] = col < D ? *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + r16) * LDK + col) : z8;
       fa[kb] = col < D ? *reinterpret_cast<const bf16x8 *>(sK + (16 * w + r16) * LDK + col) : z8;
-      *reinterpret_cast<bf16x8 *>(ws.QF + Ws<D>::piece(w * NK32 + kb, lane)) = fq[kb];
+      ws_st<NT>(reinterpret_cast<uint4 *>(ws.QF + Ws<D>::piece(w * NK32 + kb, lane)), __builtin_bit_cast(uint4, fq[kb]));
 #pragma unroll
       for (int e = 0; e < 8; ++e) ssq = fmaf(float(fq[kb][e]), float(fq[kb][e]), ssq);
     }
