@@ -249,15 +249,22 @@ constexpr float inv_sqrt_d() {
   return D == 16 ? 0.25f : 0.0883883476483184405501f;
 }
 
+// V reaches step 4 one of two ways.  With a streamed workspace (NT: a large call, many
+// blocks, bound by the workspace writes) V rows are staged transposed in LDS with K; for
+// a smaller call each lane loads its V columns from memory instead (two bytes per token,
+// during the T solve), which takes the 17 KiB V^T buffer out of LDS: four blocks per CU
+// instead of three, one round of blocks for a 2048-token row (prep 41.5 -> ~37 us; with a
+// streamed workspace the column loads measured slower, transaction 645 -> 665 us).
 template <int D, bool NT>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
+__global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
+  constexpr bool STAGE_V = NT;
   __shared__ double sG[C];
   __shared__ __attribute__((aligned(16))) float sBeta[C];  // beta_m
   __shared__ __attribute__((aligned(16))) float sSK[C];    // beta_m e^{G_m}
   __shared__ __attribute__((aligned(16))) float sA[C * LDC];  // strictly lower A, then T = (I + A)^{-1}
   constexpr int LDK = D + 8;  // row length (bf16) of sK: 16-B aligned rows
   __shared__ __attribute__((aligned(16))) uint16_t sK[C * LDK];   // K (bf16): row token m, column d
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDB];  // V^T (bf16): row d, column token m
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[STAGE_V ? D * LDB : 8];  // V^T (bf16): row d, column token m
   __shared__ float sRk[C];  // per-token k scale factors (1: inputs taken as given)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -280,7 +287,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   };
 
   // 1. gates and the fp64 inclusive prefix sum of g (tokens t >= n: g = beta = 0);
-  //    K^T and V^T staged in LDS, with the k and q norms when normalising.
+  //    K (and V^T when staged) in LDS, with the k and q norms when normalising.
   double G = 0.0, Gl = 0.0;  // wave 0: lane t's prefix sum G_t and the chunk's last one
   if (w == 0) {
     float gf = 0.0f, bt = 0.0f;
@@ -304,7 +311,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
     ws.G[lane] = G;
     ws.eG[lane] = float(exp(G));
   }
-  // K rows to sK and V rows, transposed, to sVt, with the k norms when normalising.
+  // K rows to sK and (staging V) V rows, transposed, to sVt, with the k norms when normalising.
   // Thread tid takes 8 dims (16 bytes) of one token, so each load instruction reads whole
   // 256-byte rows of 4 tokens (a wave reading 16 rows of 32 bytes instead measured ~3x
   // slower per byte).  Rows past the chunk's end are zero.
@@ -320,14 +327,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
       uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw;
       if (m < n) {
         kw = *reinterpret_cast<const uint4 *>(Kc + int64_t(m) * ldqk + d8);
-        vw = *reinterpret_cast<const uint4 *>(Vc + int64_t(m) * ldv + d8);
+        if constexpr (STAGE_V) vw = *reinterpret_cast<const uint4 *>(Vc + int64_t(m) * ldv + d8);
       }
       *reinterpret_cast<uint4 *>(sK + m * LDK + d8) = kw;
-      const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+      if constexpr (STAGE_V) {
+        const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sVt[(d8 + 2 * e) * LDB + m] = uint16_t(vv[e]);
-        sVt[(d8 + 2 * e + 1) * LDB + m] = uint16_t(vv[e] >> 16);
+        for (int e = 0; e < 4; ++e) {
+          sVt[(d8 + 2 * e) * LDB + m] = uint16_t(vv[e]);
+          sVt[(d8 + 2 * e + 1) * LDB + m] = uint16_t(vv[e] >> 16);
+        }
       }
       if (norm) {  // the TPT consecutive lanes of token m hold its partial sums
         const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
@@ -437,6 +446,26 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
   }
   lds_barrier();
 
+  // Without staging, step 4's V columns are loaded here, so their latency overlaps the
+  // T solve: lane (r16, g4) of wave w takes column d = 16 nt + r16 (nt = 2 w + j) of tokens
+  // 32 kb + 8 g4 + 0..7, zero past the chunk, packed in pairs.
+  uint32_t vcol[2][2][4];
+  if constexpr (!STAGE_V) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int d = 16 * min(2 * w + j, D / 16 - 1) + r16;  // waves without a tile read tile 0, unused
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s0 = 32 * kb + 8 * g4 + 2 * e;
+          const uint32_t lo = s0 < n ? Vc[int64_t(s0) * ldv + d] : 0u;
+          const uint32_t hi = s0 + 1 < n ? Vc[int64_t(s0 + 1) * ldv + d] : 0u;
+          vcol[j][kb][e] = lo | (hi << 16);
+        }
+    }
+  }
+
   // 3. T = (I + A)^{-1}, A strictly lower triangular, by 16x16 blocks:
   //    T_ii = (I + A_ii)^{-1}, then T_ij = -T_ii (sum_{j<=k<i} A_ik T_kj) for i > j,
   //    one sub-diagonal at a time.  T_ii overwrites A_ii (no longer needed); T_ij
@@ -515,9 +544,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs args) {
         for (int e = 0; e < 4; ++e)
           kw[e] = uint32_t(sK[(s0 + 2 * e) * LDK + d]) | (uint32_t(sK[(s0 + 2 * e + 1) * LDK + d]) << 16);
         kt8[j][kb] = __builtin_bit_cast(bf16x8, u32x4v{kw[0], kw[1], kw[2], kw[3]});
-        const uint2 v0 = *reinterpret_cast<const uint2 *>(sVt + d * LDB + s0);  // 8-B aligned rows
-        const uint2 v1 = *reinterpret_cast<const uint2 *>(sVt + d * LDB + s0 + 4);
-        vt8[j][kb] = __builtin_bit_cast(bf16x8, u32x4v{v0.x, v0.y, v1.x, v1.y});
+        if constexpr (STAGE_V) {
+          const uint2 v0 = *reinterpret_cast<const uint2 *>(sVt + d * LDB + s0);  // 8-B aligned rows
+          const uint2 v1 = *reinterpret_cast<const uint2 *>(sVt + d * LDB + s0 + 4);
+          vt8[j][kb] = __builtin_bit_cast(bf16x8, u32x4v{v0.x, v0.y, v1.x, v1.y});
+        } else {
+          vt8[j][kb] = __builtin_bit_cast(bf16x8, u32x4v{vcol[j][kb][0], vcol[j][kb][1], vcol[j][kb][2], vcol[j][kb][3]});
+        }
       }
     }
     const bool has0 = 2 * w < D / 16, has1 = 2 * w + 1 < D / 16;
