@@ -183,7 +183,8 @@ __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
 // load, which bounded the chain).  With token tile tt (16 tokens), 32-wide block kb,
 // bf16 part plane p (hi, mid, lo: their sum is the fp32 value to within 2^-24 of it),
 // 16-wide state column tile nt and lane l = r + 16 g:
-//   WF [tt][kb][p][l]  W[16 tt + r][32 kb + 8 g + e]      (e = 0..7, bf16 parts)
+//   WF [tt][kb][p][l]  W[16 tt + r][32 kb + 8 g + e]      (e = 0..7, bf16 parts; in a
+//                      streamed workspace fp32 [tt][kb][l][e], 32 bytes per lane)
 //   QF [tt][kb][l]     Q[16 tt + r][32 kb + 8 g + e]      (bf16, the input q)
 //   KF [nt][kb][l]     K[32 kb + 8 g + e][16 nt + r]      (bf16, kb < 2: tokens)
 //   PF [b][p][l]       P[16 tt + r][32 kb + 8 g + e]      (bf16 parts, block b = pblk(tt, kb))
@@ -199,7 +200,9 @@ __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
 // chain kernel reads the workspace right after this one; when it fits well within the
 // 256 MB last-level cache it is read from there (the 2048-token prefill's 138 MB: 103 us
 // cached against 120 us streamed), and when it does not, streaming the writes spares the
-// caches (the 4-prefill transaction's 1.1 GB: 690 -> 662 us).
+// caches (the 4-prefill transaction's 1.1 GB: 690 -> 662 us) and W goes out in fp32, an
+// eighth less to write and read (the same transaction 650 -> 625 us; in the cached form the
+// chain kernel's split of W measured 2 us slower per 2048-token prefill).
 template <bool NT, typename T>
 __device__ __forceinline__ void ws_st(T *p, T v) {
   if constexpr (NT) {
@@ -215,16 +218,18 @@ __device__ __forceinline__ void ws_st(T *p, T v) {
   }
 }
 
-template <int D>
+template <int D, bool W32>
 struct Ws {
   static constexpr int NK = D >= 32 ? D / 32 : 1;  // 32-wide blocks over d
   static constexpr int NT = D / 16;                // 16-wide state column tiles
+  static constexpr int64_t UNIT = chunk_ws_unit_floats(D, W32);  // floats per (chunk, head)
   uint16_t *WF, *QF, *KF, *PF;
-  float *UF, *eG, *eL, *rk, *eGq;
+  float *WF32, *UF, *eG, *eL, *rk, *eGq;
   double *G;
   __device__ Ws(float *base) {
     WF = reinterpret_cast<uint16_t *>(base);
-    QF = WF + 4 * NK * 3 * 512;
+    WF32 = base;
+    QF = W32 ? reinterpret_cast<uint16_t *>(base + 4 * NK * 512) : WF + 4 * NK * 3 * 512;
     KF = QF + 4 * NK * 512;
     PF = KF + NT * 2 * 512;
     UF = reinterpret_cast<float *>(PF + 6 * 3 * 512);
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
   const uint16_t *Kc = args.k + tok_base * ldqk + int64_t(hq) * D;
   const uint16_t *Qc = args.q + tok_base * ldqk + int64_t(hq) * D;
   const uint16_t *Vc = args.v + tok_base * ldv + int64_t(h) * D;
-  Ws<D> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * ChunkArgs::ws_unit_floats(D));
+  Ws<D, NT> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * Ws<D, NT>::UNIT);
 
   auto frag32 = [&](const uint16_t *base, int64_t ld, int t, int kb) {
     return frag32_row<D>(base, ld, t, kb, n, g4);
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
       for (int tj = 0; tj < 4; ++tj)
         fk[tj][kb] = col < D ? *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + r16) * LDK + col) : z8;
       fa[kb] = col < D ? *reinterpret_cast<const bf16x8 *>(sK + (16 * w + r16) * LDK + col) : z8;
-      ws_st<NT>(reinterpret_cast<uint4 *>(ws.QF + Ws<D>::piece(w * NK32 + kb, lane)), __builtin_bit_cast(uint4, fq[kb]));
+      ws_st<NT>(reinterpret_cast<uint4 *>(ws.QF + Ws<D, NT>::piece(w * NK32 + kb, lane)), __builtin_bit_cast(uint4, fq[kb]));
 #pragma unroll
       for (int e = 0; e < 8; ++e) ssq = fmaf(float(fq[kb][e]), float(fq[kb][e]), ssq);
     }
@@ -437,10 +442,10 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
       if (w >= 2 || tj < 2) {  // wave-uniform
         const Parts4 pp = split4(make_float4(pv[0], pv[1], pv[2], pv[3]));
         const int l2 = r16 + 16 * (2 * (tj & 1) + (g4 >> 1)), half = 4 * (g4 & 1);
-        const int pb = Ws<D>::pblk(w, tj >> 1) * 3;
-        ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 0, l2) + half), pp.h);
-        ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 1, l2) + half), pp.m);
-        ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D>::piece(pb + 2, l2) + half), pp.l);
+        const int pb = Ws<D, NT>::pblk(w, tj >> 1) * 3;
+        ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D, NT>::piece(pb + 0, l2) + half), pp.h);
+        ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D, NT>::piece(pb + 1, l2) + half), pp.m);
+        ws_st<NT>(reinterpret_cast<uint2 *>(ws.PF + Ws<D, NT>::piece(pb + 2, l2) + half), pp.l);
       }
     }
   }
@@ -589,12 +594,18 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
         const int nt = 2 * w + jj;
         // W in parts, in fragment order: lane (r16, g4) holds W[16 ti + r16][16 nt + 4 g4 + 0..3],
         // half of the piece of lane r16 + 16 (2 (nt & 1) + g4 / 2) in block (ti, nt / 2, part)
-        const Parts4 wp = split4(make_float4(wa[jj][0], wa[jj][1], wa[jj][2], wa[jj][3]));
         const int l2 = r16 + 16 * (2 * (nt & 1) + (g4 >> 1)), half = 4 * (g4 & 1);
-        const int wb = (ti * Ws<D>::NK + (nt >> 1)) * 3;
-        ws_st<NT>(reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 0, l2) + half), wp.h);
-        ws_st<NT>(reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 1, l2) + half), wp.m);
-        ws_st<NT>(reinterpret_cast<uint2 *>(ws.WF + Ws<D>::piece(wb + 2, l2) + half), wp.l);
+        if constexpr (NT) {  // streamed: W in fp32, lane l2's 32-byte piece of block (ti, nt / 2)
+          const int wb = ti * Ws<D, NT>::NK + (nt >> 1);
+          ws_st<NT>(reinterpret_cast<float4 *>(ws.WF32 + (wb * 64 + l2) * 8 + half),
+                    make_float4(wa[jj][0], wa[jj][1], wa[jj][2], wa[jj][3]));
+        } else {
+          const Parts4 wp = split4(make_float4(wa[jj][0], wa[jj][1], wa[jj][2], wa[jj][3]));
+          const int wb = (ti * Ws<D, NT>::NK + (nt >> 1)) * 3;
+          ws_st<NT>(reinterpret_cast<uint2 *>(ws.WF + Ws<D, NT>::piece(wb + 0, l2) + half), wp.h);
+          ws_st<NT>(reinterpret_cast<uint2 *>(ws.WF + Ws<D, NT>::piece(wb + 1, l2) + half), wp.m);
+          ws_st<NT>(reinterpret_cast<uint2 *>(ws.WF + Ws<D, NT>::piece(wb + 2, l2) + half), wp.l);
+        }
         // U': lane (r16, g4) holds U'[16 ti + 4 g4 + v][16 nt + r16], the piece of block (nt, ti)
         ws_st<NT>(reinterpret_cast<float4 *>(ws.UF + ((nt * 4 + ti) * 64 + lane) * 4),
                   make_float4(ua[jj][0], ua[jj][1], ua[jj][2], ua[jj][3]));
@@ -604,12 +615,15 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
 }
 
 // One chunk's operands of a chain wave (w < 4, lane = r16 + 16 g4), fetched a chunk
-// ahead; every load reads one 1-KiB fragment block of the workspace.
-template <int D>
+// ahead; every load reads one 1-KiB fragment block of the workspace (2 KiB for fp32 W).
+template <int D, bool W32>
 struct CarryOps {
-  static constexpr int NK = Ws<D>::NK;
+  static constexpr int NK = Ws<D, W32>::NK;
   static constexpr int NT = (D / 16 + 3) / 4;  // 16-wide state column tiles per wave
-  Parts8 w[NK];       // W[16 w + r16][32 kb + 8 g4 + 0..7] in parts (zero past d)
+  // W[16 w + r16][32 kb + 8 g4 + 0..7] (zero past d): in parts as stored, or in fp32 from
+  // a streamed workspace, split where it is used (the same parts the prep kernel forms)
+  Parts8 w[W32 ? 1 : NK];
+  float4 wf[W32 ? NK : 1][2];
   bf16x8 kt[NT][2];   // K^T[16 nt + r16][32 kb + 8 g4 + 0..7], nt = w + 4 q
   float4 up;          // U'[16 w + 4 g4 + v][i0 + r16], v = 0..3
   float4 el;          // eL[16 w + 4 g4 + v]
@@ -617,14 +631,34 @@ struct CarryOps {
   // Two groups, each loaded where the chunk before has matrix work to hide it behind:
   // (a) W of block kb, used by the U stage; (b) K^T, U', eL, e_last, used by the U
   // exchange and the carry.
-  __device__ void load_a(const Ws<D> &ws, int kb, int wv, int lane) {
+  __device__ void load_a(const Ws<D, W32> &ws, int kb, int wv, int lane) {
     const int g4 = lane >> 4;
-    const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4v{0u, 0u, 0u, 0u});
-    const int b3 = (wv * NK + kb) * 3;
-    w[kb] = 32 * kb + 8 * g4 < D ? Parts8{frag(ws.WF, b3, lane), frag(ws.WF, b3 + 1, lane), frag(ws.WF, b3 + 2, lane)}
-                                 : Parts8{z, z, z};
+    if constexpr (W32) {
+      const float4 *src = reinterpret_cast<const float4 *>(ws.WF32 + ((wv * NK + kb) * 64 + lane) * 8);
+      if (32 * kb + 8 * g4 < D) {
+        wf[kb][0] = src[0];
+        wf[kb][1] = src[1];
+      } else {
+        wf[kb][0] = wf[kb][1] = zf4();
+      }
+    } else {
+      const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4v{0u, 0u, 0u, 0u});
+      const int b3 = (wv * NK + kb) * 3;
+      w[kb] = 32 * kb + 8 * g4 < D ? Parts8{frag(ws.WF, b3, lane), frag(ws.WF, b3 + 1, lane), frag(ws.WF, b3 + 2, lane)}
+                                   : Parts8{z, z, z};
+    }
   }
-  __device__ void load_b(const Ws<D> &ws, int n, int wv, int lane, int tile) {
+  __device__ Parts8 w_parts(int kb) const {
+    if constexpr (W32) {
+      const Parts4 a = split4(wf[kb][0]), b = split4(wf[kb][1]);
+      return Parts8{__builtin_bit_cast(bf16x8, u32x4v{a.h.x, a.h.y, b.h.x, b.h.y}),
+                    __builtin_bit_cast(bf16x8, u32x4v{a.m.x, a.m.y, b.m.x, b.m.y}),
+                    __builtin_bit_cast(bf16x8, u32x4v{a.l.x, a.l.y, b.l.x, b.l.y})};
+    } else {
+      return w[kb];
+    }
+  }
+  __device__ void load_b(const Ws<D, W32> &ws, int n, int wv, int lane, int tile) {
     const int g4 = lane >> 4;
 #pragma unroll
     for (int qt = 0; qt < NT; ++qt) {
@@ -638,35 +672,37 @@ struct CarryOps {
     el = *reinterpret_cast<const float4 *>(ws.eL + 16 * wv + 4 * g4);
     e_last = ws.eG[n - 1];
   }
-  __device__ void load(const Ws<D> &ws, int n, int wv, int lane, int tile) {
+  __device__ void load(const Ws<D, W32> &ws, int n, int wv, int lane, int tile) {
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) load_a(ws, kb, wv, lane);
     load_b(ws, n, wv, lane, tile);
   }
   static __device__ __forceinline__ bf16x8 frag(const uint16_t *a, int blk, int lane) {
-    return *reinterpret_cast<const bf16x8 *>(a + Ws<D>::piece(blk, lane));
+    return *reinterpret_cast<const bf16x8 *>(a + Ws<D, false>::piece(blk, lane));
   }
 };
 
 // One chunk's operands of an output wave (token tile t = w - 4), fetched a chunk ahead.
-template <int D>
+template <int D, bool W32>
 struct OutOps {
-  static constexpr int NK = Ws<D>::NK;
+  static constexpr int NK = Ws<D, W32>::NK;
   bf16x8 q[NK];       // Q[16 t + r16][32 kb + 8 g4 + 0..7] (zero past d)
   Parts8 p[2];        // P[16 t + r16][32 kb + 8 g4 + 0..7] in parts (kb = 1: t >= 2 only)
   float egq;          // eGq[16 t + r16]
-  __device__ void load_q(const Ws<D> &ws, int kb, int t, int lane) { q[kb] = CarryOps<D>::frag(ws.QF, t * NK + kb, lane); }
-  __device__ void load_p(const Ws<D> &ws, int t, int lane) {
+  __device__ void load_q(const Ws<D, W32> &ws, int kb, int t, int lane) {
+    q[kb] = CarryOps<D, W32>::frag(ws.QF, t * NK + kb, lane);
+  }
+  __device__ void load_p(const Ws<D, W32> &ws, int t, int lane) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (kb == 1 && t < 2) break;  // that block of P is zero (wave-uniform)
-      const int b3 = Ws<D>::pblk(t, kb) * 3;
-      p[kb] = Parts8{CarryOps<D>::frag(ws.PF, b3, lane), CarryOps<D>::frag(ws.PF, b3 + 1, lane),
-                     CarryOps<D>::frag(ws.PF, b3 + 2, lane)};
+      const int b3 = Ws<D, false>::pblk(t, kb) * 3;
+      p[kb] = Parts8{CarryOps<D, W32>::frag(ws.PF, b3, lane), CarryOps<D, W32>::frag(ws.PF, b3 + 1, lane),
+                     CarryOps<D, W32>::frag(ws.PF, b3 + 2, lane)};
     }
     egq = ws.eGq[16 * t + (lane & 15)];
   }
-  __device__ void load(const Ws<D> &ws, int t, int lane) {
+  __device__ void load(const Ws<D, W32> &ws, int t, int lane) {
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) load_q(ws, kb, t, lane);
     load_p(ws, t, lane);
@@ -705,11 +741,11 @@ __device__ __forceinline__ void store_nt(float *dst, floatx4 x) {
 // written to the other).  Blocks of one (row, head) unit are spaced 8 apart in launch
 // order, which places all its tiles on one of the 8 chiplets and lets them share that
 // L2's copy of the chunk operands (W, K^T, P).
-template <int D>
+template <int D, bool W32>
 __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_units) {
   constexpr int TILES = D / VT;
-  constexpr int NK = CarryOps<D>::NK;
-  constexpr int NT = CarryOps<D>::NT;
+  constexpr int NK = CarryOps<D, W32>::NK;
+  constexpr int NT = CarryOps<D, W32>::NT;
   constexpr int LDS_ = D + 8;     // S part row (bf16): 16-B aligned rows
   constexpr int SPL = VT * LDS_;  // elements per plane of S parts
   constexpr int UPL = VT * LDP;   // elements per plane of U parts
@@ -736,7 +772,7 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
   const int src = args.src[row], dst = args.dst[row];
   const int tail0 = L - args.n_tail[row];  // first position with a checkpoint
   auto ws_of = [&](int c) {
-    return Ws<D>(args.ws + (int64_t(args.chunk0[row] + c) * n_v + h) * ChunkArgs::ws_unit_floats(D));
+    return Ws<D, W32>(args.ws + (int64_t(args.chunk0[row] + c) * n_v + h) * Ws<D, W32>::UNIT);
   };
   // parts of S_c for 32-wide d block kb (lane (r16, g4): S_c[i0 + r16][32 kb + 8 g4 + e])
   auto s_parts = [&](const uint16_t *buf, int kb) {
@@ -758,9 +794,9 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
   if (w >= 4) {  // ------------------------------------------------ output waves
     const int t = w - 4;
     lds_barrier();  // the start state's parts
-    auto body = [&](int c, const OutOps<D> &f, OutOps<D> &nx) {
+    auto body = [&](int c, const OutOps<D, W32> &f, OutOps<D, W32> &nx) {
       const int cn = min(c + 1, nch - 1);
-      const Ws<D> wsn = ws_of(cn);
+      const Ws<D, W32> wsn = ws_of(cn);
       const int c0 = c * C;
       const int n = min(C, L - c0);
       const int64_t tok_base = int64_t(args.tok0[row]) + c0;
@@ -791,7 +827,7 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
       tail_barriers(c0, n);
       lds_barrier();  // S_{c+1}'s parts complete; every read of this chunk's U parts done
     };
-    OutOps<D> fa, fb;
+    OutOps<D, W32> fa, fb;
     fa.load(ws_of(0), t, lane);
     for (int c = 0; c < nch; c += 2) {
       body(c, fa, fb);
@@ -821,11 +857,11 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
   put_state(sS[0]);
   lds_barrier();
 
-  auto body = [&](int c, const CarryOps<D> &f, CarryOps<D> &nx) {
-    const Ws<D> ws = ws_of(c);
+  auto body = [&](int c, const CarryOps<D, W32> &f, CarryOps<D, W32> &nx) {
+    const Ws<D, W32> ws = ws_of(c);
     // the next chunk's operands (past the end: the last chunk again, never read)
     const int cn = min(c + 1, nch - 1);
-    const Ws<D> wsn = ws_of(cn);
+    const Ws<D, W32> wsn = ws_of(cn);
     const int nn = min(C, L - cn * C);
     const int c0 = c * C;
     const int n = min(C, L - c0);
@@ -840,9 +876,9 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
       nx.load_a(wsn, kb, w, lane);
       __builtin_amdgcn_sched_barrier(0);  // the prefetch stays where it is issued
       if (kb & 1)
-        ub = mma6(ub, f.w[kb], sp);
+        ub = mma6(ub, f.w_parts(kb), sp);
       else
-        ua = mma6(ua, f.w[kb], sp);
+        ua = mma6(ua, f.w_parts(kb), sp);
     }
     ua += ub;
     const float4 u = make_float4(f.up.x - ua[0], f.up.y - ua[1], f.up.z - ua[2], f.up.w - ua[3]);
@@ -908,7 +944,7 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
   // scheduling barriers after each prefetch group keep the compiler from sinking those
   // loads toward their use a chunk later: a load issued last is one whose wait drains
   // every load before it.
-  CarryOps<D> fa, fb;
+  CarryOps<D, W32> fa, fb;
   fa.load(ws_of(0), min(C, L), w, lane, tile);
   for (int c = 0; c < nch; c += 2) {
     body(c, fa, fb);
@@ -924,22 +960,21 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
   }
 }
 
-template <int D>
-hipError_t launch_d(const ChunkArgs &args, int n_chunks, hipStream_t stream) {
-  // the workspace streamed past the caches once it is well beyond a share of the
-  // last-level cache (see ws_st)
-  const bool nt = int64_t(n_chunks) * args.n_v * ChunkArgs::ws_unit_floats(D) * 4 > (int64_t(160) << 20);
-  if (nt)
-    hipLaunchKernelGGL((chunk_prep_kernel<D, true>), dim3(unsigned(n_chunks), unsigned(args.n_v)), dim3(256), 0,
-                       stream, args);
-  else
-    hipLaunchKernelGGL((chunk_prep_kernel<D, false>), dim3(unsigned(n_chunks), unsigned(args.n_v)), dim3(256), 0,
-                       stream, args);
+template <int D, bool NT>
+hipError_t launch_form(const ChunkArgs &args, int n_chunks, hipStream_t stream) {
+  hipLaunchKernelGGL((chunk_prep_kernel<D, NT>), dim3(unsigned(n_chunks), unsigned(args.n_v)), dim3(256), 0, stream,
+                     args);
   const int n_units = args.n_rows * args.n_v;
   const int groups = (n_units + 7) / 8;  // units are dealt to the 8 chiplets in groups of 8
-  hipLaunchKernelGGL(chunk_chain_kernel<D>, dim3(unsigned(groups * 8 * (D / VT))), dim3(512), 0, stream,
+  hipLaunchKernelGGL((chunk_chain_kernel<D, NT>), dim3(unsigned(groups * 8 * (D / VT))), dim3(512), 0, stream,
                      args, n_units);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const ChunkArgs &args, int n_chunks, hipStream_t stream) {
+  // a streamed workspace (see chunk_ws_streamed and ws_st) holds W in fp32
+  return args.ws_streamed ? launch_form<D, true>(args, n_chunks, stream) : launch_form<D, false>(args, n_chunks, stream);
 }
 
 }  // namespace

@@ -129,12 +129,23 @@ struct FoldArgs {
 constexpr int kChunk = 64;
 
 // Workspace floats per (chunk, value head), the chain kernel's operands in 1-KiB
-// fragment blocks: W in three bf16 parts [4][d/32][3] blocks, Q [4][d/32], K^T [d/16][2],
-// the six nonzero blocks of P in three bf16 parts [6][3], U' [d/16][4] blocks of 256 fp32
-// each, then the 64 fp64 prefix sums of the log-decay and four 64-float factor vectors.
-constexpr int64_t chunk_ws_unit_floats(int d) {
+// fragment blocks: W in three bf16 parts [4][d/32][3] blocks (w32: fp32 [4][d/32] blocks
+// of 2 KiB), Q [4][d/32], K^T [d/16][2], the six nonzero blocks of P in three bf16 parts
+// [6][3], U' [d/16][4] blocks of 256 fp32 each, then the 64 fp64 prefix sums of the
+// log-decay and four 64-float factor vectors.
+constexpr int64_t chunk_ws_unit_floats(int d, bool w32) {
   const int64_t nk = d >= 32 ? d / 32 : 1, nt = d / 16;
-  return 3072 * nk + 1024 * nk + 512 * nt + 4608 + 1024 * nt + 2 * kChunk + 4 * kChunk;
+  return (w32 ? 2048 : 3072) * nk + 1024 * nk + 512 * nt + 4608 + 1024 * nt + 2 * kChunk + 4 * kChunk;
+}
+
+// A call's workspace is streamed: written past the caches, with W in fp32 (the chain
+// kernel forms its parts), when with W in parts it would exceed 160 MiB.  Such a call is
+// bound by the workspace traffic, which fp32 W cuts by an eighth; a smaller one is read
+// back from the last-level cache, and there the parts, formed once by the prep kernel,
+// keep that work off the chain's serial path.
+constexpr int64_t kStreamedWsBytes = int64_t(160) << 20;
+constexpr bool chunk_ws_streamed(int64_t chunks, int n_v, int d) {
+  return chunks * n_v * chunk_ws_unit_floats(d, false) * 4 > kStreamedWsBytes;
 }
 
 struct ChunkArgs {
@@ -157,7 +168,7 @@ struct ChunkArgs {
   int32_t n_tail[kRowsPerLaunch];
   int32_t ck_row[kRowsPerLaunch];
   int32_t qk_norm;                  // GDN_QK_L2NORM: normalise q and k in the kernels
-  static constexpr int64_t ws_unit_floats(int d) { return chunk_ws_unit_floats(d); }
+  int32_t ws_streamed;              // the call's workspace form (chunk_ws_streamed over all its chunks)
 };
 
 // Checkpoint select commit: slot_table[r] = bank[r] * ck_slots + accepted[r] when

@@ -402,6 +402,13 @@ def test_chunked_and_transaction_validation_codes():
     # per (chunk, value head): W parts 48 KiB, Q 16, K^T 16, the six nonzero P blocks in
     # parts 18, U' 32 KiB, 1.5 KiB of factors
     assert need == (2 + 1 + 1) * 32 * ((48 + 16 + 16 + 18 + 32) * 1024 + 1536)
+    # past 160 MiB with W in parts the workspace is streamed and holds W in fp32 (32 KiB)
+    big = [64 * 40] * 1                                    # 40 chunks x 32 heads: 168 MB with W in parts
+    assert 40 * 32 * ((48 + 16 + 16 + 18 + 32) * 1024 + 1536) > (160 << 20)
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), big) == \
+        40 * 32 * ((32 + 16 + 16 + 18 + 32) * 1024 + 1536)
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [64 * 38]) == \
+        38 * 32 * ((48 + 16 + 16 + 18 + 32) * 1024 + 1536)  # 159 MB: W in parts
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100], chunk=32) == 0
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [0]) == 0
 

@@ -126,6 +126,19 @@ def test_slow_decay_long_memory():
                      what="slow decay")
 
 
+def test_streamed_workspace_with_fp32_w_at_the_tiny_head_width():
+    """A call whose workspace with W in parts would pass 160 MiB streams it, with W in fp32
+    (its parts formed in the chain kernel): 64 value heads of width 16 over 62 chunks.  The
+    transaction tests cover that form at d = 128."""
+    shape = synth.HeadShape(32, 64, 16)
+    lens, chunks = [1984, 1984], 62
+    parts_unit = 3072 + 1024 + 512 + 4608 + 1024 + 6 * 64   # floats per (chunk, head), W in parts
+    assert chunks * 64 * parts_unit * 4 > (160 << 20)
+    fp32_unit = parts_unit - 1024                            # W in fp32: 2048 floats instead of 3072
+    assert gb.gdn_chunked_workspace_bytes(dims_of(shape), lens) == chunks * 64 * fp32_unit * 4
+    run_chunked_case(shape, lens, [4, 3], "mixed", 69, what="streamed d16")
+
+
 def test_more_than_64_chunked_rows_span_launches():
     """70 rows: the library splits a call into launches of at most 64 rows and numbers
     workspace chunks across them; tails straddle chunk boundaries, sources are mixed."""
