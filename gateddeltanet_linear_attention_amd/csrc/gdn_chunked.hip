@@ -200,7 +200,7 @@ __device__ __forceinline__ int row_of_chunk(const ChunkArgs &args, int c) {
 // chain kernel reads the workspace right after this one; when it fits well within the
 // 256 MB last-level cache it is read from there (the 2048-token prefill's 138 MB: 103 us
 // cached against 120 us streamed), and when it does not, streaming the writes spares the
-// caches (the 4-prefill transaction's 1.1 GB: 690 -> 662 us) and W goes out in fp32, an
+// caches (the 4-prefill transaction's 750 MB: 690 -> 662 us) and W goes out in fp32, an
 // eighth less to write and read (the same transaction 650 -> 625 us; in the cached form the
 // chain kernel's split of W measured 2 us slower per 2048-token prefill).
 template <bool NT, typename T>
