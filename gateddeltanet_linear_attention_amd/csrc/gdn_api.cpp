@@ -170,6 +170,14 @@ int launch_chunked_rows(const gdn_dims *d, const gdn::ChunkArgs &proto,
   return GDN_OK;
 }
 
+// The prep kernel runs one 256-thread block per (chunk, value head) in a 1-D grid, whose
+// work-item count must stay below 2^32.
+bool chunk_units_fit(const gdn_dims *d, const std::vector<int32_t> &rows, const int32_t *len) {
+  int64_t chunks = 0;
+  for (int32_t r : rows) chunks += chunks_of(len[r]);
+  return chunks * d->n_v_heads <= GDN_MAX_CHUNK_UNITS;
+}
+
 size_t chunked_ws_bytes(const gdn_dims *d, const std::vector<int32_t> &rows, const int32_t *len) {
   int64_t chunks = 0;
   for (int32_t r : rows) chunks += chunks_of(len[r]);
@@ -259,6 +267,7 @@ int chunked_prefill(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tok
     return rc;
   std::vector<int32_t> rows(static_cast<size_t>(n_rows));
   for (int32_t r = 0; r < n_rows; ++r) rows[r] = r;
+  if (!chunk_units_fit(dims, rows, row_tokens)) return GDN_E_RANGE;
   const Sizes s = sizes_of(dims);
   const size_t need = chunked_ws_bytes(dims, rows, row_tokens);
   if (use_static) {
@@ -749,6 +758,7 @@ size_t gdn_chunked_workspace_bytes(const gdn_dims *dims, int32_t n_rows,
     if (row_tokens[r] < 1) return 0;
     rows.push_back(r);
   }
+  if (!chunk_units_fit(dims, rows, row_tokens)) return 0;
   return chunked_ws_bytes(dims, rows, row_tokens);
 }
 
@@ -792,6 +802,7 @@ int gdn_run_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *row
   if ((rc = gdn_plan_transaction(dims, n_rows, row_tokens, route.data()))) return rc;
   std::vector<int32_t> rec, chk;
   for (int32_t r = 0; r < n_rows; ++r) (route[r] == GDN_ROUTE_RECURRENT ? rec : chk).push_back(r);
+  if (!chunk_units_fit(dims, chk, row_tokens)) return GDN_E_RANGE;
   const Sizes s = sizes_of(dims);
   const size_t need = chunked_ws_bytes(dims, chk, row_tokens);
   if ((rc = check_workspace(workspace, ws_bytes, need, state_pool, size_t(n_slots) * s.row_floats * 4,

@@ -314,8 +314,12 @@ int gdn_verify_window_select_commit(const gdn_dims *dims, int32_t n_rows, const 
 
 /*
  * gdn_chunked_workspace_bytes -- device workspace that gdn_chunked_prefill_with_
- * checkpoints and gdn_run_transaction need for these rows (0 on a bad argument).
+ * checkpoints and gdn_run_transaction need for these rows (0 on a bad argument, or
+ * for rows of more than GDN_MAX_CHUNK_UNITS (chunk, value head) units in all).
+ * A workspace that would pass 160 MiB holds W in fp32 instead of three bf16 parts,
+ * so the size is not linear in the token count across that point.
  */
+#define GDN_MAX_CHUNK_UNITS ((int64_t)1 << 24) /* chunks x value heads in one call */
 size_t gdn_chunked_workspace_bytes(const gdn_dims *dims, int32_t n_rows,
                                    const int32_t *row_tokens, int32_t chunk);
 
@@ -333,7 +337,8 @@ size_t gdn_chunked_workspace_bytes(const gdn_dims *dims, int32_t n_rows,
  * blocked (UT transform / WY representation) evaluation (Yang, Kautz & Hatamizadeh,
  * ICLR 2025).  Matches the sequential rule to fp32 rounding, not bit for bit.
  * Errors: GDN_E_WORKSPACE if ws_bytes < gdn_chunked_workspace_bytes(...);
- * GDN_E_UNSUPPORTED for chunk != 64; slot checks as gdn_decode_step.
+ * GDN_E_UNSUPPORTED for chunk != 64; GDN_E_RANGE for more than GDN_MAX_CHUNK_UNITS
+ * (chunk, value head) units; slot checks as gdn_decode_step.
  */
 int gdn_chunked_prefill_with_checkpoints(
     const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens, int32_t chunk,
@@ -387,7 +392,9 @@ int gdn_plan_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *ro
  * L_r - n_ckpt[r] + j + 1 tokens) and, if dst_slot[r] >= 0, its final state.
  * A verify row passes n_ckpt = T_r and dst = -1 (commit later); a prefill row
  * passes n_ckpt = 0 and its dst slot.  workspace as gdn_chunked_workspace_bytes
- * (may be NULL/0 when no row is longer than k_max + 1).
+ * (may be NULL/0 when no row is longer than k_max + 1).  GDN_E_RANGE when the rows
+ * routed to the chunked kernels hold more than GDN_MAX_CHUNK_UNITS (chunk, value head)
+ * units; otherwise errors as gdn_chunked_prefill_with_checkpoints.
  */
 int gdn_run_transaction(const gdn_dims *dims, int32_t n_rows, const int32_t *row_tokens,
                         const int32_t *n_ckpt, const uint16_t *q, const uint16_t *k,

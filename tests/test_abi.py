@@ -466,6 +466,16 @@ def test_chunked_and_transaction_validation_codes():
     assert tx([4, 100], [5, 0], [0, -1], [-1, 1]) == -3                # checkpoints > k_max + 1
     assert tx([4, 100], [4, 0], [0, -1], [-1, 0]) == -4                # prefill row overwrites a verify source
 
+    # at most GDN_MAX_CHUNK_UNITS (chunk, value head) units per call: 2^24 / 32 heads = 2^19 chunks
+    m = re.search(r"#define GDN_MAX_CHUNK_UNITS \(\(int64_t\)1 << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) == 24
+    at, past = 64 << 19, (64 << 19) + 1                               # 2^19 chunks, one token more
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [at]) > 0
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [past]) == 0
+    assert chunked([at], [0], [0], [1]) == -6        # within the limit: only the 1 TiB workspace is short
+    assert chunked([past], [0], [0], [1]) == -3
+    assert tx([4, past], [4, 0], [0, -1], [-1, 1]) == -3
+
 
 @no_gpu
 def test_header_compiles_as_c_and_a_c_program_links_the_library(tmp_path):
