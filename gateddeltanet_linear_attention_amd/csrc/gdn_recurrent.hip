@@ -161,11 +161,10 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 
   const int tid = threadIdx.x;
   const int sub = tid % LPR;
-  int bid = blockIdx.x;
-  const int tile = bid % TILES;
-  bid /= TILES;
-  const int h = bid % args.n_v;
-  const int r = bid / args.n_v;
+  // a 3-D grid (tile, value head, row): no divisions ahead of the first loads (the 16-row
+  // K=3 select verify: 29.69 against 29.83 us with the same blocks numbered in one
+  // dimension); blocks are dispatched in the same order either way
+  const int tile = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int hq = h / args.group;
   const int i_local = (tid / LPR) * RPL;  // first of this lane's RPL state rows in the block
   const int i0 = tile * ROWS + i_local;
@@ -504,7 +503,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
 template <int D, int LPR, int RPL, int WAVES, int MODE, bool STREAM, bool NTLOAD = false>
 static void launch_one(const RecurrentArgs &args, hipStream_t stream) {
   constexpr int TILES = D / (WAVES * 64 / LPR * RPL);
-  const dim3 grid(unsigned(args.n_rows) * unsigned(args.n_v) * TILES);
+  const dim3 grid(TILES, unsigned(args.n_v), unsigned(args.n_rows));
   hipLaunchKernelGGL((recurrent_kernel<D, LPR, RPL, WAVES, MODE, STREAM, NTLOAD>), grid, dim3(64 * WAVES), 0, stream,
                      args);
 }
