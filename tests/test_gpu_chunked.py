@@ -139,6 +139,49 @@ def test_streamed_workspace_with_fp32_w_at_the_tiny_head_width():
     run_chunked_case(shape, lens, [4, 3], "mixed", 69, what="streamed d16")
 
 
+@pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
+def test_streamed_and_cached_workspaces_agree_bit_for_bit(raw_qk):
+    """Rows are independent, so the same row gives the same bits in any call.  Two rows
+    together pass 160 MiB of workspace (streamed: W in fp32, V staged in LDS by the prep
+    kernel); each alone stays under it (cached: W in bf16 parts, V columns from memory).
+    Outputs, final states and tail checkpoints must agree bit for bit."""
+    import torch
+    shape = synth.HeadShape(32, 64, 16)
+    dims = dims_of(shape, raw_qk=raw_qk)
+    Hv, d = shape.n_v_heads, shape.d
+    lens, n_tail = np.array([1984, 1984], np.int32), np.array([4, 3], np.int32)
+    g = synth.streams(71, 3)
+    A_log, dt_bias = synth.head_params(g[0], shape)
+    tok = synth.tokens(g[1], shape, int(lens.sum()), raw_qk=raw_qk)
+    t, p = dev_tokens(tok), dev_params(A_log, dt_bias)
+    gen = torch.Generator(device="cpu").manual_seed(71)
+    start = (0.3 * torch.randn(2, Hv, d, d, generator=gen)).cuda()
+
+    def run(rows):
+        B = len(rows)
+        tk = index_tokens(t, np.concatenate([np.arange(lens[:r].sum(), lens[:r + 1].sum()) for r in rows]))
+        pool = torch.cat([start[list(rows)], torch.zeros(B, Hv, d, d, device="cuda")])
+        ckpt = _poison((B, 4, Hv, d, d))
+        o = torch.empty(int(lens[list(rows)].sum()), Hv, d, dtype=torch.bfloat16, device="cuda")
+        gb.gdn_chunked_prefill_with_checkpoints(dims, lens[list(rows)], n_tail[list(rows)], **tk, **p,
+                                                state_pool=pool, src_slot=np.arange(B, dtype=np.int32),
+                                                dst_slot=np.arange(B, 2 * B, dtype=np.int32), ckpt=ckpt, o=o,
+                                                workspace=_ws(dims, lens[list(rows)]))
+        return o, pool[B:], ckpt
+
+    parts_unit = 3072 + 1024 + 512 + 4608 + 1024 + 6 * 64   # floats per (chunk, head) at d = 16, W in parts
+    assert gb.gdn_chunked_workspace_bytes(dims, lens) == 62 * 64 * (parts_unit - 1024) * 4   # streamed: fp32 W
+    assert gb.gdn_chunked_workspace_bytes(dims, lens[:1]) == 31 * 64 * parts_unit * 4        # cached: parts
+    o2, s2, c2 = run([0, 1])
+    for r in range(2):
+        o1, s1, c1 = run([r])
+        o_rows = o2[int(lens[:r].sum()):int(lens[:r + 1].sum())]
+        assert_same_bits(o_rows, o1, "row %d outputs, streamed vs cached workspace" % r)
+        assert_same_bits(s2[r:r + 1], s1, "row %d final state, streamed vs cached workspace" % r)
+        assert_same_bits(c2[r:r + 1, :n_tail[r]], c1[:, :n_tail[r]], "row %d checkpoints, streamed vs cached" % r)
+    say("streamed vs cached workspace (%s): bit-identical" % ("fused" if raw_qk else "given q/k"))
+
+
 def test_more_than_64_chunked_rows_span_launches():
     """70 rows: the library splits a call into launches of at most 64 rows and numbers
     workspace chunks across them; tails straddle chunk boundaries, sources are mixed."""
