@@ -254,22 +254,19 @@ constexpr float inv_sqrt_d() {
   return D == 16 ? 0.25f : 0.0883883476483184405501f;
 }
 
-// V reaches step 4 one of two ways.  With a streamed workspace (NT: a large call, many
-// blocks, bound by the workspace writes) V rows are staged transposed in LDS with K; for
-// a smaller call each lane loads its V columns from memory instead (two bytes per token,
-// during the T solve), which takes the 17 KiB V^T buffer out of LDS: four blocks per CU
-// instead of three, one round of blocks for a 2048-token row (prep 41.5 -> ~37 us; with a
-// streamed workspace the column loads measured slower, transaction 645 -> 665 us).
+// V has no LDS buffer of its own: its rows are loaded into registers (whole 16-byte row
+// pieces) while T is solved, and written transposed into the K buffer once step 4 holds
+// its K^T columns.  36 KiB of LDS and at most 128 registers give four blocks per CU
+// instead of three (with V^T staged beside K from the start: 53.5 KiB), one round of blocks
+// for a 2048-token row (prefill 102 -> 97 us, transaction 616 -> 604 us).
 template <int D, bool NT>
 __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
-  constexpr bool STAGE_V = NT;
   __shared__ double sG[C];
   __shared__ __attribute__((aligned(16))) float sBeta[C];  // beta_m
   __shared__ __attribute__((aligned(16))) float sSK[C];    // beta_m e^{G_m}
   __shared__ __attribute__((aligned(16))) float sA[C * LDC];  // strictly lower A, then T = (I + A)^{-1}
   constexpr int LDK = D + 8;  // row length (bf16) of sK: 16-B aligned rows
   __shared__ __attribute__((aligned(16))) uint16_t sK[C * LDK];   // K (bf16): row token m, column d
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[STAGE_V ? D * LDB : 8];  // V^T (bf16): row d, column token m
   __shared__ float sRk[C];  // per-token k scale factors (1: inputs taken as given)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -308,7 +305,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
   };
 
   // 1. gates and the fp64 inclusive prefix sum of g (tokens t >= n: g = beta = 0);
-  //    K (and V^T when staged) in LDS, with the k and q norms when normalising.
+  //    K in LDS, with the k and q norms when normalising.
   double G = 0.0, Gl = 0.0;  // wave 0: lane t's prefix sum G_t and the chunk's last one
   if (w == 0) {
     float gf = 0.0f, bt = 0.0f;
@@ -332,7 +329,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
     ws.G[lane] = G;
     ws.eG[lane] = float(exp(G));
   }
-  // K rows to sK and (staging V) V rows, transposed, to sVt, with the k norms when normalising.
+  // K rows to sK, with the k norms when normalising.
   // Thread tid takes 8 dims (16 bytes) of one token, so each load instruction reads whole
   // 256-byte rows of 4 tokens (a wave reading 16 rows of 32 bytes instead measured ~3x
   // slower per byte).  Rows past the chunk's end are zero.
@@ -345,20 +342,9 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
     for (int it = 0; it < (C + TPR - 1) / TPR; ++it) {
       const int m = tid / TPT + TPR * it;
       if (m >= C) break;
-      uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw;
-      if (m < n) {
-        kw = *reinterpret_cast<const uint4 *>(Kc + int64_t(m) * ldqk + d8);
-        if constexpr (STAGE_V) vw = *reinterpret_cast<const uint4 *>(Vc + int64_t(m) * ldv + d8);
-      }
+      uint4 kw = make_uint4(0u, 0u, 0u, 0u);
+      if (m < n) kw = *reinterpret_cast<const uint4 *>(Kc + int64_t(m) * ldqk + d8);
       *reinterpret_cast<uint4 *>(sK + m * LDK + d8) = kw;
-      if constexpr (STAGE_V) {
-        const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sVt[(d8 + 2 * e) * LDB + m] = uint16_t(vv[e]);
-          sVt[(d8 + 2 * e + 1) * LDB + m] = uint16_t(vv[e] >> 16);
-        }
-      }
       if (norm) {  // the TPT consecutive lanes of token m hold its partial sums
         const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
         float ss = 0.0f;
@@ -467,24 +453,16 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
   }
   lds_barrier();
 
-  // Without staging, step 4's V columns are loaded here, so their latency overlaps the
-  // T solve: lane (r16, g4) of wave w takes column d = 16 nt + r16 (nt = 2 w + j) of tokens
-  // 32 kb + 8 g4 + 0..7, zero past the chunk, packed in pairs.
-  uint32_t vcol[2][2][4];
-  if constexpr (!STAGE_V) {
+  // V rows for step 4, loaded now so their latency overlaps the T solve: thread tid takes
+  // 8 dims of token tid / (D / 8) + 256 / (D / 8) * it, as the K staging did (zero past
+  // the chunk's end)
+  constexpr int VTPT = D / 8, VTPR = 256 / VTPT, VNIT = (C + VTPR - 1) / VTPR;
+  uint4 vrow[VNIT];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int d = 16 * min(2 * w + j, D / 16 - 1) + r16;  // waves without a tile read tile 0, unused
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s0 = 32 * kb + 8 * g4 + 2 * e;
-          const uint32_t lo = s0 < n ? Vc[int64_t(s0) * ldv + d] : 0u;
-          const uint32_t hi = s0 + 1 < n ? Vc[int64_t(s0 + 1) * ldv + d] : 0u;
-          vcol[j][kb][e] = lo | (hi << 16);
-        }
-    }
+  for (int it = 0; it < VNIT; ++it) {
+    const int m = tid / VTPT + VTPR * it;
+    vrow[it] = make_uint4(0u, 0u, 0u, 0u);
+    if (m < n) vrow[it] = *reinterpret_cast<const uint4 *>(Vc + int64_t(m) * ldv + 8 * (tid % VTPT));
   }
 
   // 3. T = (I + A)^{-1}, A strictly lower triangular, by 16x16 blocks:
@@ -565,12 +543,34 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
         for (int e = 0; e < 4; ++e)
           kw[e] = uint32_t(sK[(s0 + 2 * e) * LDK + d]) | (uint32_t(sK[(s0 + 2 * e + 1) * LDK + d]) << 16);
         kt8[j][kb] = __builtin_bit_cast(bf16x8, u32x4v{kw[0], kw[1], kw[2], kw[3]});
-        if constexpr (STAGE_V) {
+      }
+    }
+    lds_barrier();  // every wave holds its K^T columns: the K buffer takes V^T
+    {
+      uint16_t *sVt = sK;  // V^T (bf16): row d, column token m, pitch LDB
+      static_assert(D * LDB <= C * LDK, "V^T fits the K buffer");
+      const int d8 = 8 * (tid % VTPT);
+#pragma unroll
+      for (int it = 0; it < VNIT; ++it) {
+        const int m = tid / VTPT + VTPR * it;
+        if (m >= C) break;
+        const uint32_t vv[4] = {vrow[it].x, vrow[it].y, vrow[it].z, vrow[it].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sVt[(d8 + 2 * e) * LDB + m] = uint16_t(vv[e]);
+          sVt[(d8 + 2 * e + 1) * LDB + m] = uint16_t(vv[e] >> 16);
+        }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int d = 16 * min(2 * w + j, D / 16 - 1) + r16;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int s0 = 32 * kb + 8 * g4;
           const uint2 v0 = *reinterpret_cast<const uint2 *>(sVt + d * LDB + s0);  // 8-B aligned rows
           const uint2 v1 = *reinterpret_cast<const uint2 *>(sVt + d * LDB + s0 + 4);
           vt8[j][kb] = __builtin_bit_cast(bf16x8, u32x4v{v0.x, v0.y, v1.x, v1.y});
-        } else {
-          vt8[j][kb] = __builtin_bit_cast(bf16x8, u32x4v{vcol[j][kb][0], vcol[j][kb][1], vcol[j][kb][2], vcol[j][kb][3]});
         }
       }
     }
