@@ -110,6 +110,14 @@ def test_ragged_rows_tails_straddling_chunks(src_kind):
     run_chunked_case(synth.HeadShape(2, 4, 128), lens, n_tail, src_kind, 61, what="ragged/" + src_kind)
 
 
+@pytest.mark.parametrize("n_qk,n_v", [(8, 32), (8, 8), (4, 16)], ids=["group4_8qk", "group1_8qk", "group4_4qk"])
+def test_head_groupings(n_qk, n_v):
+    """Value heads per qk-head other than 2, with qk-head counts that do (8) and do not (4)
+    take the prep kernel's chiplet-grouped block order."""
+    run_chunked_case(synth.HeadShape(n_qk, n_v, 128), [130, 64, 3], [4, 2, 3], "mixed", 72 + n_v,
+                     what="%d qk / %d v heads" % (n_qk, n_v))
+
+
 def test_tiny_head_width():
     run_chunked_case(synth.TINY, [8, 70, 129], [4, 4, 1], "mixed", 62, what="d16")
 
