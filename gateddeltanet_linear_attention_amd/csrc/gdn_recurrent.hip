@@ -165,18 +165,31 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
   // K=3 select verify: 29.69 against 29.83 us with the same blocks numbered in one
   // dimension); blocks are dispatched in the same order either way
   const int tile = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
-  const int hq = h / args.group;
   const int i_local = (tid / LPR) * RPL;  // first of this lane's RPL state rows in the block
   const int i0 = tile * ROWS + i_local;
 
+  // Every argument the loads ahead of the state need, read up front and pinned in scalar
+  // registers: the compiler then issues all of them as one round of scalar loads with a
+  // single wait, where it otherwise spread them over three dependent rounds (the 16-row
+  // K=3 select verify: 29.26 against 29.63 us; the copy form's verify 28.9 against 29.6,
+  // the in-place decode 12.07 against 12.46).
   int ntok = args.ntok[r];
   const int tok0 = args.tok0[r];
   int src = args.src[r];
   const int dst = args.dst[r], ck_first = args.ck_first[r];
   const int ck_row = args.ck_row[r];
-  const int n_v = args.n_v, n_qk = args.n_qk;
+  const int n_v = args.n_v, n_qk = args.n_qk, group = args.group;
   const int prev_ntok = MODE == kSelect ? args.prev_ntok[r] : 0;
   const int prev_bank = MODE == kSelect ? args.prev_bank[r] : 0;
+  {
+    const uint16_t *const qp = args.q, *const kp = args.k, *const vp = args.v;
+    const float *const ap = args.a, *const bp = args.b, *const alp = args.A_log, *const dtp = args.dt_bias;
+    const void *const tabp = args.src_table, *const paccp = args.prev_accepted, *const sip = args.state_in;
+    const int cks = args.ck_slots, nsl = args.n_slots;
+    asm volatile("" ::"s"(ntok), "s"(tok0), "s"(src), "s"(dst), "s"(ck_first), "s"(ck_row), "s"(prev_ntok),
+                 "s"(prev_bank), "s"(group), "s"(qp), "s"(kp), "s"(vp), "s"(ap), "s"(bp), "s"(alp), "s"(dtp),
+                 "s"(tabp), "s"(paccp), "s"(sip), "s"(cks), "s"(nsl), "s"(n_v), "s"(n_qk));
+  }
   constexpr bool write_o = !REPLAY;
   // replay: a_r is read first, as a vector load like the select table below, and
   // checked once the state loads are in flight
@@ -199,6 +212,8 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(RecurrentArgs arg
     // is none) so the number of loads in flight stays fixed for the waits below
     pacc_raw = (args.prev_accepted ? args.prev_accepted : args.src_table)[idx];
   }
+  __builtin_amdgcn_sched_barrier(0);  // those loads go out before the division below
+  const int hq = h / group;
 
   // The row's token inputs are loaded before the state: one counter tracks loads in
   // issue order, so the waits that staging needs then leave the state loads in
