@@ -145,10 +145,13 @@ int launch_chunked_rows(const gdn_dims *d, const gdn::ChunkArgs &proto,
                         const int32_t *dst, hipStream_t stream) {
   int64_t chunk_base = 0, chunks = 0;
   for (int32_t r : rows) chunks += chunks_of(len[r]);
-  const bool streamed = gdn::chunk_ws_streamed(chunks, d->n_v_heads, d->d_k);  // one layout for the call
+  // one layout for the call: the qk-head units follow all the value-head units
+  const bool streamed = gdn::chunk_ws_streamed(chunks, d->n_v_heads, d->n_qk_heads, d->d_k);
+  float *const ws_qk = proto.ws + chunks * d->n_v_heads * gdn::chunk_ws_unit_floats(d->d_k, streamed);
   for (size_t base = 0; base < rows.size(); base += kRowsPerLaunch) {
     gdn::ChunkArgs ca = proto;
     ca.ws_streamed = streamed ? 1 : 0;
+    ca.ws_qk = ws_qk;
     const size_t n = std::min<size_t>(kRowsPerLaunch, rows.size() - base);
     ca.n_rows = int32_t(n);
     int32_t local = 0;
@@ -181,8 +184,8 @@ bool chunk_units_fit(const gdn_dims *d, const std::vector<int32_t> &rows, const 
 size_t chunked_ws_bytes(const gdn_dims *d, const std::vector<int32_t> &rows, const int32_t *len) {
   int64_t chunks = 0;
   for (int32_t r : rows) chunks += chunks_of(len[r]);
-  const bool streamed = gdn::chunk_ws_streamed(chunks, d->n_v_heads, d->d_k);
-  return size_t(chunks) * size_t(d->n_v_heads) * size_t(gdn::chunk_ws_unit_floats(d->d_k, streamed)) * 4;
+  const bool streamed = gdn::chunk_ws_streamed(chunks, d->n_v_heads, d->n_qk_heads, d->d_k);
+  return size_t(gdn::chunk_ws_floats(chunks, d->n_v_heads, d->n_qk_heads, d->d_k, streamed)) * 4;
 }
 
 void fill_chunk_common(gdn::ChunkArgs &ca, const gdn_dims *d, const uint16_t *q, const uint16_t *k,

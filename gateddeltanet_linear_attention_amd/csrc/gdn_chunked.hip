@@ -222,23 +222,28 @@ template <int D, bool W32>
 struct Ws {
   static constexpr int NK = D >= 32 ? D / 32 : 1;  // 32-wide blocks over d
   static constexpr int NT = D / 16;                // 16-wide state column tiles
-  static constexpr int64_t UNIT = chunk_ws_unit_floats(D, W32);  // floats per (chunk, head)
+  static constexpr int64_t UNIT = chunk_ws_unit_floats(D, W32);  // floats per (chunk, value head)
+  static constexpr int64_t QK = chunk_ws_qk_floats(D);           // floats per (chunk, qk-head)
   uint16_t *WF, *QF, *KF, *PF;
   float *WF32, *UF, *eG, *eL, *rk, *eGq;
   double *G;
-  __device__ Ws(float *base) {
+  // the value-head unit at `base`, its qk-head's Q and K^T at `qk`
+  __device__ Ws(float *base, float *qk) {
     WF = reinterpret_cast<uint16_t *>(base);
     WF32 = base;
-    QF = W32 ? reinterpret_cast<uint16_t *>(base + 4 * NK * 512) : WF + 4 * NK * 3 * 512;
-    KF = QF + 4 * NK * 512;
-    PF = KF + NT * 2 * 512;
+    PF = W32 ? reinterpret_cast<uint16_t *>(base + 4 * NK * 512) : WF + 4 * NK * 3 * 512;
     UF = reinterpret_cast<float *>(PF + 6 * 3 * 512);
     G = reinterpret_cast<double *>(UF + NT * 4 * 256);
     eG = reinterpret_cast<float *>(G + C);
     eL = eG + C;
     rk = eL + C;
     eGq = rk + C;
+    QF = reinterpret_cast<uint16_t *>(qk);
+    KF = QF + 4 * NK * 512;
   }
+  // the units of workspace chunk `chunk`, value head h of qk-head hq
+  __device__ Ws(const ChunkArgs &a, int64_t chunk, int h, int hq)
+      : Ws(a.ws + (chunk * a.n_v + h) * UNIT, a.ws_qk + (chunk * a.n_qk + hq) * QK) {}
   // element offset of lane l's 16-byte piece in 1-KiB fragment block `blk` of a bf16 array
   static __device__ __forceinline__ int piece(int blk, int l) { return (blk * 64 + l) * 8; }
   // P block of token tile tt and 32-wide key block kb (kb = 1 only for tt >= 2)
@@ -298,7 +303,9 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
   const uint16_t *Kc = args.k + tok_base * ldqk + int64_t(hq) * D;
   const uint16_t *Qc = args.q + tok_base * ldqk + int64_t(hq) * D;
   const uint16_t *Vc = args.v + tok_base * ldv + int64_t(h) * D;
-  Ws<D, NT> ws(args.ws + (int64_t(args.chunk0[row] + cin) * n_v + h) * Ws<D, NT>::UNIT);
+  Ws<D, NT> ws(args, args.chunk0[row] + cin, h, hq);
+  // Q and K^T depend on the qk-head only: the first of its value heads stores them
+  const bool qk_owner = h == hq * args.group;
 
   auto frag32 = [&](const uint16_t *base, int64_t ld, int t, int kb) {
     return frag32_row<D>(base, ld, t, kb, n, g4);
@@ -372,7 +379,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
   }
   // K^T in fragment order for the chain kernel's carry: piece (nt, kb, l = r + 16 g) is
   // K^T[16 nt + r][32 kb + 8 g .. +7], a column of sK
-  for (int idx = tid; idx < (D / 16) * 2 * 64; idx += 256) {
+  for (int idx = tid; qk_owner && idx < (D / 16) * 2 * 64; idx += 256) {
     const int nt = idx >> 7, kb = (idx >> 6) & 1, l = idx & 63;
     const uint16_t *src = sK + (32 * kb + 8 * (l >> 4)) * LDK + 16 * nt + (l & 15);
     uint32_t wv[4];
@@ -403,7 +410,8 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
       for (int tj = 0; tj < 4; ++tj)
         fk[tj][kb] = col < D ? *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + r16) * LDK + col) : z8;
       fa[kb] = col < D ? *reinterpret_cast<const bf16x8 *>(sK + (16 * w + r16) * LDK + col) : z8;
-      ws_st<NT>(reinterpret_cast<uint4 *>(ws.QF + Ws<D, NT>::piece(w * NK32 + kb, lane)), __builtin_bit_cast(uint4, fq[kb]));
+      if (qk_owner)
+        ws_st<NT>(reinterpret_cast<uint4 *>(ws.QF + Ws<D, NT>::piece(w * NK32 + kb, lane)), __builtin_bit_cast(uint4, fq[kb]));
 #pragma unroll
       for (int e = 0; e < 8; ++e) ssq = fmaf(float(fq[kb][e]), float(fq[kb][e]), ssq);
     }
@@ -779,17 +787,27 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
   const int tile = k8 % TILES;
   const int unit = (k8 / TILES) * 8 + (b & 7);
   if (unit >= n_units) return;  // the whole block
-  const int h = unit % args.n_v;
-  const int row = unit / args.n_v;
+  // unit -> (row, value head): with qk-heads in multiples of 8, the value heads of one
+  // qk-head go to one chiplet (unit % 8), as in the prep kernel, and share its L2 copy
+  // of their Q and K^T
+  int h, row;
+  if (args.n_qk % 8 == 0) {
+    const int x = unit % 8, j = unit / 8, per = args.n_v / 8;
+    row = j / per;
+    const int l = j % per;
+    h = (x + 8 * (l / args.group)) * args.group + l % args.group;
+  } else {
+    h = unit % args.n_v;
+    row = unit / args.n_v;
+  }
   const int i0 = tile * VT;
   const int L = args.len[row];
   const int nch = (L + C - 1) / C;
   const int n_v = args.n_v;
   const int src = args.src[row], dst = args.dst[row];
   const int tail0 = L - args.n_tail[row];  // first position with a checkpoint
-  auto ws_of = [&](int c) {
-    return Ws<D, W32>(args.ws + (int64_t(args.chunk0[row] + c) * n_v + h) * Ws<D, W32>::UNIT);
-  };
+  const int hq = h / args.group;
+  auto ws_of = [&](int c) { return Ws<D, W32>(args, args.chunk0[row] + c, h, hq); };
   // parts of S_c for 32-wide d block kb (lane (r16, g4): S_c[i0 + r16][32 kb + 8 g4 + e])
   auto s_parts = [&](const uint16_t *buf, int kb) {
     const int col = 32 * kb + 8 * g4;

@@ -130,22 +130,31 @@ constexpr int kChunk = 64;
 
 // Workspace floats per (chunk, value head), the chain kernel's operands in 1-KiB
 // fragment blocks: W in three bf16 parts [4][d/32][3] blocks (w32: fp32 [4][d/32] blocks
-// of 2 KiB), Q [4][d/32], K^T [d/16][2], the six nonzero blocks of P in three bf16 parts
-// [6][3], U' [d/16][4] blocks of 256 fp32 each, then the 64 fp64 prefix sums of the
-// log-decay and four 64-float factor vectors.
+// of 2 KiB), the six nonzero blocks of P in three bf16 parts [6][3], U' [d/16][4] blocks
+// of 256 fp32 each, then the 64 fp64 prefix sums of the log-decay and four 64-float
+// factor vectors.
 constexpr int64_t chunk_ws_unit_floats(int d, bool w32) {
   const int64_t nk = d >= 32 ? d / 32 : 1, nt = d / 16;
-  return (w32 ? 2048 : 3072) * nk + 1024 * nk + 512 * nt + 4608 + 1024 * nt + 2 * kChunk + 4 * kChunk;
+  return (w32 ? 2048 : 3072) * nk + 4608 + 1024 * nt + 2 * kChunk + 4 * kChunk;
+}
+// Workspace floats per (chunk, qk-head), after all the value-head units: Q [4][d/32] and
+// K^T [d/16][2] fragment blocks, which the value heads sharing the qk-head read alike.
+constexpr int64_t chunk_ws_qk_floats(int d) {
+  const int64_t nk = d >= 32 ? d / 32 : 1, nt = d / 16;
+  return 1024 * nk + 512 * nt;
+}
+constexpr int64_t chunk_ws_floats(int64_t chunks, int n_v, int n_qk, int d, bool w32) {
+  return chunks * (n_v * chunk_ws_unit_floats(d, w32) + n_qk * chunk_ws_qk_floats(d));
 }
 
 // A call's workspace is streamed: written past the caches, with W in fp32 (the chain
 // kernel forms its parts), when with W in parts it would exceed 160 MiB.  Such a call is
-// bound by the workspace traffic, which fp32 W cuts by an eighth; a smaller one is read
-// back from the last-level cache, and there the parts, formed once by the prep kernel,
-// keep that work off the chain's serial path.
+// bound by the workspace traffic, which fp32 W cuts by 14 % (d = 128, two value heads
+// per qk-head); a smaller one is read back from the last-level cache, and there the
+// parts, formed once by the prep kernel, keep that work off the chain's serial path.
 constexpr int64_t kStreamedWsBytes = int64_t(160) << 20;
-constexpr bool chunk_ws_streamed(int64_t chunks, int n_v, int d) {
-  return chunks * n_v * chunk_ws_unit_floats(d, false) * 4 > kStreamedWsBytes;
+constexpr bool chunk_ws_streamed(int64_t chunks, int n_v, int n_qk, int d) {
+  return chunk_ws_floats(chunks, n_v, n_qk, d, false) * 4 > kStreamedWsBytes;
 }
 
 struct ChunkArgs {
@@ -155,7 +164,8 @@ struct ChunkArgs {
   float *state_out;
   float *ckpt;
   uint16_t *o;
-  float *ws;
+  float *ws;                        // the (chunk, value head) units
+  float *ws_qk;                     // the (chunk, qk-head) units, after all the others
   int32_t n_qk, n_v, group;
   int32_t ck_slots;
   int32_t n_rows;

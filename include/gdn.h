@@ -56,7 +56,8 @@
  *    per-row count: they were fixed when the window was launched, so only the accepted
  *    counts need to stay on the device.
  *  - gdn_chunked_workspace_bytes takes the per-row token counts, not a token total: the
- *    workspace holds one unit per (chunk, value head), and chunks never span rows.
+ *    workspace holds one unit per (chunk, value head) and a smaller one per (chunk,
+ *    qk-head), and chunks never span rows.
  *  - gdn_plan_transaction returns one route per row: the plan depends on row lengths
  *    only (every row gets its checkpoints on either route), so no checkpoint counts and
  *    no plan structure are needed.

@@ -399,16 +399,19 @@ def test_chunked_and_transaction_validation_codes():
     b = Bufs()
     d = _dims()
     need = gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100, 64, 1])
-    # per (chunk, value head): W parts 48 KiB, Q 16, K^T 16, the six nonzero P blocks in
-    # parts 18, U' 32 KiB, 1.5 KiB of factors
-    assert need == (2 + 1 + 1) * 32 * ((48 + 16 + 16 + 18 + 32) * 1024 + 1536)
+    # per (chunk, value head): W parts 48 KiB, the six nonzero P blocks in parts 18, U' 32
+    # KiB, 1.5 KiB of factors; per (chunk, qk-head): Q 16 KiB, K^T 16
+    def ws(chunks, w_kib):
+        return chunks * (32 * ((w_kib + 18 + 32) * 1024 + 1536) + 16 * (16 + 16) * 1024)
+    assert need == ws(2 + 1 + 1, 48)
     # past 160 MiB with W in parts the workspace is streamed and holds W in fp32 (32 KiB)
-    big = [64 * 40] * 1                                    # 40 chunks x 32 heads: 168 MB with W in parts
-    assert 40 * 32 * ((48 + 16 + 16 + 18 + 32) * 1024 + 1536) > (160 << 20)
-    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), big) == \
-        40 * 32 * ((32 + 16 + 16 + 18 + 32) * 1024 + 1536)
-    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [64 * 38]) == \
-        38 * 32 * ((48 + 16 + 16 + 18 + 32) * 1024 + 1536)  # 159 MB: W in parts
+    assert ws(44, 48) <= (160 << 20) < ws(45, 48)
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [64 * 45]) == ws(45, 32)
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [64 * 44]) == ws(44, 48)  # W in parts
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [64 * 44 + 1]) == ws(45, 32)
+    # one qk-head for all value heads: one Q/K^T unit per chunk
+    assert gb.gdn_chunked_workspace_bytes(gb.Dims(1, 32, 128, 128, 3), [64]) == \
+        32 * ((48 + 18 + 32) * 1024 + 1536) + 32 * 1024
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [100], chunk=32) == 0
     assert gb.gdn_chunked_workspace_bytes(gb.Dims(16, 32, 128, 128, 3), [0]) == 0
 

@@ -136,15 +136,21 @@ def test_slow_decay_long_memory():
 
 def test_streamed_workspace_with_fp32_w_at_the_tiny_head_width():
     """A call whose workspace with W in parts would pass 160 MiB streams it, with W in fp32
-    (its parts formed in the chain kernel): 64 value heads of width 16 over 62 chunks.  The
+    (its parts formed in the chain kernel): 64 value heads of width 16 over 68 chunks.  The
     transaction tests cover that form at d = 128."""
     shape = synth.HeadShape(32, 64, 16)
-    lens, chunks = [1984, 1984], 62
-    parts_unit = 3072 + 1024 + 512 + 4608 + 1024 + 6 * 64   # floats per (chunk, head), W in parts
-    assert chunks * 64 * parts_unit * 4 > (160 << 20)
-    fp32_unit = parts_unit - 1024                            # W in fp32: 2048 floats instead of 3072
-    assert gb.gdn_chunked_workspace_bytes(dims_of(shape), lens) == chunks * 64 * fp32_unit * 4
+    lens, chunks = [2176, 2150], 68
+    assert ws_bytes_d16(chunks, fp32_w=False) > (160 << 20)
+    assert gb.gdn_chunked_workspace_bytes(dims_of(shape), lens) == ws_bytes_d16(chunks, fp32_w=True)
     run_chunked_case(shape, lens, [4, 3], "mixed", 69, what="streamed d16")
+
+
+def ws_bytes_d16(chunks, fp32_w):
+    """Workspace bytes at d = 16 with 64 value heads over 32 qk-heads: per (chunk, value
+    head) W (3072 floats in parts, 2048 in fp32), P 4608, U' 1024 and 6 * 64 factor floats;
+    per (chunk, qk-head) Q 1024 and K^T 512 floats."""
+    unit = (2048 if fp32_w else 3072) + 4608 + 1024 + 6 * 64
+    return chunks * (64 * unit + 32 * (1024 + 512)) * 4
 
 
 @pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
@@ -157,7 +163,7 @@ def test_streamed_and_cached_workspaces_agree_bit_for_bit(raw_qk):
     shape = synth.HeadShape(32, 64, 16)
     dims = dims_of(shape, raw_qk=raw_qk)
     Hv, d = shape.n_v_heads, shape.d
-    lens, n_tail = np.array([1984, 1984], np.int32), np.array([4, 3], np.int32)
+    lens, n_tail = np.array([2176, 2176], np.int32), np.array([4, 3], np.int32)
     g = synth.streams(71, 3)
     A_log, dt_bias = synth.head_params(g[0], shape)
     tok = synth.tokens(g[1], shape, int(lens.sum()), raw_qk=raw_qk)
@@ -177,9 +183,8 @@ def test_streamed_and_cached_workspaces_agree_bit_for_bit(raw_qk):
                                                 workspace=_ws(dims, lens[list(rows)]))
         return o, pool[B:], ckpt
 
-    parts_unit = 3072 + 1024 + 512 + 4608 + 1024 + 6 * 64   # floats per (chunk, head) at d = 16, W in parts
-    assert gb.gdn_chunked_workspace_bytes(dims, lens) == 62 * 64 * (parts_unit - 1024) * 4   # streamed: fp32 W
-    assert gb.gdn_chunked_workspace_bytes(dims, lens[:1]) == 31 * 64 * parts_unit * 4        # cached: parts
+    assert gb.gdn_chunked_workspace_bytes(dims, lens) == ws_bytes_d16(68, fp32_w=True)     # streamed: fp32 W
+    assert gb.gdn_chunked_workspace_bytes(dims, lens[:1]) == ws_bytes_d16(34, fp32_w=False)  # cached: parts
     o2, s2, c2 = run([0, 1])
     for r in range(2):
         o1, s1, c1 = run([r])
