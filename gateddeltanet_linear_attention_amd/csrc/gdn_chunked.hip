@@ -640,7 +640,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(ChunkArgs args) {
 
 // One chunk's operands of a chain wave (w < 4, lane = r16 + 16 g4), fetched a chunk
 // ahead; every load reads one 1-KiB fragment block of the workspace (2 KiB for fp32 W).
-template <int D, bool W32>
+template <int D, bool W32, int TPB>
 struct CarryOps {
   static constexpr int NK = Ws<D, W32>::NK;
   static constexpr int NT = (D / 16 + 3) / 4;  // 16-wide state column tiles per wave
@@ -649,7 +649,7 @@ struct CarryOps {
   Parts8 w[W32 ? 1 : NK];
   float4 wf[W32 ? NK : 1][2];
   bf16x8 kt[NT][2];   // K^T[16 nt + r16][32 kb + 8 g4 + 0..7], nt = w + 4 q
-  float4 up;          // U'[16 w + 4 g4 + v][i0 + r16], v = 0..3
+  float4 up[TPB];     // U'[16 w + 4 g4 + v][i0_j + r16], v = 0..3, for each of the block's tiles j
   float4 el;          // eL[16 w + 4 g4 + v]
   float e_last;       // e^{G_{n-1}}
   // Two groups, each loaded where the chunk before has matrix work to hide it behind:
@@ -692,7 +692,8 @@ struct CarryOps {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) kt[qt][kb] = frag(ws.KF, nt * 2 + kb, lane);
     }
-    up = *reinterpret_cast<const float4 *>(ws.UF + ((tile * 4 + wv) * 64 + lane) * 4);
+#pragma unroll
+    for (int j = 0; j < TPB; ++j) up[j] = *reinterpret_cast<const float4 *>(ws.UF + (((tile * TPB + j) * 4 + wv) * 64 + lane) * 4);
     el = *reinterpret_cast<const float4 *>(ws.eL + 16 * wv + 4 * g4);
     e_last = ws.eG[n - 1];
   }
@@ -714,15 +715,15 @@ struct OutOps {
   Parts8 p[2];        // P[16 t + r16][32 kb + 8 g4 + 0..7] in parts (kb = 1: t >= 2 only)
   float egq;          // eGq[16 t + r16]
   __device__ void load_q(const Ws<D, W32> &ws, int kb, int t, int lane) {
-    q[kb] = CarryOps<D, W32>::frag(ws.QF, t * NK + kb, lane);
+    q[kb] = CarryOps<D, W32, 1>::frag(ws.QF, t * NK + kb, lane);
   }
   __device__ void load_p(const Ws<D, W32> &ws, int t, int lane) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (kb == 1 && t < 2) break;  // that block of P is zero (wave-uniform)
       const int b3 = Ws<D, false>::pblk(t, kb) * 3;
-      p[kb] = Parts8{CarryOps<D, W32>::frag(ws.PF, b3, lane), CarryOps<D, W32>::frag(ws.PF, b3 + 1, lane),
-                     CarryOps<D, W32>::frag(ws.PF, b3 + 2, lane)};
+      p[kb] = Parts8{CarryOps<D, W32, 1>::frag(ws.PF, b3, lane), CarryOps<D, W32, 1>::frag(ws.PF, b3 + 1, lane),
+                     CarryOps<D, W32, 1>::frag(ws.PF, b3 + 2, lane)};
     }
     egq = ws.eGq[16 * t + (lane & 15)];
   }
@@ -742,9 +743,10 @@ __device__ __forceinline__ void store_nt(float *dst, floatx4 x) {
   __builtin_nontemporal_store(x, reinterpret_cast<floatx4 *>(dst));
 }
 
-// The chain of one (row, value head, 16 value channels i0..i0+15): chunks in order, in
-// blocks of 8 waves, two per SIMD.  Waves 0..3 carry the state: wave w owns tokens
-// 16w..16w+15 of each chunk for U and state column tiles w and w + 4 for the carry.
+// The chains of one (row, value head) and TPB tiles of 16 value channels (tile j:
+// i0 + 16 j .. i0 + 16 j + 15): chunks in order, in blocks of 8 waves, two per SIMD.
+// Waves 0..3 carry the state: wave w owns tokens 16w..16w+15 of each chunk for U and
+// state column tiles w and w + 4 for the carry.
 // Waves 4..7 compute the outputs: wave 4 + t those of tokens 16t..16t+15.  Per chunk:
 //   A  chain waves: U = U' - W S_c^T for their tokens (S_c's parts from LDS, W split in
 //      registers); U^T diag(e^{G_n - G}) and U^T in parts -> LDS.
@@ -765,19 +767,25 @@ __device__ __forceinline__ void store_nt(float *dst, floatx4 x) {
 // written to the other).  Blocks of one (row, head) unit are spaced 8 apart in launch
 // order, which places all its tiles on one of the 8 chiplets and lets them share that
 // L2's copy of the chunk operands (W, K^T, P).
-template <int D, bool W32>
+// Two tiles per block (TPB = 2) share each wave's W, K^T, Q and P registers and their
+// splitting, and run their products interleaved; a block step takes about 1.8 times as
+// long as with one tile, so the form pays where chains outnumber the CUs twice over
+// (4-prefill transaction 572 -> 527 us), and a single 2048-token row keeps one tile per
+// block on every CU.
+template <int D, bool W32, int TPB>
 __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_units) {
-  constexpr int TILES = D / VT;
-  constexpr int NK = CarryOps<D, W32>::NK;
-  constexpr int NT = CarryOps<D, W32>::NT;
+  constexpr int TILES = D / VT / TPB;  // blocks per unit; each holds TPB 16-channel tiles
+  static_assert(TILES >= 1, "tiles per block");
+  constexpr int NK = CarryOps<D, W32, TPB>::NK;
+  constexpr int NT = CarryOps<D, W32, TPB>::NT;
   constexpr int LDS_ = D + 8;     // S part row (bf16): 16-B aligned rows
   constexpr int SPL = VT * LDS_;  // elements per plane of S parts
   constexpr int UPL = VT * LDP;   // elements per plane of U parts
   constexpr size_t UNIT = size_t(D) * D;
-  __shared__ __attribute__((aligned(16))) uint16_t sS[2][3 * SPL];  // S_c in parts: row i, column d
-  __shared__ __attribute__((aligned(16))) uint16_t sUc[3 * UPL];    // (U^T diag(e^{G_n - G})): row i, token s
-  __shared__ __attribute__((aligned(16))) uint16_t sUr[3 * UPL];    // U^T
-  __shared__ __attribute__((aligned(16))) uint16_t sUt[3 * UPL];    // U^T diag(e^{G_j - G}) of a checkpoint
+  __shared__ __attribute__((aligned(16))) uint16_t sS[2][TPB][3 * SPL];  // S_c in parts: row i, column d
+  __shared__ __attribute__((aligned(16))) uint16_t sUc[TPB][3 * UPL];    // (U^T diag(e^{G_n - G})): row i, token s
+  __shared__ __attribute__((aligned(16))) uint16_t sUr[TPB][3 * UPL];    // U^T
+  __shared__ __attribute__((aligned(16))) uint16_t sUt[TPB][3 * UPL];    // U^T diag(e^{G_j - G}) of a checkpoint
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
@@ -800,7 +808,7 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
     h = unit % args.n_v;
     row = unit / args.n_v;
   }
-  const int i0 = tile * VT;
+  const int i0 = tile * TPB * VT;  // tile j of the block: channels i0 + 16 j .. + 15
   const int L = args.len[row];
   const int nch = (L + C - 1) / C;
   const int n_v = args.n_v;
@@ -808,7 +816,8 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
   const int tail0 = L - args.n_tail[row];  // first position with a checkpoint
   const int hq = h / args.group;
   auto ws_of = [&](int c) { return Ws<D, W32>(args, args.chunk0[row] + c, h, hq); };
-  // parts of S_c for 32-wide d block kb (lane (r16, g4): S_c[i0 + r16][32 kb + 8 g4 + e])
+  // parts of S_c for 32-wide d block kb (lane (r16, g4): S_c[i0 + 16 j + r16][32 kb + 8 g4 + e]
+  // from tile j's buffer)
   auto s_parts = [&](const uint16_t *buf, int kb) {
     const int col = 32 * kb + 8 * g4;
     if (col < D) return lds_get8<LDS_>(buf, SPL, r16, col);
@@ -834,29 +843,40 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
       const int c0 = c * C;
       const int n = min(C, L - c0);
       const int64_t tok_base = int64_t(args.tok0[row]) + c0;
-      const uint16_t *sSc = sS[c & 1];
-      floatx4 oq = zero4();
+      floatx4 oq[TPB];
+#pragma unroll
+      for (int j = 0; j < TPB; ++j) oq[j] = zero4();
 #pragma unroll
       for (int kb = 0; kb < NK; ++kb) {
-        const Parts8 sp = s_parts(sSc, kb);
+        Parts8 sp[TPB];
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) sp[j] = s_parts(sS[c & 1][j], kb);
         nx.load_q(wsn, kb, t, lane);
         __builtin_amdgcn_sched_barrier(0);  // the prefetch stays where it is issued
-        oq = mma3a(oq, sp, f.q[kb]);  // O^T: rows are channels, columns tokens
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) oq[j] = mma3a(oq[j], sp[j], f.q[kb]);  // O^T: rows are channels, columns tokens
       }
       lds_barrier();  // U of all 64 tokens in LDS
       // O^T = S_c Q^T diag(e^G rq) + U^T P^T, lane (r16, g4) holding
-      // O[16 t + r16][i0 + 4 g4 + 0..3] (one 8-byte store)
-      floatx4 op = zero4();
+      // O[16 t + r16][i0 + 16 j + 4 g4 + 0..3] (one 8-byte store per tile)
+      floatx4 op[TPB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)  // P is zero right of the diagonal: tokens >= 32 only for t >= 2
-        if (kb == 0 || t >= 2) op = mma6(op, lds_get8<LDP>(sUr, UPL, r16, 32 * kb + 8 * g4), f.p[kb]);
+      for (int j = 0; j < TPB; ++j) {
+        op[j] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)  // P is zero right of the diagonal: tokens >= 32 only for t >= 2
+          if (kb == 0 || t >= 2) op[j] = mma6(op[j], lds_get8<LDP>(sUr[j], UPL, r16, 32 * kb + 8 * g4), f.p[kb]);
+      }
       const float egq = f.egq;
       nx.load_p(wsn, t, lane);
       __builtin_amdgcn_sched_barrier(0);
       if (16 * t + r16 < n) {
-        const uint2 ob = make_uint2(bf16x2_rn(egq * oq[0] + op[0], egq * oq[1] + op[1]),
-                                    bf16x2_rn(egq * oq[2] + op[2], egq * oq[3] + op[3]));
-        *reinterpret_cast<uint2 *>(args.o + ((tok_base + 16 * t + r16) * n_v + h) * D + i0 + 4 * g4) = ob;
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) {
+          const uint2 ob = make_uint2(bf16x2_rn(egq * oq[j][0] + op[j][0], egq * oq[j][1] + op[j][1]),
+                                      bf16x2_rn(egq * oq[j][2] + op[j][2], egq * oq[j][3] + op[j][3]));
+          *reinterpret_cast<uint2 *>(args.o + ((tok_base + 16 * t + r16) * n_v + h) * D + i0 + 16 * j + 4 * g4) = ob;
+        }
       }
       tail_barriers(c0, n);
       lds_barrier();  // S_{c+1}'s parts complete; every read of this chunk's U parts done
@@ -875,23 +895,27 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
   // every wave has all NT column tiles when D / 16 is a multiple of 4 (d = 128)
   auto has_tile = [&](int q) { return (D / 16) % 4 == 0 || w + 4 * q < D / 16; };
   // the start state: registers, and its parts in LDS
-  float4 S[NT];
+  float4 S[TPB][NT];
 #pragma unroll
-  for (int q = 0; q < NT; ++q) {
-    S[q] = zf4();
-    if (src >= 0 && has_tile(q))
-      S[q] = *reinterpret_cast<const float4 *>(args.state_in + (int64_t(src) * n_v + h) * UNIT +
-                                               int64_t(i0 + r16) * D + 16 * (w + 4 * q) + 4 * g4);
-  }
-  auto put_state = [&](uint16_t *buf) {
+  for (int j = 0; j < TPB; ++j)
 #pragma unroll
-    for (int q = 0; q < NT; ++q)
-      if (has_tile(q)) lds_put4<LDS_>(buf, SPL, r16, 16 * (w + 4 * q) + 4 * g4, split4(S[q]));
+    for (int q = 0; q < NT; ++q) {
+      S[j][q] = zf4();
+      if (src >= 0 && has_tile(q))
+        S[j][q] = *reinterpret_cast<const float4 *>(args.state_in + (int64_t(src) * n_v + h) * UNIT +
+                                                    int64_t(i0 + 16 * j + r16) * D + 16 * (w + 4 * q) + 4 * g4);
+    }
+  auto put_state = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < TPB; ++j)
+#pragma unroll
+      for (int q = 0; q < NT; ++q)
+        if (has_tile(q)) lds_put4<LDS_>(sS[buf][j], SPL, r16, 16 * (w + 4 * q) + 4 * g4, split4(S[j][q]));
   };
-  put_state(sS[0]);
+  put_state(0);
   lds_barrier();
 
-  auto body = [&](int c, const CarryOps<D, W32> &f, CarryOps<D, W32> &nx) {
+  auto body = [&](int c, const CarryOps<D, W32, TPB> &f, CarryOps<D, W32, TPB> &nx) {
     const Ws<D, W32> ws = ws_of(c);
     // the next chunk's operands (past the end: the last chunk again, never read)
     const int cn = min(c + 1, nch - 1);
@@ -899,40 +923,54 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
     const int nn = min(C, L - cn * C);
     const int c0 = c * C;
     const int n = min(C, L - c0);
-    const uint16_t *sSc = sS[c & 1];
 
-    // A. U = U' - W S_c^T for tokens 16w..16w+15, channels i0..i0+15 (two accumulators
-    //    interleave the chains)
-    floatx4 ua = zero4(), ub = zero4();
+    // A. U = U' - W S_c^T for tokens 16w..16w+15, each tile's channels (two accumulators
+    //    interleave the chains; W is split once for all tiles)
+    floatx4 ua[TPB], ub[TPB];
+#pragma unroll
+    for (int j = 0; j < TPB; ++j) ua[j] = ub[j] = zero4();
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) {
-      const Parts8 sp = s_parts(sSc, kb);
+      Parts8 sp[TPB];
+#pragma unroll
+      for (int j = 0; j < TPB; ++j) sp[j] = s_parts(sS[c & 1][j], kb);
       nx.load_a(wsn, kb, w, lane);
       __builtin_amdgcn_sched_barrier(0);  // the prefetch stays where it is issued
-      if (kb & 1)
-        ub = mma6(ub, f.w_parts(kb), sp);
-      else
-        ua = mma6(ua, f.w_parts(kb), sp);
+      const Parts8 wp = f.w_parts(kb);
+#pragma unroll
+      for (int j = 0; j < TPB; ++j) {
+        if (kb & 1)
+          ub[j] = mma6(ub[j], wp, sp[j]);
+        else
+          ua[j] = mma6(ua[j], wp, sp[j]);
+      }
     }
-    ua += ub;
-    const float4 u = make_float4(f.up.x - ua[0], f.up.y - ua[1], f.up.z - ua[2], f.up.w - ua[3]);
-    lds_put4<LDP>(sUc, UPL, r16, 16 * w + 4 * g4, split4(mul4(u, f.el)));
-    lds_put4<LDP>(sUr, UPL, r16, 16 * w + 4 * g4, split4(u));
+    float4 u[TPB];
+#pragma unroll
+    for (int j = 0; j < TPB; ++j) {
+      ua[j] += ub[j];
+      u[j] = make_float4(f.up[j].x - ua[j][0], f.up[j].y - ua[j][1], f.up[j].z - ua[j][2], f.up[j].w - ua[j][3]);
+      lds_put4<LDP>(sUc[j], UPL, r16, 16 * w + 4 * g4, split4(mul4(u[j], f.el)));
+      lds_put4<LDP>(sUr[j], UPL, r16, 16 * w + 4 * g4, split4(u[j]));
+    }
     nx.load_b(wsn, nn, w, lane, tile);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // U of all 64 tokens in LDS
 
     // B. the carry on the wave's column tiles
-    float4 Sn[NT];
-    const Parts8 uc0 = lds_get8<LDP>(sUc, UPL, r16, 8 * g4), uc1 = lds_get8<LDP>(sUc, UPL, r16, 32 + 8 * g4);
+    float4 Sn[TPB][NT];
 #pragma unroll
-    for (int q = 0; q < NT; ++q) {
-      floatx4 a = {f.e_last * S[q].x, f.e_last * S[q].y, f.e_last * S[q].z, f.e_last * S[q].w};
-      if (has_tile(q)) {
-        a = mma3b(a, f.kt[q][0], uc0);
-        a = mma3b(a, f.kt[q][1], uc1);
+    for (int j = 0; j < TPB; ++j) {
+      const Parts8 uc0 = lds_get8<LDP>(sUc[j], UPL, r16, 8 * g4), uc1 = lds_get8<LDP>(sUc[j], UPL, r16, 32 + 8 * g4);
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+        floatx4 a = {f.e_last * S[j][q].x, f.e_last * S[j][q].y, f.e_last * S[j][q].z, f.e_last * S[j][q].w};
+        if (has_tile(q)) {
+          a = mma3b(a, f.kt[q][0], uc0);
+          a = mma3b(a, f.kt[q][1], uc1);
+        }
+        Sn[j][q] = make_float4(a[0], a[1], a[2], a[3]);
       }
-      Sn[q] = make_float4(a[0], a[1], a[2], a[3]);
     }
     // checkpoints at the positions p of this chunk with p >= tail0: slot p - tail0
     const int p_hi = c0 + n;
@@ -941,8 +979,10 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
                     int64_t(i0 + r16) * D + 4 * g4;
       if (p == L - 1) {  // the row's last state is the carry's result
 #pragma unroll
-        for (int q = 0; q < NT; ++q)
-          if (has_tile(q)) store_nt(cdst + 16 * (w + 4 * q), Sn[q]);
+        for (int j = 0; j < TPB; ++j)
+#pragma unroll
+          for (int q = 0; q < NT; ++q)
+            if (has_tile(q)) store_nt(cdst + 16 * j * D + 16 * (w + 4 * q), Sn[j][q]);
         continue;
       }
       const int jj = p - c0;
@@ -953,22 +993,28 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
         const int s = 16 * w + 4 * g4 + v;
         sc[v] = s <= jj ? float(exp(Gj - ws.G[s])) * ws.rk[s] : 0.0f;
       }
-      lds_put4<LDP>(sUt, UPL, r16, 16 * w + 4 * g4, split4(mul4(u, make_float4(sc[0], sc[1], sc[2], sc[3]))));
+#pragma unroll
+      for (int j = 0; j < TPB; ++j)
+        lds_put4<LDP>(sUt[j], UPL, r16, 16 * w + 4 * g4, split4(mul4(u[j], make_float4(sc[0], sc[1], sc[2], sc[3]))));
       lds_barrier();
       const float ej = ws.eG[jj];
 #pragma unroll
-      for (int q = 0; q < NT; ++q) {
-        if (!has_tile(q)) continue;
-        floatx4 a = {ej * S[q].x, ej * S[q].y, ej * S[q].z, ej * S[q].w};
+      for (int j = 0; j < TPB; ++j)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) a = mma3b(a, f.kt[q][kb], lds_get8<LDP>(sUt, UPL, r16, 32 * kb + 8 * g4));
-        store_nt(cdst + 16 * (w + 4 * q), a);
-      }
+        for (int q = 0; q < NT; ++q) {
+          if (!has_tile(q)) continue;
+          floatx4 a = {ej * S[j][q].x, ej * S[j][q].y, ej * S[j][q].z, ej * S[j][q].w};
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) a = mma3b(a, f.kt[q][kb], lds_get8<LDP>(sUt[j], UPL, r16, 32 * kb + 8 * g4));
+          store_nt(cdst + 16 * j * D + 16 * (w + 4 * q), a);
+        }
       lds_barrier();  // sUt is rewritten by the next position
     }
 #pragma unroll
-    for (int q = 0; q < NT; ++q) S[q] = Sn[q];
-    put_state(sS[(c + 1) & 1]);
+    for (int j = 0; j < TPB; ++j)
+#pragma unroll
+      for (int q = 0; q < NT; ++q) S[j][q] = Sn[j][q];
+    put_state((c + 1) & 1);
     lds_barrier();  // S_{c+1}'s parts complete; every read of this chunk's U parts done
   };
   // Chunks in pairs with two operand sets: while chunk c runs on one set, chunk c + 1's
@@ -978,7 +1024,7 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
   // scheduling barriers after each prefetch group keep the compiler from sinking those
   // loads toward their use a chunk later: a load issued last is one whose wait drains
   // every load before it.
-  CarryOps<D, W32> fa, fb;
+  CarryOps<D, W32, TPB> fa, fb;
   fa.load(ws_of(0), min(C, L), w, lane, tile);
   for (int c = 0; c < nch; c += 2) {
     body(c, fa, fb);
@@ -987,10 +1033,13 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_
   }
   if (dst >= 0) {
 #pragma unroll
-    for (int q = 0; q < NT; ++q)
-      if (has_tile(q))
-        store_nt(args.state_out + (int64_t(dst) * n_v + h) * UNIT + int64_t(i0 + r16) * D + 16 * (w + 4 * q) + 4 * g4,
-                 S[q]);
+    for (int j = 0; j < TPB; ++j)
+#pragma unroll
+      for (int q = 0; q < NT; ++q)
+        if (has_tile(q))
+          store_nt(args.state_out + (int64_t(dst) * n_v + h) * UNIT + int64_t(i0 + 16 * j + r16) * D + 16 * (w + 4 * q) +
+                       4 * g4,
+                   S[j][q]);
   }
 }
 
@@ -1000,8 +1049,15 @@ hipError_t launch_form(const ChunkArgs &args, int n_chunks, hipStream_t stream) 
                      args);
   const int n_units = args.n_rows * args.n_v;
   const int groups = (n_units + 7) / 8;  // units are dealt to the 8 chiplets in groups of 8
-  hipLaunchKernelGGL((chunk_chain_kernel<D, NT>), dim3(unsigned(groups * 8 * (D / VT))), dim3(512), 0, stream,
-                     args, n_units);
+  // two 16-channel tiles per block when there are chains enough to fill every CU twice
+  // (the chip's 256 CUs; one chain block per CU)
+  constexpr int TPB2 = D % (2 * VT) == 0 ? 2 : 1;
+  if (TPB2 == 2 && int64_t(n_units) * (D / VT) >= 2 * 256)
+    hipLaunchKernelGGL((chunk_chain_kernel<D, NT, TPB2>), dim3(unsigned(groups * 8 * (D / VT / TPB2))),
+                       dim3(512), 0, stream, args, n_units);
+  else
+    hipLaunchKernelGGL((chunk_chain_kernel<D, NT, 1>), dim3(unsigned(groups * 8 * (D / VT))), dim3(512), 0, stream,
+                       args, n_units);
   return hipGetLastError();
 }
 

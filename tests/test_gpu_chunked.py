@@ -153,23 +153,19 @@ def ws_bytes_d16(chunks, fp32_w):
     return chunks * (64 * unit + 32 * (1024 + 512)) * 4
 
 
-@pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
-def test_streamed_and_cached_workspaces_agree_bit_for_bit(raw_qk):
-    """Rows are independent, so the same row gives the same bits in any call.  Two rows
-    together pass 160 MiB of workspace (streamed: W in fp32, V staged in LDS by the prep
-    kernel); each alone stays under it (cached: W in bf16 parts, V columns from memory).
-    Outputs, final states and tail checkpoints must agree bit for bit."""
+def compare_rows_alone_and_together(shape, lens, n_tail, raw_qk, seed, what):
+    """Rows are independent, so the same row gives the same bits in any call: run the
+    rows together and each alone, from random start states, and compare every row's
+    outputs, final state and tail checkpoints bit for bit."""
     import torch
-    shape = synth.HeadShape(32, 64, 16)
     dims = dims_of(shape, raw_qk=raw_qk)
     Hv, d = shape.n_v_heads, shape.d
-    lens, n_tail = np.array([2176, 2176], np.int32), np.array([4, 3], np.int32)
-    g = synth.streams(71, 3)
+    g = synth.streams(seed, 3)
     A_log, dt_bias = synth.head_params(g[0], shape)
     tok = synth.tokens(g[1], shape, int(lens.sum()), raw_qk=raw_qk)
     t, p = dev_tokens(tok), dev_params(A_log, dt_bias)
-    gen = torch.Generator(device="cpu").manual_seed(71)
-    start = (0.3 * torch.randn(2, Hv, d, d, generator=gen)).cuda()
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    start = (0.3 * torch.randn(len(lens), Hv, d, d, generator=gen)).cuda()
 
     def run(rows):
         B = len(rows)
@@ -183,16 +179,39 @@ def test_streamed_and_cached_workspaces_agree_bit_for_bit(raw_qk):
                                                 workspace=_ws(dims, lens[list(rows)]))
         return o, pool[B:], ckpt
 
-    assert gb.gdn_chunked_workspace_bytes(dims, lens) == ws_bytes_d16(68, fp32_w=True)     # streamed: fp32 W
-    assert gb.gdn_chunked_workspace_bytes(dims, lens[:1]) == ws_bytes_d16(34, fp32_w=False)  # cached: parts
-    o2, s2, c2 = run([0, 1])
-    for r in range(2):
+    o2, s2, c2 = run(list(range(len(lens))))
+    for r in range(len(lens)):
         o1, s1, c1 = run([r])
         o_rows = o2[int(lens[:r].sum()):int(lens[:r + 1].sum())]
-        assert_same_bits(o_rows, o1, "row %d outputs, streamed vs cached workspace" % r)
-        assert_same_bits(s2[r:r + 1], s1, "row %d final state, streamed vs cached workspace" % r)
-        assert_same_bits(c2[r:r + 1, :n_tail[r]], c1[:, :n_tail[r]], "row %d checkpoints, streamed vs cached" % r)
-    say("streamed vs cached workspace (%s): bit-identical" % ("fused" if raw_qk else "given q/k"))
+        assert_same_bits(o_rows, o1, "row %d outputs, %s" % (r, what))
+        assert_same_bits(s2[r:r + 1], s1, "row %d final state, %s" % (r, what))
+        assert_same_bits(c2[r:r + 1, :n_tail[r]], c1[:, :n_tail[r]], "row %d checkpoints, %s" % (r, what))
+    say("%s (%s): bit-identical" % (what, "fused" if raw_qk else "given q/k"))
+
+
+@pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
+def test_streamed_and_cached_workspaces_agree_bit_for_bit(raw_qk):
+    """Two rows together pass 160 MiB of workspace (streamed: W in fp32); each alone stays
+    under it (cached: W in bf16 parts).  Outputs, final states and tail checkpoints must
+    agree bit for bit."""
+    shape = synth.HeadShape(32, 64, 16)
+    lens, n_tail = np.array([2176, 2176], np.int32), np.array([4, 3], np.int32)
+    dims = dims_of(shape, raw_qk=raw_qk)
+    assert gb.gdn_chunked_workspace_bytes(dims, lens) == ws_bytes_d16(68, fp32_w=True)     # streamed: fp32 W
+    assert gb.gdn_chunked_workspace_bytes(dims, lens[:1]) == ws_bytes_d16(34, fp32_w=False)  # cached: parts
+    compare_rows_alone_and_together(shape, lens, n_tail, raw_qk, 71, "streamed vs cached workspace")
+
+
+@pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
+def test_one_and_two_state_tiles_per_chain_block_agree_bit_for_bit(raw_qk):
+    """At d = 128 the chain kernel holds two 16-channel state tiles per block once a
+    launch has at least 512 (row, value head, tile) chains, one below that: one row of 32
+    value heads (256 chains) runs with one tile per block, two rows (512) with two.  Rows
+    are independent, so both forms must give the same bits."""
+    shape = synth.FULL
+    lens, n_tail = np.array([300, 191], np.int32), np.array([4, 3], np.int32)
+    assert len(lens) * shape.n_v_heads * (shape.d // 16) == 512
+    compare_rows_alone_and_together(shape, lens, n_tail, raw_qk, 73, "one vs two tiles per chain block")
 
 
 def test_more_than_64_chunked_rows_span_launches():
