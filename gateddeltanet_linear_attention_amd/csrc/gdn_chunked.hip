@@ -768,10 +768,11 @@ __device__ __forceinline__ void store_nt(float *dst, floatx4 x) {
 // order, which places all its tiles on one of the 8 chiplets and lets them share that
 // L2's copy of the chunk operands (W, K^T, P).
 // Two tiles per block (TPB = 2) share each wave's W, K^T, Q and P registers and their
-// splitting, and run their products interleaved; a block step takes about 1.8 times as
-// long as with one tile, so the form pays where chains outnumber the CUs twice over
-// (4-prefill transaction 572 -> 527 us), and a single 2048-token row keeps one tile per
-// block on every CU.
+// splitting, and run their products interleaved; a block step takes about 1.3 times as
+// long as with one tile, so the form pays where the chains outnumber the CUs (rows of
+// 2048 tokens, 32 value heads: two rows 206 -> 174 us, four 431 -> 366 us; the 4-prefill
+// transaction 572 -> 527 us), and a single such row (256 chains) keeps one tile per block
+// on every CU (96 against 113 us).
 template <int D, bool W32, int TPB>
 __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args, int n_units) {
   constexpr int TILES = D / VT / TPB;  // blocks per unit; each holds TPB 16-channel tiles
@@ -1049,10 +1050,10 @@ hipError_t launch_form(const ChunkArgs &args, int n_chunks, hipStream_t stream) 
                      args);
   const int n_units = args.n_rows * args.n_v;
   const int groups = (n_units + 7) / 8;  // units are dealt to the 8 chiplets in groups of 8
-  // two 16-channel tiles per block when there are chains enough to fill every CU twice
-  // (the chip's 256 CUs; one chain block per CU)
+  // two 16-channel tiles per block when the chains outnumber the chip's 256 CUs (one
+  // chain block per CU)
   constexpr int TPB2 = D % (2 * VT) == 0 ? 2 : 1;
-  if (TPB2 == 2 && int64_t(n_units) * (D / VT) >= 2 * 256)
+  if (TPB2 == 2 && int64_t(n_units) * (D / VT) > 256)
     hipLaunchKernelGGL((chunk_chain_kernel<D, NT, TPB2>), dim3(unsigned(groups * 8 * (D / VT / TPB2))),
                        dim3(512), 0, stream, args, n_units);
   else

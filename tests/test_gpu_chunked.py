@@ -204,10 +204,10 @@ def test_streamed_and_cached_workspaces_agree_bit_for_bit(raw_qk):
 
 @pytest.mark.parametrize("raw_qk", [False, True], ids=["given_qk", "fused_l2norm"])
 def test_one_and_two_state_tiles_per_chain_block_agree_bit_for_bit(raw_qk):
-    """At d = 128 the chain kernel holds two 16-channel state tiles per block once a
-    launch has at least 512 (row, value head, tile) chains, one below that: one row of 32
-    value heads (256 chains) runs with one tile per block, two rows (512) with two.  Rows
-    are independent, so both forms must give the same bits."""
+    """At d = 128 the chain kernel holds two 16-channel state tiles per block when a launch
+    has more (row, value head, tile) chains than the chip's 256 CUs, one otherwise: one row
+    of 32 value heads (256 chains) runs with one tile per block, two rows (512) with two.
+    Rows are independent, so both forms must give the same bits."""
     shape = synth.FULL
     lens, n_tail = np.array([300, 191], np.int32), np.array([4, 3], np.int32)
     assert len(lens) * shape.n_v_heads * (shape.d // 16) == 512
